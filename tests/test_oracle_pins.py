@@ -1,0 +1,346 @@
+"""Pins of the CPU oracle to facts fixed by the pages and by mathematics.
+
+Each test checks the oracle against something other than itself: a published generator,
+a library routine, a closed form, an invariant of the definitions, a statistical law that
+the method must satisfy, or brute force on tiny inputs.
+"""
+import itertools
+
+import numpy as np
+import pytest
+from scipy import special, stats
+
+from oracle import svref
+
+RNG = np.random.default_rng(12345)
+
+
+def _logits(shape, scale=2.0, rng=RNG):
+    return (scale * rng.standard_normal(shape)).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------------------
+# Philox4x64-10: known answers from numpy's independent implementation (numpy advances the
+# counter once before its first block) and the Random123 zero vector.
+# ---------------------------------------------------------------------------------------
+
+def test_philox_zero_vector():
+    out = svref.philox4x64_10([0, 0, 0, 0], [0, 0])
+    assert [int(x) for x in out] == [0x16554D9ECA36314C, 0xDB20FE9D672D0FDC,
+                                     0xD7E772CEE186176B, 0x7E68B68AEC7BA23B]
+
+
+@pytest.mark.parametrize("trial", range(8))
+def test_philox_matches_numpy(trial):
+    rng = np.random.default_rng(trial)
+    ctr = [int(x) for x in rng.integers(0, 2**63, size=4, dtype=np.int64)]
+    key = [int(x) for x in rng.integers(0, 2**63, size=2, dtype=np.int64)]
+    bg = np.random.Philox(counter=ctr, key=key)
+    want = bg.random_raw(8)
+    got0 = svref.philox4x64_10([ctr[0] + 1] + ctr[1:], key)
+    got1 = svref.philox4x64_10([ctr[0] + 2] + ctr[1:], key)
+    assert list(got0) == list(want[:4])
+    assert list(got1) == list(want[4:])
+
+
+def test_uniform_is_top_24_bits_of_word0():
+    for c in [(0, 0, 0, 0), (3, 7, 1, 11), (63, 15, 0, 2**40)]:
+        w0 = int(svref.philox4x64_10(list(c), [42, 0])[0])
+        u = svref.uniform(42, *c)
+        assert u == (w0 >> 40) / 2.0**24
+        assert 0.0 <= u < 1.0
+        assert np.float32(u) == u  # exactly representable in binary32
+
+
+# ---------------------------------------------------------------------------------------
+# Softmax, argmax, overlap (overlap equation: alpha = sum min(p, q) = 1 - TV)
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [0.5, 0.9, 1.0, 2.0])
+def test_lse_matches_scipy(T):
+    z = _logits(1000, 3.0)
+    assert svref.row_lse(z, "f32", T) == pytest.approx(special.logsumexp(z.astype(np.float64) / T), rel=1e-13)
+
+
+def test_lse_bf16_widening_is_exact():
+    z = _logits(4096, 3.0)
+    bits = (z.view(np.uint32) >> 16).astype(np.uint16)  # truncation gives valid bf16 values
+    widened = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert svref.row_lse(bits, "bf16", 0.9) == pytest.approx(special.logsumexp(widened / 0.9), rel=1e-13)
+
+
+def test_lse_with_minus_inf_entries():
+    z = _logits(64)
+    z[::3] = -np.inf
+    assert svref.row_lse(z, "f32", 1.0) == pytest.approx(special.logsumexp(z[np.isfinite(z)].astype(np.float64)), rel=1e-13)
+
+
+def test_argmax_lowest_index_on_ties():
+    rng = np.random.default_rng(7)
+    for _ in range(200):
+        z = rng.integers(-3, 4, size=50).astype(np.float32)  # many ties
+        assert svref.row_argmax(z, "f32") == int(np.argmax(z))  # numpy: first occurrence
+
+
+@pytest.mark.parametrize("T", [0.7, 1.0])
+def test_alpha_plus_tv_is_one(T):
+    for _ in range(20):
+        zt, zd = _logits(300), _logits(300)
+        p = special.softmax(zt.astype(np.float64) / T)
+        q = special.softmax(zd.astype(np.float64) / T)
+        tv = 0.5 * np.abs(p - q).sum()
+        assert svref.alpha(zt, zd, "f32", T) + tv == pytest.approx(1.0, abs=1e-12)
+
+
+def test_alpha_identity_symmetry_disjoint():
+    zt, zd = _logits(500), _logits(500)
+    assert svref.alpha(zt, zt, "f32", 0.9) == pytest.approx(1.0, abs=1e-12)
+    assert svref.alpha(zt, zd, "f32", 0.9) == pytest.approx(svref.alpha(zd, zt, "f32", 0.9), abs=1e-15)
+    a, b = zt.copy(), zd.copy()
+    a[:250] = -np.inf
+    b[250:] = -np.inf
+    assert svref.alpha(a, b, "f32", 1.0) == 0.0
+
+
+# ---------------------------------------------------------------------------------------
+# Verification statistics: serial acceptance gives E[tau] = sum_m prod_{k<=m} alpha_k, and
+# rejection sampling with the residual/bonus draw leaves the target distribution intact.
+# ---------------------------------------------------------------------------------------
+
+def _mc_batch(B, K, V, T, seed, scale_t=1.5, noise=1.0):
+    rng = np.random.default_rng(seed)
+    zt = _logits((K + 1, V), scale_t, rng)
+    zd = (zt[:K] + noise * rng.standard_normal((K, V))).astype(np.float32)
+    q = special.softmax(zd.astype(np.float64) / T, axis=-1)
+    # the drafter samples its own tokens: x_{r,k} ~ q_k, independently per request
+    toks = np.stack([rng.choice(V, size=B, p=q[k]) for k in range(K)], axis=1).astype(np.int32)
+    target = np.broadcast_to(zt, (B, K + 1, V)).copy()
+    draft = np.broadcast_to(zd, (B, K, V)).copy()
+    return zt, zd, target, draft, toks
+
+
+@pytest.mark.parametrize("T", [0.9, 1.3])
+def test_expected_accept_len_closed_form(T):
+    B, K, V = 100_000, 3, 12
+    zt, zd, target, draft, toks = _mc_batch(B, K, V, T, seed=11)
+    out = svref.verify_batch(target, draft, toks, T, "f32", seed=5, step=3)
+    a = np.array([svref.alpha(zt[k], zd[k], "f32", T) for k in range(K)])
+    closed = sum(np.prod(a[: m + 1]) for m in range(K))
+    tau = out["accept_len"].astype(np.float64)
+    se = tau.std() / np.sqrt(B)
+    assert abs(tau.mean() - closed) < 4 * se, (tau.mean(), closed, se)
+    # per-position acceptance: P(accept_k) = alpha_k, independent of the other positions
+    acc = out["accept"].astype(np.float64)
+    for k in range(K):
+        assert abs(acc[:, k].mean() - a[k]) < 4 * np.sqrt(a[k] * (1 - a[k]) / B)
+    # oracle alpha equals the standalone definition
+    np.testing.assert_allclose(out["alpha"][0], a, rtol=1e-14)
+    # 1 - L_e2e = E[tau] / D: ties the end-to-end objective to the serial acceptance law
+    loss, _ = svref.tv_e2e_loss(zt[None, :K].copy(), zd[None].copy(), T, "f32")
+    assert abs((1.0 - loss) - tau.mean() / K) < 4 * se / K
+
+
+def _chi2_ok(counts, probs, min_p=1e-3):
+    n = counts.sum()
+    exp = probs * n
+    keep = exp > 5
+    obs = np.append(counts[keep], counts[~keep].sum())
+    e = np.append(exp[keep], exp[~keep].sum())
+    if e[-1] == 0:
+        obs, e = obs[:-1], e[:-1]
+    stat, pval = stats.chisquare(obs, e * obs.sum() / e.sum())
+    return pval > min_p, pval
+
+
+@pytest.mark.parametrize("T", [0.9, 1.0])
+def test_emitted_tokens_follow_target(T):
+    """Token j of the output, given tau >= j, is distributed as p_j (rows 0..K)."""
+    B, K, V = 200_000, 2, 8
+    zt, zd, target, draft, toks = _mc_batch(B, K, V, T, seed=21)
+    out = svref.verify_batch(target, draft, toks, T, "f32", seed=9, step=1)
+    p = special.softmax(zt.astype(np.float64) / T, axis=-1)
+    tau, ot = out["accept_len"], out["out_tokens"]
+    for j in range(K + 1):
+        sel = tau >= j
+        counts = np.bincount(ot[sel, j], minlength=V).astype(np.float64)
+        ok, pval = _chi2_ok(counts, p[j])
+        assert ok, (j, pval)
+
+
+def test_correction_token_follows_residual():
+    """Given a rejection at position 0, the correction is norm(max(p0 - q0, 0))."""
+    B, K, V, T = 200_000, 1, 8, 1.0
+    zt, zd, target, draft, toks = _mc_batch(B, K, V, T, seed=31, noise=1.5)
+    out = svref.verify_batch(target, draft, toks, T, "f32", seed=2, step=0)
+    p = special.softmax(zt.astype(np.float64) / T, axis=-1)
+    q = special.softmax(zd.astype(np.float64) / T, axis=-1)
+    w = np.maximum(p[0] - q[0], 0.0)
+    sel = out["accept_len"] == 0
+    counts = np.bincount(out["out_tokens"][sel, 0], minlength=V).astype(np.float64)
+    assert counts[w == 0].sum() == 0
+    ok, pval = _chi2_ok(counts, w / w.sum())
+    assert ok, pval
+
+
+def test_inverse_cdf_is_searchsorted():
+    """The draw is the smallest v with sum_{j<=v} w_j > u R (numpy searchsorted, right)."""
+    B, K, V, T = 64, 1, 20, 1.0
+    zt, zd, target, draft, toks = _mc_batch(B, K, V, T, seed=41)
+    out = svref.verify_batch(target, draft, toks, T, "f32", seed=77, step=5, diagnostics=True)
+    p = special.softmax(zt.astype(np.float64) / T, axis=-1)
+    q = special.softmax(zd.astype(np.float64) / T, axis=-1)
+    for r in range(B):
+        tau = out["accept_len"][r]
+        w = np.maximum(p[0] - q[0], 0) if tau == 0 else p[1]
+        u = svref.uniform(77, r, tau, 1, 5)
+        assert out["u_corr"][r] == u
+        cw = np.cumsum(w)
+        assert out["out_tokens"][r, tau] == int(np.searchsorted(cw, u * cw[-1], side="right"))
+
+
+def test_greedy_accept_len_is_argmax_match_prefix():
+    rng = np.random.default_rng(5)
+    B, K, V = 300, 5, 40
+    target = rng.integers(-4, 5, size=(B, K + 1, V)).astype(np.float32)  # ties are frequent
+    draft = target[:, :K] + rng.integers(-1, 2, size=(B, K, V)).astype(np.float32)
+    toks = np.argmax(draft, axis=-1).astype(np.int32)
+    out = svref.verify_batch(target, draft, toks, 0.0, "f32")
+    amax_t = np.argmax(target, axis=-1)
+    for r in range(B):
+        match = toks[r] == amax_t[r, :K]
+        tau = K if match.all() else int(np.argmin(match))
+        assert out["accept_len"][r] == tau
+        assert out["n_out"][r] == tau + 1
+        assert list(out["out_tokens"][r, :tau]) == list(toks[r, :tau])
+        assert out["out_tokens"][r, tau] == amax_t[r, tau]
+        assert (out["out_tokens"][r, tau + 1:] == -1).all()
+        np.testing.assert_array_equal(out["alpha"][r], (amax_t[r, :K] == np.argmax(draft[r], -1)).astype(float))
+
+
+def test_draft_len_masks_positions():
+    B, K, V, T = 32, 4, 30, 0.9
+    rng = np.random.default_rng(3)
+    zt = _logits((B, K + 1, V), 2.0, rng)
+    zd = (zt[:, :K] + 0.3 * rng.standard_normal((B, K, V))).astype(np.float32)
+    toks = np.argmax(zd, -1).astype(np.int32)
+    dl = rng.integers(0, K + 1, size=B).astype(np.int32)
+    out = svref.verify_batch(zt, zd, toks, T, "f32", seed=1, draft_len=dl)
+    for r in range(B):
+        assert out["accept_len"][r] <= dl[r]
+        assert (out["alpha"][r, dl[r]:] == 0).all() and (out["accept"][r, dl[r]:] == 0).all()
+        assert (out["alpha"][r, :dl[r]] > 0).all()
+    # a request with L_r = 0 gets exactly its bonus token, drawn from p at row 0
+    assert (out["n_out"][dl == 0] == 1).all()
+
+
+def test_accept_len_and_residual_sample_agree_with_verify():
+    B, K, V, T = 40, 3, 50, 0.9
+    rng = np.random.default_rng(8)
+    zt = _logits((B, K + 1, V), 2.0, rng)
+    zd = (zt[:, :K] + rng.standard_normal((B, K, V))).astype(np.float32)
+    toks = np.argmax(zd, -1).astype(np.int32)
+    dl = rng.integers(0, K + 1, size=B).astype(np.int32)
+    out = svref.verify_batch(zt, zd, toks, T, "f32", seed=4, step=2, draft_len=dl)
+    assert (svref.accept_len(out["accept"], dl) == out["accept_len"]).all()
+    tok = svref.residual_sample(zt, zd, out["accept_len"], T, "f32", seed=4, step=2, draft_len=dl)
+    assert (tok == out["out_tokens"][np.arange(B), out["accept_len"]]).all()
+
+
+def test_accept_len_first_reject():
+    rng = np.random.default_rng(1)
+    acc = (rng.random((500, 7)) < 0.7).astype(np.uint8)
+    got = svref.accept_len(acc)
+    want = np.where(acc.all(1), 7, np.argmin(acc, axis=1))
+    np.testing.assert_array_equal(got, want)
+
+
+# ---------------------------------------------------------------------------------------
+# End-to-end TV objective: closed forms of the L_e2e equation
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("a,D", [(0.3, 3), (0.75, 5), (0.5, 1), (0.9, 16)])
+def test_e2e_constant_alpha(a, D):
+    alpha = np.full((17, D), a)
+    want = 1.0 - sum(a ** (m + 1) for m in range(D)) / D
+    assert svref.e2e_from_alpha(alpha) == pytest.approx(want, abs=1e-14)
+
+
+def test_e2e_special_cases():
+    rng = np.random.default_rng(2)
+    a = rng.random((100, 1))
+    assert svref.e2e_from_alpha(a) == pytest.approx(1.0 - a.mean(), abs=1e-14)
+    assert svref.e2e_from_alpha(np.ones((9, 4))) == 0.0
+    assert svref.e2e_from_alpha(np.zeros((9, 4))) == 1.0
+    # a rejection at depth 0 voids the rest: alpha_{i,0} = 0 makes row i contribute 0
+    b = rng.random((10, 3))
+    b[:, 0] = 0.0
+    assert svref.e2e_from_alpha(b) == 1.0
+
+
+# ---------------------------------------------------------------------------------------
+# Batch-level budget: the greedy selection is the best prefix allocation (brute force)
+# ---------------------------------------------------------------------------------------
+
+def _brute_best(C, N):
+    B, K = C.shape
+    total = min(N, B * K)
+    best = -1.0
+    for lens in itertools.product(range(K + 1), repeat=B):
+        if sum(lens) != total:
+            continue
+        s = sum(float(C[r, :lens[r]].astype(np.float64).sum()) for r in range(B))
+        best = max(best, s)
+    return best
+
+
+@pytest.mark.parametrize("trial", range(25))
+def test_budget_matches_brute_force(trial):
+    rng = np.random.default_rng(100 + trial)
+    B, K = int(rng.integers(1, 5)), int(rng.integers(1, 5))
+    conf = rng.beta(5, 2, size=(B, K)).astype(np.float32)
+    C = np.multiply.accumulate(conf, axis=1, dtype=np.float32)  # sequential binary32
+    for N in range(0, B * K + 2):
+        lens, off, rl = svref.alloc_verify_budget(conf, N)
+        assert lens.sum() == min(N, B * K)
+        assert (np.diff(off) == lens).all() and off[0] == 0
+        got = sum(float(C[r, :lens[r]].astype(np.float64).sum()) for r in range(B))
+        assert got == pytest.approx(_brute_best(C, N), abs=1e-6)
+        # prefix-closed: every selected (r,k) has all k' < k selected
+        want_rows = [r * K + k for r in range(B) for k in range(lens[r])]
+        assert list(rl) == want_rows
+
+
+def test_budget_edges_and_ties():
+    conf = np.array([[0.5, 1.0, 0.5], [0.5, 0.5, 1.0]], np.float32)
+    # C = [[.5,.5,.25],[.5,.25,.25]]; ties broken by request then position
+    lens, off, _ = svref.alloc_verify_budget(conf, 3)
+    assert list(lens) == [2, 1]
+    lens, off, _ = svref.alloc_verify_budget(conf, 4)
+    assert list(lens) == [3, 1]
+    lens, _, _ = svref.alloc_verify_budget(conf, 0)
+    assert list(lens) == [0, 0]
+    lens, _, rl = svref.alloc_verify_budget(conf, 100)
+    assert list(lens) == [3, 3] and len(rl) == 6
+    dl = np.array([1, 3], np.int32)
+    lens, _, _ = svref.alloc_verify_budget(conf, 100, draft_len=dl)
+    assert list(lens) == [1, 3]
+
+
+def test_budget_binary32_cumprod_is_sequential():
+    conf = np.array([[0.9999999, 0.3333333, 0.7777777, 0.1234567, 0.999]], np.float32)
+    C = np.float32(conf[0, 0])
+    seq = [C]
+    for c in conf[0, 1:]:
+        C = np.float32(C * c)
+        seq.append(C)
+    # with N = k+1 exactly the first k+1 are chosen; compare against a second request
+    # whose single confidence equals the k-th product bit for bit (tie -> lower r wins)
+    for k in range(5):
+        conf2 = np.zeros((2, 5), np.float32)
+        conf2[0] = conf[0]
+        conf2[1, 0] = seq[k]
+        dl = np.array([5, 1], np.int32)
+        lens, _, _ = svref.alloc_verify_budget(conf2, k + 1, draft_len=dl)
+        assert list(lens) == [k + 1, 0]
+        lens, _, _ = svref.alloc_verify_budget(conf2, k + 2, draft_len=dl)
+        assert list(lens) == [k + 1, 1] or k == 4
