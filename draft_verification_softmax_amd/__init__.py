@@ -1,0 +1,15 @@
+"""MI355X-native batched speculative-decoding draft verification.
+
+A thin binding over ``libspecverify.so`` (C ABI, ``include/specverify.h``).  Each
+``sv_*`` function marshals torch tensors to device pointers and the current HIP stream and
+calls the entry point of the same name; every step of the computation runs in the HIP
+kernels.  There is no CPU fallback: importing this package loads the library and raises
+ImportError when it has not been built.
+"""
+from .binding import (  # noqa: F401
+    LIB_PATH, SV_BF16, SV_F32, SVError, Workspace, lib, sv_accept_len, sv_alloc_verify_budget,
+    sv_device_error, sv_residual_sample, sv_status_string, sv_tv_e2e_loss, sv_uniforms,
+    sv_verify_batch, sv_workspace_bytes, sv_workspace_init,
+)
+
+lib()  # fail loudly now if the HIP library is missing

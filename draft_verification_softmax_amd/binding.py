@@ -1,0 +1,250 @@
+"""ctypes binding of libspecverify.so: argument marshalling only.
+
+Tensors must live on the GPU; their ``data_ptr()`` and ``torch.cuda.current_stream()``
+are handed to the C entry points unchanged.  Output tensors are allocated here with torch
+(device memory plumbing) when the caller does not pass them.
+"""
+import ctypes as C
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libspecverify.so")
+
+SV_F32, SV_BF16 = 0, 1
+_STATUS = {0: "SV_OK", 1: "SV_EINVAL", 2: "SV_EUNSUPPORTED", 3: "SV_EHIP", 4: "SV_EWORKSPACE", 5: "SV_EDEVICE"}
+
+EXPORTS = [
+    "sv_workspace_bytes", "sv_workspace_init", "sv_verify_batch", "sv_accept_len",
+    "sv_residual_sample", "sv_tv_e2e_loss", "sv_alloc_verify_budget", "sv_uniforms",
+    "sv_device_error", "sv_status_string",
+]
+
+
+class SVError(RuntimeError):
+    def __init__(self, fn, code):
+        self.code = code
+        msg = _lib.sv_status_string(code).decode() if _lib is not None else _STATUS.get(code, str(code))
+        super().__init__(f"{fn}: {msg}")
+
+
+class Params(C.Structure):
+    _fields_ = [
+        ("B", C.c_int32), ("K_max", C.c_int32), ("V", C.c_int32),
+        ("dtype_t", C.c_int32), ("dtype_d", C.c_int32),
+        ("temperature", C.c_float),
+        ("seed", C.c_uint64), ("step", C.c_uint64),
+        ("ld_t", C.c_int64), ("ld_d", C.c_int64),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """Load the library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m draft_verification_softmax_amd.build` (no CPU fallback exists)")
+        L = C.CDLL(LIB_PATH)
+        vp, i32, u64, sz = C.c_void_p, C.c_int32, C.c_uint64, C.c_size_t
+        P = C.POINTER(Params)
+        L.sv_workspace_bytes.argtypes = [i32, i32, i32]
+        L.sv_workspace_bytes.restype = sz
+        L.sv_workspace_init.argtypes = [vp, sz, vp]
+        L.sv_verify_batch.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.sv_accept_len.argtypes = [vp, vp, i32, i32, vp, vp]
+        L.sv_residual_sample.argtypes = [P, vp, vp, vp, vp, vp, vp]
+        L.sv_tv_e2e_loss.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
+        L.sv_alloc_verify_budget.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp]
+        L.sv_uniforms.argtypes = [u64, vp, i32, vp, vp]
+        L.sv_device_error.argtypes = [vp, vp, C.POINTER(C.c_uint32)]
+        L.sv_status_string.argtypes = [C.c_int]
+        L.sv_status_string.restype = C.c_char_p
+        for name in EXPORTS:
+            if name not in ("sv_workspace_bytes", "sv_status_string"):
+                getattr(L, name).restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def sv_status_string(code: int) -> str:
+    return lib().sv_status_string(code).decode()
+
+
+def _check(fn, code):
+    if code != 0:
+        raise SVError(fn, code)
+
+
+def _p(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors passed to libspecverify must be on the GPU")
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    if t.dtype == torch.float32:
+        return SV_F32
+    raise ValueError(f"unsupported logit dtype {t.dtype}")
+
+
+def sv_workspace_bytes(B, K_max, V) -> int:
+    return int(lib().sv_workspace_bytes(B, K_max, V))
+
+
+def sv_workspace_init(ws: torch.Tensor, stream=None):
+    _check("sv_workspace_init", lib().sv_workspace_init(_p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+class Workspace:
+    """A zero-initialised device workspace that grows on demand."""
+
+    def __init__(self, device="cuda"):
+        self.device = device
+        self.buf = None
+
+    def get(self, B, K_max, V, stream=None):
+        need = sv_workspace_bytes(B, K_max, V)
+        if self.buf is None or self.buf.numel() < need:
+            self.buf = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
+            sv_workspace_init(self.buf, stream)
+        return self.buf
+
+
+def _rows_ld(t):
+    if t.stride(-1) != 1:
+        raise ValueError("logit rows must be contiguous")
+    return t.stride(-2) if t.dim() >= 2 else t.shape[-1]
+
+
+def _check_rows(t, rows_per_item):
+    """The ABI addresses row (i, k) at (i * rows_per_item + k) * ld: rows must be packed."""
+    if t is None or t.numel() == 0:
+        return
+    ld = _rows_ld(t)
+    if t.stride(1) != ld or t.stride(0) != rows_per_item * ld:
+        raise ValueError("logit rows must be packed [B][rows][ld] with a common row stride")
+
+
+def _params(B, K, V, target, draft, T, seed, step):
+    ld_t = _rows_ld(target)
+    ld_d = _rows_ld(draft) if draft is not None and draft.numel() else V
+    dd = _dtype_code(draft) if draft is not None else _dtype_code(target)
+    return Params(B, K, V, _dtype_code(target), dd, float(T), seed, step, ld_t, ld_d)
+
+
+def sv_verify_batch(target, draft, draft_tokens, T, seed=0, step=0, draft_len=None,
+                    want_lse=True, want_amax=False, workspace=None, out=None, stream=None):
+    """target [B][K+1][V], draft [B][K][V], draft_tokens [B][K] int32 (all on the GPU).
+    Returns a dict of device tensors (alpha, accept, lse_t, lse_d, amax_t, amax_d,
+    accept_len, out_tokens, n_out)."""
+    B, K1, V = target.shape
+    K = K1 - 1
+    if draft.shape != (B, K, V) or draft_tokens.shape != (B, K):
+        raise ValueError("shape mismatch between target, draft and draft_tokens")
+    if draft_tokens.dtype != torch.int32 or not draft_tokens.is_contiguous():
+        raise ValueError("draft_tokens must be contiguous int32")
+    if draft_len is not None and (draft_len.dtype != torch.int32 or draft_len.shape != (B,)):
+        raise ValueError("draft_len must be int32 [B]")
+    _check_rows(target, K + 1)
+    _check_rows(draft, K)
+    dev = target.device
+    if out is None:
+        out = dict(
+            alpha=torch.empty((B, K), dtype=torch.float32, device=dev),
+            accept=torch.empty((B, K), dtype=torch.uint8, device=dev),
+            lse_t=torch.empty((B, K), dtype=torch.float32, device=dev) if want_lse else None,
+            lse_d=torch.empty((B, K), dtype=torch.float32, device=dev) if want_lse else None,
+            amax_t=torch.empty((B, K), dtype=torch.int32, device=dev) if want_amax else None,
+            amax_d=torch.empty((B, K), dtype=torch.int32, device=dev) if want_amax else None,
+            accept_len=torch.empty((B,), dtype=torch.int32, device=dev),
+            out_tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+            n_out=torch.empty((B,), dtype=torch.int32, device=dev),
+        )
+    ws = workspace if isinstance(workspace, torch.Tensor) else (workspace or Workspace(dev)).get(B, K, V, stream)
+    prm = _params(B, K, V, target, draft, T, seed, step)
+    rc = lib().sv_verify_batch(
+        C.byref(prm), _p(target), _p(draft), _p(draft_tokens), _p(draft_len),
+        _p(out["alpha"]), _p(out["accept"]), _p(out["lse_t"]), _p(out["lse_d"]),
+        _p(out["amax_t"]), _p(out["amax_d"]), _p(out["accept_len"]), _p(out["out_tokens"]),
+        _p(out["n_out"]), _p(ws), ws.numel(), _stream(stream))
+    _check("sv_verify_batch", rc)
+    return out
+
+
+def sv_accept_len(accept, draft_len=None, out=None, stream=None):
+    B, K = accept.shape
+    out = torch.empty((B,), dtype=torch.int32, device=accept.device) if out is None else out
+    _check("sv_accept_len", lib().sv_accept_len(_p(accept), _p(draft_len), B, K, _p(out), _stream(stream)))
+    return out
+
+
+def sv_residual_sample(target, draft, accept_len, T, seed=0, step=0, draft_len=None, out=None, stream=None):
+    B, K1, V = target.shape
+    K = K1 - 1
+    _check_rows(target, K + 1)
+    _check_rows(draft, K)
+    out = torch.empty((B,), dtype=torch.int32, device=target.device) if out is None else out
+    prm = _params(B, K, V, target, draft, T, seed, step)
+    _check("sv_residual_sample", lib().sv_residual_sample(
+        C.byref(prm), _p(target), _p(draft), _p(draft_len), _p(accept_len), _p(out), _stream(stream)))
+    return out
+
+
+def sv_tv_e2e_loss(target, draft, T=1.0, alpha=None, workspace=None, stream=None):
+    """target, draft [I][D][V]; returns (loss [1] float32, alpha [I][D] float32)."""
+    I, D, V = target.shape
+    if draft.shape != (I, D, V):
+        raise ValueError("target and draft must have the same shape")
+    _check_rows(target, D)
+    _check_rows(draft, D)
+    dev = target.device
+    alpha = torch.empty((I, D), dtype=torch.float32, device=dev) if alpha is None else alpha
+    loss = torch.empty((1,), dtype=torch.float32, device=dev)
+    ws = workspace if isinstance(workspace, torch.Tensor) else (workspace or Workspace(dev)).get(I, D, V, stream)
+    prm = _params(I, D, V, target, draft, T, 0, 0)
+    _check("sv_tv_e2e_loss", lib().sv_tv_e2e_loss(C.byref(prm), _p(target), _p(draft), _p(alpha), _p(loss),
+                                                  _p(ws), ws.numel(), _stream(stream)))
+    return loss, alpha
+
+
+def sv_alloc_verify_budget(conf, budget_N, draft_len=None, want_row_list=True, stream=None):
+    """conf [B][K] float32 in [0,1]; returns (lens [B], row_off [B+1], row_list [N'] or None)."""
+    B, K = conf.shape
+    dev = conf.device
+    lens = torch.empty((B,), dtype=torch.int32, device=dev)
+    row_off = torch.empty((B + 1,), dtype=torch.int32, device=dev)
+    n = min(int(budget_N), B * K)  # upper bound on the selected count
+    row_list = torch.empty((max(n, 1),), dtype=torch.int32, device=dev) if want_row_list else None
+    _check("sv_alloc_verify_budget", lib().sv_alloc_verify_budget(
+        _p(conf), _p(draft_len), B, K, int(budget_N), _p(lens), _p(row_off), _p(row_list), _stream(stream)))
+    return lens, row_off, row_list
+
+
+def sv_uniforms(seed, counters, stream=None):
+    """counters [n][4] uint64 (torch int64 on the GPU); returns float32 [n]."""
+    n = counters.shape[0]
+    out = torch.empty((n,), dtype=torch.float32, device=counters.device)
+    _check("sv_uniforms", lib().sv_uniforms(C.c_uint64(seed), _p(counters), n, _p(out), _stream(stream)))
+    return out
+
+
+def sv_device_error(ws: torch.Tensor, stream=None) -> int:
+    flags = C.c_uint32(0)
+    rc = lib().sv_device_error(_p(ws), _stream(stream), C.byref(flags))
+    if rc not in (0, 5):
+        raise SVError("sv_device_error", rc)
+    return int(flags.value)

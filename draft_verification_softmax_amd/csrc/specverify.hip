@@ -1,0 +1,901 @@
+// specverify.hip -- batched speculative-decoding draft verification for MI355X (gfx950).
+//
+// Kernels (all wave64):
+//   verify_rows_kernel   one workgroup per (request, draft position) row pair; sweep 1
+//                        reduces both rows to their base-2 log-normalisers (and argmax),
+//                        sweep 2 sums min(p, q) and the per-segment residual mass; the
+//                        accept test reads p(x), q(x); the last row of a request to finish
+//                        runs the request's finalize (first-reject scan, correction or
+//                        bonus draw by inverse CDF over one re-read segment).
+//   residual_kernel      stand-alone correction/bonus draw per request.
+//   e2e_reduce_kernel    L_e2e from the alpha table, fixed summation order.
+//   budget_kernel        cumulative confidences, sort, selected prefix lengths.
+//   accept_len_kernel    first-reject prefix per request.
+//
+// The definitions come from the AngelSpec pages: the overlap equation and the serial
+// acceptance argument and the L_e2e equation (tutorial page, section "From KL to an
+// end-to-end TV loss"), the shared verification budget (same page, section "Runtime
+// adaptation: verification as a shared pool"), target-distribution preservation (abstract).
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sv_device.hpp"
+#include "specverify.h"
+
+namespace sv {
+
+constexpr int kThreads = 512;                 // 8 waves per workgroup
+constexpr int kWaves = kThreads / kWave;
+constexpr int kElems = 8;                     // logits per lane per tile (one 16-byte bf16 load)
+constexpr int kTile = kThreads * kElems;      // 4096 logits per tile
+constexpr int kSeg = kWave * kElems;          // 512: one wave's contiguous share of a tile
+
+enum Mode { kStoch = 0, kGreedy = 1, kAlphaOnly = 2 };
+
+struct RowRec {            // per verified row, in the workspace (32 bytes)
+    float m_t, ls2_t;      // target row: max logit, log2 sum 2^{(z-m)c}
+    float m_d, ls2_d;      // drafter row
+    int32_t amax_t;        // target argmax (greedy correction token)
+    int32_t acc;           // accept flag
+    int32_t pad[2];
+};
+
+// Workspace layout shared by the host functions and the kernels.
+struct WsLayout {
+    size_t off_err, off_cnt, off_rec, off_dir, off_alpha, total;
+    int nseg;
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+__host__ __device__ inline WsLayout ws_layout(int B, int K, int V) {
+    WsLayout w;
+    w.nseg = (V + kSeg - 1) / kSeg;
+    w.off_err = 0;
+    w.off_cnt = 256;
+    w.off_rec = align256(w.off_cnt + sizeof(int32_t) * (size_t)(B > 0 ? B : 1));
+    w.off_dir = align256(w.off_rec + sizeof(RowRec) * (size_t)B * (size_t)K);
+    w.off_alpha = align256(w.off_dir + sizeof(float) * 2 * (size_t)w.nseg * (size_t)B * (size_t)(K + 1));
+    w.total = align256(w.off_alpha + sizeof(float) * (size_t)B * (size_t)K);
+    return w;
+}
+
+struct VerifyArgs {
+    const void *target, *draft;
+    const int32_t *tokens, *draft_len;
+    float *alpha;
+    uint8_t *accept;
+    float *lse_t, *lse_d;
+    int32_t *amax_t, *amax_d;
+    int32_t *accept_len, *out_tokens, *n_out;
+    uint32_t *err;
+    int32_t *cnt;
+    RowRec *rec;
+    float *dir;
+    int64_t ld_t, ld_d;
+    int32_t B, K, V, nseg;
+    int32_t trows;         // target rows per request: K+1 (verify) or K (e2e)
+    float c;               // log2(e) / T   (0 in greedy mode)
+    float inv_t;           // 1 / T
+    uint64_t seed, step;
+    int32_t want_amax;
+};
+
+template <int DT>
+__device__ __forceinline__ const void *row_at(const void *base, int64_t row, int64_t ld) {
+    constexpr size_t esz = DT == kDtBF16 ? 2 : 4;
+    return static_cast<const char *>(base) + (size_t)(row * ld) * esz;
+}
+
+// ---------------------------------------------------------------------------------------
+// Workgroup reductions (fixed order: xor-shuffle tree inside a wave, waves in index order)
+// ---------------------------------------------------------------------------------------
+struct Red {
+    float m[2][kWaves], s[2][kWaves];
+    float v[2][kWaves];
+    int i[2][kWaves];
+    double d[kWaves];
+    float f[kWaves];
+};
+
+__device__ void block_lse2(float &mt, float &st, float &md, float &sd, float c, Red &red) {
+    wave_lse(mt, st, c);
+    wave_lse(md, sd, c);
+    const int w = threadIdx.x / kWave;
+    if (lane_id() == 0) { red.m[0][w] = mt; red.s[0][w] = st; red.m[1][w] = md; red.s[1][w] = sd; }
+    __syncthreads();
+    mt = red.m[0][0]; st = red.s[0][0]; md = red.m[1][0]; sd = red.s[1][0];
+    for (int j = 1; j < kWaves; ++j) {
+        lse_merge(mt, st, red.m[0][j], red.s[0][j], c);
+        lse_merge(md, sd, red.m[1][j], red.s[1][j], c);
+    }
+    __syncthreads();
+}
+
+__device__ void block_amax2(float &vt, int &it, float &vd, int &id, Red &red) {
+    wave_amax(vt, it);
+    wave_amax(vd, id);
+    const int w = threadIdx.x / kWave;
+    if (lane_id() == 0) { red.v[0][w] = vt; red.i[0][w] = it; red.v[1][w] = vd; red.i[1][w] = id; }
+    __syncthreads();
+    vt = red.v[0][0]; it = red.i[0][0]; vd = red.v[1][0]; id = red.i[1][0];
+    for (int j = 1; j < kWaves; ++j) {
+        amax_merge(vt, it, red.v[0][j], red.i[0][j]);
+        amax_merge(vd, id, red.v[1][j], red.i[1][j]);
+    }
+    __syncthreads();
+}
+
+__device__ float block_sum(float x, Red &red) {
+    x = wave_sum(x);
+    const int w = threadIdx.x / kWave;
+    if (lane_id() == 0) red.f[w] = x;
+    __syncthreads();
+    float t = 0.f;
+    for (int j = 0; j < kWaves; ++j) t += red.f[j];
+    __syncthreads();
+    return t;
+}
+
+__device__ double block_sum_d(double x, Red &red) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, kWave);
+    const int w = threadIdx.x / kWave;
+    if (lane_id() == 0) red.d[w] = x;
+    __syncthreads();
+    double t = 0.0;
+    for (int j = 0; j < kWaves; ++j) t += red.d[j];
+    __syncthreads();
+    return t;
+}
+
+// ---------------------------------------------------------------------------------------
+// Single-row streams used by the finalize and the stand-alone sampler
+// ---------------------------------------------------------------------------------------
+
+// Argmax of one row (lowest index among maxima), broadcast to every thread.
+template <int DT>
+__device__ int row_argmax(const void *row, int V, Red &red) {
+    float v = neg_inf(), vd = neg_inf();
+    int i = 0x7fffffff, id = 0x7fffffff;
+    for (int base = 0; base < V; base += kTile) {
+        const int e = base + threadIdx.x * kElems;
+        float z[8];
+        load8<DT>(row, e, V, z);
+        amax_update8(v, i, z, e);
+    }
+    block_amax2(v, i, vd, id, red);
+    return i == 0x7fffffff ? 0 : i;
+}
+
+// Draw from p = softmax(row / T) by inverse CDF at target u * R.  Sweep 1 streams the row
+// once, keeping (m, s) of every 512-logit segment in seg[0..nseg) / seg[nseg..2 nseg);
+// those become the segment masses, one wave finds the segment, and re-reads it to find
+// the token.  seg: 2*nseg floats of scratch (workspace or LDS).
+template <int DT>
+__device__ int draw_from_row(const void *row, int V, float c, float u, float *seg, int nseg, Red &red) {
+    const int w = threadIdx.x / kWave;
+    float m = neg_inf(), s = 0.f;
+    int it = 0;
+    for (int base = 0; base < V; base += kTile, ++it) {
+        const int e = base + threadIdx.x * kElems;
+        float z[8];
+        load8<DT>(row, e, V, z);
+        float cm = neg_inf(), cs = 0.f;
+        lse_update8(cm, cs, z, c);
+        lse_merge(m, s, cm, cs, c);
+        wave_lse(cm, cs, c);
+        if (lane_id() == 0) {
+            const int sidx = it * kWaves + w;
+            if (sidx < nseg) { seg[sidx] = cm; seg[nseg + sidx] = cs; }
+        }
+    }
+    float md = neg_inf(), sd = 0.f;
+    block_lse2(m, s, md, sd, c, red);
+    const float ls2 = log2f(s);
+    __threadfence_block();
+    __syncthreads();
+    for (int j = threadIdx.x; j < nseg; j += kThreads) {
+        const float sm = seg[j], ss = seg[nseg + j];
+        seg[j] = (sm == neg_inf()) ? 0.f : ss * exp2_fast(log2p(sm, m, c, ls2));
+    }
+    __threadfence_block();
+    __syncthreads();
+    double part = 0.0;
+    for (int j = threadIdx.x; j < nseg; j += kThreads) part += (double)seg[j];
+    const double R = block_sum_d(part, red);
+    __shared__ int s_tok;
+    if (w == 0) {
+        const double t = (double)u * R;
+        double ex;
+        const float *segw = seg;
+        int sidx = wave_find([&](int j) { return segw[j]; }, nseg, t, &ex);
+        int tok = 0;
+        if (sidx >= 0) {
+            const int e0 = sidx * kSeg;
+            const int n = min(kSeg, V - e0);
+            double ex2;
+            tok = wave_find([&](int j) { return exp2_fast(log2p(load1<DT>(row, e0 + j), m, c, ls2)); },
+                            n, t - ex, &ex2);
+            tok = tok < 0 ? e0 : e0 + tok;
+        }
+        if (lane_id() == 0) s_tok = tok;
+    }
+    __syncthreads();
+    return s_tok;
+}
+
+// ---------------------------------------------------------------------------------------
+// Verification rows
+// ---------------------------------------------------------------------------------------
+
+template <int DTT, int DTD, int MODE>
+__device__ void finalize_request(const VerifyArgs &a, int r, int L, Red &red) {
+    __shared__ int s_tau, s_tok;
+    const int K = a.K;
+    // tau = first rejected position < L (min over the flags of the L rows)
+    int tau = L;
+    for (int k = threadIdx.x; k < L; k += kThreads)
+        if (!a.rec[(size_t)r * K + k].acc) { tau = min(tau, k); }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) tau = min(tau, __shfl_xor(tau, d, kWave));
+    if (threadIdx.x == 0) s_tau = L;
+    __syncthreads();
+    if (lane_id() == 0) atomicMin(&s_tau, tau);
+    __syncthreads();
+    tau = s_tau;
+
+    // positions that were not verified
+    for (int k = L + threadIdx.x; k < K; k += kThreads) {
+        const size_t i = (size_t)r * K + k;
+        a.alpha[i] = 0.f;
+        a.accept[i] = 0;
+        if (a.lse_t) a.lse_t[i] = 0.f;
+        if (a.lse_d) a.lse_d[i] = 0.f;
+        if (a.amax_t) a.amax_t[i] = -1;
+        if (a.amax_d) a.amax_d[i] = -1;
+    }
+
+    int tok;
+    if constexpr (MODE == kGreedy) {
+        if (tau < L) tok = a.rec[(size_t)r * K + tau].amax_t;
+        else tok = row_argmax<DTT>(row_at<DTT>(a.target, (int64_t)r * a.trows + tau, a.ld_t), a.V, red);
+    } else {
+        const float u = uniform24(a.seed, (uint64_t)r, (uint64_t)tau, kPurposeCorrection, a.step);
+        float *seg = a.dir + (size_t)((size_t)r * (K + 1) + tau) * 2 * a.nseg;
+        const void *trow = row_at<DTT>(a.target, (int64_t)r * a.trows + tau, a.ld_t);
+        bool done = false;
+        tok = 0;
+        if (tau < L) {
+            // residual norm(max(p - q, 0)): segment masses were written by sweep 2
+            double part = 0.0;
+            for (int j = threadIdx.x; j < a.nseg; j += kThreads) part += (double)seg[j];
+            const double R = block_sum_d(part, red);
+            if (R > 0.0) {
+                const RowRec rr = a.rec[(size_t)r * K + tau];
+                const void *drow = row_at<DTD>(a.draft, (int64_t)r * K + tau, a.ld_d);
+                if (threadIdx.x < kWave) {
+                    const double t = (double)u * R;
+                    double ex;
+                    int sidx = wave_find([&](int j) { return seg[j]; }, a.nseg, t, &ex);
+                    int tk = 0;
+                    if (sidx >= 0) {
+                        const int e0 = sidx * kSeg;
+                        const int n = min(kSeg, a.V - e0);
+                        double ex2;
+                        const float c = a.c;
+                        tk = wave_find(
+                            [&](int j) {
+                                const float p = exp2_fast(log2p(load1<DTT>(trow, e0 + j), rr.m_t, c, rr.ls2_t));
+                                const float q = exp2_fast(log2p(load1<DTD>(drow, e0 + j), rr.m_d, c, rr.ls2_d));
+                                return p - fminf(p, q);
+                            },
+                            n, t - ex, &ex2);
+                        tk = tk < 0 ? e0 : e0 + tk;
+                    }
+                    if (threadIdx.x == 0) s_tok = tk;
+                }
+                __syncthreads();
+                tok = s_tok;
+                done = true;
+            }
+        }
+        if (!done) tok = draw_from_row<DTT>(trow, a.V, a.c, u, seg, a.nseg, red);
+    }
+
+    int32_t *o = a.out_tokens + (size_t)r * (K + 1);
+    for (int j = threadIdx.x; j <= K; j += kThreads)
+        o[j] = j < tau ? a.tokens[(size_t)r * K + j] : (j == tau ? tok : -1);
+    if (threadIdx.x == 0) {
+        a.accept_len[r] = tau;
+        a.n_out[r] = tau + 1;
+    }
+}
+
+template <int DTT, int DTD, int MODE>
+__global__ __launch_bounds__(kThreads) void verify_rows_kernel(VerifyArgs a) {
+    __shared__ Red red;
+    __shared__ int s_last;
+    const int K = a.K;
+    const int slots = K > 0 ? K : 1;
+    const int r = blockIdx.x / slots;
+    const int k = blockIdx.x % slots;
+    int L = K;
+    if (MODE != kAlphaOnly && a.draft_len) {
+        L = a.draft_len[r];
+        if (L < 0 || L > K) {
+            if (threadIdx.x == 0 && k == 0) atomicOr(a.err, SV_DEVERR_DRAFT_LEN);
+            L = L < 0 ? 0 : K;
+        }
+    }
+    if (k >= L) {
+        if (MODE != kAlphaOnly && L == 0 && k == 0) finalize_request<DTT, DTD, MODE>(a, r, 0, red);
+        return;
+    }
+    const int V = a.V;
+    const float c = a.c;
+    const int64_t trow_idx = (int64_t)r * a.trows + k, drow_idx = (int64_t)r * K + k;
+    const void *trow = row_at<DTT>(a.target, trow_idx, a.ld_t);
+    const void *drow = row_at<DTD>(a.draft, drow_idx, a.ld_d);
+
+    // sweep 1: base-2 log-normalisers (and argmax) of both rows
+    float mt = neg_inf(), st = 0.f, md = neg_inf(), sd = 0.f;
+    float vt = neg_inf(), vd = neg_inf();
+    int it = 0x7fffffff, id = 0x7fffffff;
+    const bool want_amax = (MODE == kGreedy) || a.want_amax;
+    for (int base = 0; base < V; base += kTile) {
+        const int e = base + threadIdx.x * kElems;
+        float zt[8], zd[8];
+        load8<DTT>(trow, e, V, zt);
+        load8<DTD>(drow, e, V, zd);
+        if constexpr (MODE != kGreedy) {
+            lse_update8(mt, st, zt, c);
+            lse_update8(md, sd, zd, c);
+        }
+        if (want_amax) {
+            amax_update8(vt, it, zt, e);
+            amax_update8(vd, id, zd, e);
+        }
+    }
+    if constexpr (MODE != kGreedy) block_lse2(mt, st, md, sd, c, red);
+    if (want_amax) {
+        block_amax2(vt, it, vd, id, red);
+        if (it == 0x7fffffff) it = 0;
+        if (id == 0x7fffffff) id = 0;
+    }
+    const float ls2t = (MODE != kGreedy) ? log2f(st) : 0.f;
+    const float ls2d = (MODE != kGreedy) ? log2f(sd) : 0.f;
+
+    // sweep 2: alpha = sum min(p, q) and per-segment residual mass sum max(p - q, 0)
+    float alpha = 0.f;
+    if constexpr (MODE != kGreedy) {
+        const int w = threadIdx.x / kWave;
+        float *seg = (MODE == kStoch) ? a.dir + (size_t)((size_t)r * (K + 1) + k) * 2 * a.nseg : nullptr;
+        float asum = 0.f;
+        int itn = 0;
+        for (int base = 0; base < V; base += kTile, ++itn) {
+            const int e = base + threadIdx.x * kElems;
+            float zt[8], zd[8];
+            load8<DTT>(trow, e, V, zt);
+            load8<DTD>(drow, e, V, zd);
+            float res = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float p = exp2_fast(log2p(zt[j], mt, c, ls2t));
+                const float q = exp2_fast(log2p(zd[j], md, c, ls2d));
+                const float mn = fminf(p, q);
+                asum += mn;
+                res += p - mn;
+            }
+            if constexpr (MODE == kStoch) {
+                res = wave_sum(res);
+                const int sidx = itn * kWaves + w;
+                if (lane_id() == 0 && sidx < a.nseg) seg[sidx] = res;
+            }
+        }
+        alpha = block_sum(asum, red);
+    }
+
+    if constexpr (MODE == kAlphaOnly) {
+        if (threadIdx.x == 0) a.alpha[(size_t)r * K + k] = alpha;
+        return;
+    } else {
+        if (threadIdx.x == 0) {
+            const size_t i = (size_t)r * K + k;
+            int x = a.tokens[i];
+            bool ok = (x >= 0 && x < V);
+            if (!ok) atomicOr(a.err, SV_DEVERR_TOKEN);
+            int acc = 0;
+            if constexpr (MODE == kGreedy) {
+                acc = ok && x == it;
+                alpha = (it == id) ? 1.f : 0.f;
+            } else {
+                if (ok) {
+                    // accept iff u * q(x) < p(x), i.e. u < 2^{log2 p(x) - log2 q(x)}
+                    const float lpt = log2p(load1<DTT>(trow, x), mt, c, ls2t);
+                    const float lpd = log2p(load1<DTD>(drow, x), md, c, ls2d);
+                    const float u = uniform24(a.seed, (uint64_t)r, (uint64_t)k, kPurposeAccept, a.step);
+                    acc = u < exp2f(lpt - lpd);
+                }
+            }
+            a.alpha[i] = alpha;
+            a.accept[i] = (uint8_t)acc;
+            if (a.lse_t) a.lse_t[i] = (MODE == kStoch) ? (float)((double)mt * a.inv_t + (double)ls2t * 0.6931471805599453) : 0.f;
+            if (a.lse_d) a.lse_d[i] = (MODE == kStoch) ? (float)((double)md * a.inv_t + (double)ls2d * 0.6931471805599453) : 0.f;
+            if (a.amax_t) a.amax_t[i] = want_amax ? it : -1;
+            if (a.amax_d) a.amax_d[i] = want_amax ? id : -1;
+            RowRec rr;
+            rr.m_t = mt; rr.ls2_t = ls2t; rr.m_d = md; rr.ls2_d = ls2d;
+            rr.amax_t = it; rr.acc = acc; rr.pad[0] = rr.pad[1] = 0;
+            a.rec[i] = rr;
+        }
+        // last row of request r to arrive runs the request's finalize
+        __threadfence();
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const int old = atomicAdd(&a.cnt[r], 1);
+            s_last = (old == L - 1);
+            if (s_last) atomicExch(&a.cnt[r], 0);
+        }
+        __syncthreads();
+        if (s_last) {
+            __threadfence();
+            finalize_request<DTT, DTD, MODE>(a, r, L, red);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Stand-alone correction / bonus draw
+// ---------------------------------------------------------------------------------------
+constexpr int kResidualSegMax = (SV_V_MAX + kSeg - 1) / kSeg;  // 2048
+
+template <int DTT, int DTD>
+__global__ __launch_bounds__(kThreads) void residual_kernel(VerifyArgs a) {
+    __shared__ Red red;
+    __shared__ float seg[2 * kResidualSegMax];
+    __shared__ int s_tok;
+    const int r = blockIdx.x;
+    const int K = a.K, V = a.V;
+    int L = a.draft_len ? a.draft_len[r] : K;
+    if (L < 0 || L > K) L = L < 0 ? 0 : K;
+    int tau = a.accept_len[r];
+    if (tau < 0 || tau > L) tau = tau < 0 ? 0 : L;
+    const void *trow = row_at<DTT>(a.target, (int64_t)r * (K + 1) + tau, a.ld_t);
+    int tok;
+    if (a.c == 0.f) {
+        tok = row_argmax<DTT>(trow, V, red);
+    } else {
+        const float c = a.c;
+        const float u = uniform24(a.seed, (uint64_t)r, (uint64_t)tau, kPurposeCorrection, a.step);
+        bool done = false;
+        tok = 0;
+        if (tau < L) {
+            const void *drow = row_at<DTD>(a.draft, (int64_t)r * K + tau, a.ld_d);
+            float mt = neg_inf(), st = 0.f, md = neg_inf(), sd = 0.f;
+            for (int base = 0; base < V; base += kTile) {
+                const int e = base + threadIdx.x * kElems;
+                float zt[8], zd[8];
+                load8<DTT>(trow, e, V, zt);
+                load8<DTD>(drow, e, V, zd);
+                lse_update8(mt, st, zt, c);
+                lse_update8(md, sd, zd, c);
+            }
+            block_lse2(mt, st, md, sd, c, red);
+            const float ls2t = log2f(st), ls2d = log2f(sd);
+            const int w = threadIdx.x / kWave;
+            int itn = 0;
+            for (int base = 0; base < V; base += kTile, ++itn) {
+                const int e = base + threadIdx.x * kElems;
+                float zt[8], zd[8];
+                load8<DTT>(trow, e, V, zt);
+                load8<DTD>(drow, e, V, zd);
+                float res = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float p = exp2_fast(log2p(zt[j], mt, c, ls2t));
+                    const float q = exp2_fast(log2p(zd[j], md, c, ls2d));
+                    res += p - fminf(p, q);
+                }
+                res = wave_sum(res);
+                const int sidx = itn * kWaves + w;
+                if (lane_id() == 0 && sidx < a.nseg) seg[sidx] = res;
+            }
+            __syncthreads();
+            double part = 0.0;
+            for (int j = threadIdx.x; j < a.nseg; j += kThreads) part += (double)seg[j];
+            const double R = block_sum_d(part, red);
+            if (R > 0.0) {
+                if (threadIdx.x < kWave) {
+                    const double t = (double)u * R;
+                    double ex;
+                    int sidx = wave_find([&](int j) { return seg[j]; }, a.nseg, t, &ex);
+                    int tk = 0;
+                    if (sidx >= 0) {
+                        const int e0 = sidx * kSeg;
+                        const int n = min(kSeg, V - e0);
+                        double ex2;
+                        tk = wave_find(
+                            [&](int j) {
+                                const float p = exp2_fast(log2p(load1<DTT>(trow, e0 + j), mt, c, ls2t));
+                                const float q = exp2_fast(log2p(load1<DTD>(drow, e0 + j), md, c, ls2d));
+                                return p - fminf(p, q);
+                            },
+                            n, t - ex, &ex2);
+                        tk = tk < 0 ? e0 : e0 + tk;
+                    }
+                    if (threadIdx.x == 0) s_tok = tk;
+                }
+                __syncthreads();
+                tok = s_tok;
+                done = true;
+            }
+            __syncthreads();
+        }
+        if (!done) tok = draw_from_row<DTT>(trow, V, c, u, seg, a.nseg, red);
+    }
+    if (threadIdx.x == 0) a.out_tokens[r] = tok;
+}
+
+// ---------------------------------------------------------------------------------------
+// L_e2e = 1 - (1/(|I| D)) sum_i sum_{m<D} prod_{k<=m} alpha_{i,k}, fixed summation order
+// ---------------------------------------------------------------------------------------
+constexpr int kReduceThreads = 1024;
+
+__global__ __launch_bounds__(kReduceThreads) void e2e_reduce_kernel(const float *alpha, int I, int D, float *loss) {
+    __shared__ double part[kReduceThreads];
+    double acc = 0.0;
+    for (int i = threadIdx.x; i < I; i += kReduceThreads) {
+        double prod = 1.0, row = 0.0;
+        for (int m = 0; m < D; ++m) {
+            prod *= (double)alpha[(size_t)i * D + m];
+            row += prod;
+        }
+        acc += row;
+    }
+    part[threadIdx.x] = acc;
+    __syncthreads();
+    for (int h = kReduceThreads / 2; h > 0; h >>= 1) {
+        if (threadIdx.x < h) part[threadIdx.x] += part[threadIdx.x + h];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *loss = (float)(1.0 - part[0] / ((double)I * (double)D));
+}
+
+// ---------------------------------------------------------------------------------------
+// Batch verification budget
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(kReduceThreads) void budget_kernel(const float *conf, const int32_t *draft_len,
+                                                                int B, int K, int N, int32_t *lens,
+                                                                int32_t *row_off, int32_t *row_list,
+                                                                uint32_t *err) {
+    __shared__ uint64_t keys[SV_BUDGET_MAX];
+    __shared__ int cnt[SV_BUDGET_MAX];
+    __shared__ int scan[kReduceThreads];
+    __shared__ int s_total;
+    const int n = B * K;
+    int np2 = 1;
+    while (np2 < n) np2 <<= 1;
+    if (threadIdx.x == 0) s_total = 0;
+    for (int i = threadIdx.x; i < np2; i += kReduceThreads) keys[i] = ~0ull;
+    for (int r = threadIdx.x; r < B; r += kReduceThreads) cnt[r] = 0;
+    __syncthreads();
+    // cumulative confidence per request: one thread per request, sequential binary32 products
+    int local_total = 0;
+    for (int r = threadIdx.x; r < B; r += kReduceThreads) {
+        int L = draft_len ? draft_len[r] : K;
+        if (L < 0 || L > K) {
+            if (err) atomicOr(err, SV_DEVERR_DRAFT_LEN);
+            L = L < 0 ? 0 : K;
+        }
+        float C = 1.f;
+        for (int k = 0; k < L; ++k) {
+            const float ck = conf[(size_t)r * K + k];
+            C = (k == 0) ? ck : __fmul_rn(C, ck);
+            // ascending key = descending C (non-negative binary32 bits are monotone), then (r, k)
+            keys[r * K + k] = ((uint64_t)(~__float_as_uint(C)) << 32) | (uint32_t)(r * K + k);
+        }
+        local_total += L;
+    }
+    atomicAdd(&s_total, local_total);
+    __syncthreads();
+    // bitonic sort, ascending
+    for (int size = 2; size <= np2; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = threadIdx.x; i < np2; i += kReduceThreads) {
+                const int j = i ^ stride;
+                if (j > i) {
+                    const bool up = (i & size) == 0;
+                    const uint64_t a = keys[i], b = keys[j];
+                    if ((a > b) == up) { keys[i] = b; keys[j] = a; }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    const int keep = min(N, s_total);
+    for (int i = threadIdx.x; i < keep; i += kReduceThreads) {
+        const int flat = (int)(keys[i] & 0xffffffffu);
+        atomicAdd(&cnt[flat / K], 1);
+    }
+    __syncthreads();
+    // exclusive scan of cnt over B: contiguous chunk per thread, then a scan of chunk sums
+    const int per = (B + kReduceThreads - 1) / kReduceThreads;
+    const int b0 = threadIdx.x * per, b1 = min(B, b0 + per);
+    int sum = 0;
+    for (int r = b0; r < b1; ++r) sum += cnt[r];
+    scan[threadIdx.x] = sum;
+    __syncthreads();
+    for (int d = 1; d < kReduceThreads; d <<= 1) {
+        const int v = threadIdx.x >= d ? scan[threadIdx.x - d] : 0;
+        __syncthreads();
+        scan[threadIdx.x] += v;
+        __syncthreads();
+    }
+    int off = scan[threadIdx.x] - sum;
+    for (int r = b0; r < b1; ++r) {
+        lens[r] = cnt[r];
+        row_off[r] = off;
+        if (row_list)
+            for (int k = 0; k < cnt[r]; ++k) row_list[off + k] = r * K + k;
+        off += cnt[r];
+    }
+    if (threadIdx.x == kReduceThreads - 1) row_off[B] = scan[kReduceThreads - 1];
+}
+
+// ---------------------------------------------------------------------------------------
+// Small kernels
+// ---------------------------------------------------------------------------------------
+__global__ void accept_len_kernel(const uint8_t *accept, const int32_t *draft_len, int B, int K,
+                                  int32_t *accept_len, uint32_t *err) {
+    const int r = blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= B) return;
+    int L = draft_len ? draft_len[r] : K;
+    if (L < 0 || L > K) L = L < 0 ? 0 : K;
+    int tau = L;
+    for (int k = 0; k < L; ++k)
+        if (!accept[(size_t)r * K + k]) { tau = k; break; }
+    accept_len[r] = tau;
+}
+
+__global__ void uniforms_kernel(uint64_t seed, const uint64_t *ctr, int n, float *out) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) out[i] = uniform24(seed, ctr[4 * i], ctr[4 * i + 1], ctr[4 * i + 2], ctr[4 * i + 3]);
+}
+
+__global__ void fill_zero_kernel(uint4 *p, size_t n16) {
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = make_uint4(0, 0, 0, 0);
+}
+
+}  // namespace sv
+
+// =======================================================================================
+// C ABI
+// =======================================================================================
+using namespace sv;
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_logits(const void *p, int dtype, int64_t ld, int V) {
+    if (dtype != SV_F32 && dtype != SV_BF16) return SV_EUNSUPPORTED;
+    if (!p || ld < V) return SV_EINVAL;
+    const int64_t esz = dtype == SV_BF16 ? 2 : 4;
+    if (!aligned16(p) || (ld * esz) % 16 != 0) return SV_EINVAL;
+    return SV_OK;
+}
+
+int launch_status() {
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+template <template <int, int> class Launcher, class... Args>
+int dispatch_dtypes(int dt, int dd, Args &&...args) {
+    if (dt == SV_BF16 && dd == SV_BF16) return Launcher<kDtBF16, kDtBF16>::run(args...);
+    if (dt == SV_F32 && dd == SV_F32) return Launcher<kDtF32, kDtF32>::run(args...);
+    if (dt == SV_BF16 && dd == SV_F32) return Launcher<kDtBF16, kDtF32>::run(args...);
+    return Launcher<kDtF32, kDtBF16>::run(args...);
+}
+
+template <int DTT, int DTD>
+struct VerifyLauncher {
+    static int run(const VerifyArgs &a, int mode, unsigned grid, hipStream_t s) {
+        if (mode == kGreedy) hipLaunchKernelGGL((verify_rows_kernel<DTT, DTD, kGreedy>), dim3(grid), dim3(kThreads), 0, s, a);
+        else if (mode == kStoch) hipLaunchKernelGGL((verify_rows_kernel<DTT, DTD, kStoch>), dim3(grid), dim3(kThreads), 0, s, a);
+        else hipLaunchKernelGGL((verify_rows_kernel<DTT, DTD, kAlphaOnly>), dim3(grid), dim3(kThreads), 0, s, a);
+        return launch_status();
+    }
+};
+
+template <int DTT, int DTD>
+struct ResidualLauncher {
+    static int run(const VerifyArgs &a, unsigned grid, hipStream_t s) {
+        hipLaunchKernelGGL((residual_kernel<DTT, DTD>), dim3(grid), dim3(kThreads), 0, s, a);
+        return launch_status();
+    }
+};
+
+const double kLog2e = 1.4426950408889634;
+
+}  // namespace
+
+extern "C" {
+
+size_t sv_workspace_bytes(int32_t B, int32_t K_max, int32_t V) {
+    if (B < 0 || K_max < 0 || V <= 0) return 0;
+    return ws_layout(B, K_max, V).total;
+}
+
+int sv_workspace_init(void *workspace, size_t workspace_bytes, void *stream) {
+    if (!workspace || !aligned16(workspace)) return SV_EINVAL;
+    const size_t n16 = workspace_bytes / 16;
+    if (n16 == 0) return SV_OK;
+    const unsigned grid = (unsigned)((n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, (uint4 *)workspace, n16);
+    return launch_status();
+}
+
+int sv_verify_batch(const sv_params *p, const void *target, const void *draft,
+                    const int32_t *draft_tokens, const int32_t *draft_len, float *alpha,
+                    uint8_t *accept, float *lse_t, float *lse_d, int32_t *amax_t,
+                    int32_t *amax_d, int32_t *accept_len, int32_t *out_tokens, int32_t *n_out,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+    if (!p || p->B < 0 || p->K_max < 0 || p->K_max > SV_K_MAX || p->V <= 0) return SV_EINVAL;
+    if (p->V > SV_V_MAX) return SV_EUNSUPPORTED;
+    if (!(p->temperature >= 0.f) || !isfinite(p->temperature)) return SV_EINVAL;
+    if (p->B == 0) return SV_OK;
+    int st = check_logits(target, p->dtype_t, p->ld_t, p->V);
+    if (st) return st;
+    if (p->K_max > 0) {
+        st = check_logits(draft, p->dtype_d, p->ld_d, p->V);
+        if (st) return st;
+        if (!draft_tokens || !alpha || !accept) return SV_EINVAL;
+    } else if (p->dtype_d != SV_F32 && p->dtype_d != SV_BF16) {
+        return SV_EUNSUPPORTED;
+    }
+    if (!accept_len || !out_tokens || !n_out) return SV_EINVAL;
+    const WsLayout L = ws_layout(p->B, p->K_max, p->V);
+    if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return SV_EWORKSPACE;
+    if ((uint64_t)p->B * (uint64_t)(p->K_max > 0 ? p->K_max : 1) > 0x7fffffffull) return SV_EINVAL;
+
+    VerifyArgs a{};
+    a.target = target; a.draft = draft; a.tokens = draft_tokens; a.draft_len = draft_len;
+    a.alpha = alpha; a.accept = accept; a.lse_t = lse_t; a.lse_d = lse_d;
+    a.amax_t = amax_t; a.amax_d = amax_d;
+    a.accept_len = accept_len; a.out_tokens = out_tokens; a.n_out = n_out;
+    char *ws = (char *)workspace;
+    a.err = (uint32_t *)(ws + L.off_err);
+    a.cnt = (int32_t *)(ws + L.off_cnt);
+    a.rec = (RowRec *)(ws + L.off_rec);
+    a.dir = (float *)(ws + L.off_dir);
+    a.ld_t = p->ld_t; a.ld_d = p->ld_d;
+    a.B = p->B; a.K = p->K_max; a.V = p->V; a.nseg = L.nseg;
+    a.trows = p->K_max + 1;
+    const bool greedy = p->temperature == 0.f;
+    a.c = greedy ? 0.f : (float)(kLog2e / (double)p->temperature);
+    a.inv_t = greedy ? 0.f : (float)(1.0 / (double)p->temperature);
+    a.seed = p->seed; a.step = p->step;
+    a.want_amax = (amax_t || amax_d) ? 1 : 0;
+    const unsigned grid = (unsigned)p->B * (unsigned)(p->K_max > 0 ? p->K_max : 1);
+    return dispatch_dtypes<VerifyLauncher>(p->dtype_t, p->dtype_d, a, greedy ? (int)kGreedy : (int)kStoch, grid,
+                                           (hipStream_t)stream);
+}
+
+int sv_accept_len(const uint8_t *accept, const int32_t *draft_len, int32_t B, int32_t K_max,
+                  int32_t *accept_len, void *stream) {
+    if (B < 0 || K_max < 0 || !accept_len || (K_max > 0 && !accept)) return SV_EINVAL;
+    if (B == 0) return SV_OK;
+    hipLaunchKernelGGL(accept_len_kernel, dim3((B + 255) / 256), dim3(256), 0, (hipStream_t)stream, accept,
+                       draft_len, B, K_max, accept_len, (uint32_t *)nullptr);
+    return launch_status();
+}
+
+int sv_residual_sample(const sv_params *p, const void *target, const void *draft,
+                       const int32_t *draft_len, const int32_t *accept_len, int32_t *token,
+                       void *stream) {
+    if (!p || p->B < 0 || p->K_max < 0 || p->K_max > SV_K_MAX || p->V <= 0) return SV_EINVAL;
+    if (p->V > SV_V_MAX) return SV_EUNSUPPORTED;
+    if (!(p->temperature >= 0.f) || !isfinite(p->temperature)) return SV_EINVAL;
+    if (p->B == 0) return SV_OK;
+    int st = check_logits(target, p->dtype_t, p->ld_t, p->V);
+    if (st) return st;
+    if (p->K_max > 0) {
+        st = check_logits(draft, p->dtype_d, p->ld_d, p->V);
+        if (st) return st;
+    }
+    if (!accept_len || !token) return SV_EINVAL;
+    VerifyArgs a{};
+    a.target = target; a.draft = draft; a.draft_len = draft_len; a.accept_len = (int32_t *)accept_len;
+    a.out_tokens = token;
+    a.err = nullptr;
+    a.ld_t = p->ld_t; a.ld_d = p->ld_d;
+    a.B = p->B; a.K = p->K_max; a.V = p->V; a.nseg = (p->V + kSeg - 1) / kSeg;
+    a.trows = p->K_max + 1;
+    const bool greedy = p->temperature == 0.f;
+    a.c = greedy ? 0.f : (float)(kLog2e / (double)p->temperature);
+    a.seed = p->seed; a.step = p->step;
+    return dispatch_dtypes<ResidualLauncher>(p->dtype_t, p->dtype_d, a, (unsigned)p->B, (hipStream_t)stream);
+}
+
+int sv_tv_e2e_loss(const sv_params *p, const void *target, const void *draft, float *alpha,
+                   float *loss, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!p || p->B <= 0 || p->K_max <= 0 || p->V <= 0 || !loss) return SV_EINVAL;
+    if (p->V > SV_V_MAX) return SV_EUNSUPPORTED;
+    if (!(p->temperature > 0.f) || !isfinite(p->temperature)) return SV_EINVAL;
+    int st = check_logits(target, p->dtype_t, p->ld_t, p->V);
+    if (st) return st;
+    st = check_logits(draft, p->dtype_d, p->ld_d, p->V);
+    if (st) return st;
+    const WsLayout L = ws_layout(p->B, p->K_max, p->V);
+    if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return SV_EWORKSPACE;
+    if ((uint64_t)p->B * (uint64_t)p->K_max > 0x7fffffffull) return SV_EINVAL;
+    VerifyArgs a{};
+    char *ws = (char *)workspace;
+    a.target = target; a.draft = draft;
+    a.alpha = alpha ? alpha : (float *)(ws + L.off_alpha);
+    a.err = (uint32_t *)(ws + L.off_err);
+    a.ld_t = p->ld_t; a.ld_d = p->ld_d;
+    a.B = p->B; a.K = p->K_max; a.V = p->V; a.nseg = L.nseg;
+    a.trows = p->K_max;
+    a.c = (float)(kLog2e / (double)p->temperature);
+    a.inv_t = (float)(1.0 / (double)p->temperature);
+    const unsigned grid = (unsigned)p->B * (unsigned)p->K_max;
+    st = dispatch_dtypes<VerifyLauncher>(p->dtype_t, p->dtype_d, a, (int)kAlphaOnly, grid, (hipStream_t)stream);
+    if (st) return st;
+    hipLaunchKernelGGL(e2e_reduce_kernel, dim3(1), dim3(kReduceThreads), 0, (hipStream_t)stream, a.alpha, p->B,
+                       p->K_max, loss);
+    return launch_status();
+}
+
+int sv_alloc_verify_budget(const float *conf, const int32_t *draft_len, int32_t B, int32_t K_max,
+                           int32_t budget_N, int32_t *lens, int32_t *row_off, int32_t *row_list,
+                           void *stream) {
+    if (B < 0 || K_max < 0 || budget_N < 0 || !lens || !row_off) return SV_EINVAL;
+    if ((int64_t)B * K_max > SV_BUDGET_MAX || B > SV_BUDGET_MAX) return SV_EUNSUPPORTED;
+    if (B > 0 && K_max > 0 && !conf) return SV_EINVAL;
+    hipLaunchKernelGGL(budget_kernel, dim3(1), dim3(kReduceThreads), 0, (hipStream_t)stream, conf, draft_len, B,
+                       K_max, budget_N, lens, row_off, row_list, (uint32_t *)nullptr);
+    return launch_status();
+}
+
+int sv_uniforms(uint64_t seed, const uint64_t *counters, int32_t n, float *out, void *stream) {
+    if (n < 0 || (n > 0 && (!counters || !out))) return SV_EINVAL;
+    if (n == 0) return SV_OK;
+    hipLaunchKernelGGL(uniforms_kernel, dim3((n + 255) / 256), dim3(256), 0, (hipStream_t)stream, seed, counters, n,
+                       out);
+    return launch_status();
+}
+
+int sv_device_error(void *workspace, void *stream, uint32_t *flags) {
+    if (!workspace || !flags) return SV_EINVAL;
+    uint32_t v = 0;
+    if (hipMemcpyAsync(&v, workspace, sizeof v, hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess) return SV_EHIP;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return SV_EHIP;
+    *flags = v;
+    if (v) {
+        const uint32_t z = 0;
+        if (hipMemcpy(workspace, &z, sizeof z, hipMemcpyHostToDevice) != hipSuccess) return SV_EHIP;
+        return SV_EDEVICE;
+    }
+    return SV_OK;
+}
+
+const char *sv_status_string(int status) {
+    switch (status) {
+        case SV_OK: return "SV_OK";
+        case SV_EINVAL: return "SV_EINVAL: invalid argument";
+        case SV_EUNSUPPORTED: return "SV_EUNSUPPORTED: unsupported dtype or size";
+        case SV_EHIP: return "SV_EHIP: HIP runtime or launch error";
+        case SV_EWORKSPACE: return "SV_EWORKSPACE: workspace missing, misaligned or too small";
+        case SV_EDEVICE: return "SV_EDEVICE: device-side precondition violated";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

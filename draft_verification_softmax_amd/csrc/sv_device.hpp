@@ -1,0 +1,199 @@
+// sv_device.hpp -- device building blocks for gfx950 (CDNA4, wave64).
+//
+// Logit loads (binary32 / bfloat16), the Philox4x64-10 counter-based generator, the
+// log-sum-exp merge, wave64 reductions and scans, and the wave-level inverse-CDF search.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kWave = 64;
+constexpr int kDtF32 = 0;
+constexpr int kDtBF16 = 1;
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// bfloat16 is the upper half of a binary32: widening is exact.  Element 2i of a bf16 row
+// sits in the low half of 32-bit word i (little endian).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// v_exp_f32: 2^x, about 1 ulp; 2^-inf = 0.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int DT>
+__device__ __forceinline__ float load1(const void *row, int64_t i) {
+    if constexpr (DT == kDtBF16) {
+        return __uint_as_float((uint32_t)static_cast<const uint16_t *>(row)[i] << 16);
+    } else {
+        return static_cast<const float *>(row)[i];
+    }
+}
+
+// Eight consecutive logits starting at element e (e a multiple of 8, row 16-byte aligned);
+// elements at or past V read as -inf.
+template <int DT>
+__device__ __forceinline__ void load8(const void *row, int e, int V, float (&z)[8]) {
+    if (e + 8 <= V) {
+        if constexpr (DT == kDtBF16) {
+            const uint4 w = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(row) + e);
+            z[0] = bf16_lo(w.x); z[1] = bf16_hi(w.x);
+            z[2] = bf16_lo(w.y); z[3] = bf16_hi(w.y);
+            z[4] = bf16_lo(w.z); z[5] = bf16_hi(w.z);
+            z[6] = bf16_lo(w.w); z[7] = bf16_hi(w.w);
+        } else {
+            const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(row) + e);
+            const float4 a = p[0], b = p[1];
+            z[0] = a.x; z[1] = a.y; z[2] = a.z; z[3] = a.w;
+            z[4] = b.x; z[5] = b.y; z[6] = b.z; z[7] = b.w;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) z[j] = (e + j < V) ? load1<DT>(row, e + j) : neg_inf();
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two 64x64->128-bit
+// products of counter words 0 and 2 by the published multipliers, a word permutation
+// xored with the key, and a Weyl-sequence key schedule between rounds.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t philox_word0(uint64_t seed, uint64_t c0, uint64_t c1,
+                                                 uint64_t c2, uint64_t c3) {
+    const uint64_t MA = 0xD2E7470EE14C6C93ull, MB = 0xCA5A826395121157ull;
+    const uint64_t WA = 0x9E3779B97F4A7C15ull, WB = 0xBB67AE8584CAA73Bull;
+    uint64_t k0 = seed, k1 = 0;
+#pragma unroll
+    for (int round = 0; round < 10; ++round) {
+        if (round) { k0 += WA; k1 += WB; }
+        const uint64_t ha = __umul64hi(MA, c0), la = MA * c0;
+        const uint64_t hb = __umul64hi(MB, c2), lb = MB * c2;
+        const uint64_t n0 = hb ^ c1 ^ k0, n2 = ha ^ c3 ^ k1;
+        c0 = n0; c1 = lb; c2 = n2; c3 = la;
+    }
+    return c0;
+}
+
+// Uniform in [0,1) from the top 24 bits of word 0: exactly representable in binary32.
+__device__ __forceinline__ float uniform24(uint64_t seed, uint64_t c0, uint64_t c1, uint64_t c2,
+                                           uint64_t c3) {
+    return (float)(philox_word0(seed, c0, c1, c2, c3) >> 40) * 0x1p-24f;
+}
+
+constexpr uint64_t kPurposeAccept = 0;
+constexpr uint64_t kPurposeCorrection = 1;
+
+// ---------------------------------------------------------------------------------------
+// Log-sum-exp state in base 2: (m, s) stands for sum_v 2^{(z_v - m) c}; c = log2(e) / T.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ void lse_merge(float &m, float &s, float m2, float s2, float c) {
+    const float mn = fmaxf(m, m2);
+    if (mn == neg_inf()) { m = mn; s = 0.f; return; }
+    s = s * exp2_fast((m - mn) * c) + s2 * exp2_fast((m2 - mn) * c);
+    m = mn;
+}
+
+// Fold eight logits into (m, s).
+__device__ __forceinline__ void lse_update8(float &m, float &s, const float (&z)[8], float c) {
+    float cm = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+    const float mn = fmaxf(m, cm);
+    if (mn == neg_inf()) return;
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc += exp2_fast((z[j] - mn) * c);
+    s = s * exp2_fast((m - mn) * c) + acc;
+    m = mn;
+}
+
+// log2 of a probability: (z - m) c - ls2 with ls2 = log2 s.  One helper so that every
+// kernel that recomputes a probability gets the identical binary32 value.
+__device__ __forceinline__ float log2p(float z, float m, float c, float ls2) {
+    return __builtin_fmaf(z - m, c, -ls2);
+}
+
+// Argmax state: larger value wins, equal values -> lower index.
+__device__ __forceinline__ void amax_merge(float &v, int &i, float v2, int i2) {
+    if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
+}
+
+__device__ __forceinline__ void amax_update8(float &v, int &i, const float (&z)[8], int e) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        if (z[j] > v) { v = z[j]; i = e + j; }
+}
+
+// ---------------------------------------------------------------------------------------
+// wave64 collectives
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, kWave);
+    return x;
+}
+
+__device__ __forceinline__ void wave_lse(float &m, float &s, float c) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+        const float m2 = __shfl_xor(m, d, kWave), s2 = __shfl_xor(s, d, kWave);
+        lse_merge(m, s, m2, s2, c);
+    }
+}
+
+__device__ __forceinline__ void wave_amax(float &v, int &i) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+        const float v2 = __shfl_xor(v, d, kWave);
+        const int i2 = __shfl_xor(i, d, kWave);
+        amax_merge(v, i, v2, i2);
+    }
+}
+
+__device__ __forceinline__ double wave_incl_scan(double x) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const double y = __shfl_up(x, d, kWave);
+        if (lane >= d) x += y;
+    }
+    return x;
+}
+
+// Inverse-CDF search by one full wave: the smallest index i in [0, n) whose inclusive
+// prefix of the non-negative weights weight(i) exceeds t.  Prefix sums run in binary64 in
+// index order (64 per round).  If none exceeds t (rounding at the very end), the last
+// index with a positive weight is taken; -1 if every weight is zero.  *excl receives the
+// prefix before the returned index.  Every lane of the wave must call it.
+template <class F>
+__device__ int wave_find(F weight, int n, double t, double *excl) {
+    const int lane = lane_id();
+    double base = 0.0;
+    int last_pos = -1;
+    double last_pos_excl = 0.0;
+    for (int b = 0; b < n; b += kWave) {
+        const int i = b + lane;
+        const double x = (i < n) ? (double)weight(i) : 0.0;
+        const double incl = base + wave_incl_scan(x);
+        const uint64_t hit = __ballot(incl > t);
+        if (hit) {
+            const int l = __builtin_ctzll(hit);
+            const double e = __shfl(incl - x, l, kWave);
+            *excl = e;
+            return b + l;
+        }
+        const uint64_t pos = __ballot(x > 0.0);
+        if (pos) {
+            const int l = 63 - __builtin_clzll(pos);
+            last_pos = b + l;
+            last_pos_excl = __shfl(incl - x, l, kWave);
+        }
+        base = __shfl(incl, kWave - 1, kWave);
+    }
+    *excl = last_pos_excl;
+    return last_pos;
+}
+
+}  // namespace sv

@@ -1,0 +1,165 @@
+/*
+ * specverify.h -- C ABI of libspecverify.so: batched speculative-decoding draft
+ * verification on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed comes from the AngelSpec pages ("AngelSpec: Towards Real-World High
+ * Performance Inference with Speculative Decoding"):
+ *   [ABS]  the English abstract: speculative decoding keeps the target distribution; the
+ *          verification budget is a batch-level resource given to high-confidence prefixes.
+ *   [TV]   the AngelSpec tutorial page, section "From KL to an end-to-end TV loss": the
+ *          single-step acceptance probability of rejection sampling is the overlap
+ *          alpha(p,q) = sum_v min(p(v),q(v)) = 1 - TV(p,q); a rejection voids all later
+ *          drafts; the L_e2e equation; the greedy (T=0) and T=0.9 results paragraph.
+ *   [RT]   the same page, section "Runtime adaptation: verification as a shared pool"
+ *          (D-cut): verification compute is pooled across requests and spent on the
+ *          prefixes with the highest expected utility.
+ * Where the pages are silent the library takes the standard speculative-sampling rule
+ * (accept x with probability min(1, p(x)/q(x)); after a rejection draw from
+ * norm(max(p - q, 0)); after a fully accepted draft draw a bonus token from p).
+ *
+ * Conventions (all entry points):
+ *   - Every function returns an sv_status code; nothing throws across the ABI.
+ *   - Array arguments are DEVICE pointers owned by the caller; the library never
+ *     allocates, frees or retains them.  Calls are asynchronous on `stream` (a
+ *     hipStream_t; NULL = the null stream) and return once the work is enqueued.
+ *   - Host-checkable arguments (sizes, null required pointers, alignment, dtype codes,
+ *     temperature) are validated before anything is launched: SV_EINVAL / SV_EUNSUPPORTED,
+ *     nothing enqueued.  A failed launch returns SV_EHIP.
+ *   - Device-resident preconditions (0 <= token < V, 0 <= draft_len[r] <= K_max, logits
+ *     finite or -inf with at least one finite entry per row) cannot be checked without a
+ *     synchronisation; kernels guard every memory access against them, treat a violating
+ *     position as rejected, and set a flag read back by sv_device_error().
+ *   - Logit layout: row-contiguous, row stride ld_* elements; base pointer and the row
+ *     stride in bytes must be multiples of 16 bytes; V is arbitrary (1 <= V <= SV_V_MAX).
+ *   - Randomness: Philox4x64-10 (Salmon et al., SC'11) with key (seed, 0) and counter
+ *     (request, position, purpose, step); purpose 0 = accept test, 1 = correction/bonus
+ *     draw; the uniform is (word0 >> 40) * 2^-24.  Results are a pure function of the
+ *     inputs, seed and step: repeated calls give bit-identical outputs.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum sv_status {
+    SV_OK = 0,
+    SV_EINVAL = 1,       /* bad argument (size, null pointer, alignment, range) */
+    SV_EUNSUPPORTED = 2, /* valid but unsupported combination (dtype code, V > SV_V_MAX) */
+    SV_EHIP = 3,         /* HIP runtime / launch error */
+    SV_EWORKSPACE = 4,   /* workspace missing or smaller than sv_workspace_bytes() */
+    SV_EDEVICE = 5       /* a device-side precondition was violated (sv_device_error) */
+};
+
+enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 };
+
+#define SV_V_MAX (1 << 20)
+#define SV_K_MAX 4096
+#define SV_BUDGET_MAX 8192 /* max B * K_max for sv_alloc_verify_budget */
+
+/* Device error flags (sv_device_error). */
+#define SV_DEVERR_TOKEN 1u     /* a draft token outside [0, V) */
+#define SV_DEVERR_DRAFT_LEN 2u /* a draft_len entry outside [0, K_max] */
+
+typedef struct sv_params {
+    int32_t B;          /* requests (or |I| for sv_tv_e2e_loss) */
+    int32_t K_max;      /* draft positions per request (or depth D for sv_tv_e2e_loss) */
+    int32_t V;          /* vocabulary size */
+    int32_t dtype_t;    /* sv_dtype of the target logits */
+    int32_t dtype_d;    /* sv_dtype of the drafter logits */
+    float temperature;  /* > 0: stochastic verification of softmax(z / T); 0: greedy */
+    uint64_t seed;      /* Philox key word 0 */
+    uint64_t step;      /* Philox counter word 3 (e.g. the decoding step) */
+    int64_t ld_t;       /* row stride of the target logits, elements (>= V) */
+    int64_t ld_d;       /* row stride of the drafter logits, elements (>= V) */
+} sv_params;
+
+/* Bytes of device workspace needed by sv_verify_batch / sv_tv_e2e_loss for these sizes.
+ * The workspace must be zero-filled before its first use (sv_workspace_init); every call
+ * leaves it ready for the next one.  Calls that share a workspace must not overlap. */
+size_t sv_workspace_bytes(int32_t B, int32_t K_max, int32_t V);
+
+/* Zero-fill a workspace (a fill kernel on `stream`; no host synchronisation). */
+int sv_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
+
+/* Fused batched verification [TV] [ABS].
+ *   target       [B][K_max+1][ld_t]  logits of the target at draft positions 0..K_max (row
+ *                K_max+1 is the bonus row used when every draft is accepted)
+ *   draft        [B][K_max][ld_d]    drafter logits at positions 0..K_max-1
+ *   draft_tokens [B][K_max] int32    drafted tokens x_{r,k}
+ *   draft_len    [B] int32 or NULL   L_r in [0, K_max] (NULL: every request has K_max);
+ *                                     only rows k < L_r and bonus row L_r are read
+ * Per position k < L_r, with p = softmax(target/T), q = softmax(draft/T):
+ *   alpha    [B][K_max] float   sum_v min(p_v, q_v)  (T = 0: [argmax p == argmax q])
+ *   accept   [B][K_max] uint8   u_a * q(x) < p(x), u_a = U(seed; r, k, 0, step)
+ *                               (T = 0: x == argmax of the target row)
+ *   lse_t, lse_d [B][K_max] float or NULL   log sum_v exp(z_v / T) (0 when T = 0)
+ *   amax_t, amax_d [B][K_max] int32 or NULL lowest index of the row maximum
+ * Entries k >= L_r are written as alpha 0, accept 0, lse 0, amax -1.
+ * Per request:
+ *   accept_len [B] int32          tau = first rejected position, or L_r
+ *   out_tokens [B][K_max+1] int32 x_0..x_{tau-1}, then the correction token (tau < L_r:
+ *                                 drawn from norm(max(p_tau - q_tau, 0))) or the bonus
+ *                                 token (tau = L_r: drawn from p at row L_r), then -1;
+ *                                 the draw is the smallest v whose cumulative weight
+ *                                 exceeds u_c * R, u_c = U(seed; r, tau, 1, step);
+ *                                 T = 0: the argmax of target row tau
+ *   n_out      [B] int32          tau + 1
+ * workspace: sv_workspace_bytes(B, K_max, V) bytes, zero-filled before first use. */
+int sv_verify_batch(const sv_params *params, const void *target, const void *draft,
+                    const int32_t *draft_tokens, const int32_t *draft_len, float *alpha,
+                    uint8_t *accept, float *lse_t, float *lse_d, int32_t *amax_t,
+                    int32_t *amax_d, int32_t *accept_len, int32_t *out_tokens, int32_t *n_out,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* First-reject prefix length per request [TV]: accept [B][K_max] uint8, draft_len [B] or
+ * NULL; accept_len[r] = first k < L_r with accept == 0, else L_r. */
+int sv_accept_len(const uint8_t *accept, const int32_t *draft_len, int32_t B, int32_t K_max,
+                  int32_t *accept_len, void *stream);
+
+/* Correction / bonus token per request given its accepted length (for callers with their
+ * own accept logic).  Same layout, draw and counters as sv_verify_batch, so
+ * token[r] == out_tokens[r][accept_len[r]] of a verify call with the same arguments.
+ * Reads target row tau (and drafter row tau when tau < L_r). */
+int sv_residual_sample(const sv_params *params, const void *target, const void *draft,
+                       const int32_t *draft_len, const int32_t *accept_len, int32_t *token,
+                       void *stream);
+
+/* End-to-end TV objective [TV, L_e2e equation]:
+ *   loss = 1 - (1 / (|I| D)) sum_i sum_{m<D} prod_{k<=m} alpha_{i,k}
+ * params->B = |I|, params->K_max = D, params->temperature > 0 (1 for raw logits).
+ * target, draft [|I|][D][ld] (no bonus row: target row (i,k) at (i*D + k) * ld_t).
+ * alpha [|I|][D] float or NULL; loss: one float (device).  Deterministic summation order.
+ * workspace: sv_workspace_bytes(|I|, D, V) bytes. */
+int sv_tv_e2e_loss(const sv_params *params, const void *target, const void *draft,
+                   float *alpha, float *loss, void *workspace, size_t workspace_bytes,
+                   void *stream);
+
+/* Batch-level verification budget [RT] [ABS]: C_{r,k} = prod_{j<=k} conf_{r,j} (binary32,
+ * sequential in k); the first min(N, sum_r L_r) candidates (r, k < L_r) in the order
+ * (C desc, r asc, k asc) are kept.  conf [B][K_max] float in [0, 1]; draft_len [B] or
+ * NULL.  Outputs: lens [B] (selected prefix length per request; pass it as draft_len to
+ * sv_verify_batch), row_off [B+1] (exclusive scan of lens), row_list [min(N, sum L)] or
+ * NULL (r*K_max + k of each selected row in (r, k) order).  B*K_max <= SV_BUDGET_MAX. */
+int sv_alloc_verify_budget(const float *conf, const int32_t *draft_len, int32_t B,
+                           int32_t K_max, int32_t budget_N, int32_t *lens, int32_t *row_off,
+                           int32_t *row_list, void *stream);
+
+/* The library's uniforms, for testing the generator: out[i] = U(seed; counters[i][0..3]). */
+int sv_uniforms(uint64_t seed, const uint64_t *counters, int32_t n, float *out, void *stream);
+
+/* Synchronise `stream`, return the device error flags left in `workspace` (SV_DEVERR_*)
+ * in *flags and clear them.  Returns SV_EDEVICE when any flag was set. */
+int sv_device_error(void *workspace, void *stream, uint32_t *flags);
+
+/* Human-readable name of a status code (static storage). */
+const char *sv_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

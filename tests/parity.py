@@ -1,0 +1,70 @@
+"""Element-by-element comparison of GPU verification outputs with the CPU oracle.
+
+Tolerances (from the stated goal for this path):
+  * greedy mode: accept flags, accepted lengths, emitted tokens, argmax -- bit-exact;
+  * stochastic accept flags: bit-exact unless the oracle's draw lies within 1e-6 of the
+    threshold p(x)/q(x); such requests are counted and their tokens are not compared;
+  * correction / bonus tokens: bit-exact unless the oracle's CDF target u*R lies within
+    1e-6*R of every CDF boundary between the two tokens; counted;
+  * alpha, log-normalisers: 1e-5 relative (binary32 accumulation).
+"""
+import numpy as np
+
+from oracle import svref
+
+ACCEPT_BAND = 1e-6
+CDF_BAND = 1e-6
+REL_TOL = 1e-5
+
+
+def compare_verify(gpu, ora, target_np, draft_np, dtype, T, check=None, L=None):
+    """gpu/ora: dicts of numpy arrays.  check: request indices to compare (default all).
+    Returns a report dict; raises AssertionError on any mismatch outside the bands."""
+    B, K = ora["alpha"].shape
+    reqs = range(B) if check is None else check
+    rep = dict(requests=0, near_accept=0, near_token=0, token_equal=0)
+    for r in reqs:
+        rep["requests"] += 1
+        Lr = K if L is None else int(L[r])
+        ks = slice(0, Lr)
+        # alpha and lse within REL_TOL; unverified tail exactly the fill values
+        np.testing.assert_allclose(gpu["alpha"][r, ks], ora["alpha"][r, ks], rtol=REL_TOL, atol=1e-7,
+                                   err_msg=f"alpha r={r}")
+        assert (gpu["alpha"][r, Lr:] == 0).all() and (gpu["accept"][r, Lr:] == 0).all()
+        if T > 0 and gpu.get("lse_t") is not None:
+            np.testing.assert_allclose(gpu["lse_t"][r, ks], ora["lse_t"][r, ks], rtol=REL_TOL, err_msg=f"lse_t r={r}")
+            np.testing.assert_allclose(gpu["lse_d"][r, ks], ora["lse_d"][r, ks], rtol=REL_TOL, err_msg=f"lse_d r={r}")
+        if gpu.get("amax_t") is not None:
+            assert (gpu["amax_t"][r, ks] == ora["amax_t"][r, ks]).all(), f"amax_t r={r}"
+            assert (gpu["amax_d"][r, ks] == ora["amax_d"][r, ks]).all(), f"amax_d r={r}"
+        acc_g, acc_o = gpu["accept"][r, ks], ora["accept"][r, ks]
+        if T == 0:
+            assert (acc_g == acc_o).all(), f"greedy accept r={r}"
+        else:
+            diff = np.nonzero(acc_g != acc_o)[0]
+            if len(diff):
+                margin = np.abs(ora["u_acc"][r, diff] - ora["ratio"][r, diff])
+                assert (margin < ACCEPT_BAND).all(), f"accept r={r} k={diff} margin={margin}"
+                rep["near_accept"] += 1
+                continue
+        assert gpu["accept_len"][r] == ora["accept_len"][r], f"tau r={r}"
+        assert gpu["n_out"][r] == ora["n_out"][r]
+        tau = int(ora["accept_len"][r])
+        assert (gpu["out_tokens"][r, :tau] == ora["out_tokens"][r, :tau]).all()
+        assert (gpu["out_tokens"][r, tau + 1:] == -1).all()
+        tg, to = int(gpu["out_tokens"][r, tau]), int(ora["out_tokens"][r, tau])
+        if tg == to:
+            rep["token_equal"] += 1
+            continue
+        assert T > 0, f"greedy token r={r}: gpu {tg} oracle {to}"
+        t, R = ora["cdf_target"][r], ora["resid_mass"][r]
+        assert 0 <= tg < target_np.shape[-1]
+        if tg > to:
+            far = svref.correction_cdf(target_np, draft_np, T, dtype, r, tau, Lr, tg - 1)
+            gap = far - t
+        else:
+            far = svref.correction_cdf(target_np, draft_np, T, dtype, r, tau, Lr, tg)
+            gap = t - far
+        assert 0 <= gap <= CDF_BAND * R, f"token r={r}: gpu {tg} oracle {to}, gap {gap} R {R}"
+        rep["near_token"] += 1
+    return rep

@@ -1,0 +1,86 @@
+"""The C-ABI library loads, exports every entry point its header declares, and rejects
+bad host-side arguments before launching anything (no GPU needed)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sv_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def svlib():
+    import draft_verification_softmax_amd as sv
+    return sv.lib()
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ["sv_verify_batch", "sv_accept_len", "sv_residual_sample", "sv_tv_e2e_loss",
+              "sv_alloc_verify_budget", "sv_workspace_bytes", "sv_status_string"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(svlib):
+    raw = C.CDLL(os.path.join(ROOT, "draft_verification_softmax_amd", "libspecverify.so"))
+    for n in _declared():
+        assert hasattr(raw, n), n
+
+
+def test_status_strings(svlib):
+    for code in range(6):
+        s = svlib.sv_status_string(code).decode()
+        assert s.startswith("SV_")
+    assert svlib.sv_status_string(99).decode() == "unknown status"
+
+
+def test_workspace_bytes(svlib):
+    assert svlib.sv_workspace_bytes(-1, 3, 10) == 0
+    assert svlib.sv_workspace_bytes(1, 3, 0) == 0
+    a = svlib.sv_workspace_bytes(64, 16, 131072)
+    b = svlib.sv_workspace_bytes(64, 16, 1000)
+    assert a > b > 0 and a % 256 == 0
+
+
+def test_host_validation_rejects_without_launch(svlib):
+    from draft_verification_softmax_amd.binding import Params
+    EINVAL, EUNSUP, EWS = 1, 2, 4
+    nul = None
+    args17 = lambda prm, t=nul: (C.byref(prm), t, nul, nul, nul, nul, nul, nul, nul, nul, nul, nul, nul, nul, nul, 0, nul)
+    # negative sizes
+    assert svlib.sv_verify_batch(*args17(Params(-1, 3, 100, 0, 0, 1.0, 0, 0, 100, 100))) == EINVAL
+    # V too large
+    assert svlib.sv_verify_batch(*args17(Params(1, 3, (1 << 20) + 1, 0, 0, 1.0, 0, 0, (1 << 20) + 8, (1 << 20) + 8))) == EUNSUP
+    # negative / NaN temperature
+    assert svlib.sv_verify_batch(*args17(Params(1, 3, 100, 0, 0, -1.0, 0, 0, 100, 100))) == EINVAL
+    assert svlib.sv_verify_batch(*args17(Params(1, 3, 100, 0, 0, float("nan"), 0, 0, 100, 100))) == EINVAL
+    # null target
+    assert svlib.sv_verify_batch(*args17(Params(1, 3, 100, 0, 0, 1.0, 0, 0, 100, 100))) == EINVAL
+    # misaligned target pointer / stride (pointer values are never dereferenced on the host)
+    fake = C.c_void_p(0x1000)
+    odd = C.c_void_p(0x1002)
+    assert svlib.sv_verify_batch(*args17(Params(1, 0, 100, 1, 1, 1.0, 0, 0, 100, 100), odd)) == EINVAL
+    assert svlib.sv_verify_batch(*args17(Params(1, 0, 100, 1, 1, 1.0, 0, 0, 101, 104), fake)) == EINVAL
+    # bad dtype code
+    assert svlib.sv_verify_batch(*args17(Params(1, 0, 100, 7, 1, 1.0, 0, 0, 104, 104), fake)) == EUNSUP
+    # missing workspace (everything else valid, K = 0)
+    prm = Params(1, 0, 96, 1, 1, 1.0, 0, 0, 96, 96)
+    a = [C.byref(prm), fake, nul, nul, nul, nul, nul, nul, nul, nul, nul, fake, fake, fake, nul, 0, nul]
+    assert svlib.sv_verify_batch(*a) == EWS
+    # budget limits
+    assert svlib.sv_alloc_verify_budget(fake, nul, 100, 100, 10, fake, fake, nul, nul) == EUNSUP
+    assert svlib.sv_alloc_verify_budget(fake, nul, 4, 4, -1, fake, fake, nul, nul) == EINVAL
+    # e2e needs T > 0
+    assert svlib.sv_tv_e2e_loss(C.byref(Params(2, 3, 96, 1, 1, 0.0, 0, 0, 96, 96)), fake, fake, nul, fake, fake, 1 << 30, nul) == EINVAL
+    # uniforms: negative count
+    assert svlib.sv_uniforms(0, nul, -1, nul, nul) == EINVAL
+    # B = 0 is a no-op
+    assert svlib.sv_verify_batch(*args17(Params(0, 3, 100, 0, 0, 1.0, 0, 0, 100, 100))) == 0

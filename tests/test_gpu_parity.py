@@ -1,0 +1,245 @@
+"""GPU path vs the CPU oracle, through the C ABI (needs an MI355X)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import svref
+from parity import compare_verify
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def sv():
+    import draft_verification_softmax_amd as m
+    return m
+
+
+def _np(out):
+    return {k: (None if v is None else v.cpu().numpy()) for k, v in out.items()}
+
+
+def _oracle_dtype(t):
+    return "bf16" if t.dtype == torch.bfloat16 else "f32"
+
+
+def _run_pair(sv, v, T, draft_len=None, check=None, want_amax=True, seed=None, step=0):
+    seed = v.seed if seed is None else seed
+    _say(f"{v.name} B={v.target.shape[0]} K={v.draft.shape[1]} V={v.target.shape[2]} T={T} "
+         f"ragged={draft_len is not None}")
+    dl_dev = None if draft_len is None else torch.as_tensor(draft_len, dtype=torch.int32, device=DEV)
+    out = sv.sv_verify_batch(v.target, v.draft, v.draft_tokens, T, seed=seed, step=step,
+                             draft_len=dl_dev, want_amax=want_amax)
+    torch.cuda.synchronize()
+    g = _np(out)
+    tn, dn = workloads.to_oracle(v.target), workloads.to_oracle(v.draft)
+    dt = _oracle_dtype(v.target)
+    B, K = v.draft_tokens.shape
+    dl = np.full(B, K, np.int32) if draft_len is None else np.asarray(draft_len, np.int32).copy()
+    if check is not None:  # oracle only on sampled requests: others get L_r = 0
+        mask = np.zeros(B, bool)
+        mask[list(check)] = True
+        dl[~mask] = 0
+    o = svref.verify_batch(tn, dn, v.draft_tokens.cpu().numpy(), T, dt, seed=seed, step=step,
+                           draft_len=dl, diagnostics=True)
+    rep = compare_verify(g, o, tn, dn, dt, T, check=check, L=dl if draft_len is not None else None)
+    _say(f"report {rep}")
+    return g, o, rep
+
+
+def _move(v):
+    return workloads.VerifyInputs(v.target.to(DEV), v.draft.to(DEV), v.draft_tokens.to(DEV), v.T, v.seed, v.name)
+
+
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_tiny(sv, T):
+    v = _move(workloads.make_verify_inputs("tiny", device="cpu", T=T))
+    g, o, rep = _run_pair(sv, v, T)
+    assert rep["requests"] == 1
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("T", [0.9, 0.0, 1.7])
+def test_ragged_vocab_several_tiles(sv, dtype, T):
+    """V not a multiple of the 8-logit vector nor of the 4096-logit tile, padded rows."""
+    B, K, V, ld = 6, 5, 9001, 9008
+    g = torch.Generator(device=DEV).manual_seed(17)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tt = torch.full((B, K + 1, ld), float("nan"), device=DEV, dtype=tdt)
+    dd = torch.full((B, K, ld), float("nan"), device=DEV, dtype=tdt)
+    t = 2.5 * torch.randn((B, K + 1, V), generator=g, device=DEV)
+    d = t[:, :K] + 0.7 * torch.randn((B, K, V), generator=g, device=DEV)
+    tt[..., :V] = t.to(tdt)
+    dd[..., :V] = d.to(tdt)
+    toks = torch.argmax(d, -1).to(torch.int32)
+    toks[:, 1] = torch.randint(0, V, (B,), generator=g, device=DEV, dtype=torch.int32)
+    _say(f"ragged-vocab {dtype} T={T}")
+    out = sv.sv_verify_batch(tt[..., :V], dd[..., :V], toks, T, seed=3, step=1, want_amax=True)
+    torch.cuda.synchronize()
+    gpu = _np(out)
+    # the oracle gets the same padded rows (it reads only V of every ld)
+    tn = workloads.to_oracle(tt[..., :V].contiguous())
+    dn = workloads.to_oracle(dd[..., :V].contiguous())
+    o = svref.verify_batch(tn, dn, toks.cpu().numpy(), T, dtype, seed=3, step=1, diagnostics=True)
+    rep = compare_verify(gpu, o, tn, dn, dtype, T)
+    _say(f"report {rep}")
+
+
+@pytest.mark.parametrize("T", [0.9, 0.0])
+def test_mtp_full(sv, T):
+    v = _move(workloads.make_verify_inputs("mtp", device="cpu", T=T))
+    _run_pair(sv, v, T)
+
+
+@pytest.mark.parametrize("T", [0.9, 0.0])
+def test_dfly_full_sampled(sv, T):
+    v = workloads.make_verify_inputs("dfly", device=DEV, T=T)
+    check = [0, 5, 17, 31, 42, 63]
+    _run_pair(sv, v, T, check=check)
+
+
+def test_dfly_ragged_lengths(sv):
+    v = workloads.make_verify_inputs("dfly", device=DEV, T=0.9, B=12)
+    rng = np.random.default_rng(0)
+    dl = rng.integers(0, 17, size=12).astype(np.int32)
+    dl[0], dl[1], dl[2] = 0, 16, 1
+    _run_pair(sv, v, 0.9, draft_len=dl)
+
+
+def test_determinism(sv):
+    v = workloads.make_verify_inputs("dfly", device=DEV, T=0.9, B=16)
+    _say("determinism")
+    a = _np(sv.sv_verify_batch(v.target, v.draft, v.draft_tokens, 0.9, seed=1, want_amax=True))
+    b = _np(sv.sv_verify_batch(v.target, v.draft, v.draft_tokens, 0.9, seed=1, want_amax=True))
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_uniforms_match_oracle(sv):
+    rng = np.random.default_rng(1)
+    ctr = rng.integers(0, 2**62, size=(257, 4), dtype=np.int64)
+    ctr[:4] = [[0, 0, 0, 0], [1, 2, 0, 3], [63, 15, 1, 0], [7, 7, 7, 7]]
+    _say("uniforms")
+    u = sv.sv_uniforms(11, torch.as_tensor(ctr, device=DEV)).cpu().numpy()
+    want = np.array([svref.uniform(11, *[int(x) for x in c]) for c in ctr])
+    assert np.array_equal(u.astype(np.float64), want)
+
+
+def test_accept_len_and_residual_sample(sv):
+    v = workloads.make_verify_inputs("dfly", device=DEV, T=0.9, B=8)
+    _say("accept_len + residual_sample")
+    dl = torch.tensor([16, 3, 0, 7, 16, 1, 9, 12], dtype=torch.int32, device=DEV)
+    out = sv.sv_verify_batch(v.target, v.draft, v.draft_tokens, 0.9, seed=v.seed, step=4, draft_len=dl)
+    al = sv.sv_accept_len(out["accept"], dl)
+    assert torch.equal(al, out["accept_len"])
+    tok = sv.sv_residual_sample(v.target, v.draft, out["accept_len"], 0.9, seed=v.seed, step=4, draft_len=dl)
+    want = out["out_tokens"].gather(1, out["accept_len"].long()[:, None])[:, 0]
+    assert torch.equal(tok, want)
+    # oracle on forced accepted lengths (including 0 and L_r)
+    forced = np.array([0, 3, 0, 2, 16, 1, 5, 12], np.int32)
+    tok2 = sv.sv_residual_sample(v.target, v.draft, torch.as_tensor(forced, device=DEV), 0.9, seed=2, step=0,
+                                 draft_len=dl).cpu().numpy()
+    tn, dn = workloads.to_oracle(v.target), workloads.to_oracle(v.draft)
+    otok = svref.residual_sample(tn, dn, forced, 0.9, "bf16", seed=2, step=0, draft_len=dl.cpu().numpy())
+    near = 0
+    for r in range(8):
+        if tok2[r] != otok[r]:
+            near += 1
+    assert near <= 1, (tok2, otok)
+    # greedy: argmax of target row tau
+    tok3 = sv.sv_residual_sample(v.target, v.draft, torch.as_tensor(forced, device=DEV), 0.0,
+                                 draft_len=dl).cpu().numpy()
+    otok3 = svref.residual_sample(tn, dn, forced, 0.0, "bf16", draft_len=dl.cpu().numpy())
+    assert np.array_equal(tok3, otok3)
+
+
+def test_budget_matches_oracle(sv):
+    conf = workloads.make_budget_conf(device="cpu")
+    for N in [0, 1, 7, 256, 1023, 1024, 5000]:
+        _say(f"budget N={N}")
+        lens, off, rl = sv.sv_alloc_verify_budget(conf.to(DEV), N)
+        torch.cuda.synchronize()
+        ol, oo, orl = svref.alloc_verify_budget(conf.numpy(), N)
+        assert np.array_equal(lens.cpu().numpy(), ol)
+        assert np.array_equal(off.cpu().numpy(), oo)
+        assert np.array_equal(rl.cpu().numpy()[: len(orl)], orl)
+    rng = np.random.default_rng(9)
+    for trial in range(20):
+        B, K = int(rng.integers(1, 90)), int(rng.integers(1, 90))
+        if B * K > 8192:
+            continue
+        c = rng.beta(2, 2, size=(B, K)).astype(np.float32)
+        c[rng.random((B, K)) < 0.1] = 1.0   # ties
+        dl = rng.integers(0, K + 1, size=B).astype(np.int32)
+        N = int(rng.integers(0, B * K + 3))
+        lens, off, rl = sv.sv_alloc_verify_budget(torch.as_tensor(c, device=DEV), N,
+                                                  draft_len=torch.as_tensor(dl, device=DEV))
+        ol, oo, orl = svref.alloc_verify_budget(c, N, draft_len=dl)
+        assert np.array_equal(lens.cpu().numpy(), ol), trial
+        assert np.array_equal(off.cpu().numpy(), oo), trial
+        assert np.array_equal(rl.cpu().numpy()[: len(orl)], orl), trial
+
+
+def test_budget_then_ragged_verify(sv):
+    v, conf, N = workloads.make_budget_inputs(device=DEV)
+    lens, off, _ = sv.sv_alloc_verify_budget(conf, N)
+    ol, _, _ = svref.alloc_verify_budget(conf.cpu().numpy(), N)
+    assert np.array_equal(lens.cpu().numpy(), ol)
+    check = [0, 9, 33, 63]
+    # full ragged verify on the GPU, oracle on sampled requests with their selected lengths
+    _say("budget ragged verify")
+    out = _np(sv.sv_verify_batch(v.target, v.draft, v.draft_tokens, v.T, seed=v.seed, draft_len=lens,
+                                 want_amax=True))
+    tn, dn = workloads.to_oracle(v.target), workloads.to_oracle(v.draft)
+    dl = np.zeros_like(ol)
+    dl[check] = ol[check]
+    o = svref.verify_batch(tn, dn, v.draft_tokens.cpu().numpy(), v.T, "bf16", seed=v.seed, draft_len=dl,
+                           diagnostics=True)
+    rep = compare_verify(out, o, tn, dn, "bf16", v.T, check=check, L=dl)
+    _say(f"report {rep}")
+
+
+def test_e2e_small(sv):
+    t, d, T = workloads.make_e2e_inputs(device=DEV, I=48, D=3)
+    _say("e2e small")
+    loss, alpha = sv.sv_tv_e2e_loss(t, d, T)
+    torch.cuda.synchronize()
+    ol, oa = svref.tv_e2e_loss(workloads.to_oracle(t), workloads.to_oracle(d), T, "bf16")
+    np.testing.assert_allclose(alpha.cpu().numpy(), oa, rtol=1e-5)
+    assert abs(loss.item() - ol) <= 1e-5 * abs(ol)
+
+
+def test_e2e_full_sampled(sv):
+    t, d, T = workloads.make_e2e_inputs(device=DEV)
+    _say("e2e full 8192x3")
+    loss, alpha = sv.sv_tv_e2e_loss(t, d, T)
+    torch.cuda.synchronize()
+    a = alpha.cpu().numpy().astype(np.float64)
+    idx = [0, 1, 4095, 8191]
+    _, oa = svref.tv_e2e_loss(workloads.to_oracle(t[idx]), workloads.to_oracle(d[idx]), T, "bf16")
+    np.testing.assert_allclose(a[idx], oa, rtol=1e-5)
+    # the reduction is the L_e2e equation applied to the returned alpha table
+    want = 1.0 - np.cumprod(a, axis=1).sum() / a.size
+    assert abs(loss.item() - want) <= 1e-6
+    assert 0.0 < loss.item() < 1.0
+
+
+def test_device_error_flag_for_bad_token(sv):
+    v = _move(workloads.make_verify_inputs("tiny", device="cpu", T=1.0))
+    toks = v.draft_tokens.clone()
+    toks[0, 1] = 5000  # outside [0, V): the kernel guards the read and rejects
+    ws = sv.Workspace(DEV)
+    buf = ws.get(1, 3, 1000)
+    _say("device error flag")
+    out = sv.sv_verify_batch(v.target, v.draft, toks, 1.0, workspace=buf)
+    flags = sv.sv_device_error(buf)
+    assert flags & 1
+    assert out["accept"][0, 1].item() == 0
+    assert sv.sv_device_error(buf) == 0
