@@ -1,12 +1,8 @@
 // specverify.hip -- batched speculative-decoding draft verification for MI355X (gfx950).
 //
 // Kernels (all wave64):
-//   verify_rows_kernel   one workgroup per (request, draft position) row pair; sweep 1
-//                        reduces both rows to their base-2 log-normalisers (and argmax),
-//                        sweep 2 sums min(p, q) and the per-segment residual mass; the
-//                        accept test reads p(x), q(x); the last row of a request to finish
-//                        runs the request's finalize (first-reject scan, correction or
-//                        bonus draw by inverse CDF over one re-read segment).
+//   team_kernel          (team_kernel.hip) fused verification and L_e2e alpha: one team
+//                        of workgroups per row pair, each row read from HBM once.
 //   residual_kernel      stand-alone correction/bonus draw per request.
 //   e2e_reduce_kernel    L_e2e from the alpha table, fixed summation order.
 //   budget_kernel        cumulative confidences, sort, selected prefix lengths.
@@ -24,6 +20,7 @@
 
 #include "sv_device.hpp"
 #include "specverify.h"
+#include "team.hpp"
 
 namespace sv {
 
@@ -33,36 +30,7 @@ constexpr int kElems = 8;                     // logits per lane per tile (one 1
 constexpr int kTile = kThreads * kElems;      // 4096 logits per tile
 constexpr int kSeg = kWave * kElems;          // 512: one wave's contiguous share of a tile
 
-enum Mode { kStoch = 0, kGreedy = 1, kAlphaOnly = 2 };
-
-struct RowRec {            // per verified row, in the workspace (32 bytes)
-    float m_t, ls2_t;      // target row: max logit, log2 sum 2^{(z-m)c}
-    float m_d, ls2_d;      // drafter row
-    int32_t amax_t;        // target argmax (greedy correction token)
-    int32_t acc;           // accept flag
-    int32_t pad[2];
-};
-
-// Workspace layout shared by the host functions and the kernels.
-struct WsLayout {
-    size_t off_err, off_cnt, off_rec, off_dir, off_alpha, total;
-    int nseg;
-};
-
-__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-__host__ __device__ inline WsLayout ws_layout(int B, int K, int V) {
-    WsLayout w;
-    w.nseg = (V + kSeg - 1) / kSeg;
-    w.off_err = 0;
-    w.off_cnt = 256;
-    w.off_rec = align256(w.off_cnt + sizeof(int32_t) * (size_t)(B > 0 ? B : 1));
-    w.off_dir = align256(w.off_rec + sizeof(RowRec) * (size_t)B * (size_t)K);
-    w.off_alpha = align256(w.off_dir + sizeof(float) * 2 * (size_t)w.nseg * (size_t)B * (size_t)(K + 1));
-    w.total = align256(w.off_alpha + sizeof(float) * (size_t)B * (size_t)K);
-    return w;
-}
-
+// Arguments of the stand-alone correction/bonus sampler.
 struct VerifyArgs {
     const void *target, *draft;
     const int32_t *tokens, *draft_len;
@@ -72,9 +40,6 @@ struct VerifyArgs {
     int32_t *amax_t, *amax_d;
     int32_t *accept_len, *out_tokens, *n_out;
     uint32_t *err;
-    int32_t *cnt;
-    RowRec *rec;
-    float *dir;
     int64_t ld_t, ld_d;
     int32_t B, K, V, nseg;
     int32_t trows;         // target rows per request: K+1 (verify) or K (e2e)
@@ -226,226 +191,6 @@ __device__ int draw_from_row(const void *row, int V, float c, float u, float *se
     }
     __syncthreads();
     return s_tok;
-}
-
-// ---------------------------------------------------------------------------------------
-// Verification rows
-// ---------------------------------------------------------------------------------------
-
-template <int DTT, int DTD, int MODE>
-__device__ void finalize_request(const VerifyArgs &a, int r, int L, Red &red) {
-    __shared__ int s_tau, s_tok;
-    const int K = a.K;
-    // tau = first rejected position < L (min over the flags of the L rows)
-    int tau = L;
-    for (int k = threadIdx.x; k < L; k += kThreads)
-        if (!a.rec[(size_t)r * K + k].acc) { tau = min(tau, k); }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) tau = min(tau, __shfl_xor(tau, d, kWave));
-    if (threadIdx.x == 0) s_tau = L;
-    __syncthreads();
-    if (lane_id() == 0) atomicMin(&s_tau, tau);
-    __syncthreads();
-    tau = s_tau;
-
-    // positions that were not verified
-    for (int k = L + threadIdx.x; k < K; k += kThreads) {
-        const size_t i = (size_t)r * K + k;
-        a.alpha[i] = 0.f;
-        a.accept[i] = 0;
-        if (a.lse_t) a.lse_t[i] = 0.f;
-        if (a.lse_d) a.lse_d[i] = 0.f;
-        if (a.amax_t) a.amax_t[i] = -1;
-        if (a.amax_d) a.amax_d[i] = -1;
-    }
-
-    int tok;
-    if constexpr (MODE == kGreedy) {
-        if (tau < L) tok = a.rec[(size_t)r * K + tau].amax_t;
-        else tok = row_argmax<DTT>(row_at<DTT>(a.target, (int64_t)r * a.trows + tau, a.ld_t), a.V, red);
-    } else {
-        const float u = uniform24(a.seed, (uint64_t)r, (uint64_t)tau, kPurposeCorrection, a.step);
-        float *seg = a.dir + (size_t)((size_t)r * (K + 1) + tau) * 2 * a.nseg;
-        const void *trow = row_at<DTT>(a.target, (int64_t)r * a.trows + tau, a.ld_t);
-        bool done = false;
-        tok = 0;
-        if (tau < L) {
-            // residual norm(max(p - q, 0)): segment masses were written by sweep 2
-            double part = 0.0;
-            for (int j = threadIdx.x; j < a.nseg; j += kThreads) part += (double)seg[j];
-            const double R = block_sum_d(part, red);
-            if (R > 0.0) {
-                const RowRec rr = a.rec[(size_t)r * K + tau];
-                const void *drow = row_at<DTD>(a.draft, (int64_t)r * K + tau, a.ld_d);
-                if (threadIdx.x < kWave) {
-                    const double t = (double)u * R;
-                    double ex;
-                    int sidx = wave_find([&](int j) { return seg[j]; }, a.nseg, t, &ex);
-                    int tk = 0;
-                    if (sidx >= 0) {
-                        const int e0 = sidx * kSeg;
-                        const int n = min(kSeg, a.V - e0);
-                        double ex2;
-                        const float c = a.c;
-                        tk = wave_find(
-                            [&](int j) {
-                                const float p = exp2_fast(log2p(load1<DTT>(trow, e0 + j), rr.m_t, c, rr.ls2_t));
-                                const float q = exp2_fast(log2p(load1<DTD>(drow, e0 + j), rr.m_d, c, rr.ls2_d));
-                                return p - fminf(p, q);
-                            },
-                            n, t - ex, &ex2);
-                        tk = tk < 0 ? e0 : e0 + tk;
-                    }
-                    if (threadIdx.x == 0) s_tok = tk;
-                }
-                __syncthreads();
-                tok = s_tok;
-                done = true;
-            }
-        }
-        if (!done) tok = draw_from_row<DTT>(trow, a.V, a.c, u, seg, a.nseg, red);
-    }
-
-    int32_t *o = a.out_tokens + (size_t)r * (K + 1);
-    for (int j = threadIdx.x; j <= K; j += kThreads)
-        o[j] = j < tau ? a.tokens[(size_t)r * K + j] : (j == tau ? tok : -1);
-    if (threadIdx.x == 0) {
-        a.accept_len[r] = tau;
-        a.n_out[r] = tau + 1;
-    }
-}
-
-template <int DTT, int DTD, int MODE>
-__global__ __launch_bounds__(kThreads) void verify_rows_kernel(VerifyArgs a) {
-    __shared__ Red red;
-    __shared__ int s_last;
-    const int K = a.K;
-    const int slots = K > 0 ? K : 1;
-    const int r = blockIdx.x / slots;
-    const int k = blockIdx.x % slots;
-    int L = K;
-    if (MODE != kAlphaOnly && a.draft_len) {
-        L = a.draft_len[r];
-        if (L < 0 || L > K) {
-            if (threadIdx.x == 0 && k == 0) atomicOr(a.err, SV_DEVERR_DRAFT_LEN);
-            L = L < 0 ? 0 : K;
-        }
-    }
-    if (k >= L) {
-        if (MODE != kAlphaOnly && L == 0 && k == 0) finalize_request<DTT, DTD, MODE>(a, r, 0, red);
-        return;
-    }
-    const int V = a.V;
-    const float c = a.c;
-    const int64_t trow_idx = (int64_t)r * a.trows + k, drow_idx = (int64_t)r * K + k;
-    const void *trow = row_at<DTT>(a.target, trow_idx, a.ld_t);
-    const void *drow = row_at<DTD>(a.draft, drow_idx, a.ld_d);
-
-    // sweep 1: base-2 log-normalisers (and argmax) of both rows
-    float mt = neg_inf(), st = 0.f, md = neg_inf(), sd = 0.f;
-    float vt = neg_inf(), vd = neg_inf();
-    int it = 0x7fffffff, id = 0x7fffffff;
-    const bool want_amax = (MODE == kGreedy) || a.want_amax;
-    for (int base = 0; base < V; base += kTile) {
-        const int e = base + threadIdx.x * kElems;
-        float zt[8], zd[8];
-        load8<DTT>(trow, e, V, zt);
-        load8<DTD>(drow, e, V, zd);
-        if constexpr (MODE != kGreedy) {
-            lse_update8(mt, st, zt, c);
-            lse_update8(md, sd, zd, c);
-        }
-        if (want_amax) {
-            amax_update8(vt, it, zt, e);
-            amax_update8(vd, id, zd, e);
-        }
-    }
-    if constexpr (MODE != kGreedy) block_lse2(mt, st, md, sd, c, red);
-    if (want_amax) {
-        block_amax2(vt, it, vd, id, red);
-        if (it == 0x7fffffff) it = 0;
-        if (id == 0x7fffffff) id = 0;
-    }
-    const float ls2t = (MODE != kGreedy) ? log2f(st) : 0.f;
-    const float ls2d = (MODE != kGreedy) ? log2f(sd) : 0.f;
-
-    // sweep 2: alpha = sum min(p, q) and per-segment residual mass sum max(p - q, 0)
-    float alpha = 0.f;
-    if constexpr (MODE != kGreedy) {
-        const int w = threadIdx.x / kWave;
-        float *seg = (MODE == kStoch) ? a.dir + (size_t)((size_t)r * (K + 1) + k) * 2 * a.nseg : nullptr;
-        float asum = 0.f;
-        int itn = 0;
-        for (int base = 0; base < V; base += kTile, ++itn) {
-            const int e = base + threadIdx.x * kElems;
-            float zt[8], zd[8];
-            load8<DTT>(trow, e, V, zt);
-            load8<DTD>(drow, e, V, zd);
-            float res = 0.f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float p = exp2_fast(log2p(zt[j], mt, c, ls2t));
-                const float q = exp2_fast(log2p(zd[j], md, c, ls2d));
-                const float mn = fminf(p, q);
-                asum += mn;
-                res += p - mn;
-            }
-            if constexpr (MODE == kStoch) {
-                res = wave_sum(res);
-                const int sidx = itn * kWaves + w;
-                if (lane_id() == 0 && sidx < a.nseg) seg[sidx] = res;
-            }
-        }
-        alpha = block_sum(asum, red);
-    }
-
-    if constexpr (MODE == kAlphaOnly) {
-        if (threadIdx.x == 0) a.alpha[(size_t)r * K + k] = alpha;
-        return;
-    } else {
-        if (threadIdx.x == 0) {
-            const size_t i = (size_t)r * K + k;
-            int x = a.tokens[i];
-            bool ok = (x >= 0 && x < V);
-            if (!ok) atomicOr(a.err, SV_DEVERR_TOKEN);
-            int acc = 0;
-            if constexpr (MODE == kGreedy) {
-                acc = ok && x == it;
-                alpha = (it == id) ? 1.f : 0.f;
-            } else {
-                if (ok) {
-                    // accept iff u * q(x) < p(x), i.e. u < 2^{log2 p(x) - log2 q(x)}
-                    const float lpt = log2p(load1<DTT>(trow, x), mt, c, ls2t);
-                    const float lpd = log2p(load1<DTD>(drow, x), md, c, ls2d);
-                    const float u = uniform24(a.seed, (uint64_t)r, (uint64_t)k, kPurposeAccept, a.step);
-                    acc = u < exp2f(lpt - lpd);
-                }
-            }
-            a.alpha[i] = alpha;
-            a.accept[i] = (uint8_t)acc;
-            if (a.lse_t) a.lse_t[i] = (MODE == kStoch) ? (float)((double)mt * a.inv_t + (double)ls2t * 0.6931471805599453) : 0.f;
-            if (a.lse_d) a.lse_d[i] = (MODE == kStoch) ? (float)((double)md * a.inv_t + (double)ls2d * 0.6931471805599453) : 0.f;
-            if (a.amax_t) a.amax_t[i] = want_amax ? it : -1;
-            if (a.amax_d) a.amax_d[i] = want_amax ? id : -1;
-            RowRec rr;
-            rr.m_t = mt; rr.ls2_t = ls2t; rr.m_d = md; rr.ls2_d = ls2d;
-            rr.amax_t = it; rr.acc = acc; rr.pad[0] = rr.pad[1] = 0;
-            a.rec[i] = rr;
-        }
-        // last row of request r to arrive runs the request's finalize
-        __threadfence();
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            const int old = atomicAdd(&a.cnt[r], 1);
-            s_last = (old == L - 1);
-            if (s_last) atomicExch(&a.cnt[r], 0);
-        }
-        __syncthreads();
-        if (s_last) {
-            __threadfence();
-            finalize_request<DTT, DTD, MODE>(a, r, L, red);
-        }
-    }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -704,16 +449,6 @@ int dispatch_dtypes(int dt, int dd, Args &&...args) {
 }
 
 template <int DTT, int DTD>
-struct VerifyLauncher {
-    static int run(const VerifyArgs &a, int mode, unsigned grid, hipStream_t s) {
-        if (mode == kGreedy) hipLaunchKernelGGL((verify_rows_kernel<DTT, DTD, kGreedy>), dim3(grid), dim3(kThreads), 0, s, a);
-        else if (mode == kStoch) hipLaunchKernelGGL((verify_rows_kernel<DTT, DTD, kStoch>), dim3(grid), dim3(kThreads), 0, s, a);
-        else hipLaunchKernelGGL((verify_rows_kernel<DTT, DTD, kAlphaOnly>), dim3(grid), dim3(kThreads), 0, s, a);
-        return launch_status();
-    }
-};
-
-template <int DTT, int DTD>
 struct ResidualLauncher {
     static int run(const VerifyArgs &a, unsigned grid, hipStream_t s) {
         hipLaunchKernelGGL((residual_kernel<DTT, DTD>), dim3(grid), dim3(kThreads), 0, s, a);
@@ -723,13 +458,41 @@ struct ResidualLauncher {
 
 const double kLog2e = 1.4426950408889634;
 
+void fill_team_args(TeamArgs &a, const sv_params *p, const TeamLayout &L, char *ws) {
+    a.err = (uint32_t *)(ws + L.off_err);
+    a.epoch = (uint32_t *)(ws + L.off_epoch);
+    a.gdone = (int32_t *)(ws + L.off_gdone);
+    a.grp_cnt = (int32_t *)(ws + L.off_grp);
+    a.row_cnt = (int32_t *)(ws + L.off_rowcnt);
+    a.req_cnt = (int32_t *)(ws + L.off_reqcnt);
+    a.part = (uint64_t *)(ws + L.off_part);
+    a.apart = (uint64_t *)(ws + L.off_apart);
+    a.dir = (uint64_t *)(ws + L.off_dir);
+    a.rec = (uint64_t *)(ws + L.off_rec);
+    a.bonus = (float *)(ws + L.off_bonus);
+    a.ld_t = p->ld_t;
+    a.ld_d = p->ld_d;
+    a.B = p->B;
+    a.K = p->K_max;
+    a.V = p->V;
+    a.S = L.S;
+    a.nseg = L.nseg;
+    a.nseg_b = L.nseg_b;
+    a.n_grp = L.n_grp;
+    a.c = p->temperature > 0.f ? (float)(kLog2e / (double)p->temperature) : 0.f;
+    a.seed = p->seed;
+    a.step = p->step;
+    a.spin_ticks = 20000;        // 200 us before a member hands its share to the last arriver
+    a.spin_ticks_max = 20000000; // 200 ms bound on waits for stores that were already issued
+}
+
 }  // namespace
 
 extern "C" {
 
 size_t sv_workspace_bytes(int32_t B, int32_t K_max, int32_t V) {
     if (B < 0 || K_max < 0 || V <= 0) return 0;
-    return ws_layout(B, K_max, V).total;
+    return team_layout(B, K_max, V).total;
 }
 
 int sv_workspace_init(void *workspace, size_t workspace_bytes, void *stream) {
@@ -760,31 +523,23 @@ int sv_verify_batch(const sv_params *p, const void *target, const void *draft,
         return SV_EUNSUPPORTED;
     }
     if (!accept_len || !out_tokens || !n_out) return SV_EINVAL;
-    const WsLayout L = ws_layout(p->B, p->K_max, p->V);
+    const TeamLayout L = team_layout(p->B, p->K_max, p->V, workspace_bytes);
     if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return SV_EWORKSPACE;
-    if ((uint64_t)p->B * (uint64_t)(p->K_max > 0 ? p->K_max : 1) > 0x7fffffffull) return SV_EINVAL;
+    const uint64_t grid64 = (uint64_t)L.rows * (uint64_t)L.S;
+    if (grid64 > 0x7fffffffull) return SV_EINVAL;
 
-    VerifyArgs a{};
+    TeamArgs a{};
+    fill_team_args(a, p, L, (char *)workspace);
     a.target = target; a.draft = draft; a.tokens = draft_tokens; a.draft_len = draft_len;
     a.alpha = alpha; a.accept = accept; a.lse_t = lse_t; a.lse_d = lse_d;
     a.amax_t = amax_t; a.amax_d = amax_d;
     a.accept_len = accept_len; a.out_tokens = out_tokens; a.n_out = n_out;
-    char *ws = (char *)workspace;
-    a.err = (uint32_t *)(ws + L.off_err);
-    a.cnt = (int32_t *)(ws + L.off_cnt);
-    a.rec = (RowRec *)(ws + L.off_rec);
-    a.dir = (float *)(ws + L.off_dir);
-    a.ld_t = p->ld_t; a.ld_d = p->ld_d;
-    a.B = p->B; a.K = p->K_max; a.V = p->V; a.nseg = L.nseg;
     a.trows = p->K_max + 1;
-    const bool greedy = p->temperature == 0.f;
-    a.c = greedy ? 0.f : (float)(kLog2e / (double)p->temperature);
-    a.inv_t = greedy ? 0.f : (float)(1.0 / (double)p->temperature);
-    a.seed = p->seed; a.step = p->step;
     a.want_amax = (amax_t || amax_d) ? 1 : 0;
-    const unsigned grid = (unsigned)p->B * (unsigned)(p->K_max > 0 ? p->K_max : 1);
-    return dispatch_dtypes<VerifyLauncher>(p->dtype_t, p->dtype_d, a, greedy ? (int)kGreedy : (int)kStoch, grid,
-                                           (hipStream_t)stream);
+    const bool greedy = p->temperature == 0.f;
+    const hipError_t e = team_launch(a, p->dtype_t, p->dtype_d, greedy ? kTeamGreedy : kTeamStoch, (unsigned)grid64,
+                                     (hipStream_t)stream);
+    return e == hipSuccess ? SV_OK : SV_EHIP;
 }
 
 int sv_accept_len(const uint8_t *accept, const int32_t *draft_len, int32_t B, int32_t K_max,
@@ -832,23 +587,19 @@ int sv_tv_e2e_loss(const sv_params *p, const void *target, const void *draft, fl
     if (st) return st;
     st = check_logits(draft, p->dtype_d, p->ld_d, p->V);
     if (st) return st;
-    const WsLayout L = ws_layout(p->B, p->K_max, p->V);
+    const TeamLayout L = team_layout(p->B, p->K_max, p->V, workspace_bytes);
     if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return SV_EWORKSPACE;
-    if ((uint64_t)p->B * (uint64_t)p->K_max > 0x7fffffffull) return SV_EINVAL;
-    VerifyArgs a{};
-    char *ws = (char *)workspace;
+    const uint64_t grid64 = (uint64_t)L.rows * (uint64_t)L.S;
+    if (grid64 > 0x7fffffffull) return SV_EINVAL;
+    float *alpha_buf = alpha ? alpha : (float *)((char *)workspace + L.off_alpha);
+    TeamArgs a{};
+    fill_team_args(a, p, L, (char *)workspace);
     a.target = target; a.draft = draft;
-    a.alpha = alpha ? alpha : (float *)(ws + L.off_alpha);
-    a.err = (uint32_t *)(ws + L.off_err);
-    a.ld_t = p->ld_t; a.ld_d = p->ld_d;
-    a.B = p->B; a.K = p->K_max; a.V = p->V; a.nseg = L.nseg;
+    a.alpha = alpha_buf;
     a.trows = p->K_max;
-    a.c = (float)(kLog2e / (double)p->temperature);
-    a.inv_t = (float)(1.0 / (double)p->temperature);
-    const unsigned grid = (unsigned)p->B * (unsigned)p->K_max;
-    st = dispatch_dtypes<VerifyLauncher>(p->dtype_t, p->dtype_d, a, (int)kAlphaOnly, grid, (hipStream_t)stream);
-    if (st) return st;
-    hipLaunchKernelGGL(e2e_reduce_kernel, dim3(1), dim3(kReduceThreads), 0, (hipStream_t)stream, a.alpha, p->B,
+    hipError_t e = team_launch(a, p->dtype_t, p->dtype_d, kTeamAlpha, (unsigned)grid64, (hipStream_t)stream);
+    if (e != hipSuccess) return SV_EHIP;
+    hipLaunchKernelGGL(e2e_reduce_kernel, dim3(1), dim3(kReduceThreads), 0, (hipStream_t)stream, alpha_buf, p->B,
                        p->K_max, loss);
     return launch_status();
 }

@@ -64,6 +64,7 @@ enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 };
 /* Device error flags (sv_device_error). */
 #define SV_DEVERR_TOKEN 1u     /* a draft token outside [0, V) */
 #define SV_DEVERR_DRAFT_LEN 2u /* a draft_len entry outside [0, K_max] */
+#define SV_DEVERR_TIMEOUT 4u   /* an internal wait for already-issued stores exceeded its bound */
 
 typedef struct sv_params {
     int32_t B;          /* requests (or |I| for sv_tv_e2e_loss) */
@@ -80,7 +81,9 @@ typedef struct sv_params {
 
 /* Bytes of device workspace needed by sv_verify_batch / sv_tv_e2e_loss for these sizes.
  * The workspace must be zero-filled before its first use (sv_workspace_init); every call
- * leaves it ready for the next one.  Calls that share a workspace must not overlap. */
+ * leaves it ready for the next one.  One workspace may serve calls of different shapes if
+ * it is large enough for each and is always passed with the same workspace_bytes.  Calls
+ * that share a workspace must not overlap (same stream, or ordered by events). */
 size_t sv_workspace_bytes(int32_t B, int32_t K_max, int32_t V);
 
 /* Zero-fill a workspace (a fill kernel on `stream`; no host synchronisation). */

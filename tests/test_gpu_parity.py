@@ -243,3 +243,29 @@ def test_device_error_flag_for_bad_token(sv):
     assert flags & 1
     assert out["accept"][0, 1].item() == 0
     assert sv.sv_device_error(buf) == 0
+
+
+def test_workspace_reuse_across_calls_and_modes(sv):
+    """One workspace, many calls (the per-call epoch advances inside the kernel): every
+    call equals the same call on a fresh workspace."""
+    v = workloads.make_verify_inputs("dfly", device=DEV, T=0.9, B=6)
+    t2, d2, _ = workloads.make_e2e_inputs(device=DEV, I=5, D=3, V=131072, seed=8)
+    ws = sv.Workspace(DEV)
+    buf = ws.get(64, 16, 131072)
+    plan = [(0.9, None, 0), (0.0, None, 1), (0.9, [3, 0, 16, 1, 7, 2], 2), ("e2e", None, 0), (1.3, None, 3),
+            (0.9, [16, 16, 0, 0, 5, 9], 4), (0.0, [2, 0, 1, 16, 16, 3], 5), ("e2e", None, 0), (0.9, None, 0)]
+    for i, (T, dl, step) in enumerate(plan):
+        _say(f"reuse call {i}: T={T} dl={dl}")
+        if T == "e2e":
+            l1, a1 = sv.sv_tv_e2e_loss(t2, d2, 1.0, workspace=buf)
+            l2, a2 = sv.sv_tv_e2e_loss(t2, d2, 1.0)
+            assert torch.equal(a1, a2) and torch.equal(l1, l2)
+            continue
+        dlt = None if dl is None else torch.tensor(dl, dtype=torch.int32, device=DEV)
+        a = _np(sv.sv_verify_batch(v.target, v.draft, v.draft_tokens, T, seed=7, step=step, draft_len=dlt,
+                                   workspace=buf, want_amax=True))
+        b = _np(sv.sv_verify_batch(v.target, v.draft, v.draft_tokens, T, seed=7, step=step, draft_len=dlt,
+                                   want_amax=True))
+        for k in a:
+            assert np.array_equal(a[k], b[k]), (i, k)
+    assert sv.sv_device_error(buf) == 0
