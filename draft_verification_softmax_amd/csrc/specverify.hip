@@ -290,7 +290,8 @@ __global__ __launch_bounds__(kThreads) void residual_kernel(VerifyArgs a) {
 // ---------------------------------------------------------------------------------------
 constexpr int kReduceThreads = 1024;
 
-__global__ __launch_bounds__(kReduceThreads) void e2e_reduce_kernel(const float *alpha, int I, int D, float *loss) {
+__global__ __launch_bounds__(kReduceThreads) void e2e_reduce_kernel(const float *alpha, int I, int D, float *loss,
+                                                                    uint32_t *epoch) {
     __shared__ double part[kReduceThreads];
     double acc = 0.0;
     for (int i = threadIdx.x; i < I; i += kReduceThreads) {
@@ -307,7 +308,11 @@ __global__ __launch_bounds__(kReduceThreads) void e2e_reduce_kernel(const float 
         if (threadIdx.x < h) part[threadIdx.x] += part[threadIdx.x + h];
         __syncthreads();
     }
-    if (threadIdx.x == 0) *loss = (float)(1.0 - part[0] / ((double)I * (double)D));
+    if (threadIdx.x == 0) {
+        *loss = (float)(1.0 - part[0] / ((double)I * (double)D));
+        // the team kernels of this call are complete: advance the workspace epoch
+        __hip_atomic_store(epoch, *epoch + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -462,13 +467,10 @@ void fill_team_args(TeamArgs &a, const sv_params *p, const TeamLayout &L, char *
     a.err = (uint32_t *)(ws + L.off_err);
     a.epoch = (uint32_t *)(ws + L.off_epoch);
     a.gdone = (int32_t *)(ws + L.off_gdone);
-    a.grp_cnt = (int32_t *)(ws + L.off_grp);
-    a.row_cnt = (int32_t *)(ws + L.off_rowcnt);
-    a.req_cnt = (int32_t *)(ws + L.off_reqcnt);
     a.part = (uint64_t *)(ws + L.off_part);
     a.apart = (uint64_t *)(ws + L.off_apart);
     a.dir = (uint64_t *)(ws + L.off_dir);
-    a.rec = (uint64_t *)(ws + L.off_rec);
+    a.acc = (uint64_t *)(ws + L.off_acc);
     a.bonus = (float *)(ws + L.off_bonus);
     a.ld_t = p->ld_t;
     a.ld_d = p->ld_d;
@@ -478,12 +480,10 @@ void fill_team_args(TeamArgs &a, const sv_params *p, const TeamLayout &L, char *
     a.S = L.S;
     a.nseg = L.nseg;
     a.nseg_b = L.nseg_b;
-    a.n_grp = L.n_grp;
     a.c = p->temperature > 0.f ? (float)(kLog2e / (double)p->temperature) : 0.f;
     a.seed = p->seed;
     a.step = p->step;
-    a.spin_ticks = 20000;        // 200 us before a member hands its share to the last arriver
-    a.spin_ticks_max = 20000000; // 200 ms bound on waits for stores that were already issued
+    a.spin_ticks = 20000;  // 200 us: then a member hands its share to the finalize kernel
 }
 
 }  // namespace
@@ -492,7 +492,7 @@ extern "C" {
 
 size_t sv_workspace_bytes(int32_t B, int32_t K_max, int32_t V) {
     if (B < 0 || K_max < 0 || V <= 0) return 0;
-    return team_layout(B, K_max, V).total;
+    return team_layout(B, K_max + 1, V).total;   // K_max + 1 slots also cover L_e2e with D = K_max
 }
 
 int sv_workspace_init(void *workspace, size_t workspace_bytes, void *stream) {
@@ -523,7 +523,7 @@ int sv_verify_batch(const sv_params *p, const void *target, const void *draft,
         return SV_EUNSUPPORTED;
     }
     if (!accept_len || !out_tokens || !n_out) return SV_EINVAL;
-    const TeamLayout L = team_layout(p->B, p->K_max, p->V, workspace_bytes);
+    const TeamLayout L = team_layout(p->B, p->K_max + 1, p->V, workspace_bytes);
     if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return SV_EWORKSPACE;
     const uint64_t grid64 = (uint64_t)L.rows * (uint64_t)L.S;
     if (grid64 > 0x7fffffffull) return SV_EINVAL;
@@ -535,10 +535,11 @@ int sv_verify_batch(const sv_params *p, const void *target, const void *draft,
     a.amax_t = amax_t; a.amax_d = amax_d;
     a.accept_len = accept_len; a.out_tokens = out_tokens; a.n_out = n_out;
     a.trows = p->K_max + 1;
+    a.slots = p->K_max + 1;
     a.want_amax = (amax_t || amax_d) ? 1 : 0;
-    const bool greedy = p->temperature == 0.f;
-    const hipError_t e = team_launch(a, p->dtype_t, p->dtype_d, greedy ? kTeamGreedy : kTeamStoch, (unsigned)grid64,
-                                     (hipStream_t)stream);
+    const int mode = p->temperature == 0.f ? kTeamGreedy : kTeamStoch;
+    hipError_t e = team_launch_stream(a, p->dtype_t, p->dtype_d, mode, (unsigned)grid64, (hipStream_t)stream);
+    if (e == hipSuccess) e = team_launch_finalize(a, p->dtype_t, p->dtype_d, mode, (hipStream_t)stream);
     return e == hipSuccess ? SV_OK : SV_EHIP;
 }
 
@@ -597,10 +598,12 @@ int sv_tv_e2e_loss(const sv_params *p, const void *target, const void *draft, fl
     a.target = target; a.draft = draft;
     a.alpha = alpha_buf;
     a.trows = p->K_max;
-    hipError_t e = team_launch(a, p->dtype_t, p->dtype_d, kTeamAlpha, (unsigned)grid64, (hipStream_t)stream);
+    a.slots = p->K_max;
+    hipError_t e = team_launch_stream(a, p->dtype_t, p->dtype_d, kTeamAlpha, (unsigned)grid64, (hipStream_t)stream);
+    if (e == hipSuccess) e = team_launch_e2e_alpha(a, p->dtype_t, p->dtype_d, (hipStream_t)stream);
     if (e != hipSuccess) return SV_EHIP;
     hipLaunchKernelGGL(e2e_reduce_kernel, dim3(1), dim3(kReduceThreads), 0, (hipStream_t)stream, alpha_buf, p->B,
-                       p->K_max, loss);
+                       p->K_max, loss, a.epoch);
     return launch_status();
 }
 

@@ -20,29 +20,25 @@
 
 namespace sv {
 
-TeamLayout team_layout(int B, int K, int V, size_t ws_bytes) {
+TeamLayout team_layout(int B, int slots, int V, size_t ws_bytes) {
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
     TeamLayout L;
     L.S = (V + kTeamChunk - 1) / kTeamChunk;
     L.nseg = L.S * kTeamWaves;
     L.nseg_b = (V + kBonusSeg - 1) / kBonusSeg;
-    L.rows = (int64_t)(B > 0 ? B : 1) * (K > 0 ? K : 1);
-    L.n_grp = (int)((L.rows + 255) / 256);
+    L.rows = (int64_t)(B > 0 ? B : 1) * (slots > 0 ? slots : 1);
     const size_t nB = (size_t)(B > 0 ? B : 1);
     // counters, from the start
     L.off_err = 0;
     L.off_epoch = 64;
     L.off_gdone = 128;
-    L.off_grp = 256;
-    L.off_rowcnt = al(L.off_grp + sizeof(int32_t) * (size_t)L.n_grp);
-    L.off_reqcnt = al(L.off_rowcnt + sizeof(int32_t) * (size_t)L.rows);
-    const size_t counters = al(L.off_reqcnt + sizeof(int32_t) * nB);
+    const size_t counters = 256;
     // tagged words and scratch, relative to their own base
     size_t o = 0;
     L.off_part = o;  o = al(o + sizeof(uint64_t) * 8 * (size_t)L.S * (size_t)L.rows);
     L.off_apart = o; o = al(o + sizeof(uint64_t) * (size_t)L.S * (size_t)L.rows);
     L.off_dir = o;   o = al(o + sizeof(uint64_t) * (size_t)L.nseg * (size_t)L.rows);
-    L.off_rec = o;   o = al(o + sizeof(uint64_t) * 4 * (size_t)L.rows);
+    L.off_acc = o;   o = al(o + sizeof(uint64_t) * 4 * (size_t)L.rows);
     L.off_bonus = o; o = al(o + sizeof(float) * 2 * (size_t)L.nseg_b * nB);
     L.off_alpha = o; o = al(o + sizeof(float) * (size_t)L.rows);
     const size_t tagged = o;
@@ -50,7 +46,7 @@ TeamLayout team_layout(int B, int K, int V, size_t ws_bytes) {
     const size_t size = ws_bytes >= L.total ? ws_bytes : L.total;
     const size_t base = (size - tagged) & ~(size_t)255;   // >= counters since size >= total
     L.off_part += base; L.off_apart += base; L.off_dir += base;
-    L.off_rec += base; L.off_bonus += base; L.off_alpha += base;
+    L.off_acc += base; L.off_bonus += base; L.off_alpha += base;
     return L;
 }
 
@@ -97,29 +93,6 @@ __device__ __forceinline__ uint32_t read_epoch(const uint32_t *e) {
 
 // ---- row chunk loads -----------------------------------------------------------------
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// Eight logits at v0 (multiple of 8) of a 16-byte-aligned row, -inf past V.
-template <int DT>
-__device__ __forceinline__ void load8nt(const void *row, int v0, int V, float *z) {
-    if (v0 + 8 <= V) {
-        if constexpr (DT == kDtBF16) {
-            const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row) + (v0 >> 3));
-            z[0] = bf16_lo(w.x); z[1] = bf16_hi(w.x); z[2] = bf16_lo(w.y); z[3] = bf16_hi(w.y);
-            z[4] = bf16_lo(w.z); z[5] = bf16_hi(w.z); z[6] = bf16_lo(w.w); z[7] = bf16_hi(w.w);
-        } else {
-            const u32x4 *q = reinterpret_cast<const u32x4 *>(row) + (v0 >> 2);
-            const u32x4 w0 = __builtin_nontemporal_load(q), w1 = __builtin_nontemporal_load(q + 1);
-            z[0] = __uint_as_float(w0.x); z[1] = __uint_as_float(w0.y); z[2] = __uint_as_float(w0.z); z[3] = __uint_as_float(w0.w);
-            z[4] = __uint_as_float(w1.x); z[5] = __uint_as_float(w1.y); z[6] = __uint_as_float(w1.z); z[7] = __uint_as_float(w1.w);
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) z[e] = (v0 + e < V) ? load1<DT>(row, v0 + e) : neg_inf();
-    }
-}
-
-// Vocabulary index of register slot i (group i / 8, element i % 8) of this lane.
-__device__ __forceinline__ int slot_index(int base, int i) { return base + (i >> 3) * 512 + lane_id() * 8 + (i & 7); }
 
 // ---- workgroup reductions (fixed order) ------------------------------------------------
 struct TeamRed {
@@ -172,93 +145,122 @@ __device__ float block_sumf(float x, TeamRed &red) {
     return t;
 }
 
-// ---- one member's chunk ----------------------------------------------------------------
-struct Chunk {
-    float xt[kTeamE], xd[kTeamE];
+// ---- one member's chunk, kept as loaded ----------------------------------------------
+// Lane l of wave w of member j holds logits base + g * 512 + l * 8 + (0..7), g < kTeamE / 8,
+// base = j * kTeamChunk + w * kTeamSeg: bfloat16 as packed pairs, binary32 as is.
+template <int DT>
+struct LaneRow {
+    static constexpr int kWords = DT == kDtBF16 ? kTeamE / 2 : kTeamE;
+    uint32_t w[kWords];
+
+    // Widen slot i.  For bfloat16 the widening is an opaque instruction so that each pass
+    // re-widens from the packed registers instead of the compiler keeping all widened
+    // values live across passes (which would double the registers the chunk occupies).
+    __device__ __forceinline__ float get(int i) const {
+        if constexpr (DT == kDtBF16) {
+            float f;
+            if (i & 1) asm volatile("v_and_b32 %0, 0xffff0000, %1" : "=v"(f) : "v"(w[i >> 1]));
+            else asm volatile("v_lshlrev_b32 %0, 16, %1" : "=v"(f) : "v"(w[i >> 1]));
+            return f;
+        } else {
+            return __uint_as_float(w[i]);
+        }
+    }
+
+    __device__ __forceinline__ void load(const void *row, int base, int V) {
+#pragma unroll
+        for (int g = 0; g < kTeamE / 8; ++g) {
+            const int v0 = base + g * 512 + lane_id() * 8;
+            if (v0 + 8 <= V) {
+                if constexpr (DT == kDtBF16) {
+                    const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row) + (v0 >> 3));
+                    w[g * 4 + 0] = q.x; w[g * 4 + 1] = q.y; w[g * 4 + 2] = q.z; w[g * 4 + 3] = q.w;
+                } else {
+                    const u32x4 *p = reinterpret_cast<const u32x4 *>(row) + (v0 >> 2);
+                    const u32x4 q0 = __builtin_nontemporal_load(p), q1 = __builtin_nontemporal_load(p + 1);
+                    w[g * 8 + 0] = q0.x; w[g * 8 + 1] = q0.y; w[g * 8 + 2] = q0.z; w[g * 8 + 3] = q0.w;
+                    w[g * 8 + 4] = q1.x; w[g * 8 + 5] = q1.y; w[g * 8 + 6] = q1.z; w[g * 8 + 7] = q1.w;
+                }
+            } else {
+                // ragged end of the row: -inf past V
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int v = v0 + e;
+                    if constexpr (DT == kDtBF16) {
+                        const uint32_t h = v < V ? (uint32_t) static_cast<const uint16_t *>(row)[v] : 0xff80u;
+                        if (e & 1) w[g * 4 + (e >> 1)] |= h << 16;
+                        else w[g * 4 + (e >> 1)] = h;
+                    } else {
+                        w[g * 8 + e] = v < V ? static_cast<const uint32_t *>(row)[v] : 0xff800000u;
+                    }
+                }
+            }
+        }
+    }
+
+    __device__ __forceinline__ float max() const {
+        float m0 = neg_inf(), m1 = neg_inf();
+#pragma unroll
+        for (int i = 0; i < kTeamE; i += 2) { m0 = fmaxf(m0, get(i)); m1 = fmaxf(m1, get(i + 1)); }
+        return fmaxf(m0, m1);
+    }
+
+    // first slot (in vocabulary order) holding m; its vocabulary index
+    __device__ __forceinline__ int first_index(float m, int base) const {
+        int idx = 0x7fffffff;
+#pragma unroll
+        for (int i = kTeamE - 1; i >= 0; --i)
+            if (get(i) == m) idx = base + (i >> 3) * 512 + lane_id() * 8 + (i & 7);
+        return idx;
+    }
+
+    // sum_i 2^{x_i c - M}
+    __device__ __forceinline__ float exp_sum(float c, float M) const {
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < kTeamE; i += 2) {
+            a0 += exp2_fast(__builtin_fmaf(get(i), c, -M));
+            a1 += exp2_fast(__builtin_fmaf(get(i + 1), c, -M));
+        }
+        return a0 + a1;
+    }
+};
+
+// sum_i min(p_i, q_i) with p = 2^{t c - L2t}, q = 2^{d c - L2d}: the same per-logit formula
+// as the inverse-CDF scan of the finalize kernel.
+template <int DTT, int DTD>
+__device__ __forceinline__ float min_sum(const LaneRow<DTT> &t, const LaneRow<DTD> &d, float c, float L2t, float L2d) {
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < kTeamE; i += 2) {
+        a0 += exp2_fast(fminf(__builtin_fmaf(t.get(i), c, -L2t), __builtin_fmaf(d.get(i), c, -L2d)));
+        a1 += exp2_fast(fminf(__builtin_fmaf(t.get(i + 1), c, -L2t), __builtin_fmaf(d.get(i + 1), c, -L2d)));
+    }
+    return a0 + a1;
+}
+
+// Pass 1 of a lane: base-2 log-sum-exp state (M = max * c, s = sum 2^{x c - M}) per row.
+struct ThreadStats {
+    float Mt, st, Md, sd;
 };
 
 template <int DTT, int DTD>
-__device__ __forceinline__ void load_chunk(Chunk &ch, const void *trow, const void *drow, int base, int V) {
-#pragma unroll
-    for (int g = 0; g < kTeamE / 8; ++g) {
-        const int v0 = base + g * 512 + lane_id() * 8;
-        load8nt<DTT>(trow, v0, V, ch.xt + g * 8);
-        load8nt<DTD>(drow, v0, V, ch.xd + g * 8);
-    }
-}
-
-__device__ __forceinline__ float max_of(const float *x) {
-    float m0 = neg_inf(), m1 = neg_inf(), m2 = neg_inf(), m3 = neg_inf();
-#pragma unroll
-    for (int i = 0; i < kTeamE; i += 4) { m0 = fmaxf(m0, x[i]); m1 = fmaxf(m1, x[i + 1]); m2 = fmaxf(m2, x[i + 2]); m3 = fmaxf(m3, x[i + 3]); }
-    return fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
-}
-
-// First register slot holding value m (slots are in increasing vocabulary order).
-__device__ __forceinline__ int first_index_of(const float *x, float m, int base) {
-    int idx = 0x7fffffff;
-#pragma unroll
-    for (int i = kTeamE - 1; i >= 0; --i)
-        if (x[i] == m) idx = slot_index(base, i);
-    return idx;
-}
-
-// In place: x_i <- 2^{x_i c - M}; returns the sum in a fixed association order.
-__device__ __forceinline__ float exp_sum(float *x, float c, float M) {
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-#pragma unroll
-    for (int i = 0; i < kTeamE; i += 4) {
-        x[i] = exp2_fast(__builtin_fmaf(x[i], c, -M));
-        x[i + 1] = exp2_fast(__builtin_fmaf(x[i + 1], c, -M));
-        x[i + 2] = exp2_fast(__builtin_fmaf(x[i + 2], c, -M));
-        x[i + 3] = exp2_fast(__builtin_fmaf(x[i + 3], c, -M));
-        a0 += x[i]; a1 += x[i + 1]; a2 += x[i + 2]; a3 += x[i + 3];
-    }
-    return (a0 + a1) + (a2 + a3);
-}
-
-// sum_i min(et_i, ed_i * rho), same association as exp_sum (so it never exceeds it).
-__device__ __forceinline__ float min_sum(const float *et, const float *ed, float rho) {
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-#pragma unroll
-    for (int i = 0; i < kTeamE; i += 4) {
-        a0 += fminf(et[i], ed[i] * rho);
-        a1 += fminf(et[i + 1], ed[i + 1] * rho);
-        a2 += fminf(et[i + 2], ed[i + 2] * rho);
-        a3 += fminf(et[i + 3], ed[i + 3] * rho);
-    }
-    return (a0 + a1) + (a2 + a3);
-}
-
-// Pass 1 on a loaded chunk: thread reference M = max * c (-inf if empty), exps in place.
-struct ThreadStats {
-    float Mt, st, Md, sd;   // base-2 log-sum-exp states of this lane's slice
-};
-
-__device__ __forceinline__ ThreadStats pass1(Chunk &ch, float c) {
+__device__ __forceinline__ ThreadStats pass1(const LaneRow<DTT> &t, const LaneRow<DTD> &d, float mt, float md, float c) {
     ThreadStats s;
-    const float mt = max_of(ch.xt), md = max_of(ch.xd);
     s.Mt = (mt == neg_inf()) ? neg_inf() : mt * c;
     s.Md = (md == neg_inf()) ? neg_inf() : md * c;
-    s.st = exp_sum(ch.xt, c, s.Mt == neg_inf() ? 0.f : s.Mt);
-    s.sd = exp_sum(ch.xd, c, s.Md == neg_inf() ? 0.f : s.Md);
+    s.st = (mt == neg_inf()) ? 0.f : t.exp_sum(c, s.Mt);
+    s.sd = (md == neg_inf()) ? 0.f : d.exp_sum(c, s.Md);
     return s;
 }
 
-// Pass 2: this lane's share of sum_v min(p_v, q_v) and of the residual mass
-// sum_v max(p_v - q_v, 0), given the row normalisers L2t, L2d (base 2).
-__device__ __forceinline__ void pass2(const Chunk &ch, const ThreadStats &s, float L2t, float L2d, float &alpha,
-                                      float &resid) {
-    alpha = 0.f;
-    resid = 0.f;
-    if (s.Mt == neg_inf()) return;             // no target mass in this slice
-    const float lrt = s.Mt - L2t;              // log2 of the factor turning x_t into p
-    const float lrd = (s.Md == neg_inf()) ? neg_inf() : s.Md - L2d;
-    const float rho = exp2_fast(fminf(lrd - lrt, 126.f));
-    const float sm = min_sum(ch.xt, ch.xd, rho);
-    const float rt = exp2_fast(lrt);
-    alpha = rt * sm;
-    resid = rt * (s.st - sm);
+// Pass 2 of a lane: its share of alpha and of the residual mass sum max(p - q, 0).
+template <int DTT, int DTD>
+__device__ __forceinline__ void pass2(const LaneRow<DTT> &t, const LaneRow<DTD> &d, const ThreadStats &s, float c,
+                                      float L2t, float L2d, float &alpha, float &resid) {
+    alpha = min_sum(t, d, c, L2t, L2d);
+    const float P = (s.Mt == neg_inf()) ? 0.f : s.st * exp2_fast(s.Mt - L2t);   // this lane's target mass
+    resid = P - alpha;
 }
 
 // ---- request-level helpers --------------------------------------------------------------
@@ -341,12 +343,13 @@ __device__ int row_argmax(const void *row, int V, TeamRed &red) {
     return i == 0x7fffffff ? 0 : i;
 }
 
-// Correction token after a rejection at row tau: inverse CDF of w = max(p - q, 0) at
-// u * R.  The directory (residual mass of each 2048-logit wave range) picks the range; the
-// workgroup re-reads it (8 logits per thread) and scans it in binary64.
-template <int DTT, int DTD>
-__device__ int draw_residual(const void *trow, const void *drow, int V, float c, float L2t, float L2d,
-                             const float *dirv, int nseg, double t, TeamRed &red) {
+// Token drawn by inverse CDF at target t over weights w: the residual max(p - q, 0) after
+// a rejection (RESID), else p (the bonus token).  The per-range masses (one per
+// kTeamSeg-logit wave range) pick the range; the workgroup re-reads that range and scans
+// it in binary64.
+template <int DTT, int DTD, bool RESID>
+__device__ int draw_ranges(const void *trow, const void *drow, int V, float c, float L2t, float L2d,
+                           const float *dirv, int nseg, double t, TeamRed &red) {
     __shared__ int s_seg;
     __shared__ double s_ex;
     __shared__ double s_scan[kTeamThreads];
@@ -361,19 +364,27 @@ __device__ int draw_residual(const void *trow, const void *drow, int V, float c,
     const int sidx = s_seg;
     if (sidx < 0) return -1;
     const double rem = t - s_ex;
-    const int e0 = sidx * kTeamSeg + threadIdx.x * 8;
-    float wt[8];
+    // the range's kTeamSeg logits, kPer consecutive ones per thread
+    constexpr int kPer = kTeamSeg / kTeamThreads;
+    const int e0 = sidx * kTeamSeg + threadIdx.x * kPer;
+    const int vend = min(V, (sidx + 1) * kTeamSeg);
+    float wt[kPer];
     double my = 0.0;
-    {
+#pragma unroll
+    for (int e8 = 0; e8 < kPer; e8 += 8) {
         float zt[8], zd[8];
-        load8<DTT>(trow, e0, V, zt);
-        load8<DTD>(drow, e0, V, zd);
+        load8<DTT>(trow, e0 + e8, vend, zt);
+        if constexpr (RESID) load8<DTD>(drow, e0 + e8, vend, zd);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float p = exp2_fast(__builtin_fmaf(zt[e], c, -L2t));
-            const float q = exp2_fast(__builtin_fmaf(zd[e], c, -L2d));
-            wt[e] = p - fminf(p, q);
-            my += (double)wt[e];
+            if constexpr (RESID) {
+                const float q = exp2_fast(__builtin_fmaf(zd[e], c, -L2d));
+                wt[e8 + e] = p - fminf(p, q);
+            } else {
+                wt[e8 + e] = p;
+            }
+            my += (double)wt[e8 + e];
         }
     }
     // inclusive scan of per-thread sums in thread order
@@ -389,8 +400,8 @@ __device__ int draw_residual(const void *trow, const void *drow, int V, float c,
     if (incl > rem && incl - my <= rem) {
         // this thread's 8 logits hold the crossing
         double run = incl - my;
-        int k = 7;
-        for (int e = 0; e < 8; ++e) {
+        int k = kPer - 1;
+        for (int e = 0; e < kPer; ++e) {
             run += (double)wt[e];
             if (run > rem) { k = e; break; }
         }
@@ -401,12 +412,12 @@ __device__ int draw_residual(const void *trow, const void *drow, int V, float c,
     if (tok == 0x7fffffff) {
         // rounding ran past the range: the last logit of the range with positive weight
         int last = -1;
-        for (int e = 7; e >= 0; --e)
+        for (int e = kPer - 1; e >= 0; --e)
             if (wt[e] > 0.f) { last = e0 + e; break; }
         s_scan[threadIdx.x] = (double)last;
         __syncthreads();
         if (threadIdx.x == 0) {
-            int best = sidx * kTeamSeg;
+            int best = min(sidx * kTeamSeg, V - 1);
             for (int q = kTeamThreads - 1; q >= 0; --q)
                 if (s_scan[q] >= 0.0) { best = (int)s_scan[q]; break; }
             s_tok = best;
@@ -418,70 +429,490 @@ __device__ int draw_residual(const void *trow, const void *drow, int V, float c,
     return tok;
 }
 
+// Row normalisers (base 2) from the S member partials, in member order.  The stream
+// kernel and the finalize kernel both call this on the same payloads, so they agree bit
+// for bit.
+__device__ __forceinline__ void team_totals(const uint32_t *pay, int S, float &L2t, float &L2d) {
+    float Tt = neg_inf(), Ts = 0.f, Dt = neg_inf(), Ds = 0.f;
+    for (int q = 0; q < S; ++q) {
+        ms_merge(Tt, Ts, __uint_as_float(pay[q]), __uint_as_float(pay[S + q]));
+        ms_merge(Dt, Ds, __uint_as_float(pay[2 * S + q]), __uint_as_float(pay[3 * S + q]));
+    }
+    L2t = Tt + log2f(Ts);
+    L2d = Dt + log2f(Ds);
+}
+
+__device__ __forceinline__ int row_limit(const TeamArgs &a, int r) {
+    int L = a.draft_len ? a.draft_len[r] : a.K;
+    return L < 0 ? 0 : (L > a.K ? a.K : L);
+}
+
+template <int DT>
+__device__ __forceinline__ const void *row_ptr(const void *base, int64_t row, int64_t ld) {
+    return static_cast<const char *>(base) + (size_t)(row * ld) * (DT == kDtBF16 ? 2 : 4);
+}
+
+// Accept iff u * q(x) < p(x), i.e. u < 2^{log2 p(x) - log2 q(x)}.
+__device__ __forceinline__ int accept_test(float zt, float zd, float c, float L2t, float L2d, uint64_t seed, int r,
+                                           int k, uint64_t step) {
+    const float lpt = __builtin_fmaf(zt, c, -L2t);
+    const float lpd = __builtin_fmaf(zd, c, -L2d);
+    const float u = uniform24(seed, (uint64_t)r, (uint64_t)k, kPurposeAccept, step);
+    return u < exp2f(lpt - lpd) ? 1 : 0;
+}
+
+}  // namespace
+
+// =======================================================================================
+// Stream kernel: one member workgroup per (row pair, vocabulary chunk)
+// =======================================================================================
 template <int DTT, int DTD, int MODE>
-__device__ void request_finalize(const TeamArgs &a, int r, int L, uint32_t tag, TeamRed &red, uint32_t *pay) {
-    __shared__ int s_tau, s_tok;
+__global__ __launch_bounds__(kTeamThreads) void stream_kernel(TeamArgs a) {
+    __shared__ TeamRed red;
+    __shared__ uint32_t pay[4 * 128];
+    __shared__ float s_tot[2];
+    __shared__ int s_ok;
+
+    const int S = a.S;
+    const int j = blockIdx.x % S;
+    const int64_t row = blockIdx.x / S;
     const int K = a.K;
-    const int slots = K > 0 ? K : 1;
-    const int64_t row0 = (int64_t)r * slots;
-    const int64_t rows = (int64_t)a.B * slots;
-    bool ok = true;
-    // first-reject scan over the accept words of rows 0..L-1
-    if (threadIdx.x == 0) s_tau = L;
+    const int slots = a.slots;
+    const int r = (int)(row / slots);
+    const int k = (int)(row % slots);
+    const bool bonus = (MODE != kTeamAlpha) && k == K;
+    int L = K;
+    if constexpr (MODE != kTeamAlpha) {
+        if (a.draft_len) {
+            const int l0 = a.draft_len[r];
+            if ((l0 < 0 || l0 > K) && threadIdx.x == 0 && bonus && j == 0) atomicOr(a.err, SV_DEVERR_DRAFT_LEN);
+            L = l0 < 0 ? 0 : (l0 > K ? K : l0);
+        }
+    }
+    if (!bonus && k >= L) return;
+    const int V = a.V;
+    const float c = a.c;
+    const int w = threadIdx.x / kWave;
+    const int base = j * kTeamChunk + w * kTeamSeg;
+    uint64_t *part = a.part + row * (int64_t)(8 * S);
+    if (bonus) {
+        // the bonus row (target row L_r): per-wave-range states (stochastic) or argmax (greedy)
+        const void *brow = row_ptr<DTT>(a.target, (int64_t)r * a.trows + L, a.ld_t);
+        LaneRow<DTT> br;
+        br.load(brow, base, V);
+        const uint32_t tag = read_epoch(a.epoch) + 1;
+        const float mb = br.max();
+        if constexpr (MODE == kTeamGreedy) {
+            float wb = mb, wz = neg_inf();
+            int i0 = 0, i1 = 0;
+            block_amax2(wb, i0, wz, i1, red);
+            int ib = (mb == wb && mb != neg_inf()) ? br.first_index(mb, base) : 0x7fffffff;
+            float fb = wb, fz = neg_inf();
+            int iz = 0x7fffffff;
+            block_amax2(fb, ib, fz, iz, red);
+            if (threadIdx.x == 0) {
+                putf(part + 4 * S + j, wb, tag);
+                put(part + 5 * S + j, (uint32_t)ib, tag);
+            }
+        } else {
+            float M = (mb == neg_inf()) ? neg_inf() : mb * c;
+            float sm = (mb == neg_inf()) ? 0.f : br.exp_sum(c, M);
+            wave_ms(M, sm);
+            if (lane_id() == 0) {
+                putf(part + (2 * w) * S + j, M, tag);
+                putf(part + (2 * w + 1) * S + j, sm, tag);
+            }
+        }
+        return;
+    }
+    const void *trow = row_ptr<DTT>(a.target, (int64_t)r * a.trows + k, a.ld_t);
+    const void *drow = row_ptr<DTD>(a.draft, (int64_t)r * K + k, a.ld_d);
+
+    LaneRow<DTT> tr;
+    LaneRow<DTD> dr;
+    tr.load(trow, base, V);
+    dr.load(drow, base, V);
+
+    // the member whose chunk holds the drafted token fetches its two logits
+    float zx_t = 0.f, zx_d = 0.f;
+    bool owner = false;
+    if (MODE == kTeamStoch && threadIdx.x == 0) {
+        const int x = a.tokens[(size_t)r * K + k];
+        owner = (x >= 0 && x < V && x / kTeamChunk == j);
+        if (owner) {
+            zx_t = load1<DTT>(trow, x);
+            zx_d = load1<DTD>(drow, x);
+        }
+    }
+    const uint32_t tag = read_epoch(a.epoch) + 1;
+
+    const float mt = tr.max(), md = dr.max();
+    // ---- argmax partials: chunk maximum, then the first index holding it ----
+    if (MODE == kTeamGreedy || a.want_amax) {
+        float wt = mt, wd = md;
+        int i0 = 0, i1 = 0;
+        block_amax2(wt, i0, wd, i1, red);   // chunk maxima
+        int it = (mt == wt && mt != neg_inf()) ? tr.first_index(mt, base) : 0x7fffffff;
+        int id = (md == wd && md != neg_inf()) ? dr.first_index(md, base) : 0x7fffffff;
+        float ft = wt, fd = wd;
+        block_amax2(ft, it, fd, id, red);   // equal values: lowest index
+        if (threadIdx.x == 0) {
+            putf(part + 4 * S + j, wt, tag);
+            put(part + 5 * S + j, (uint32_t)it, tag);
+            putf(part + 6 * S + j, wd, tag);
+            put(part + 7 * S + j, (uint32_t)id, tag);
+        }
+    }
+    if constexpr (MODE == kTeamGreedy) return;
+
+    // ---- phase 1: log-sum-exp partial of this member ----
+    const ThreadStats ts = pass1(tr, dr, mt, md, c);
+    {
+        float Mt = ts.Mt, st = ts.st, Md = ts.Md, sd = ts.sd;
+        block_ms2(Mt, st, Md, sd, red);
+        if (threadIdx.x == 0) {
+            putf(part + 0 * S + j, Mt, tag);
+            putf(part + 1 * S + j, st, tag);
+            putf(part + 2 * S + j, Md, tag);
+            putf(part + 3 * S + j, sd, tag);
+        }
+    }
+    // ---- every member reduces all partials (bounded wait) ----
+    if (threadIdx.x < kWave) {
+        const bool got = wave_poll(part, 4 * S, tag, pay, a.spin_ticks);
+        if (threadIdx.x == 0) {
+            s_ok = got ? 1 : 0;
+            if (got) team_totals(pay, S, s_tot[0], s_tot[1]);
+        }
+    }
     __syncthreads();
-    for (int k0 = 0; k0 < L; k0 += 2048) {
-        const int n = min(2048, L - k0);
+    if (!s_ok) {
+        if (threadIdx.x == 0) put(a.apart + row * S + j, kGaveUp, tag);   // the finalize takes over
+        return;
+    }
+    const float L2t = s_tot[0], L2d = s_tot[1];
+
+    // ---- phase 2: this member's share of alpha and of the residual mass ----
+    float al, rs;
+    pass2(tr, dr, ts, c, L2t, L2d, al, rs);
+    if constexpr (MODE == kTeamStoch) {
+        rs = fmaxf(wave_sum(rs), 0.f);
+        if (lane_id() == 0) putf(a.dir + row * a.nseg + j * kTeamWaves + w, rs, tag);
+    }
+    al = block_sumf(al, red);
+    if (threadIdx.x == 0) {
+        putf(a.apart + row * S + j, al, tag);
+        if (MODE == kTeamStoch && owner) {   // accept test and the row normalisers of this row
+            put(a.acc + 4 * row, (uint32_t)accept_test(zx_t, zx_d, c, L2t, L2d, a.seed, r, k, a.step), tag);
+            putf(a.acc + 4 * row + 1, L2t, tag);
+            putf(a.acc + 4 * row + 2, L2d, tag);
+        }
+    }
+}
+
+namespace {
+
+// Recompute member j's share of a row (alpha, and residual directory entries) from HBM;
+// used only when that member handed its share over.  Whole workgroup.
+template <int DTT, int DTD>
+__device__ float recompute_share(const TeamArgs &a, const void *trow, const void *drow, int j, float L2t, float L2d,
+                                 int64_t row, uint32_t tag, TeamRed &red, bool publish_dir) {
+    LaneRow<DTT> tr;
+    LaneRow<DTD> dr;
+    const int w = threadIdx.x / kWave;
+    const int base = j * kTeamChunk + w * kTeamSeg;
+    tr.load(trow, base, a.V);
+    dr.load(drow, base, a.V);
+    const ThreadStats s = pass1(tr, dr, tr.max(), dr.max(), a.c);
+    float al, rs;
+    pass2(tr, dr, s, a.c, L2t, L2d, al, rs);
+    rs = fmaxf(wave_sum(rs), 0.f);
+    if (publish_dir && lane_id() == 0) putf(a.dir + row * a.nseg + j * kTeamWaves + w, rs, tag);
+    return block_sumf(al, red);
+}
+
+// Workgroup-cooperative load of n tagged words into dst (payloads); returns the number of
+// words whose tag is not `tag` (their payload is replaced by `missing`).
+__device__ int load_tagged(const uint64_t *p, int n, uint32_t tag, uint32_t *dst, uint32_t missing) {
+    constexpr int U = 8;
+    int bad = 0;
+    for (int i0 = 0; i0 < n; i0 += U * kTeamThreads) {
+        uint64_t w[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * kTeamThreads + threadIdx.x;
+            w[u] = i < n ? peek(p + i) : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * kTeamThreads + threadIdx.x;
+            if (i < n) {
+                const bool ok = (uint32_t)(w[u] >> 32) == tag;
+                dst[i] = ok ? (uint32_t)w[u] : missing;
+                bad += ok ? 0 : 1;
+            }
+        }
+    }
+    return bad;
+}
+
+constexpr int kFinWords = 8192;   // LDS words staged per batch of rows
+
+}  // namespace
+
+// =======================================================================================
+// Finalize kernel: one workgroup per request
+// =======================================================================================
+template <int DTT, int DTD, int MODE>
+__global__ __launch_bounds__(kTeamThreads) void finalize_kernel(TeamArgs a) {
+    __shared__ TeamRed red;
+    __shared__ uint32_t stage[kFinWords];
+    __shared__ uint32_t pay[8 * 128 + 8];
+    __shared__ float s_mass[4 * 128 + 8];
+    __shared__ int s_tau, s_tok;
+    __shared__ float s_L2[2];
+    __shared__ int s_at;
+    __shared__ float s_rt[kTeamThreads], s_rd[kTeamThreads];
+    __shared__ int s_ra[kTeamThreads];
+
+    const int r = blockIdx.x;
+    const int K = a.K;
+    const int S = a.S;
+    const int nseg = a.nseg;
+    const int L = row_limit(a, r);
+    const uint32_t tag = read_epoch(a.epoch) + 1;
+    const int64_t row0 = (int64_t)r * a.slots;
+    const int64_t brow = row0 + K;   // the bonus slot
+    const float c = a.c;
+    const bool want_amax = (MODE == kTeamGreedy) || a.want_amax;
+
+    if (threadIdx.x == 0) { s_tau = L; s_at = 0; s_L2[0] = s_L2[1] = 0.f; }
+    __syncthreads();
+
+    // rows are staged in batches: acc [nb][4] | shares [nb][S] | directory [nb][4S] |
+    // argmax words [nb][4S], all in one gather
+    const int nA = (MODE == kTeamStoch) ? 4 : 0;
+    const int nB = (MODE != kTeamGreedy) ? S : 0;
+    const int nC = (MODE == kTeamStoch) ? nseg : 0;
+    const int nD = want_amax ? 4 * S : 0;
+    const int per_row = nA + nB + nC + nD;
+    const int batch = max(1, min(kTeamThreads, kFinWords / max(per_row, 1)));
+    for (int k0 = 0; k0 < L; k0 += batch) {
+        const int nb = min(batch, L - k0);
+        uint32_t *sx = stage;                // [nb][4]
+        uint32_t *sa = sx + nb * nA;         // [nb][S]
+        uint32_t *sd = sa + nb * nB;         // [nb][4S]
+        uint32_t *sm = sd + nb * nC;         // [nb][4S]
+        const int x_mine = threadIdx.x < nb ? a.tokens[(size_t)r * K + k0 + threadIdx.x] : 0;
+        {
+            const int n = nb * per_row;
+            constexpr int U = 8;
+            for (int i0 = 0; i0 < n; i0 += U * kTeamThreads) {
+                uint64_t wv[U];
+                uint32_t miss[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    int i = i0 + u * kTeamThreads + threadIdx.x;
+                    const uint64_t *src = nullptr;
+                    miss[u] = 0xffffffffu;
+                    if (i < n) {
+                        if (i < nb * nA) {
+                            src = a.acc + 4 * (row0 + k0) + i;
+                        } else if ((i -= nb * nA) < nb * nB) {
+                            src = a.apart + (row0 + k0) * S + i;
+                            miss[u] = kGaveUp;
+                        } else if ((i -= nb * nB) < nb * nC) {
+                            src = a.dir + (row0 + k0) * nseg + i;
+                            miss[u] = 0u;
+                        } else {
+                            i -= nb * nC;
+                            src = a.part + (row0 + k0 + i / (4 * S)) * 8 * S + 4 * S + i % (4 * S);
+                            miss[u] = 0x7fffffffu;
+                        }
+                    }
+                    wv[u] = src ? peek(src) : 0;
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int i = i0 + u * kTeamThreads + threadIdx.x;
+                    if (i < n) stage[i] = (uint32_t)(wv[u] >> 32) == tag ? (uint32_t)wv[u] : miss[u];
+                }
+            }
+        }
+        __syncthreads();
+
+        // rows whose normalisers were not published (a member handed over, or the drafted
+        // token is out of range): reduce the partials here
+        if constexpr (MODE == kTeamStoch) {
+            for (int q = 0; q < nb; ++q) {
+                if (sx[q * 4 + 1] != 0xffffffffu) continue;
+                load_tagged(a.part + (row0 + k0 + q) * 8 * S, 4 * S, tag, pay, 0u);
+                __syncthreads();
+                if (threadIdx.x == 0) {
+                    float L2t, L2d;
+                    team_totals(pay, S, L2t, L2d);
+                    sx[q * 4 + 1] = __float_as_uint(L2t);
+                    sx[q * 4 + 2] = __float_as_uint(L2d);
+                }
+                __syncthreads();
+            }
+        }
+        // handed-over shares: recompute them (and their directory entries) from HBM
+        if constexpr (MODE != kTeamGreedy) {
+            for (int q = 0; q < nb; ++q) {
+                for (int m = 0; m < S; ++m) {
+                    if (sa[q * S + m] != kGaveUp) continue;
+                    float L2t, L2d;
+                    if (MODE == kTeamStoch) {
+                        L2t = __uint_as_float(sx[q * 4 + 1]);
+                        L2d = __uint_as_float(sx[q * 4 + 2]);
+                    } else {
+                        load_tagged(a.part + (row0 + k0 + q) * 8 * S, 4 * S, tag, pay, 0u);
+                        __syncthreads();
+                        team_totals(pay, S, L2t, L2d);
+                    }
+                    const int k = k0 + q;
+                    const void *trow = row_ptr<DTT>(a.target, (int64_t)r * a.trows + k, a.ld_t);
+                    const void *drow = row_ptr<DTD>(a.draft, (int64_t)r * K + k, a.ld_d);
+                    const float sh = recompute_share<DTT, DTD>(a, trow, drow, m, L2t, L2d, row0 + k, tag, red,
+                                                               MODE == kTeamStoch);
+                    __syncthreads();
+                    if (threadIdx.x == 0) sa[q * S + m] = __float_as_uint(sh);
+                    if (MODE == kTeamStoch) {   // the fresh directory entries of this member
+                        load_tagged(a.dir + (row0 + k) * nseg + m * kTeamWaves, kTeamWaves, tag,
+                                    sd + q * nseg + m * kTeamWaves, 0u);
+                    }
+                    __syncthreads();
+                }
+            }
+        }
+
+        // one thread per row of the batch
+        if (threadIdx.x < nb) {
+            const int q = threadIdx.x;
+            const int k = k0 + q;
+            const size_t i = (size_t)r * K + k;
+            int at = 0, ad = 0;
+            if (want_amax) {
+                const uint32_t *pp = sm + q * 4 * S;
+                float bv = neg_inf(), bd = neg_inf();
+                int bi = 0x7fffffff, bj = 0x7fffffff;
+                for (int m = 0; m < S; ++m) {
+                    amax_merge(bv, bi, __uint_as_float(pp[m]), (int)pp[S + m]);
+                    amax_merge(bd, bj, __uint_as_float(pp[2 * S + m]), (int)pp[3 * S + m]);
+                }
+                at = bi == 0x7fffffff ? 0 : bi;
+                ad = bj == 0x7fffffff ? 0 : bj;
+            }
+            const int x = x_mine;
+            const bool okx = x >= 0 && x < a.V;
+            if (!okx) atomicOr(a.err, SV_DEVERR_TOKEN);
+            float alpha, L2t = 0.f, L2d = 0.f;
+            int acc;
+            if constexpr (MODE == kTeamGreedy) {
+                alpha = (at == ad) ? 1.f : 0.f;
+                acc = okx && x == at;
+            } else {
+                double sum = 0.0;
+                for (int m = 0; m < S; ++m) sum += (double)__uint_as_float(sa[q * S + m]);
+                alpha = (float)sum;
+                L2t = __uint_as_float(sx[q * 4 + 1]);
+                L2d = __uint_as_float(sx[q * 4 + 2]);
+                if (sx[q * 4] != 0xffffffffu) {
+                    acc = (int)sx[q * 4];
+                } else if (okx) {   // the owner member handed over: run the test here
+                    const float zt = load1<DTT>(row_ptr<DTT>(a.target, (int64_t)r * a.trows + k, a.ld_t), x);
+                    const float zd = load1<DTD>(row_ptr<DTD>(a.draft, (int64_t)r * K + k, a.ld_d), x);
+                    acc = accept_test(zt, zd, c, L2t, L2d, a.seed, r, k, a.step);
+                } else {
+                    acc = 0;
+                }
+            }
+            a.alpha[i] = alpha;
+            a.accept[i] = (uint8_t)acc;
+            if (a.lse_t) a.lse_t[i] = (MODE == kTeamStoch) ? L2t * 0.69314718055994531f : 0.f;
+            if (a.lse_d) a.lse_d[i] = (MODE == kTeamStoch) ? L2d * 0.69314718055994531f : 0.f;
+            if (a.amax_t) a.amax_t[i] = want_amax ? at : -1;
+            if (a.amax_d) a.amax_d[i] = want_amax ? ad : -1;
+            if (!acc) atomicMin(&s_tau, k);
+            s_rt[q] = L2t;
+            s_rd[q] = L2d;
+            s_ra[q] = at;
+        }
+        __syncthreads();
+        const int tau = s_tau;
+        if (tau >= k0 && tau < k0 + nb) {
+            // keep what the draw after the rejection at tau needs
+            if (threadIdx.x == 0) {
+                s_L2[0] = s_rt[tau - k0];
+                s_L2[1] = s_rd[tau - k0];
+                s_at = s_ra[tau - k0];
+            }
+            if (MODE == kTeamStoch)
+                for (int q = threadIdx.x; q < nseg; q += kTeamThreads) s_mass[q] = __uint_as_float(sd[(tau - k0) * nseg + q]);
+        }
+        __syncthreads();
+    }
+
+    const int tau = s_tau;
+    int tok = 0;
+    const void *trow = row_ptr<DTT>(a.target, (int64_t)r * a.trows + tau, a.ld_t);
+    if (tau == L) {
+        // every draft accepted: the bonus token from the bonus slot's published states
         if (threadIdx.x < kWave) {
-            const bool got = wave_poll(a.rec + row0 + k0, n, tag, pay, a.spin_ticks_max);
+            // one pass: the stream kernel has written them (greedy: argmax words 4S..6S only)
+            const bool got = MODE == kTeamGreedy ? wave_poll(a.part + brow * 8 * S + 4 * S, 2 * S, tag, pay + 4 * S, 0)
+                                                 : wave_poll(a.part + brow * 8 * S, 8 * S, tag, pay, 0);
             if (!got && threadIdx.x == 0) atomicOr(a.err, SV_DEVERR_TIMEOUT);
         }
         __syncthreads();
-        for (int q = threadIdx.x; q < n; q += kTeamThreads)
-            if (pay[q] == 0) atomicMin(&s_tau, k0 + q);
-        __syncthreads();
-    }
-    const int tau = s_tau;
-    (void)ok;
-
-    int tok = 0;
-    const void *trow = static_cast<const char *>(a.target) +
-                       (size_t)((r * (int64_t)a.trows + tau) * a.ld_t) * (DTT == kDtBF16 ? 2 : 4);
-    if constexpr (MODE == kTeamGreedy) {
-        if (tau < L) {
-            if (threadIdx.x < kWave) wave_poll(a.rec + rows + row0 + tau, 1, tag, pay, a.spin_ticks_max);
+        if constexpr (MODE == kTeamGreedy) {
+            if (threadIdx.x == 0) {
+                float bv = neg_inf();
+                int bi = 0x7fffffff;
+                for (int m = 0; m < S; ++m) amax_merge(bv, bi, __uint_as_float(pay[4 * S + m]), (int)pay[5 * S + m]);
+                s_at = bi == 0x7fffffff ? 0 : bi;
+            }
             __syncthreads();
-            tok = (int)pay[0];
-            __syncthreads();
+            tok = s_at;
         } else {
-            tok = row_argmax<DTT>(trow, a.V, red);
-        }
-    } else {
-        const float u = uniform24(a.seed, (uint64_t)r, (uint64_t)tau, kPurposeCorrection, a.step);
-        bool done = false;
-        if (tau < L) {
-            const int64_t row = row0 + tau;
-            const int nseg = a.nseg;
-            // payloads: [0, nseg) directory, nseg: L2t, nseg + 1: L2d
-            if (threadIdx.x < kWave) {
-                bool g1 = wave_poll(a.dir + row * nseg, nseg, tag, pay, a.spin_ticks_max);
-                bool g2 = wave_poll(a.rec + 2 * rows + row, 1, tag, pay + nseg, a.spin_ticks_max);
-                bool g3 = wave_poll(a.rec + 3 * rows + row, 1, tag, pay + nseg + 1, a.spin_ticks_max);
-                if (!(g1 && g2 && g3) && threadIdx.x == 0) atomicOr(a.err, SV_DEVERR_TIMEOUT);
+            if (threadIdx.x == 0) {
+                float M = neg_inf(), sm = 0.f;
+                for (int m = 0; m < S; ++m)
+                    for (int w = 0; w < kTeamWaves; ++w)
+                        ms_merge(M, sm, __uint_as_float(pay[(2 * w) * S + m]), __uint_as_float(pay[(2 * w + 1) * S + m]));
+                s_L2[0] = M + log2f(sm);
             }
             __syncthreads();
-            float *dirv = reinterpret_cast<float *>(pay);
-            const float L2t = dirv[nseg], L2d = dirv[nseg + 1];
+            const float L2 = s_L2[0];
+            for (int q = threadIdx.x; q < nseg; q += kTeamThreads) {
+                const int m = q / kTeamWaves, w = q % kTeamWaves;
+                const float Mq = __uint_as_float(pay[(2 * w) * S + m]), sq = __uint_as_float(pay[(2 * w + 1) * S + m]);
+                s_mass[q] = (Mq == neg_inf()) ? 0.f : sq * exp2_fast(Mq - L2);
+            }
+            __syncthreads();
             double R = 0.0;
-            for (int q = 0; q < nseg; ++q) R += (double)dirv[q];
-            if (R > 0.0) {
-                const void *drow = static_cast<const char *>(a.draft) +
-                                   (size_t)((row0 + tau) * a.ld_d) * (DTD == kDtBF16 ? 2 : 4);
-                const int t = draw_residual<DTT, DTD>(trow, drow, a.V, a.c, L2t, L2d, dirv, nseg, (double)u * R, red);
-                if (t >= 0) { tok = t; done = true; }
-            }
-            __syncthreads();
+            for (int q = 0; q < nseg; ++q) R += (double)s_mass[q];
+            const float u = uniform24(a.seed, (uint64_t)r, (uint64_t)tau, kPurposeCorrection, a.step);
+            tok = draw_ranges<DTT, DTD, false>(trow, nullptr, a.V, c, L2, 0.f, s_mass, nseg, (double)u * R, red);
+            if (tok < 0) tok = 0;
         }
-        if (!done) tok = draw_from_row<DTT>(trow, a.V, a.c, u, a.bonus + (size_t)r * 2 * a.nseg_b, a.nseg_b, red);
+    } else if constexpr (MODE == kTeamGreedy) {
+        tok = s_at;
+    } else {
+        // rejection at tau: the residual max(p - q, 0) of row tau
+        const float u = uniform24(a.seed, (uint64_t)r, (uint64_t)tau, kPurposeCorrection, a.step);
+        double R = 0.0;
+        for (int q = 0; q < nseg; ++q) R += (double)s_mass[q];
+        bool done = false;
+        if (R > 0.0) {
+            const void *drow = row_ptr<DTD>(a.draft, (int64_t)r * K + tau, a.ld_d);
+            const int t = draw_ranges<DTT, DTD, true>(trow, drow, a.V, c, s_L2[0], s_L2[1], s_mass, nseg, (double)u * R, red);
+            if (t >= 0) { tok = t; done = true; }
+        }
+        __syncthreads();
+        // an empty residual (p == q everywhere in binary32): draw from p_tau
+        if (!done) tok = draw_from_row<DTT>(trow, a.V, c, u, a.bonus + (size_t)r * 2 * a.nseg_b, a.nseg_b, red);
     }
     if (threadIdx.x == 0) s_tok = tok;
     __syncthreads();
@@ -503,276 +934,91 @@ __device__ void request_finalize(const TeamArgs &a, int r, int L, uint32_t tag, 
         a.accept_len[r] = tau;
         a.n_out[r] = tau + 1;
         // the last request of the call advances the epoch for the next call
-        const int old = atomicAdd(a.gdone, 1);
-        if (old == a.B - 1) {
+        if (atomicAdd(a.gdone, 1) == a.B - 1) {
             __hip_atomic_store(a.gdone, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(a.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
 
-// Recompute member j's share of a row from HBM (used only when that member gave up).
+// =======================================================================================
+// L_e2e: alpha of each row from the member shares (one thread per row)
+// =======================================================================================
 template <int DTT, int DTD>
-__device__ float recompute_share(const TeamArgs &a, const void *trow, const void *drow, int j, float L2t, float L2d,
-                                 int64_t row, uint32_t tag, TeamRed &red, bool publish_dir) {
-    Chunk ch;
-    const int w = threadIdx.x / kWave;
-    const int base = j * kTeamChunk + w * kTeamSeg;
-    load_chunk<DTT, DTD>(ch, trow, drow, base, a.V);
-    const ThreadStats s = pass1(ch, a.c);
-    float al, rs;
-    pass2(ch, s, L2t, L2d, al, rs);
-    rs = wave_sum(rs);
-    if (publish_dir && lane_id() == 0) putf(a.dir + row * a.nseg + j * kTeamWaves + w, rs, tag);
-    return block_sumf(al, red);
-}
-
-}  // namespace
-
-template <int DTT, int DTD, int MODE>
-__global__ __launch_bounds__(kTeamThreads) void team_kernel(TeamArgs a) {
+__global__ __launch_bounds__(kTeamThreads) void e2e_alpha_kernel(TeamArgs a) {
     __shared__ TeamRed red;
-    __shared__ uint32_t pay[2048 + 8];
-    __shared__ int s_flag, s_rank;
-    __shared__ float s_tot[8];
-
-    const int S = a.S;
-    const int j = blockIdx.x % S;
-    const int64_t row = blockIdx.x / S;
-    const int K = a.K;
-    const int slots = K > 0 ? K : 1;
-    const int r = (int)(row / slots);
-    const int k = (int)(row % slots);
-    int L = K;
-    if (MODE != kTeamAlpha && a.draft_len) {
-        L = a.draft_len[r];
-        if (L < 0 || L > K) {
-            if (threadIdx.x == 0 && k == 0 && j == 0) atomicOr(a.err, SV_DEVERR_DRAFT_LEN);
-            L = L < 0 ? 0 : K;
-        }
-    }
-    if (k >= L) {
-        if (MODE != kTeamAlpha && L == 0 && k == 0 && j == 0) {
-            const uint32_t tag = read_epoch(a.epoch) + 1;
-            request_finalize<DTT, DTD, MODE>(a, r, 0, tag, red, pay);
-        }
-        return;
-    }
+    __shared__ int s_list[kTeamThreads], s_n;
+    __shared__ uint32_t pay[4 * 128 + 8];
+    const int64_t rows = (int64_t)a.B * a.K;
+    const int64_t row = (int64_t)blockIdx.x * kTeamThreads + threadIdx.x;
     const uint32_t tag = read_epoch(a.epoch) + 1;
-    const int64_t rows = (int64_t)a.B * slots;
-    const size_t et = DTT == kDtBF16 ? 2 : 4, ed = DTD == kDtBF16 ? 2 : 4;
-    const void *trow = static_cast<const char *>(a.target) + (size_t)(((int64_t)r * a.trows + k) * a.ld_t) * et;
-    const void *drow = static_cast<const char *>(a.draft) + (size_t)(row * a.ld_d) * ed;
-    const int w = threadIdx.x / kWave;
-    const int base = j * kTeamChunk + w * kTeamSeg;
-    const float c = a.c;
-
-    Chunk ch;
-    load_chunk<DTT, DTD>(ch, trow, drow, base, a.V);
-
-    // ---------------- phase 1: per-member partials ----------------
-    uint64_t *part = a.part + row * (int64_t)(8 * S);
-    const bool want_amax = (MODE == kTeamGreedy) || a.want_amax;
-    float vt = neg_inf(), vd = neg_inf();
-    int it = 0x7fffffff, id = 0x7fffffff;
-    if (want_amax) {
-        vt = max_of(ch.xt);
-        vd = max_of(ch.xd);
-        it = vt == neg_inf() ? 0x7fffffff : first_index_of(ch.xt, vt, base);
-        id = vd == neg_inf() ? 0x7fffffff : first_index_of(ch.xd, vd, base);
-        block_amax2(vt, it, vd, id, red);
+    const int S = a.S;
+    if (threadIdx.x == 0) s_n = 0;
+    __syncthreads();
+    double sum = 0.0;
+    bool handed = false;
+    if (row < rows) {
+        for (int m = 0; m < S; ++m) {
+            const uint64_t w = peek(a.apart + row * S + m);
+            if ((uint32_t)(w >> 32) != tag || (uint32_t)w == kGaveUp) { handed = true; break; }
+            sum += (double)__uint_as_float((uint32_t)w);
+        }
+        if (handed) s_list[atomicAdd(&s_n, 1)] = threadIdx.x;
+        else a.alpha[row] = (float)sum;
     }
-    ThreadStats ts{};
-    float Mt = neg_inf(), st = 0.f, Md = neg_inf(), sd = 0.f;
-    if constexpr (MODE != kTeamGreedy) {
-        ts = pass1(ch, c);
-        Mt = ts.Mt; st = ts.st; Md = ts.Md; sd = ts.sd;
-        block_ms2(Mt, st, Md, sd, red);
-    }
-    int my_rank = -1;
-    if (threadIdx.x == 0) {
-        if constexpr (MODE != kTeamGreedy) {
-            putf(part + 0 * S + j, Mt, tag);
-            putf(part + 1 * S + j, st, tag);
-            putf(part + 2 * S + j, Md, tag);
-            putf(part + 3 * S + j, sd, tag);
-        }
-        if (want_amax) {
-            putf(part + 4 * S + j, vt, tag);
-            put(part + 5 * S + j, (uint32_t)it, tag);
-            putf(part + 6 * S + j, vd, tag);
-            put(part + 7 * S + j, (uint32_t)id, tag);
-        }
-        my_rank = atomicAdd(a.row_cnt + row, 1);
-    }
-
-    if constexpr (MODE == kTeamGreedy) {
-        if (threadIdx.x == 0) s_rank = my_rank;
+    __syncthreads();
+    // rows with a handed-over share: recompute the whole row's alpha (rare)
+    for (int q = 0; q < s_n; ++q) {
+        const int64_t rr = (int64_t)blockIdx.x * kTeamThreads + s_list[q];
+        load_tagged(a.part + rr * 8 * S, 4 * S, tag, pay, 0u);
         __syncthreads();
-        if (s_rank != S - 1) return;
-    }
-
-    // ---------------- row normalisers: every member reduces all partials ----------------
-    float L2t = 0.f, L2d = 0.f;
-    if constexpr (MODE != kTeamGreedy) {
-        if (threadIdx.x < kWave) {
-            bool got = wave_poll(part, 4 * S, tag, pay, a.spin_ticks);
-            int flag = got ? 1 : 0;
-            if (!got) {
-                // only the last arriver is sure that every partial has been written
-                const int rank = __shfl(my_rank, 0, kWave);
-                if (rank == S - 1) {
-                    got = wave_poll(part, 4 * S, tag, pay, a.spin_ticks_max);
-                    if (!got && threadIdx.x == 0) atomicOr(a.err, SV_DEVERR_TIMEOUT);
-                    flag = 1;
-                }
-            }
-            if (threadIdx.x == 0) {
-                float Tt = neg_inf(), Ts = 0.f, Dt = neg_inf(), Ds = 0.f;
-                for (int q = 0; q < S; ++q) {
-                    ms_merge(Tt, Ts, __uint_as_float(pay[q]), __uint_as_float(pay[S + q]));
-                    ms_merge(Dt, Ds, __uint_as_float(pay[2 * S + q]), __uint_as_float(pay[3 * S + q]));
-                }
-                s_tot[0] = Tt + log2f(Ts);
-                s_tot[1] = Dt + log2f(Ds);
-                s_flag = flag;
-                s_rank = my_rank;
-            }
-        }
+        float L2t, L2d;
+        team_totals(pay, S, L2t, L2d);
+        const int ri = (int)(rr / a.K), ki = (int)(rr % a.K);
+        const void *trow = row_ptr<DTT>(a.target, (int64_t)ri * a.trows + ki, a.ld_t);
+        const void *drow = row_ptr<DTD>(a.draft, rr, a.ld_d);
+        double t = 0.0;
+        for (int m = 0; m < S; ++m) t += (double)recompute_share<DTT, DTD>(a, trow, drow, m, L2t, L2d, rr, tag, red, false);
+        if (threadIdx.x == 0) a.alpha[rr] = (float)t;
         __syncthreads();
-        if (!s_flag) {
-            // gave up waiting: hand this member's share to the last arriver
-            if (threadIdx.x == 0) put(a.apart + row * S + j, kGaveUp, tag);
-            return;
-        }
-        L2t = s_tot[0];
-        L2d = s_tot[1];
-
-        // ---------------- phase 2: this member's share of alpha and residual mass -------------
-        float al, rs;
-        pass2(ch, ts, L2t, L2d, al, rs);
-        if constexpr (MODE == kTeamStoch) {
-            rs = wave_sum(rs);
-            if (lane_id() == 0) putf(a.dir + row * a.nseg + j * kTeamWaves + w, rs, tag);
-        }
-        al = block_sumf(al, red);
-        if (threadIdx.x == 0) putf(a.apart + row * S + j, al, tag);
-        if (s_rank != S - 1) return;
-    }
-
-    // ---------------- the last arriver completes the row ----------------
-    float alpha = 0.f;
-    int at = 0, ad = 0;
-    if (want_amax) {
-        if (threadIdx.x < kWave) {
-            const bool got = wave_poll(part + 4 * S, 4 * S, tag, pay, a.spin_ticks_max);
-            if (!got && threadIdx.x == 0) atomicOr(a.err, SV_DEVERR_TIMEOUT);
-            if (threadIdx.x == 0) {
-                float bv = neg_inf(), bd = neg_inf();
-                int bi = 0x7fffffff, bj = 0x7fffffff;
-                for (int q = 0; q < S; ++q) {
-                    amax_merge(bv, bi, __uint_as_float(pay[q]), (int)pay[S + q]);
-                    amax_merge(bd, bj, __uint_as_float(pay[2 * S + q]), (int)pay[3 * S + q]);
-                }
-                red.i[2][0] = bi == 0x7fffffff ? 0 : bi;
-                red.i[3][0] = bj == 0x7fffffff ? 0 : bj;
-            }
-        }
-        __syncthreads();
-        at = red.i[2][0];
-        ad = red.i[3][0];
-        __syncthreads();
-    }
-    if constexpr (MODE != kTeamGreedy) {
-        if (threadIdx.x < kWave) {
-            const bool got = wave_poll(a.apart + row * S, S, tag, pay, a.spin_ticks_max);
-            if (!got && threadIdx.x == 0) atomicOr(a.err, SV_DEVERR_TIMEOUT);
-        }
-        __syncthreads();
-        // members that gave up: recompute their shares (and directory entries) from HBM
-        for (int q = 0; q < S; ++q) {
-            if (pay[q] == kGaveUp) {
-                const float sh = recompute_share<DTT, DTD>(a, trow, drow, q, L2t, L2d, row, tag, red, MODE == kTeamStoch);
-                __syncthreads();
-                if (threadIdx.x == 0) pay[q] = __float_as_uint(sh);
-                __syncthreads();
-            }
-        }
-        if (threadIdx.x == 0) {
-            double s = 0.0;
-            for (int q = 0; q < S; ++q) s += (double)__uint_as_float(pay[q]);
-            s_tot[2] = (float)s;
-        }
-        __syncthreads();
-        alpha = s_tot[2];
-    }
-
-    if constexpr (MODE == kTeamAlpha) {
-        if (threadIdx.x == 0) {
-            a.alpha[row] = alpha;
-            __hip_atomic_store(a.row_cnt + row, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            // epoch advance once every row of the call is complete (grouped counters)
-            const int g = (int)(row / 256);
-            const int gsize = (int)min((int64_t)256, rows - (int64_t)g * 256);
-            if (atomicAdd(a.grp_cnt + g, 1) == gsize - 1) {
-                __hip_atomic_store(a.grp_cnt + g, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (atomicAdd(a.gdone, 1) == a.n_grp - 1) {
-                    __hip_atomic_store(a.gdone, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(a.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
-            }
-        }
-        return;
-    } else {
-        if (threadIdx.x == 0) {
-            const size_t i = (size_t)r * K + k;
-            const int x = a.tokens[i];
-            const bool okx = (x >= 0 && x < a.V);
-            if (!okx) atomicOr(a.err, SV_DEVERR_TOKEN);
-            int acc = 0;
-            if constexpr (MODE == kTeamGreedy) {
-                acc = okx && x == at;
-                alpha = (at == ad) ? 1.f : 0.f;
-            } else if (okx) {
-                // accept iff u * q(x) < p(x)
-                const float lpt = __builtin_fmaf(load1<DTT>(trow, x), c, -L2t);
-                const float lpd = __builtin_fmaf(load1<DTD>(drow, x), c, -L2d);
-                const float u = uniform24(a.seed, (uint64_t)r, (uint64_t)k, kPurposeAccept, a.step);
-                acc = u < exp2f(lpt - lpd);
-            }
-            a.alpha[i] = alpha;
-            a.accept[i] = (uint8_t)acc;
-            if (a.lse_t) a.lse_t[i] = (MODE == kTeamStoch) ? L2t * 0.69314718055994531f : 0.f;
-            if (a.lse_d) a.lse_d[i] = (MODE == kTeamStoch) ? L2d * 0.69314718055994531f : 0.f;
-            if (a.amax_t) a.amax_t[i] = want_amax ? at : -1;
-            if (a.amax_d) a.amax_d[i] = want_amax ? ad : -1;
-            put(a.rec + 0 * rows + row, (uint32_t)acc, tag);
-            put(a.rec + 1 * rows + row, (uint32_t)at, tag);
-            putf(a.rec + 2 * rows + row, L2t, tag);
-            putf(a.rec + 3 * rows + row, L2d, tag);
-            __hip_atomic_store(a.row_cnt + row, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const int old = atomicAdd(a.req_cnt + r, 1);
-            s_flag = (old == L - 1);
-            if (s_flag) __hip_atomic_store(a.req_cnt + r, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        __syncthreads();
-        if (s_flag) request_finalize<DTT, DTD, MODE>(a, r, L, tag, red, pay);
     }
 }
 
 template <int DTT, int DTD>
-static hipError_t launch_mode(const TeamArgs &a, int mode, unsigned grid, hipStream_t s) {
-    if (mode == kTeamStoch) hipLaunchKernelGGL((team_kernel<DTT, DTD, kTeamStoch>), dim3(grid), dim3(kTeamThreads), 0, s, a);
-    else if (mode == kTeamGreedy) hipLaunchKernelGGL((team_kernel<DTT, DTD, kTeamGreedy>), dim3(grid), dim3(kTeamThreads), 0, s, a);
-    else hipLaunchKernelGGL((team_kernel<DTT, DTD, kTeamAlpha>), dim3(grid), dim3(kTeamThreads), 0, s, a);
+static hipError_t launch_stream_t(const TeamArgs &a, int mode, unsigned grid, hipStream_t s) {
+    if (mode == kTeamStoch) hipLaunchKernelGGL((stream_kernel<DTT, DTD, kTeamStoch>), dim3(grid), dim3(kTeamThreads), 0, s, a);
+    else if (mode == kTeamGreedy) hipLaunchKernelGGL((stream_kernel<DTT, DTD, kTeamGreedy>), dim3(grid), dim3(kTeamThreads), 0, s, a);
+    else hipLaunchKernelGGL((stream_kernel<DTT, DTD, kTeamAlpha>), dim3(grid), dim3(kTeamThreads), 0, s, a);
     return hipGetLastError();
 }
 
-hipError_t team_launch(const TeamArgs &a, int dt, int dd, int mode, unsigned grid, hipStream_t s) {
-    if (dt == SV_BF16 && dd == SV_BF16) return launch_mode<kDtBF16, kDtBF16>(a, mode, grid, s);
-    if (dt == SV_F32 && dd == SV_F32) return launch_mode<kDtF32, kDtF32>(a, mode, grid, s);
-    if (dt == SV_BF16 && dd == SV_F32) return launch_mode<kDtBF16, kDtF32>(a, mode, grid, s);
-    return launch_mode<kDtF32, kDtBF16>(a, mode, grid, s);
+template <int DTT, int DTD>
+static hipError_t launch_finalize_t(const TeamArgs &a, int mode, hipStream_t s) {
+    if (mode == kTeamStoch) hipLaunchKernelGGL((finalize_kernel<DTT, DTD, kTeamStoch>), dim3(a.B), dim3(kTeamThreads), 0, s, a);
+    else hipLaunchKernelGGL((finalize_kernel<DTT, DTD, kTeamGreedy>), dim3(a.B), dim3(kTeamThreads), 0, s, a);
+    return hipGetLastError();
 }
+
+template <int DTT, int DTD>
+static hipError_t launch_e2e_t(const TeamArgs &a, hipStream_t s) {
+    const int64_t rows = (int64_t)a.B * a.K;
+    hipLaunchKernelGGL((e2e_alpha_kernel<DTT, DTD>), dim3((unsigned)((rows + kTeamThreads - 1) / kTeamThreads)),
+                       dim3(kTeamThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+#define SV_DISPATCH(F, ...)                                                        \
+    if (dt == SV_BF16 && dd == SV_BF16) return F<kDtBF16, kDtBF16>(__VA_ARGS__);   \
+    if (dt == SV_F32 && dd == SV_F32) return F<kDtF32, kDtF32>(__VA_ARGS__);       \
+    if (dt == SV_BF16 && dd == SV_F32) return F<kDtBF16, kDtF32>(__VA_ARGS__);     \
+    return F<kDtF32, kDtBF16>(__VA_ARGS__);
+
+hipError_t team_launch_stream(const TeamArgs &a, int dt, int dd, int mode, unsigned grid, hipStream_t s) {
+    SV_DISPATCH(launch_stream_t, a, mode, grid, s)
+}
+hipError_t team_launch_finalize(const TeamArgs &a, int dt, int dd, int mode, hipStream_t s) {
+    SV_DISPATCH(launch_finalize_t, a, mode, s)
+}
+hipError_t team_launch_e2e_alpha(const TeamArgs &a, int dt, int dd, hipStream_t s) { SV_DISPATCH(launch_e2e_t, a, s) }
 
 }  // namespace sv

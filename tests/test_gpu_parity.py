@@ -269,3 +269,23 @@ def test_workspace_reuse_across_calls_and_modes(sv):
         for k in a:
             assert np.array_equal(a[k], b[k]), (i, k)
     assert sv.sv_device_error(buf) == 0
+
+
+@pytest.mark.parametrize("T", [0.9, 0.0])
+def test_all_accepted_bonus_token(sv, T):
+    """Drafter logits equal to the target's: every draft is accepted (u < p/q = 1) and the
+    bonus token is drawn from the target row at L_r, for dense and ragged lengths."""
+    v = workloads.make_verify_inputs("dfly", device=DEV, T=T, B=6)
+    draft = v.target[:, :-1].contiguous()
+    z = draft.float()
+    if T > 0:
+        g = torch.Generator(device=DEV).manual_seed(5)
+        u = torch.rand(z.shape, generator=g, device=DEV).clamp_(min=1e-20)
+        z = z / T - torch.log(-torch.log(u))
+    toks = torch.argmax(z, -1).to(torch.int32)
+    w = workloads.VerifyInputs(v.target, draft, toks, T, v.seed, "dfly-all-accepted")
+    g_, o, rep = _run_pair(sv, w, T)
+    assert (o["accept_len"] == 16).all()
+    dl = np.array([16, 0, 5, 1, 16, 9], np.int32)
+    g2, o2, rep2 = _run_pair(sv, w, T, draft_len=dl)
+    assert (o2["accept_len"] == dl).all()
