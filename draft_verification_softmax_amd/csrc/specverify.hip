@@ -484,6 +484,7 @@ void fill_team_args(TeamArgs &a, const sv_params *p, const TeamLayout &L, char *
     a.seed = p->seed;
     a.step = p->step;
     a.spin_ticks = 20000;  // 200 us: then a member hands its share to the finalize kernel
+    a.rows = L.rows;
 }
 
 }  // namespace

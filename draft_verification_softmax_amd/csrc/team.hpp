@@ -16,7 +16,8 @@
 //
 // Each request also has a bonus slot: its members read the target row at the request's
 // draft length L_r (the row the bonus token is drawn from when every draft is accepted)
-// and publish per-wave-range log-sum-exp states (argmax in greedy mode) without waiting.
+// and publish per-wave-range masses against a per-member reference (argmax in greedy
+// mode) without waiting.
 //
 // Finalize kernel (one workgroup per request, after the stream kernel): sums the shares
 // in member order, recomputes handed-over shares from HBM, and runs the first-reject scan
@@ -36,6 +37,7 @@ constexpr int kTeamE = 64;                          // logits per lane per row h
 constexpr int kTeamChunk = kTeamThreads * kTeamE;   // logits of each row per member
 constexpr int kTeamSeg = 64 * kTeamE;               // one wave's contiguous range
 constexpr int kBonusSeg = 512;                      // segment of the single-row bonus draw
+constexpr int kXcds = 8;                            // accelerator complex dies of an MI355X
 
 enum TeamMode { kTeamStoch = 0, kTeamGreedy = 1, kTeamAlpha = 2 };
 
@@ -65,7 +67,8 @@ struct TeamArgs {
     uint32_t *err, *epoch;
     int32_t *gdone;
     uint64_t *part;    // [rows][8][S]: M_t, s_t, M_d, s_d, argmax value/index of both rows;
-                       // bonus slots: (M, s) of each of the member's 4 wave ranges
+                       // bonus slots: the member's base-2 reference (stochastic)
+    // dir of a bonus slot: per wave range, sum 2^{z c - M_member}
     uint64_t *apart;   // [rows][S]   alpha share of each member (or the hand-over marker)
     uint64_t *dir;     // [rows][4 S] residual mass of each kTeamSeg-logit wave range
     uint64_t *acc;     // [rows][4]   accept flag, L2t, L2d (from the member holding the token)
@@ -74,6 +77,7 @@ struct TeamArgs {
     int32_t B, K, V, S, nseg, nseg_b;
     int32_t trows;     // target rows per request (K+1 verification, K for L_e2e)
     int32_t slots;     // row slots per request (K+1 verification: the last is the bonus row)
+    int64_t rows;      // B * slots
     float c;           // log2(e) / T
     uint64_t seed, step;
     int32_t want_amax;

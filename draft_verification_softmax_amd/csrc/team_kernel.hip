@@ -473,6 +473,8 @@ __global__ __launch_bounds__(kTeamThreads) void stream_kernel(TeamArgs a) {
     __shared__ float s_tot[2];
     __shared__ int s_ok;
 
+    // The S members of a team are consecutive workgroups: round-robin dispatch spreads them
+    // over the XCDs, whose dispatchers start them at nearly the same time.
     const int S = a.S;
     const int j = blockIdx.x % S;
     const int64_t row = blockIdx.x / S;
@@ -515,12 +517,18 @@ __global__ __launch_bounds__(kTeamThreads) void stream_kernel(TeamArgs a) {
                 put(part + 5 * S + j, (uint32_t)ib, tag);
             }
         } else {
+            // per wave range: sum 2^{z c - Mj} against the member's reference Mj (the largest
+            // wave maximum), so the finalize needs one directory word per range
             float M = (mb == neg_inf()) ? neg_inf() : mb * c;
             float sm = (mb == neg_inf()) ? 0.f : br.exp_sum(c, M);
             wave_ms(M, sm);
+            if (lane_id() == 0) red.f[0][w] = M;
+            __syncthreads();
+            float Mj = red.f[0][0];
+            for (int q = 1; q < kTeamWaves; ++q) Mj = fmaxf(Mj, red.f[0][q]);
             if (lane_id() == 0) {
-                putf(part + (2 * w) * S + j, M, tag);
-                putf(part + (2 * w + 1) * S + j, sm, tag);
+                putf(a.dir + row * a.nseg + j * kTeamWaves + w, (M == neg_inf()) ? 0.f : sm * exp2_fast(M - Mj), tag);
+                if (w == 0) putf(part + j, Mj, tag);
             }
         }
         return;
@@ -667,9 +675,9 @@ template <int DTT, int DTD, int MODE>
 __global__ __launch_bounds__(kTeamThreads) void finalize_kernel(TeamArgs a) {
     __shared__ TeamRed red;
     __shared__ uint32_t stage[kFinWords];
-    __shared__ uint32_t pay[8 * 128 + 8];
-    __shared__ float s_mass[4 * 128 + 8];
-    __shared__ int s_tau, s_tok;
+    __shared__ uint32_t pay[8 * 128 + 512 + 8];
+    __shared__ float s_mass[512 + 8];
+    __shared__ int s_tau, s_tok, s_flags;
     __shared__ float s_L2[2];
     __shared__ int s_at;
     __shared__ float s_rt[kTeamThreads], s_rd[kTeamThreads];
@@ -741,9 +749,22 @@ __global__ __launch_bounds__(kTeamThreads) void finalize_kernel(TeamArgs a) {
         }
         __syncthreads();
 
+        // any row whose normalisers were not published, or any handed-over share?
+        if (threadIdx.x == 0) s_flags = 0;
+        __syncthreads();
+        {
+            int f = 0;
+            if (MODE == kTeamStoch)
+                for (int q = threadIdx.x; q < nb; q += kTeamThreads) f |= (sx[q * 4 + 1] == 0xffffffffu) ? 1 : 0;
+            if (MODE != kTeamGreedy)
+                for (int q = threadIdx.x; q < nb * S; q += kTeamThreads) f |= (sa[q] == kGaveUp) ? 2 : 0;
+            if (f) atomicOr(&s_flags, f);
+        }
+        __syncthreads();
+        const int flags = s_flags;
         // rows whose normalisers were not published (a member handed over, or the drafted
         // token is out of range): reduce the partials here
-        if constexpr (MODE == kTeamStoch) {
+        if (MODE == kTeamStoch && (flags & 1)) {
             for (int q = 0; q < nb; ++q) {
                 if (sx[q * 4 + 1] != 0xffffffffu) continue;
                 load_tagged(a.part + (row0 + k0 + q) * 8 * S, 4 * S, tag, pay, 0u);
@@ -758,7 +779,7 @@ __global__ __launch_bounds__(kTeamThreads) void finalize_kernel(TeamArgs a) {
             }
         }
         // handed-over shares: recompute them (and their directory entries) from HBM
-        if constexpr (MODE != kTeamGreedy) {
+        if (MODE != kTeamGreedy && (flags & 2)) {
             for (int q = 0; q < nb; ++q) {
                 for (int m = 0; m < S; ++m) {
                     if (sa[q * S + m] != kGaveUp) continue;
@@ -862,7 +883,7 @@ __global__ __launch_bounds__(kTeamThreads) void finalize_kernel(TeamArgs a) {
         if (threadIdx.x < kWave) {
             // one pass: the stream kernel has written them (greedy: argmax words 4S..6S only)
             const bool got = MODE == kTeamGreedy ? wave_poll(a.part + brow * 8 * S + 4 * S, 2 * S, tag, pay + 4 * S, 0)
-                                                 : wave_poll(a.part + brow * 8 * S, 8 * S, tag, pay, 0);
+                                                 : wave_poll(a.part + brow * 8 * S, S, tag, pay, 0);
             if (!got && threadIdx.x == 0) atomicOr(a.err, SV_DEVERR_TIMEOUT);
         }
         __syncthreads();
@@ -876,19 +897,26 @@ __global__ __launch_bounds__(kTeamThreads) void finalize_kernel(TeamArgs a) {
             __syncthreads();
             tok = s_at;
         } else {
+            if (threadIdx.x < kWave) {
+                const bool got = wave_poll(a.dir + brow * nseg, nseg, tag, pay + S, 0);
+                if (!got && threadIdx.x == 0) atomicOr(a.err, SV_DEVERR_TIMEOUT);
+            }
+            __syncthreads();
+            // pay[0..S): member references Mj; pay[S + j * W + w]: range sums against Mj
             if (threadIdx.x == 0) {
                 float M = neg_inf(), sm = 0.f;
-                for (int m = 0; m < S; ++m)
-                    for (int w = 0; w < kTeamWaves; ++w)
-                        ms_merge(M, sm, __uint_as_float(pay[(2 * w) * S + m]), __uint_as_float(pay[(2 * w + 1) * S + m]));
+                for (int m = 0; m < S; ++m) {
+                    float sj = 0.f;
+                    for (int w = 0; w < kTeamWaves; ++w) sj += __uint_as_float(pay[S + m * kTeamWaves + w]);
+                    ms_merge(M, sm, __uint_as_float(pay[m]), sj);
+                }
                 s_L2[0] = M + log2f(sm);
             }
             __syncthreads();
             const float L2 = s_L2[0];
             for (int q = threadIdx.x; q < nseg; q += kTeamThreads) {
-                const int m = q / kTeamWaves, w = q % kTeamWaves;
-                const float Mq = __uint_as_float(pay[(2 * w) * S + m]), sq = __uint_as_float(pay[(2 * w + 1) * S + m]);
-                s_mass[q] = (Mq == neg_inf()) ? 0.f : sq * exp2_fast(Mq - L2);
+                const float Mq = __uint_as_float(pay[q / kTeamWaves]);
+                s_mass[q] = (Mq == neg_inf()) ? 0.f : __uint_as_float(pay[S + q]) * exp2_fast(Mq - L2);
             }
             __syncthreads();
             double R = 0.0;
