@@ -36,18 +36,61 @@ def _source_digest():
     return h.hexdigest()[:16]
 
 
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "verify_dfly_traffic.json")
+COPY_BYTES = 1 << 30
+
+
 def _traffic(kernel_key, digest):
     """HBM bytes per launch from committed rocprofv3 counter summaries, if they were taken
     on the current kernel source; else None."""
-    p = os.path.join(ROOT, "profiles", "verify_dfly_traffic.json")
     try:
-        d = json.load(open(p))
+        d = json.load(open(TRAFFIC_JSON))
     except Exception:
         return None
     e = d.get(kernel_key)
     if not e or e.get("source_digest") != digest:
         return None
     return e.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(steps=5):
+    """A plain elementwise kernel of known size (float32 negation: reads and writes
+    COPY_BYTES each), timed with events; used to calibrate the HBM byte counters."""
+    import torch
+    x = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        torch.neg(x, out=y)
+    e1.record()
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) / 1e3 / steps
+    print(json.dumps({"copy_calibration": {"bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
+                                           "us": round(s * 1e6, 1), "GB/s": round(2 * COPY_BYTES / s / 1e9, 1)}}),
+          flush=True)
+
+
+def write_traffic(mode, fetch, write, copy_fetch, copy_write):
+    """Fold two counter runs of bench.py (FETCH_SIZE, WRITE_SIZE) and two of
+    --copy-calibration into profiles/verify_dfly_traffic.json (no GPU needed)."""
+    from draft_verification_softmax_amd import profiling
+    t = profiling.traffic(fetch, write, copy_fetch, copy_write, COPY_BYTES, ["stream_kernel", "finalize_kernel"])
+    per = {k: t[k] for k in ["stream_kernel", "finalize_kernel"]}
+    total = sum(v["fetch_bytes"] + v["write_bytes"] for v in per.values())
+    try:
+        d = json.load(open(TRAFFIC_JSON))
+    except Exception:
+        d = {}
+    d[f"verify_rows_{mode}"] = {"source_digest": _source_digest(), "hbm_bytes_per_launch": round(total),
+                                "fetch_scale": round(t["fetch_scale"], 5), "write_scale": round(t["write_scale"], 5),
+                                "kernels": {k: {kk: round(vv) for kk, vv in v.items()} for k, v in per.items()}}
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(d, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(d[f"verify_rows_{mode}"]))
 
 
 def cpu_baseline(inputs, T, seed):
@@ -76,7 +119,14 @@ def main():
     ap.add_argument("--mode", choices=["stoch", "greedy"], default="stoch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copies", type=int, default=2)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only the known-size elementwise kernel used to calibrate byte counters")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="fold rocprofv3 counter outputs into the committed traffic summary and exit")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(args.mode, *args.write_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the verification path is data-parallel by request and needs no collective "
@@ -84,6 +134,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import draft_verification_softmax_amd as sv
     import workloads
