@@ -539,7 +539,7 @@ int sv_verify_batch(const sv_params *p, const void *target, const void *draft,
     a.slots = p->K_max + 1;
     a.want_amax = (amax_t || amax_d) ? 1 : 0;
     const int mode = p->temperature == 0.f ? kTeamGreedy : kTeamStoch;
-    hipError_t e = team_launch_stream(a, p->dtype_t, p->dtype_d, mode, (unsigned)grid64, (hipStream_t)stream);
+    hipError_t e = team_launch_stream(a, p->dtype_t, p->dtype_d, mode, (hipStream_t)stream);
     if (e == hipSuccess) e = team_launch_finalize(a, p->dtype_t, p->dtype_d, mode, (hipStream_t)stream);
     return e == hipSuccess ? SV_OK : SV_EHIP;
 }
@@ -600,7 +600,7 @@ int sv_tv_e2e_loss(const sv_params *p, const void *target, const void *draft, fl
     a.alpha = alpha_buf;
     a.trows = p->K_max;
     a.slots = p->K_max;
-    hipError_t e = team_launch_stream(a, p->dtype_t, p->dtype_d, kTeamAlpha, (unsigned)grid64, (hipStream_t)stream);
+    hipError_t e = team_launch_stream(a, p->dtype_t, p->dtype_d, kTeamAlpha, (hipStream_t)stream);
     if (e == hipSuccess) e = team_launch_e2e_alpha(a, p->dtype_t, p->dtype_d, (hipStream_t)stream);
     if (e != hipSuccess) return SV_EHIP;
     hipLaunchKernelGGL(e2e_reduce_kernel, dim3(1), dim3(kReduceThreads), 0, (hipStream_t)stream, alpha_buf, p->B,

@@ -129,27 +129,73 @@ __device__ __forceinline__ void amax_update8(float &v, int &i, const float (&z)[
 // ---------------------------------------------------------------------------------------
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// Lane exchange inside rows of 16 lanes (DPP): CTRL 0xB1 / 0x4E swap lanes xor 1 / xor 2
+// (quad permutations), 0x141 mirrors each half-row, 0x140 each row.  Every source lane
+// is valid for these patterns.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) { return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false); }
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) { return __int_as_float(dpp_i<CTRL>(__float_as_int(x))); }
+__device__ __forceinline__ float readlane_f(float x, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l)); }
+
+// Wave reductions: a butterfly inside each row of 16 lanes (every lane of a row ends with
+// the row's value), then the four row values, read from lanes 0, 16, 32 and 48, are merged
+// in row order.  The result is wave-uniform.  Scheduling fences keep the compiler from
+// filling the exchange latency with independent work hoisted from later code, which
+// would keep that work's values live (and raise the register count) across it.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, kWave);
+    sched_fence();
+    x += dpp_f<0xB1>(x);
+    x += dpp_f<0x4E>(x);
+    x += dpp_f<0x141>(x);
+    x += dpp_f<0x140>(x);
+    x = (readlane_f(x, 0) + readlane_f(x, 16)) + (readlane_f(x, 32) + readlane_f(x, 48));
+    sched_fence();
     return x;
 }
 
+template <int CTRL>
+__device__ __forceinline__ void lse_step(float &m, float &s, float c) {
+    const float m2 = dpp_f<CTRL>(m), s2 = dpp_f<CTRL>(s);
+    lse_merge(m, s, m2, s2, c);
+}
+
 __device__ __forceinline__ void wave_lse(float &m, float &s, float c) {
+    sched_fence();
+    lse_step<0xB1>(m, s, c);
+    lse_step<0x4E>(m, s, c);
+    lse_step<0x141>(m, s, c);
+    lse_step<0x140>(m, s, c);
+    float M = readlane_f(m, 0), S = readlane_f(s, 0);
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-        const float m2 = __shfl_xor(m, d, kWave), s2 = __shfl_xor(s, d, kWave);
-        lse_merge(m, s, m2, s2, c);
-    }
+    for (int r = 1; r < 4; ++r) lse_merge(M, S, readlane_f(m, 16 * r), readlane_f(s, 16 * r), c);
+    m = M;
+    s = S;
+    sched_fence();
+}
+
+template <int CTRL>
+__device__ __forceinline__ void amax_step(float &v, int &i) {
+    const float v2 = dpp_f<CTRL>(v);
+    const int i2 = dpp_i<CTRL>(i);
+    amax_merge(v, i, v2, i2);
 }
 
 __device__ __forceinline__ void wave_amax(float &v, int &i) {
+    sched_fence();
+    amax_step<0xB1>(v, i);
+    amax_step<0x4E>(v, i);
+    amax_step<0x141>(v, i);
+    amax_step<0x140>(v, i);
+    float V = readlane_f(v, 0);
+    int I = __builtin_amdgcn_readlane(i, 0);
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-        const float v2 = __shfl_xor(v, d, kWave);
-        const int i2 = __shfl_xor(i, d, kWave);
-        amax_merge(v, i, v2, i2);
-    }
+    for (int r = 1; r < 4; ++r) amax_merge(V, I, readlane_f(v, 16 * r), __builtin_amdgcn_readlane(i, 16 * r));
+    v = V;
+    i = I;
+    sched_fence();
 }
 
 __device__ __forceinline__ double wave_incl_scan(double x) {

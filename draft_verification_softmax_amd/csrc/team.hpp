@@ -84,7 +84,8 @@ struct TeamArgs {
     int64_t spin_ticks;  // bounded wait for teammates' partials (10 ns ticks)
 };
 
-hipError_t team_launch_stream(const TeamArgs &a, int dtype_t, int dtype_d, int mode, unsigned grid, hipStream_t s);
+// Grid sizes are derived from a (rows * S workgroups at most; the caller checks they fit).
+hipError_t team_launch_stream(const TeamArgs &a, int dtype_t, int dtype_d, int mode, hipStream_t s);
 hipError_t team_launch_finalize(const TeamArgs &a, int dtype_t, int dtype_d, int mode, hipStream_t s);
 // L_e2e: alpha per row from the shares (one thread per row).
 hipError_t team_launch_e2e_alpha(const TeamArgs &a, int dtype_t, int dtype_d, hipStream_t s);

@@ -91,6 +91,14 @@ __device__ __forceinline__ uint32_t read_epoch(const uint32_t *e) {
     return __hip_atomic_load(const_cast<uint32_t *>(e), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Scalar load of a value that stays constant while the kernel runs (written, if at all, by
+// an earlier kernel on the stream), at a workgroup-uniform address.  It uses the scalar
+// counter, so waiting for it never waits for the vector loads of the chunk.
+template <class T>
+__device__ __forceinline__ T load_uniform(const T *p) {
+    return *(const __attribute__((address_space(4))) T *)(uintptr_t)p;
+}
+
 // ---- row chunk loads -----------------------------------------------------------------
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -104,13 +112,7 @@ struct TeamRed {
 // (M, s) pairs in base 2: s = sum 2^{x - M}
 __device__ __forceinline__ void ms_merge(float &M, float &s, float M2, float s2) { lse_merge(M, s, M2, s2, 1.0f); }
 
-__device__ __forceinline__ void wave_ms(float &M, float &s) {
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-        const float M2 = __shfl_xor(M, d, kWave), s2 = __shfl_xor(s, d, kWave);
-        ms_merge(M, s, M2, s2);
-    }
-}
+__device__ __forceinline__ void wave_ms(float &M, float &s) { wave_lse(M, s, 1.0f); }
 
 __device__ void block_ms2(float &Mt, float &st, float &Md, float &sd, TeamRed &red) {
     wave_ms(Mt, st);
@@ -153,25 +155,35 @@ struct LaneRow {
     static constexpr int kWords = DT == kDtBF16 ? kTeamE / 2 : kTeamE;
     uint32_t w[kWords];
 
-    // Widen slot i.  For bfloat16 the widening is an opaque instruction so that each pass
-    // re-widens from the packed registers instead of the compiler keeping all widened
-    // values live across passes (which would double the registers the chunk occupies).
+    // Widen slot i (bfloat16: a shift or a mask of its packed word).
     __device__ __forceinline__ float get(int i) const {
         if constexpr (DT == kDtBF16) {
-            float f;
-            if (i & 1) asm volatile("v_and_b32 %0, 0xffff0000, %1" : "=v"(f) : "v"(w[i >> 1]));
-            else asm volatile("v_lshlrev_b32 %0, 16, %1" : "=v"(f) : "v"(w[i >> 1]));
-            return f;
+            return (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]);
         } else {
             return __uint_as_float(w[i]);
         }
     }
 
+    // Called at the start of every pass over each group of slots: the packed words become
+    // opaque to the compiler, so each pass widens them afresh instead of the compiler keeping the
+    // widened values of an earlier pass live (which would double the registers the chunk
+    // occupies).  Emits no instruction.
+    // Per group of 8 slots (one 16-byte load of bfloat16), so that a pass can start on the
+    // first groups while later loads are still in flight.
+    __device__ __forceinline__ void refresh8(int i) {
+        constexpr int kPer8 = DT == kDtBF16 ? 4 : 8;
+#pragma unroll
+        for (int q = 0; q < kPer8; ++q) asm volatile("" : "+v"(w[(i / 8) * kPer8 + q]));
+    }
+
+    // FULL: the range lies inside the row.  Then no load sits under a condition, so the
+    // compiler can wait for each one on its own as the passes consume them.
+    template <bool FULL>
     __device__ __forceinline__ void load(const void *row, int base, int V) {
 #pragma unroll
         for (int g = 0; g < kTeamE / 8; ++g) {
             const int v0 = base + g * 512 + lane_id() * 8;
-            if (v0 + 8 <= V) {
+            if (FULL || v0 + 8 <= V) {
                 if constexpr (DT == kDtBF16) {
                     const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row) + (v0 >> 3));
                     w[g * 4 + 0] = q.x; w[g * 4 + 1] = q.y; w[g * 4 + 2] = q.z; w[g * 4 + 3] = q.w;
@@ -198,29 +210,64 @@ struct LaneRow {
         }
     }
 
-    __device__ __forceinline__ float max() const {
+    __device__ __forceinline__ float max() {
         float m0 = neg_inf(), m1 = neg_inf();
 #pragma unroll
-        for (int i = 0; i < kTeamE; i += 2) { m0 = fmaxf(m0, get(i)); m1 = fmaxf(m1, get(i + 1)); }
+        for (int g = 0; g < kTeamE; g += 8) {
+            refresh8(g);
+#pragma unroll
+            for (int i = g; i < g + 8; i += 2) {
+                m0 = fmaxf(m0, get(i));
+                m1 = fmaxf(m1, get(i + 1));
+            }
+            sched_fence();
+        }
         return fmaxf(m0, m1);
     }
 
     // first slot (in vocabulary order) holding m; its vocabulary index
-    __device__ __forceinline__ int first_index(float m, int base) const {
+    __device__ __forceinline__ int first_index(float m, int base) {
         int idx = 0x7fffffff;
 #pragma unroll
-        for (int i = kTeamE - 1; i >= 0; --i)
-            if (get(i) == m) idx = base + (i >> 3) * 512 + lane_id() * 8 + (i & 7);
+        for (int g = kTeamE - 8; g >= 0; g -= 8) {
+            refresh8(g);
+#pragma unroll
+            for (int i = g + 7; i >= g; --i)
+                if (get(i) == m) idx = base + (i >> 3) * 512 + lane_id() * 8 + (i & 7);
+            sched_fence();
+        }
         return idx;
     }
 
+    // (M, s) of this lane's logits in base 2 (s = sum_i 2^{x_i c - M}) without a pass for
+    // the maximum: the reference M is c times the largest of the first 8 logits.  Should a
+    // later logit lie so far above it that the sum leaves range (or the first 8 be -inf),
+    // the exact maximum is taken instead.
+    __device__ __forceinline__ void lane_ms(float c, float &M, float &s) {
+        refresh8(0);
+        const float m8 = fmaxf(fmaxf(fmaxf(get(0), get(1)), fmaxf(get(2), get(3))),
+                               fmaxf(fmaxf(get(4), get(5)), fmaxf(get(6), get(7))));
+        M = m8 * c;
+        s = exp_sum(c, M);
+        if (!(s < 0x1p100f)) {
+            const float m = max();
+            M = (m == neg_inf()) ? neg_inf() : m * c;
+            s = (m == neg_inf()) ? 0.f : exp_sum(c, M);
+        }
+    }
+
     // sum_i 2^{x_i c - M}
-    __device__ __forceinline__ float exp_sum(float c, float M) const {
+    __device__ __forceinline__ float exp_sum(float c, float M) {
         float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-        for (int i = 0; i < kTeamE; i += 2) {
-            a0 += exp2_fast(__builtin_fmaf(get(i), c, -M));
-            a1 += exp2_fast(__builtin_fmaf(get(i + 1), c, -M));
+        for (int g = 0; g < kTeamE; g += 8) {
+            refresh8(g);
+#pragma unroll
+            for (int i = g; i < g + 8; i += 2) {
+                a0 += exp2_fast(__builtin_fmaf(get(i), c, -M));
+                a1 += exp2_fast(__builtin_fmaf(get(i + 1), c, -M));
+            }
+            sched_fence();
         }
         return a0 + a1;
     }
@@ -229,12 +276,18 @@ struct LaneRow {
 // sum_i min(p_i, q_i) with p = 2^{t c - L2t}, q = 2^{d c - L2d}: the same per-logit formula
 // as the inverse-CDF scan of the finalize kernel.
 template <int DTT, int DTD>
-__device__ __forceinline__ float min_sum(const LaneRow<DTT> &t, const LaneRow<DTD> &d, float c, float L2t, float L2d) {
+__device__ __forceinline__ float min_sum(LaneRow<DTT> &t, LaneRow<DTD> &d, float c, float L2t, float L2d) {
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-    for (int i = 0; i < kTeamE; i += 2) {
-        a0 += exp2_fast(fminf(__builtin_fmaf(t.get(i), c, -L2t), __builtin_fmaf(d.get(i), c, -L2d)));
-        a1 += exp2_fast(fminf(__builtin_fmaf(t.get(i + 1), c, -L2t), __builtin_fmaf(d.get(i + 1), c, -L2d)));
+    for (int g = 0; g < kTeamE; g += 8) {
+        t.refresh8(g);
+        d.refresh8(g);
+#pragma unroll
+        for (int i = g; i < g + 8; i += 2) {
+            a0 += exp2_fast(fminf(__builtin_fmaf(t.get(i), c, -L2t), __builtin_fmaf(d.get(i), c, -L2d)));
+            a1 += exp2_fast(fminf(__builtin_fmaf(t.get(i + 1), c, -L2t), __builtin_fmaf(d.get(i + 1), c, -L2d)));
+        }
+        sched_fence();
     }
     return a0 + a1;
 }
@@ -245,7 +298,7 @@ struct ThreadStats {
 };
 
 template <int DTT, int DTD>
-__device__ __forceinline__ ThreadStats pass1(const LaneRow<DTT> &t, const LaneRow<DTD> &d, float mt, float md, float c) {
+__device__ __forceinline__ ThreadStats pass1(LaneRow<DTT> &t, LaneRow<DTD> &d, float mt, float md, float c) {
     ThreadStats s;
     s.Mt = (mt == neg_inf()) ? neg_inf() : mt * c;
     s.Md = (md == neg_inf()) ? neg_inf() : md * c;
@@ -256,7 +309,7 @@ __device__ __forceinline__ ThreadStats pass1(const LaneRow<DTT> &t, const LaneRo
 
 // Pass 2 of a lane: its share of alpha and of the residual mass sum max(p - q, 0).
 template <int DTT, int DTD>
-__device__ __forceinline__ void pass2(const LaneRow<DTT> &t, const LaneRow<DTD> &d, const ThreadStats &s, float c,
+__device__ __forceinline__ void pass2(LaneRow<DTT> &t, LaneRow<DTD> &d, const ThreadStats &s, float c,
                                       float L2t, float L2d, float &alpha, float &resid) {
     alpha = min_sum(t, d, c, L2t, L2d);
     const float P = (s.Mt == neg_inf()) ? 0.f : s.st * exp2_fast(s.Mt - L2t);   // this lane's target mass
@@ -434,7 +487,8 @@ __device__ int draw_ranges(const void *trow, const void *drow, int V, float c, f
 // for bit.
 __device__ __forceinline__ void team_totals(const uint32_t *pay, int S, float &L2t, float &L2d) {
     float Tt = neg_inf(), Ts = 0.f, Dt = neg_inf(), Ds = 0.f;
-    for (int q = 0; q < S; ++q) {
+#pragma unroll 1
+    for (int q = 0; q < S; ++q) {   // not unrolled: it runs beside a chunk held in registers
         ms_merge(Tt, Ts, __uint_as_float(pay[q]), __uint_as_float(pay[S + q]));
         ms_merge(Dt, Ds, __uint_as_float(pay[2 * S + q]), __uint_as_float(pay[3 * S + q]));
     }
@@ -466,141 +520,46 @@ __device__ __forceinline__ int accept_test(float zt, float zd, float c, float L2
 // =======================================================================================
 // Stream kernel: one member workgroup per (row pair, vocabulary chunk)
 // =======================================================================================
-template <int DTT, int DTD, int MODE>
-__global__ __launch_bounds__(kTeamThreads) void stream_kernel(TeamArgs a) {
-    __shared__ TeamRed red;
-    __shared__ uint32_t pay[4 * 128];
-    __shared__ float s_tot[2];
-    __shared__ int s_ok;
-
-    // The S members of a team are consecutive workgroups: round-robin dispatch spreads them
-    // over the XCDs, whose dispatchers start them at nearly the same time.
-    const int S = a.S;
-    const int j = blockIdx.x % S;
-    const int64_t row = blockIdx.x / S;
-    const int K = a.K;
-    const int slots = a.slots;
-    const int r = (int)(row / slots);
-    const int k = (int)(row % slots);
-    const bool bonus = (MODE != kTeamAlpha) && k == K;
-    int L = K;
-    if constexpr (MODE != kTeamAlpha) {
-        if (a.draft_len) {
-            const int l0 = a.draft_len[r];
-            if ((l0 < 0 || l0 > K) && threadIdx.x == 0 && bonus && j == 0) atomicOr(a.err, SV_DEVERR_DRAFT_LEN);
-            L = l0 < 0 ? 0 : (l0 > K ? K : l0);
-        }
+// Phase 1 of a row: the workgroup merges its lanes' (M, s) states of both rows and thread 0
+// publishes the member's partials.
+__device__ __forceinline__ void publish_partials(uint64_t *part, int S, int j, const ThreadStats &ts, uint32_t tag,
+                                                 TeamRed &red) {
+    float Mt = ts.Mt, st = ts.st, Md = ts.Md, sd = ts.sd;
+    block_ms2(Mt, st, Md, sd, red);
+    if (threadIdx.x == 0) {
+        putf(part + 0 * S + j, Mt, tag);
+        putf(part + 1 * S + j, st, tag);
+        putf(part + 2 * S + j, Md, tag);
+        putf(part + 3 * S + j, sd, tag);
     }
-    if (!bonus && k >= L) return;
-    const int V = a.V;
+}
+
+// Phase 2 of a row: wait (bounded) for the team's partials, reduce them in member order to
+// the row normalisers, then publish this member's share of alpha, its residual-mass
+// directory entries and (member holding the drafted token) the accept flag.  s_tot[2] and
+// s_ok are this row's own LDS slots.
+template <int DTT, int DTD, int MODE>
+__device__ __forceinline__ void finish_row(const TeamArgs &a, int64_t row, int j, int r, int k, LaneRow<DTT> &tr,
+                                           LaneRow<DTD> &dr, const ThreadStats &ts, bool owner, float zx_t,
+                                           float zx_d, uint32_t tag, TeamRed &red, uint32_t *pay, float *s_tot,
+                                           int *s_ok) {
+    const int S = a.S;
     const float c = a.c;
     const int w = threadIdx.x / kWave;
-    const int base = j * kTeamChunk + w * kTeamSeg;
-    uint64_t *part = a.part + row * (int64_t)(8 * S);
-    if (bonus) {
-        // the bonus row (target row L_r): per-wave-range states (stochastic) or argmax (greedy)
-        const void *brow = row_ptr<DTT>(a.target, (int64_t)r * a.trows + L, a.ld_t);
-        LaneRow<DTT> br;
-        br.load(brow, base, V);
-        const uint32_t tag = read_epoch(a.epoch) + 1;
-        const float mb = br.max();
-        if constexpr (MODE == kTeamGreedy) {
-            float wb = mb, wz = neg_inf();
-            int i0 = 0, i1 = 0;
-            block_amax2(wb, i0, wz, i1, red);
-            int ib = (mb == wb && mb != neg_inf()) ? br.first_index(mb, base) : 0x7fffffff;
-            float fb = wb, fz = neg_inf();
-            int iz = 0x7fffffff;
-            block_amax2(fb, ib, fz, iz, red);
-            if (threadIdx.x == 0) {
-                putf(part + 4 * S + j, wb, tag);
-                put(part + 5 * S + j, (uint32_t)ib, tag);
-            }
-        } else {
-            // per wave range: sum 2^{z c - Mj} against the member's reference Mj (the largest
-            // wave maximum), so the finalize needs one directory word per range
-            float M = (mb == neg_inf()) ? neg_inf() : mb * c;
-            float sm = (mb == neg_inf()) ? 0.f : br.exp_sum(c, M);
-            wave_ms(M, sm);
-            if (lane_id() == 0) red.f[0][w] = M;
-            __syncthreads();
-            float Mj = red.f[0][0];
-            for (int q = 1; q < kTeamWaves; ++q) Mj = fmaxf(Mj, red.f[0][q]);
-            if (lane_id() == 0) {
-                putf(a.dir + row * a.nseg + j * kTeamWaves + w, (M == neg_inf()) ? 0.f : sm * exp2_fast(M - Mj), tag);
-                if (w == 0) putf(part + j, Mj, tag);
-            }
-        }
-        return;
-    }
-    const void *trow = row_ptr<DTT>(a.target, (int64_t)r * a.trows + k, a.ld_t);
-    const void *drow = row_ptr<DTD>(a.draft, (int64_t)r * K + k, a.ld_d);
-
-    LaneRow<DTT> tr;
-    LaneRow<DTD> dr;
-    tr.load(trow, base, V);
-    dr.load(drow, base, V);
-
-    // the member whose chunk holds the drafted token fetches its two logits
-    float zx_t = 0.f, zx_d = 0.f;
-    bool owner = false;
-    if (MODE == kTeamStoch && threadIdx.x == 0) {
-        const int x = a.tokens[(size_t)r * K + k];
-        owner = (x >= 0 && x < V && x / kTeamChunk == j);
-        if (owner) {
-            zx_t = load1<DTT>(trow, x);
-            zx_d = load1<DTD>(drow, x);
-        }
-    }
-    const uint32_t tag = read_epoch(a.epoch) + 1;
-
-    const float mt = tr.max(), md = dr.max();
-    // ---- argmax partials: chunk maximum, then the first index holding it ----
-    if (MODE == kTeamGreedy || a.want_amax) {
-        float wt = mt, wd = md;
-        int i0 = 0, i1 = 0;
-        block_amax2(wt, i0, wd, i1, red);   // chunk maxima
-        int it = (mt == wt && mt != neg_inf()) ? tr.first_index(mt, base) : 0x7fffffff;
-        int id = (md == wd && md != neg_inf()) ? dr.first_index(md, base) : 0x7fffffff;
-        float ft = wt, fd = wd;
-        block_amax2(ft, it, fd, id, red);   // equal values: lowest index
-        if (threadIdx.x == 0) {
-            putf(part + 4 * S + j, wt, tag);
-            put(part + 5 * S + j, (uint32_t)it, tag);
-            putf(part + 6 * S + j, wd, tag);
-            put(part + 7 * S + j, (uint32_t)id, tag);
-        }
-    }
-    if constexpr (MODE == kTeamGreedy) return;
-
-    // ---- phase 1: log-sum-exp partial of this member ----
-    const ThreadStats ts = pass1(tr, dr, mt, md, c);
-    {
-        float Mt = ts.Mt, st = ts.st, Md = ts.Md, sd = ts.sd;
-        block_ms2(Mt, st, Md, sd, red);
-        if (threadIdx.x == 0) {
-            putf(part + 0 * S + j, Mt, tag);
-            putf(part + 1 * S + j, st, tag);
-            putf(part + 2 * S + j, Md, tag);
-            putf(part + 3 * S + j, sd, tag);
-        }
-    }
-    // ---- every member reduces all partials (bounded wait) ----
+    const uint64_t *part = a.part + row * (int64_t)(8 * S);
     if (threadIdx.x < kWave) {
         const bool got = wave_poll(part, 4 * S, tag, pay, a.spin_ticks);
         if (threadIdx.x == 0) {
-            s_ok = got ? 1 : 0;
+            *s_ok = got ? 1 : 0;
             if (got) team_totals(pay, S, s_tot[0], s_tot[1]);
         }
     }
     __syncthreads();
-    if (!s_ok) {
+    if (!*s_ok) {
         if (threadIdx.x == 0) put(a.apart + row * S + j, kGaveUp, tag);   // the finalize takes over
         return;
     }
     const float L2t = s_tot[0], L2d = s_tot[1];
-
-    // ---- phase 2: this member's share of alpha and of the residual mass ----
     float al, rs;
     pass2(tr, dr, ts, c, L2t, L2d, al, rs);
     if constexpr (MODE == kTeamStoch) {
@@ -618,6 +577,171 @@ __global__ __launch_bounds__(kTeamThreads) void stream_kernel(TeamArgs a) {
     }
 }
 
+// The token's two logits, fetched by every lane at a clamped index (only the member whose
+// chunk holds the token uses them; thread 0 of that member is the owner).
+template <int DTT, int DTD>
+__device__ __forceinline__ void token_logits(const void *trow, const void *drow, int x, int V, int j, float &zx_t,
+                                             float &zx_d, bool &owner) {
+    const int xs = x < 0 ? 0 : (x >= V ? V - 1 : x);
+    zx_t = load1<DTT>(trow, xs);
+    zx_d = load1<DTD>(drow, xs);
+    owner = threadIdx.x == 0 && x >= 0 && x < V && x / kTeamChunk == j;
+}
+
+// One member's work on a verified row pair (not a bonus slot).  FULL: its chunk lies inside
+// the row.
+template <int DTT, int DTD, int MODE, bool AMAX, bool FULL>
+__device__ __forceinline__ void row_member(const TeamArgs &a, int j, int64_t row, int r, int k, TeamRed &red,
+                                           uint32_t *pay, float *s_tot, int *s_ok) {
+    const int S = a.S;
+    const int K = a.K;
+    const int V = a.V;
+    const float c = a.c;
+    const int w = threadIdx.x / kWave;
+    const int base = j * kTeamChunk + w * kTeamSeg;
+    uint64_t *part = a.part + row * (int64_t)(8 * S);
+    const void *trow = row_ptr<DTT>(a.target, (int64_t)r * a.trows + k, a.ld_t);
+    const void *drow = row_ptr<DTD>(a.draft, (int64_t)r * K + k, a.ld_d);
+
+    // The drafted token and the call epoch come by scalar loads; the token's two logits are
+    // fetched after the chunk, so no wait for them holds up the passes.
+    int x = 0;
+    if constexpr (MODE == kTeamStoch) x = load_uniform(a.tokens + (size_t)r * K + k);
+    const uint32_t epoch = load_uniform(a.epoch);
+
+    LaneRow<DTT> tr;
+    LaneRow<DTD> dr;
+    tr.template load<FULL>(trow, base, V);
+    dr.template load<FULL>(drow, base, V);
+    sched_fence();   // what uses the scalar loads goes after the chunk loads, not before
+    const uint32_t tag = epoch + 1;
+
+    float zx_t = 0.f, zx_d = 0.f;
+    bool owner = false;
+    if constexpr (MODE == kTeamStoch) token_logits<DTT, DTD>(trow, drow, x, V, j, zx_t, zx_d, owner);
+
+    constexpr bool want_amax = MODE == kTeamGreedy || AMAX;
+    float mt = 0.f, md = 0.f;
+    // ---- argmax partials: chunk maximum, then the first index holding it ----
+    if constexpr (want_amax) {
+        mt = tr.max();
+        md = dr.max();
+        float wt = mt, wd = md;
+        int i0 = 0, i1 = 0;
+        block_amax2(wt, i0, wd, i1, red);   // chunk maxima
+        int it = (mt == wt && mt != neg_inf()) ? tr.first_index(mt, base) : 0x7fffffff;
+        int id = (md == wd && md != neg_inf()) ? dr.first_index(md, base) : 0x7fffffff;
+        float ft = wt, fd = wd;
+        block_amax2(ft, it, fd, id, red);   // equal values: lowest index
+        if (threadIdx.x == 0) {
+            putf(part + 4 * S + j, wt, tag);
+            put(part + 5 * S + j, (uint32_t)it, tag);
+            putf(part + 6 * S + j, wd, tag);
+            put(part + 7 * S + j, (uint32_t)id, tag);
+        }
+    }
+    if constexpr (MODE == kTeamGreedy) return;
+
+    // ---- phase 1 (the exact maxima serve as the references when they were needed anyway) ----
+    ThreadStats ts;
+    if constexpr (want_amax) {
+        ts = pass1(tr, dr, mt, md, c);
+    } else {
+        tr.lane_ms(c, ts.Mt, ts.st);
+        dr.lane_ms(c, ts.Md, ts.sd);
+    }
+    publish_partials(part, S, j, ts, tag, red);
+    // ---- phase 2 ----
+    finish_row<DTT, DTD, MODE>(a, row, j, r, k, tr, dr, ts, owner, zx_t, zx_d, tag, red, pay, s_tot, s_ok);
+}
+
+// Bonus slot of request r (target row L): per-wave-range masses against the member's
+// reference (stochastic) or the argmax partials (greedy), published without waiting.
+template <int DTT, int MODE>
+__device__ __forceinline__ void bonus_member(const TeamArgs &a, int j, int64_t row, int r, int L, TeamRed &red) {
+    const int S = a.S;
+    const int V = a.V;
+    const float c = a.c;
+    const int w = threadIdx.x / kWave;
+    const int base = j * kTeamChunk + w * kTeamSeg;
+    uint64_t *part = a.part + row * (int64_t)(8 * S);
+    const void *brow = row_ptr<DTT>(a.target, (int64_t)r * a.trows + L, a.ld_t);
+    const uint32_t epoch = load_uniform(a.epoch);
+    LaneRow<DTT> br;
+    br.template load<false>(brow, base, V);
+    sched_fence();
+    const uint32_t tag = epoch + 1;
+    if constexpr (MODE == kTeamGreedy) {
+        const float mb = br.max();
+        float wb = mb, wz = neg_inf();
+        int i0 = 0, i1 = 0;
+        block_amax2(wb, i0, wz, i1, red);
+        int ib = (mb == wb && mb != neg_inf()) ? br.first_index(mb, base) : 0x7fffffff;
+        float fb = wb, fz = neg_inf();
+        int iz = 0x7fffffff;
+        block_amax2(fb, ib, fz, iz, red);
+        if (threadIdx.x == 0) {
+            putf(part + 4 * S + j, wb, tag);
+            put(part + 5 * S + j, (uint32_t)ib, tag);
+        }
+    } else {
+        // per wave range: sum 2^{z c - Mj} against the member's reference Mj (the largest
+        // wave maximum), so the finalize needs one directory word per range
+        float M, sm;
+        br.lane_ms(c, M, sm);
+        wave_ms(M, sm);
+        if (lane_id() == 0) red.f[0][w] = M;
+        __syncthreads();
+        float Mj = red.f[0][0];
+        for (int q = 1; q < kTeamWaves; ++q) Mj = fmaxf(Mj, red.f[0][q]);
+        if (lane_id() == 0) {
+            putf(a.dir + row * a.nseg + j * kTeamWaves + w, (M == neg_inf()) ? 0.f : sm * exp2_fast(M - Mj), tag);
+            if (w == 0) putf(part + j, Mj, tag);
+        }
+    }
+}
+
+__device__ __forceinline__ int request_limit(const TeamArgs &a, int r, bool report) {
+    int L = a.K;
+    if (a.draft_len) {
+        const int l0 = a.draft_len[r];
+        if ((l0 < 0 || l0 > a.K) && report) atomicOr(a.err, SV_DEVERR_DRAFT_LEN);
+        L = l0 < 0 ? 0 : (l0 > a.K ? a.K : l0);
+    }
+    return L;
+}
+
+// AMAX: also publish the argmax partials (always in greedy mode; on request otherwise).
+// At most 96 registers per lane, so five waves share each SIMD.
+template <int DTT, int DTD, int MODE, bool AMAX>
+__global__ __launch_bounds__(kTeamThreads) __attribute__((amdgpu_waves_per_eu(5))) void stream_kernel(TeamArgs a) {
+    __shared__ TeamRed red;
+    __shared__ uint32_t pay[4 * 128];
+    __shared__ float s_tot[2];
+    __shared__ int s_ok;
+
+    // The S members of a team are consecutive workgroups: round-robin dispatch spreads them
+    // over the XCDs, whose dispatchers start them at nearly the same time.
+    // (divisions by runtime values are done on the vector unit: readfirstlane returns the
+    // uniform results to scalar registers)
+    const int S = a.S;
+    const int j = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % (unsigned)S));
+    const int64_t row = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / (unsigned)S));
+    const int K = a.K;
+    const int slots = a.slots;
+    const int r = __builtin_amdgcn_readfirstlane((int)(row / slots));
+    const int k = __builtin_amdgcn_readfirstlane((int)(row % slots));
+    const bool bonus = (MODE != kTeamAlpha) && k == K;
+    const int L = (MODE != kTeamAlpha) ? request_limit(a, r, bonus && j == 0 && threadIdx.x == 0) : K;
+    if (!bonus && k >= L) return;
+    if (bonus) {
+        bonus_member<DTT, MODE>(a, j, row, r, L, red);
+        return;
+    }
+    if ((j + 1) * kTeamChunk <= a.V) row_member<DTT, DTD, MODE, AMAX, true>(a, j, row, r, k, red, pay, s_tot, &s_ok);
+    else row_member<DTT, DTD, MODE, AMAX, false>(a, j, row, r, k, red, pay, s_tot, &s_ok);
+}
+
 namespace {
 
 // Recompute member j's share of a row (alpha, and residual directory entries) from HBM;
@@ -629,8 +753,8 @@ __device__ float recompute_share(const TeamArgs &a, const void *trow, const void
     LaneRow<DTD> dr;
     const int w = threadIdx.x / kWave;
     const int base = j * kTeamChunk + w * kTeamSeg;
-    tr.load(trow, base, a.V);
-    dr.load(drow, base, a.V);
+    tr.template load<false>(trow, base, a.V);
+    dr.template load<false>(drow, base, a.V);
     const ThreadStats s = pass1(tr, dr, tr.max(), dr.max(), a.c);
     float al, rs;
     pass2(tr, dr, s, a.c, L2t, L2d, al, rs);
@@ -1013,10 +1137,16 @@ __global__ __launch_bounds__(kTeamThreads) void e2e_alpha_kernel(TeamArgs a) {
 }
 
 template <int DTT, int DTD>
-static hipError_t launch_stream_t(const TeamArgs &a, int mode, unsigned grid, hipStream_t s) {
-    if (mode == kTeamStoch) hipLaunchKernelGGL((stream_kernel<DTT, DTD, kTeamStoch>), dim3(grid), dim3(kTeamThreads), 0, s, a);
-    else if (mode == kTeamGreedy) hipLaunchKernelGGL((stream_kernel<DTT, DTD, kTeamGreedy>), dim3(grid), dim3(kTeamThreads), 0, s, a);
-    else hipLaunchKernelGGL((stream_kernel<DTT, DTD, kTeamAlpha>), dim3(grid), dim3(kTeamThreads), 0, s, a);
+static hipError_t launch_stream_t(const TeamArgs &a, int mode, hipStream_t s) {
+    const unsigned grid = (unsigned)((uint64_t)a.rows * (uint64_t)a.S);
+    if (mode == kTeamStoch && a.want_amax)
+        hipLaunchKernelGGL((stream_kernel<DTT, DTD, kTeamStoch, true>), dim3(grid), dim3(kTeamThreads), 0, s, a);
+    else if (mode == kTeamStoch)
+        hipLaunchKernelGGL((stream_kernel<DTT, DTD, kTeamStoch, false>), dim3(grid), dim3(kTeamThreads), 0, s, a);
+    else if (mode == kTeamGreedy)
+        hipLaunchKernelGGL((stream_kernel<DTT, DTD, kTeamGreedy, true>), dim3(grid), dim3(kTeamThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((stream_kernel<DTT, DTD, kTeamAlpha, false>), dim3(grid), dim3(kTeamThreads), 0, s, a);
     return hipGetLastError();
 }
 
@@ -1041,8 +1171,8 @@ static hipError_t launch_e2e_t(const TeamArgs &a, hipStream_t s) {
     if (dt == SV_BF16 && dd == SV_F32) return F<kDtBF16, kDtF32>(__VA_ARGS__);     \
     return F<kDtF32, kDtBF16>(__VA_ARGS__);
 
-hipError_t team_launch_stream(const TeamArgs &a, int dt, int dd, int mode, unsigned grid, hipStream_t s) {
-    SV_DISPATCH(launch_stream_t, a, mode, grid, s)
+hipError_t team_launch_stream(const TeamArgs &a, int dt, int dd, int mode, hipStream_t s) {
+    SV_DISPATCH(launch_stream_t, a, mode, s)
 }
 hipError_t team_launch_finalize(const TeamArgs &a, int dt, int dd, int mode, hipStream_t s) {
     SV_DISPATCH(launch_finalize_t, a, mode, s)
