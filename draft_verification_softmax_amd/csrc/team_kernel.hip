@@ -400,23 +400,46 @@ __device__ int row_argmax(const void *row, int V, TeamRed &red) {
 // a rejection (RESID), else p (the bonus token).  The per-range masses (one per
 // kTeamSeg-logit wave range) pick the range; the workgroup re-reads that range and scans
 // it in binary64.
+// The total R of the range masses is summed in binary64 in range order and the target is
+// u * R; -1 when every mass is zero.
 template <int DTT, int DTD, bool RESID>
 __device__ int draw_ranges(const void *trow, const void *drow, int V, float c, float L2t, float L2d,
-                           const float *dirv, int nseg, double t, TeamRed &red) {
+                           const float *dirv, int nseg, float u, TeamRed &red) {
     __shared__ int s_seg;
     __shared__ double s_ex;
     __shared__ double s_scan[kTeamThreads];
     __shared__ int s_tok;
     const int w = threadIdx.x / kWave;
     if (w == 0) {
-        double ex;
-        const int sidx = wave_find([&](int q) { return dirv[q]; }, nseg, t, &ex);
-        if (lane_id() == 0) { s_seg = sidx; s_ex = ex; }
+        const int lane = lane_id();
+        double ex = 0.0;
+        int sidx = -1;
+        if (nseg <= kWave) {
+            // one pass: the inclusive scan gives R at its last lane and the crossing at once
+            const double x = lane < nseg ? (double)dirv[lane] : 0.0;
+            const double incl = wave_incl_scan(x);
+            const double t = (double)u * __shfl(incl, kWave - 1, kWave);
+            const uint64_t hit = __ballot(incl > t);
+            const uint64_t pos = __ballot(x > 0.0);
+            const int l = hit ? __builtin_ctzll(hit) : (pos ? 63 - __builtin_clzll(pos) : 0);
+            ex = __shfl(incl - x, l, kWave);
+            sidx = (hit || pos) ? l : -1;
+            if (lane == 0) s_ex = t - ex;
+        } else {
+            double part = 0.0;
+            for (int q = lane; q < nseg; q += kWave) part += (double)dirv[q];
+            // fixed order: lane partials summed in lane order
+            const double R = __shfl(wave_incl_scan(part), kWave - 1, kWave);
+            const double t = (double)u * R;
+            sidx = wave_find([&](int q) { return dirv[q]; }, nseg, t, &ex);
+            if (lane == 0) s_ex = t - ex;
+        }
+        if (lane == 0) s_seg = sidx;
     }
     __syncthreads();
     const int sidx = s_seg;
     if (sidx < 0) return -1;
-    const double rem = t - s_ex;
+    const double rem = s_ex;
     // the range's kTeamSeg logits, kPer consecutive ones per thread
     constexpr int kPer = kTeamSeg / kTeamThreads;
     const int e0 = sidx * kTeamSeg + threadIdx.x * kPer;
@@ -806,6 +829,7 @@ __global__ __launch_bounds__(kTeamThreads) void finalize_kernel(TeamArgs a) {
     __shared__ int s_at;
     __shared__ float s_rt[kTeamThreads], s_rd[kTeamThreads];
     __shared__ int s_ra[kTeamThreads];
+    __shared__ float s_u[kTeamThreads];   // correction/bonus uniform for each candidate tau
 
     const int r = blockIdx.x;
     const int K = a.K;
@@ -818,7 +842,16 @@ __global__ __launch_bounds__(kTeamThreads) void finalize_kernel(TeamArgs a) {
     const float c = a.c;
     const bool want_amax = (MODE == kTeamGreedy) || a.want_amax;
 
+    // The uniform of the draw after the scan, for every candidate tau <= K: computed while
+    // the first gather is in flight (here when there is no gather) if K + 1 <= kTeamThreads,
+    // else on demand.
+    const bool pre_u = MODE == kTeamStoch && K + 1 <= kTeamThreads;
+    auto tau_u = [&](int t) {
+        return pre_u ? s_u[t] : uniform24(a.seed, (uint64_t)r, (uint64_t)t, kPurposeCorrection, a.step);
+    };
     if (threadIdx.x == 0) { s_tau = L; s_at = 0; s_L2[0] = s_L2[1] = 0.f; }
+    if (pre_u && L == 0 && threadIdx.x <= K)
+        s_u[threadIdx.x] = uniform24(a.seed, (uint64_t)r, (uint64_t)threadIdx.x, kPurposeCorrection, a.step);
     __syncthreads();
 
     // rows are staged in batches: acc [nb][4] | shares [nb][S] | directory [nb][4S] |
@@ -864,6 +897,8 @@ __global__ __launch_bounds__(kTeamThreads) void finalize_kernel(TeamArgs a) {
                     }
                     wv[u] = src ? peek(src) : 0;
                 }
+                if (pre_u && k0 == 0 && i0 == 0 && threadIdx.x <= K)
+                    s_u[threadIdx.x] = uniform24(a.seed, (uint64_t)r, (uint64_t)threadIdx.x, kPurposeCorrection, a.step);
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int i = i0 + u * kTeamThreads + threadIdx.x;
@@ -1027,14 +1062,15 @@ __global__ __launch_bounds__(kTeamThreads) void finalize_kernel(TeamArgs a) {
             }
             __syncthreads();
             // pay[0..S): member references Mj; pay[S + j * W + w]: range sums against Mj
-            if (threadIdx.x == 0) {
+            if (threadIdx.x < kWave) {
                 float M = neg_inf(), sm = 0.f;
-                for (int m = 0; m < S; ++m) {
+                for (int m = threadIdx.x; m < S; m += kWave) {
                     float sj = 0.f;
                     for (int w = 0; w < kTeamWaves; ++w) sj += __uint_as_float(pay[S + m * kTeamWaves + w]);
                     ms_merge(M, sm, __uint_as_float(pay[m]), sj);
                 }
-                s_L2[0] = M + log2f(sm);
+                wave_ms(M, sm);
+                if (threadIdx.x == 0) s_L2[0] = M + log2f(sm);
             }
             __syncthreads();
             const float L2 = s_L2[0];
@@ -1043,23 +1079,18 @@ __global__ __launch_bounds__(kTeamThreads) void finalize_kernel(TeamArgs a) {
                 s_mass[q] = (Mq == neg_inf()) ? 0.f : __uint_as_float(pay[S + q]) * exp2_fast(Mq - L2);
             }
             __syncthreads();
-            double R = 0.0;
-            for (int q = 0; q < nseg; ++q) R += (double)s_mass[q];
-            const float u = uniform24(a.seed, (uint64_t)r, (uint64_t)tau, kPurposeCorrection, a.step);
-            tok = draw_ranges<DTT, DTD, false>(trow, nullptr, a.V, c, L2, 0.f, s_mass, nseg, (double)u * R, red);
+            tok = draw_ranges<DTT, DTD, false>(trow, nullptr, a.V, c, L2, 0.f, s_mass, nseg, tau_u(tau), red);
             if (tok < 0) tok = 0;
         }
     } else if constexpr (MODE == kTeamGreedy) {
         tok = s_at;
     } else {
         // rejection at tau: the residual max(p - q, 0) of row tau
-        const float u = uniform24(a.seed, (uint64_t)r, (uint64_t)tau, kPurposeCorrection, a.step);
-        double R = 0.0;
-        for (int q = 0; q < nseg; ++q) R += (double)s_mass[q];
+        const float u = tau_u(tau);
         bool done = false;
-        if (R > 0.0) {
+        {
             const void *drow = row_ptr<DTD>(a.draft, (int64_t)r * K + tau, a.ld_d);
-            const int t = draw_ranges<DTT, DTD, true>(trow, drow, a.V, c, s_L2[0], s_L2[1], s_mass, nseg, (double)u * R, red);
+            const int t = draw_ranges<DTT, DTD, true>(trow, drow, a.V, c, s_L2[0], s_L2[1], s_mass, nseg, u, red);
             if (t >= 0) { tok = t; done = true; }
         }
         __syncthreads();
