@@ -6,7 +6,9 @@ A step is one sv_verify_batch call over the DFly block workload (B=64 requests, 
 16 drafts, V=131072, bfloat16 logits, T=0.9): temperature softmax of both rows, alpha,
 accept test, first-reject scan and correction/bonus draw, all in the HIP kernels.  Inputs
 are resident in HBM before timing starts and rotate through two copies (1.1 GB > 2x the
-256 MB Infinity Cache) so every step reads from HBM.
+256 MB Infinity Cache) so every step reads from HBM.  --workload mtp | budget | e2e measure
+the other workloads (MTP chat verify, budget allocation + ragged verify, the L_e2e objective)
+the same way.
 
 Prints one JSON line (rank 0).  `value` is verified draft positions per second.  The
 `roofline` object divides the algorithmic bytes of one launch (2 * V * 2 bytes per
@@ -93,22 +95,157 @@ def write_traffic(mode, fetch, write, copy_fetch, copy_write):
     print(json.dumps(d[f"verify_rows_{mode}"]))
 
 
-def cpu_baseline(inputs, T, seed):
-    """The oracle, as it stands, on the whole batch (single thread)."""
-    import numpy as np  # noqa: F401
+def _oracle_time(fn):
+    t0 = time.perf_counter()
+    fn()
+    return time.perf_counter() - t0
 
+
+def cpu_baseline_verify(inputs, T, seed, draft_len=None, what="DFly"):
+    """The oracle, as it stands, on the whole batch (single thread)."""
     import workloads
     from oracle import svref
 
     tn, dn = workloads.to_oracle(inputs.target), workloads.to_oracle(inputs.draft)
     toks = inputs.draft_tokens.cpu().numpy()
+    dl = None if draft_len is None else draft_len.cpu().numpy()
     B, K = toks.shape
-    t0 = time.perf_counter()
-    svref.verify_batch(tn, dn, toks, T, "bf16", seed=seed)
-    dt = time.perf_counter() - t0
-    return {"value": B * K / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
-            "sample": f"whole DFly batch: {B} requests x {K} positions, V={tn.shape[-1]}, T={T}, "
+    dtype = "bf16" if inputs.target.dtype.__str__().endswith("bfloat16") else "f32"
+    dt = _oracle_time(lambda: svref.verify_batch(tn, dn, toks, T, dtype, seed=seed, draft_len=dl))
+    npos = int(dl.sum()) if dl is not None else B * K
+    return {"value": npos / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
+            "sample": f"whole {what} batch: {npos} verified positions of {B} requests, V={tn.shape[-1]}, T={T}, "
                       f"one pass, {dt:.1f} s single-threaded"}
+
+
+def cpu_baseline_e2e(target, draft, T, n_i=256):
+    """The oracle's L_e2e on the first n_i positions (all D depths) of the set, single thread."""
+    import workloads
+    from oracle import svref
+
+    tn, dn = workloads.to_oracle(target[:n_i]), workloads.to_oracle(draft[:n_i])
+    D = target.shape[1]
+    dt = _oracle_time(lambda: svref.tv_e2e_loss(tn, dn, T, "bf16"))
+    return {"value": n_i * D / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n_i} of {target.shape[0]} positions x D={D}, V={target.shape[2]}, "
+                      f"{dt:.1f} s single-threaded"}
+
+
+class Timed:
+    """Times `step(i)` over n launches with HIP events on the launch stream."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def run(self, step, warmup, n):
+        torch = self.torch
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        t_all0, t_all1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        t_all0.record(self.stream)
+        for i in range(n):
+            ev[i][0].record(self.stream)
+            step(warmup + i)
+            ev[i][1].record(self.stream)
+        t_all1.record(self.stream)
+        torch.cuda.synchronize()
+        self.wall = time.perf_counter() - wall0
+        self.per_launch_ms = [a.elapsed_time(b) for a, b in ev]
+        self.total_ms = t_all0.elapsed_time(t_all1)
+        self.avg_launch_s = sum(self.per_launch_ms) / n / 1e3
+        return self
+
+
+def bench_verify(args, sv, workloads, torch, name):
+    """dfly | mtp | budget: sv_verify_batch (after sv_alloc_verify_budget for budget)."""
+    dev = "cuda"
+    T = 0.9 if args.mode == "stoch" else 0.0
+    conf = None
+    N = None
+    if name == "budget":
+        base, conf, N = workloads.make_budget_inputs(device=dev, T=T)
+    else:
+        base = workloads.make_verify_inputs(name, device=dev, T=T)
+    B, K1, V = base.target.shape
+    K = K1 - 1
+    ncopy = args.copies if args.copies else {"dfly": 2, "mtp": 24, "budget": 4}[name]
+    copies = [base] + [workloads.VerifyInputs(base.target.clone(), base.draft.clone(), base.draft_tokens.clone(),
+                                              base.T, base.seed, base.name) for _ in range(ncopy - 1)]
+    ws = sv.Workspace(dev).get(B, K, V)
+    stream = torch.cuda.current_stream()
+    state = {"out": None, "lens": None}
+
+    def step(i):
+        c = copies[i % len(copies)]
+        if conf is not None:
+            # allocation, then verification laid out over the selected rows only
+            lens, _, rl = sv.sv_alloc_verify_budget(conf, N)
+            state["lens"] = lens
+            state["out"] = sv.sv_verify_selected(c.target, c.draft, c.draft_tokens, T, lens, rl, min(N, B * K),
+                                                 seed=c.seed, step=i, workspace=ws, out=state["out"], want_lse=True)
+        else:
+            state["out"] = sv.sv_verify_batch(c.target, c.draft, c.draft_tokens, T, seed=c.seed, step=i,
+                                              workspace=ws, out=state["out"], want_lse=True)
+
+    tm = Timed(torch, stream).run(step, args.warmup, args.steps)
+    # the draws differ per step (the step counter keys the generator): replay the timed steps
+    # untimed to count the fully accepted requests of each
+    n_full = []
+    taus = []
+    for i in range(args.steps):
+        step(args.warmup + i)
+        tau = state["out"]["accept_len"].cpu()
+        L = state["lens"].cpu() if state["lens"] is not None else torch.full((B,), K, dtype=torch.int32)
+        n_full.append(int((tau == L).sum()))
+        taus.append(float(tau.float().mean()))
+    npos = int(state["lens"].sum()) if state["lens"] is not None else B * K
+    alg_bytes = npos * 2 * V * 2 + (sum(n_full) / len(n_full)) * V * 2
+    achieved = alg_bytes / tm.avg_launch_s / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        what = {"dfly": "DFly", "mtp": "MTP chat", "budget": "budget-selected ragged"}[name]
+        cpu = cpu_baseline_verify(base, T, base.seed, draft_len=state["lens"], what=what)
+    desc = {
+        "dfly": f"DFly block verify: B={B} requests x block {K}, V={V}, bf16 logits",
+        "mtp": f"MTP chat verify: B={B} requests x depth {K}, V={V}, bf16 logits",
+        "budget": f"budget {N} of {B}x{K} by cumulative confidence, then verification of the selected rows: "
+                  f"V={V}, bf16 logits (step = sv_alloc_verify_budget + sv_verify_selected)",
+    }[name]
+    mode = "T=0.9 stochastic" if T > 0 else "T=0 greedy"
+    return dict(
+        positions=npos, tm=tm, alg_bytes=alg_bytes, achieved=achieved, cpu=cpu,
+        key=f"verify_rows_{args.mode}" if name == "dfly" else f"{name}_{args.mode}",
+        config={"workload": f"{desc}, {mode}; cache-cold ({len(copies)} rotating input copies)",
+                "B": B, "K": K, "V": V, "T": T, **({"budget_N": N} if N else {})},
+        extra={"alpha_mean": round(float(state["out"]["alpha"].float().mean()), 4),
+               "tau_mean": round(sum(taus) / len(taus), 3), "n_full_accept_mean": sum(n_full) / len(n_full)})
+
+
+def bench_e2e(args, sv, workloads, torch):
+    dev = "cuda"
+    target, draft, T = workloads.make_e2e_inputs(device=dev)
+    I, D, V = target.shape
+    ws = sv.Workspace(dev).get(I, D, V)
+    alpha = torch.empty((I, D), dtype=torch.float32, device=dev)
+    state = {}
+
+    def step(i):
+        state["loss"], _ = sv.sv_tv_e2e_loss(target, draft, T, alpha=alpha, workspace=ws)
+
+    tm = Timed(torch, torch.cuda.current_stream()).run(step, min(args.warmup, 3), min(args.steps, 10))
+    npos = I * D
+    alg_bytes = npos * 2 * V * 2
+    cpu = None if args.no_cpu_baseline else cpu_baseline_e2e(target, draft, T)
+    return dict(positions=npos, tm=tm, alg_bytes=alg_bytes, achieved=alg_bytes / tm.avg_launch_s / 1e9, cpu=cpu,
+                key="e2e_alpha",
+                config={"workload": f"end-to-end TV objective: |I|={I} positions x D={D}, V={V}, bf16 logits, "
+                                    f"T={T} ({2 * target.numel() * 2 / 1e9:.1f} GB read per call)",
+                        "I": I, "D": D, "V": V, "T": T},
+                extra={"loss": float(state["loss"].item()), "alpha_mean": round(float(alpha.mean()), 4)})
 
 
 def main():
@@ -117,8 +254,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--mode", choices=["stoch", "greedy"], default="stoch")
+    ap.add_argument("--workload", choices=["dfly", "mtp", "budget", "e2e"], default="dfly",
+                    help="dfly (default: the headline line), mtp, budget (allocation + ragged verify) or e2e")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copies", type=int, default=2)
+    ap.add_argument("--copies", type=int, default=0, help="rotating input copies (0: per-workload default)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only the known-size elementwise kernel used to calibrate byte counters")
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -142,97 +281,41 @@ def main():
     import draft_verification_softmax_amd as sv
     import workloads
 
-    dev = "cuda"
-    T = 0.9 if args.mode == "stoch" else 0.0
-    base = workloads.make_verify_inputs("dfly", device=dev, T=T)
-    B, K1, V = base.target.shape
-    K = K1 - 1
-    copies = [base] + [workloads.VerifyInputs(base.target.clone(), base.draft.clone(), base.draft_tokens.clone(),
-                                              base.T, base.seed, base.name) for _ in range(args.copies - 1)]
-    ws = sv.Workspace(dev).get(B, K, V)
-    out = None
-    stream = torch.cuda.current_stream()
-
-    def step(i):
-        nonlocal out
-        c = copies[i % len(copies)]
-        out = sv.sv_verify_batch(c.target, c.draft, c.draft_tokens, T, seed=c.seed, step=i, workspace=ws,
-                                 out=out, want_lse=True)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    n = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-    t_all0, t_all1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_all0.record(stream)
-    for i in range(n):
-        ev[i][0].record(stream)
-        step(args.warmup + i)
-        ev[i][1].record(stream)
-    t_all1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    per_launch_ms = [a.elapsed_time(b) for a, b in ev]
-    total_ms = t_all0.elapsed_time(t_all1)
-    avg_launch_s = sum(per_launch_ms) / n / 1e3
-
-    tau = out["accept_len"].cpu()
-    n_full = int((tau == K).sum())
-    alpha_mean = float(out["alpha"].float().mean())
-    positions = B * K
-    alg_bytes = positions * 2 * V * 2 + n_full * V * 2
-    achieved = alg_bytes / avg_launch_s / 1e9
+    if args.workload == "e2e":
+        r = bench_e2e(args, sv, workloads, torch)
+    else:
+        r = bench_verify(args, sv, workloads, torch, args.workload)
+    tm = r["tm"]
+    n = len(tm.per_launch_ms)
     digest = _source_digest()
-    key = f"verify_rows_{args.mode}"
-    traffic = _traffic(key, digest)
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(base, T, base.seed)
-
     line = {
         "metric": METRIC,
-        "value": positions * n / (total_ms / 1e3),
+        "value": r["positions"] * n / (tm.total_ms / 1e3),
         "unit": "positions/s",
         "n_gpus": 1,
         "steps": n,
         "warmup": args.warmup,
-        "ms_per_step": total_ms / n,
+        "ms_per_step": tm.total_ms / n,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {
-            "workload": f"DFly block verify: B={B} requests x block {K}, V={V}, bf16 logits, "
-                        f"{'T=0.9 stochastic' if T > 0 else 'T=0 greedy'}; cache-cold ({len(copies)} rotating "
-                        f"input copies)",
-            "B": B, "K": K, "V": V, "T": T,
-        },
+        "config": r["config"],
         "roofline": {
             "bound": "hbm",
-            "achieved": round(achieved, 1),
+            "achieved": round(r["achieved"], 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "kernel": key,
-            "alg_bytes_per_launch": alg_bytes,
-            "avg_launch_us": round(avg_launch_s * 1e6, 2),
+            "frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
+            "traffic": _traffic(r["key"], digest),
+            "kernel": r["key"],
+            "alg_bytes_per_launch": round(r["alg_bytes"]),
+            "avg_launch_us": round(tm.avg_launch_s * 1e6, 2),
         },
-        "cpu_baseline": cpu,
-        "extra": {
-            "hbm_gbs": round(achieved, 1),
-            "alpha_mean": round(alpha_mean, 4),
-            "tau_mean": round(float(tau.float().mean()), 3),
-            "n_full_accept": n_full,
-            "wall_s_timed_region": round(wall, 4),
-            "source_digest": digest,
-        },
+        "cpu_baseline": r["cpu"],
+        "extra": {"hbm_gbs": round(r["achieved"], 1), **r["extra"], "wall_s_timed_region": round(tm.wall, 4),
+                  "source_digest": digest},
     }
     print(json.dumps(line), flush=True)
 

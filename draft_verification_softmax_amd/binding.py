@@ -16,7 +16,7 @@ SV_F32, SV_BF16 = 0, 1
 _STATUS = {0: "SV_OK", 1: "SV_EINVAL", 2: "SV_EUNSUPPORTED", 3: "SV_EHIP", 4: "SV_EWORKSPACE", 5: "SV_EDEVICE"}
 
 EXPORTS = [
-    "sv_workspace_bytes", "sv_workspace_init", "sv_verify_batch", "sv_accept_len",
+    "sv_workspace_bytes", "sv_workspace_init", "sv_verify_batch", "sv_verify_selected", "sv_accept_len",
     "sv_residual_sample", "sv_tv_e2e_loss", "sv_alloc_verify_budget", "sv_uniforms",
     "sv_device_error", "sv_status_string",
 ]
@@ -56,6 +56,7 @@ def lib():
         L.sv_workspace_bytes.restype = sz
         L.sv_workspace_init.argtypes = [vp, sz, vp]
         L.sv_verify_batch.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.sv_verify_selected.argtypes = [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.sv_accept_len.argtypes = [vp, vp, i32, i32, vp, vp]
         L.sv_residual_sample.argtypes = [P, vp, vp, vp, vp, vp, vp]
         L.sv_tv_e2e_loss.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
@@ -151,6 +152,26 @@ def sv_verify_batch(target, draft, draft_tokens, T, seed=0, step=0, draft_len=No
     """target [B][K+1][V], draft [B][K][V], draft_tokens [B][K] int32 (all on the GPU).
     Returns a dict of device tensors (alpha, accept, lse_t, lse_d, amax_t, amax_d,
     accept_len, out_tokens, n_out)."""
+    return _verify(target, draft, draft_tokens, T, seed, step, draft_len, None, 0, want_lse, want_amax, workspace,
+                   out, stream)
+
+
+def sv_verify_selected(target, draft, draft_tokens, T, lens, row_list, n_rows, seed=0, step=0, want_lse=True,
+                       want_amax=False, workspace=None, out=None, stream=None):
+    """Verification of the rows one sv_alloc_verify_budget call selected: lens [B] and
+    row_list are its outputs, n_rows their number (host int).  Same outputs as
+    sv_verify_batch(draft_len=lens)."""
+    if lens is None or lens.dtype != torch.int32:
+        raise ValueError("lens must be int32 [B]")
+    n_rows = int(n_rows)
+    if n_rows > 0 and (row_list is None or row_list.dtype != torch.int32 or row_list.numel() < n_rows):
+        raise ValueError("row_list must be int32 with at least n_rows entries")
+    return _verify(target, draft, draft_tokens, T, seed, step, lens, row_list, n_rows, want_lse, want_amax,
+                   workspace, out, stream, selected=True)
+
+
+def _verify(target, draft, draft_tokens, T, seed, step, draft_len, row_list, n_rows, want_lse, want_amax, workspace,
+            out, stream, selected=False):
     B, K1, V = target.shape
     K = K1 - 1
     if draft.shape != (B, K, V) or draft_tokens.shape != (B, K):
@@ -176,12 +197,16 @@ def sv_verify_batch(target, draft, draft_tokens, T, seed=0, step=0, draft_len=No
         )
     ws = workspace if isinstance(workspace, torch.Tensor) else (workspace or Workspace(dev)).get(B, K, V, stream)
     prm = _params(B, K, V, target, draft, T, seed, step)
-    rc = lib().sv_verify_batch(
-        C.byref(prm), _p(target), _p(draft), _p(draft_tokens), _p(draft_len),
-        _p(out["alpha"]), _p(out["accept"]), _p(out["lse_t"]), _p(out["lse_d"]),
-        _p(out["amax_t"]), _p(out["amax_d"]), _p(out["accept_len"]), _p(out["out_tokens"]),
-        _p(out["n_out"]), _p(ws), ws.numel(), _stream(stream))
-    _check("sv_verify_batch", rc)
+    outs = (_p(out["alpha"]), _p(out["accept"]), _p(out["lse_t"]), _p(out["lse_d"]), _p(out["amax_t"]),
+            _p(out["amax_d"]), _p(out["accept_len"]), _p(out["out_tokens"]), _p(out["n_out"]))
+    if selected:
+        rc = lib().sv_verify_selected(C.byref(prm), _p(target), _p(draft), _p(draft_tokens), _p(draft_len),
+                                      _p(row_list), n_rows, *outs, _p(ws), ws.numel(), _stream(stream))
+        _check("sv_verify_selected", rc)
+    else:
+        rc = lib().sv_verify_batch(C.byref(prm), _p(target), _p(draft), _p(draft_tokens), _p(draft_len), *outs,
+                                   _p(ws), ws.numel(), _stream(stream))
+        _check("sv_verify_batch", rc)
     return out
 
 

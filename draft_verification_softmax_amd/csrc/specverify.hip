@@ -331,7 +331,10 @@ __global__ __launch_bounds__(kReduceThreads) void budget_kernel(const float *con
     while (np2 < n) np2 <<= 1;
     if (threadIdx.x == 0) s_total = 0;
     for (int i = threadIdx.x; i < np2; i += kReduceThreads) keys[i] = ~0ull;
-    for (int r = threadIdx.x; r < B; r += kReduceThreads) cnt[r] = 0;
+    // the confidences are staged in LDS first (one coalesced sweep; cnt serves as the
+    // staging area) so that the per-request products below read no global memory
+    float *cstage = reinterpret_cast<float *>(cnt);
+    for (int i = threadIdx.x; i < n; i += kReduceThreads) cstage[i] = conf[i];
     __syncthreads();
     // cumulative confidence per request: one thread per request, sequential binary32 products
     int local_total = 0;
@@ -343,7 +346,7 @@ __global__ __launch_bounds__(kReduceThreads) void budget_kernel(const float *con
         }
         float C = 1.f;
         for (int k = 0; k < L; ++k) {
-            const float ck = conf[(size_t)r * K + k];
+            const float ck = cstage[r * K + k];
             C = (k == 0) ? ck : __fmul_rn(C, ck);
             // ascending key = descending C (non-negative binary32 bits are monotone), then (r, k)
             keys[r * K + k] = ((uint64_t)(~__float_as_uint(C)) << 32) | (uint32_t)(r * K + k);
@@ -352,18 +355,45 @@ __global__ __launch_bounds__(kReduceThreads) void budget_kernel(const float *con
     }
     atomicAdd(&s_total, local_total);
     __syncthreads();
+    for (int r = threadIdx.x; r < B; r += kReduceThreads) cnt[r] = 0;
+    __syncthreads();
     // bitonic sort, ascending
-    for (int size = 2; size <= np2; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = threadIdx.x; i < np2; i += kReduceThreads) {
-                const int j = i ^ stride;
-                if (j > i) {
-                    const bool up = (i & size) == 0;
-                    const uint64_t a = keys[i], b = keys[j];
-                    if ((a > b) == up) { keys[i] = b; keys[j] = a; }
+    if (np2 <= kReduceThreads) {
+        // one key per thread in registers: exchanges within a wave (partner distance < 64)
+        // by lane shuffles, wider ones through LDS
+        const int i = threadIdx.x;
+        uint64_t key = i < np2 ? keys[i] : ~0ull;
+        for (int size = 2; size <= np2; size <<= 1) {
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                uint64_t other;
+                if (stride >= kWave) {
+                    keys[i] = key;
+                    __syncthreads();
+                    other = keys[i ^ stride];
+                    __syncthreads();
+                } else {
+                    other = __shfl_xor(key, stride, kWave);
                 }
+                // the lower index of a pair keeps the minimum in an ascending block
+                const bool up = (i & size) == 0, lower = (i & stride) == 0;
+                key = (lower == up) ? (key < other ? key : other) : (key < other ? other : key);
             }
-            __syncthreads();
+        }
+        keys[i] = key;
+        __syncthreads();
+    } else {
+        for (int size = 2; size <= np2; size <<= 1) {
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                for (int i = threadIdx.x; i < np2; i += kReduceThreads) {
+                    const int j = i ^ stride;
+                    if (j > i) {
+                        const bool up = (i & size) == 0;
+                        const uint64_t a = keys[i], b = keys[j];
+                        if ((a > b) == up) { keys[i] = b; keys[j] = a; }
+                    }
+                }
+                __syncthreads();
+            }
         }
     }
     const int keep = min(N, s_total);
@@ -377,15 +407,24 @@ __global__ __launch_bounds__(kReduceThreads) void budget_kernel(const float *con
     const int b0 = threadIdx.x * per, b1 = min(B, b0 + per);
     int sum = 0;
     for (int r = b0; r < b1; ++r) sum += cnt[r];
-    scan[threadIdx.x] = sum;
-    __syncthreads();
-    for (int d = 1; d < kReduceThreads; d <<= 1) {
-        const int v = threadIdx.x >= d ? scan[threadIdx.x - d] : 0;
-        __syncthreads();
-        scan[threadIdx.x] += v;
-        __syncthreads();
+    // inclusive scan of the chunk sums in thread order: within each wave by shuffles, then
+    // the wave totals
+    int incl = sum;
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int y = __shfl_up(incl, d, kWave);
+        if (lane >= d) incl += y;
     }
-    int off = scan[threadIdx.x] - sum;
+    if (lane == kWave - 1) scan[wv] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int q = 0; q < wv; ++q) before += scan[q];
+    incl += before;
+    __syncthreads();
+    scan[threadIdx.x] = incl;
+    __syncthreads();
+    int off = incl - sum;
     for (int r = b0; r < b1; ++r) {
         lens[r] = cnt[r];
         row_off[r] = off;
@@ -505,11 +544,13 @@ int sv_workspace_init(void *workspace, size_t workspace_bytes, void *stream) {
     return launch_status();
 }
 
-int sv_verify_batch(const sv_params *p, const void *target, const void *draft,
-                    const int32_t *draft_tokens, const int32_t *draft_len, float *alpha,
-                    uint8_t *accept, float *lse_t, float *lse_d, int32_t *amax_t,
-                    int32_t *amax_d, int32_t *accept_len, int32_t *out_tokens, int32_t *n_out,
-                    void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+static int verify_impl(const sv_params *p, const void *target, const void *draft,
+                       const int32_t *draft_tokens, const int32_t *draft_len, bool selected,
+                       const int32_t *row_list, int32_t n_rows, float *alpha, uint8_t *accept, float *lse_t, float *lse_d,
+                       int32_t *amax_t, int32_t *amax_d, int32_t *accept_len, int32_t *out_tokens,
+                       int32_t *n_out, void *workspace, size_t workspace_bytes, void *stream) {
     if (!p || p->B < 0 || p->K_max < 0 || p->K_max > SV_K_MAX || p->V <= 0) return SV_EINVAL;
     if (p->V > SV_V_MAX) return SV_EUNSUPPORTED;
     if (!(p->temperature >= 0.f) || !isfinite(p->temperature)) return SV_EINVAL;
@@ -538,10 +579,37 @@ int sv_verify_batch(const sv_params *p, const void *target, const void *draft,
     a.trows = p->K_max + 1;
     a.slots = p->K_max + 1;
     a.want_amax = (amax_t || amax_d) ? 1 : 0;
+    a.selected = selected ? 1 : 0;
+    a.row_list = row_list;
+    a.n_rows = n_rows;
     const int mode = p->temperature == 0.f ? kTeamGreedy : kTeamStoch;
     hipError_t e = team_launch_stream(a, p->dtype_t, p->dtype_d, mode, (hipStream_t)stream);
     if (e == hipSuccess) e = team_launch_finalize(a, p->dtype_t, p->dtype_d, mode, (hipStream_t)stream);
     return e == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+extern "C" {
+
+int sv_verify_batch(const sv_params *p, const void *target, const void *draft,
+                    const int32_t *draft_tokens, const int32_t *draft_len, float *alpha,
+                    uint8_t *accept, float *lse_t, float *lse_d, int32_t *amax_t,
+                    int32_t *amax_d, int32_t *accept_len, int32_t *out_tokens, int32_t *n_out,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+    return verify_impl(p, target, draft, draft_tokens, draft_len, false, nullptr, 0, alpha, accept, lse_t, lse_d, amax_t,
+                       amax_d, accept_len, out_tokens, n_out, workspace, workspace_bytes, stream);
+}
+
+int sv_verify_selected(const sv_params *p, const void *target, const void *draft,
+                       const int32_t *draft_tokens, const int32_t *lens, const int32_t *row_list,
+                       int32_t n_rows, float *alpha, uint8_t *accept, float *lse_t, float *lse_d,
+                       int32_t *amax_t, int32_t *amax_d, int32_t *accept_len, int32_t *out_tokens,
+                       int32_t *n_out, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!p || p->B < 0 || p->K_max < 0) return SV_EINVAL;
+    if (n_rows < 0 || (int64_t)n_rows > (int64_t)p->B * p->K_max) return SV_EINVAL;
+    if (p->B > 0 && !lens) return SV_EINVAL;
+    if (n_rows > 0 && !row_list) return SV_EINVAL;
+    return verify_impl(p, target, draft, draft_tokens, lens, true, row_list, n_rows, alpha, accept, lse_t, lse_d,
+                       amax_t, amax_d, accept_len, out_tokens, n_out, workspace, workspace_bytes, stream);
 }
 
 int sv_accept_len(const uint8_t *accept, const int32_t *draft_len, int32_t B, int32_t K_max,

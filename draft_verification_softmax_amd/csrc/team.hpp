@@ -81,6 +81,9 @@ struct TeamArgs {
     float c;           // log2(e) / T
     uint64_t seed, step;
     int32_t want_amax;
+    int32_t selected;         // 1: the verified rows are the n_rows rows r * K + k of row_list
+    const int32_t *row_list;  //    (0: every row k < L_r)
+    int32_t n_rows;
     int64_t spin_ticks;  // bounded wait for teammates' partials (10 ns ticks)
 };
 

@@ -745,15 +745,30 @@ __global__ __launch_bounds__(kTeamThreads) __attribute__((amdgpu_waves_per_eu(5)
 
     // The S members of a team are consecutive workgroups: round-robin dispatch spreads them
     // over the XCDs, whose dispatchers start them at nearly the same time.
-    // (divisions by runtime values are done on the vector unit: readfirstlane returns the
-    // uniform results to scalar registers)
+    // Work items in grid order: the verified rows (r, k < K) request by request, then every
+    // request's bonus slot, so the short bonus workgroups are dispatched last and fill the
+    // tail of the grid.  (Divisions by runtime values are done on the vector unit:
+    // readfirstlane returns the uniform results to scalar registers.)
     const int S = a.S;
     const int j = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % (unsigned)S));
-    const int64_t row = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / (unsigned)S));
+    const int item = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / (unsigned)S));
     const int K = a.K;
     const int slots = a.slots;
-    const int r = __builtin_amdgcn_readfirstlane((int)(row / slots));
-    const int k = __builtin_amdgcn_readfirstlane((int)(row % slots));
+    // With a row list, the verified items are the listed rows only.
+    const int nv = a.selected ? a.n_rows : a.B * K;
+    int r = item - nv, k = K;
+    if (item < nv) {
+        const int f = a.selected ? load_uniform(a.row_list + item) : item;
+        if (f < 0 || f >= a.B * K) {   // not a row of this batch: nothing to do
+            if (threadIdx.x == 0 && j == 0) atomicOr(a.err, SV_DEVERR_DRAFT_LEN);
+            return;
+        }
+        r = f / K;
+        k = f - r * K;
+    }
+    r = __builtin_amdgcn_readfirstlane(r);
+    k = __builtin_amdgcn_readfirstlane(k);
+    const int64_t row = (int64_t)r * slots + k;
     const bool bonus = (MODE != kTeamAlpha) && k == K;
     const int L = (MODE != kTeamAlpha) ? request_limit(a, r, bonus && j == 0 && threadIdx.x == 0) : K;
     if (!bonus && k >= L) return;
@@ -926,7 +941,8 @@ __global__ __launch_bounds__(kTeamThreads) void finalize_kernel(TeamArgs a) {
         if (MODE == kTeamStoch && (flags & 1)) {
             for (int q = 0; q < nb; ++q) {
                 if (sx[q * 4 + 1] != 0xffffffffu) continue;
-                load_tagged(a.part + (row0 + k0 + q) * 8 * S, 4 * S, tag, pay, 0u);
+                const int missing = load_tagged(a.part + (row0 + k0 + q) * 8 * S, 4 * S, tag, pay, 0u);
+                if (missing && threadIdx.x == 0) atomicOr(a.err, SV_DEVERR_DRAFT_LEN);   // the row was never streamed
                 __syncthreads();
                 if (threadIdx.x == 0) {
                     float L2t, L2d;
@@ -1169,7 +1185,9 @@ __global__ __launch_bounds__(kTeamThreads) void e2e_alpha_kernel(TeamArgs a) {
 
 template <int DTT, int DTD>
 static hipError_t launch_stream_t(const TeamArgs &a, int mode, hipStream_t s) {
-    const unsigned grid = (unsigned)((uint64_t)a.rows * (uint64_t)a.S);
+    const uint64_t items = a.selected ? (uint64_t)a.n_rows + (uint64_t)a.B : (uint64_t)a.rows;
+    const unsigned grid = (unsigned)(items * (uint64_t)a.S);
+    if (grid == 0) return hipSuccess;
     if (mode == kTeamStoch && a.want_amax)
         hipLaunchKernelGGL((stream_kernel<DTT, DTD, kTeamStoch, true>), dim3(grid), dim3(kTeamThreads), 0, s, a);
     else if (mode == kTeamStoch)

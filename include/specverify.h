@@ -63,7 +63,8 @@ enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 };
 
 /* Device error flags (sv_device_error). */
 #define SV_DEVERR_TOKEN 1u     /* a draft token outside [0, V) */
-#define SV_DEVERR_DRAFT_LEN 2u /* a draft_len entry outside [0, K_max] */
+#define SV_DEVERR_DRAFT_LEN 2u /* a draft_len entry outside [0, K_max], or a row list that does not
+                                  match its lengths (sv_verify_selected) */
 #define SV_DEVERR_TIMEOUT 4u   /* an internal wait for already-issued stores exceeded its bound */
 
 typedef struct sv_params {
@@ -118,6 +119,20 @@ int sv_verify_batch(const sv_params *params, const void *target, const void *dra
                     uint8_t *accept, float *lse_t, float *lse_d, int32_t *amax_t,
                     int32_t *amax_d, int32_t *accept_len, int32_t *out_tokens, int32_t *n_out,
                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* Verification of the rows a budget allocation selected [RT]: as sv_verify_batch with
+ * draft_len = lens, but the work is laid out over the n_rows listed rows only (plus each
+ * request's bonus row), so unselected rows cost nothing.  lens [B] and row_list [n_rows]
+ * (r * K_max + k, in (r, k) order) are the outputs of one sv_alloc_verify_budget call: row_list
+ * must list exactly the rows k < lens[r], and n_rows = sum_r lens[r] = min(budget_N, B * K_max)
+ * when that call had no draft_len (the caller knows it without reading the device).  A listed
+ * row outside the batch, or a row k < lens[r] left out, sets SV_DEVERR_DRAFT_LEN.
+ * Outputs, workspace and errors as sv_verify_batch. */
+int sv_verify_selected(const sv_params *params, const void *target, const void *draft,
+                       const int32_t *draft_tokens, const int32_t *lens, const int32_t *row_list,
+                       int32_t n_rows, float *alpha, uint8_t *accept, float *lse_t, float *lse_d,
+                       int32_t *amax_t, int32_t *amax_d, int32_t *accept_len, int32_t *out_tokens,
+                       int32_t *n_out, void *workspace, size_t workspace_bytes, void *stream);
 
 /* First-reject prefix length per request [TV]: accept [B][K_max] uint8, draft_len [B] or
  * NULL; accept_len[r] = first k < L_r with accept == 0, else L_r. */

@@ -84,3 +84,21 @@ def test_host_validation_rejects_without_launch(svlib):
     assert svlib.sv_uniforms(0, nul, -1, nul, nul) == EINVAL
     # B = 0 is a no-op
     assert svlib.sv_verify_batch(*args17(Params(0, 3, 100, 0, 0, 1.0, 0, 0, 100, 100))) == 0
+
+
+def test_verify_selected_host_validation(svlib):
+    from draft_verification_softmax_amd.binding import Params
+    EINVAL, EWS = 1, 4
+    nul = None
+    fake = C.c_void_p(0x1000)
+    prm = Params(2, 3, 96, 1, 1, 1.0, 0, 0, 96, 96)
+
+    def call(lens, rows, n, ws=nul):
+        return svlib.sv_verify_selected(C.byref(prm), fake, fake, fake, lens, rows, n, fake, fake, nul, nul, nul,
+                                        nul, fake, fake, fake, ws, 0, nul)
+    assert call(fake, fake, -1) == EINVAL          # negative row count
+    assert call(fake, fake, 2 * 3 + 1) == EINVAL   # more rows than the batch has
+    assert call(nul, fake, 2) == EINVAL            # no lengths
+    assert call(fake, nul, 2) == EINVAL            # rows without a list
+    assert call(fake, nul, 0) == EWS               # zero rows is valid; then the workspace is missing
+    assert call(fake, fake, 6) == EWS

@@ -206,6 +206,72 @@ def test_budget_then_ragged_verify(sv):
     _say(f"report {rep}")
 
 
+def test_budget_selected_verify(sv):
+    """sv_verify_selected over the allocation's row list equals sv_verify_batch with
+    draft_len = lens (same kernels, same member order), and the oracle on sampled requests."""
+    v, conf, N = workloads.make_budget_inputs(device=DEV)
+    B, K = conf.shape
+    lens, off, rl = sv.sv_alloc_verify_budget(conf, N)
+    n_rows = min(N, B * K)
+    assert int(off[-1].item()) == n_rows
+    ws = sv.Workspace(DEV)
+    for T in (v.T, 0.0):
+        _say(f"budget selected verify T={T}")
+        sel = _np(sv.sv_verify_selected(v.target, v.draft, v.draft_tokens, T, lens, rl, n_rows, seed=v.seed,
+                                        want_amax=True, workspace=ws))
+        bat = _np(sv.sv_verify_batch(v.target, v.draft, v.draft_tokens, T, seed=v.seed, draft_len=lens,
+                                     want_amax=True, workspace=ws))
+        for key in bat:
+            if bat[key] is not None:
+                assert np.array_equal(sel[key], bat[key]), key
+    assert sv.sv_device_error(ws.get(B, K, v.target.shape[2])) == 0
+    ol = lens.cpu().numpy()
+    check = [1, 17, 40, 62]
+    tn, dn = workloads.to_oracle(v.target), workloads.to_oracle(v.draft)
+    dl = np.zeros_like(ol)
+    dl[check] = ol[check]
+    o = svref.verify_batch(tn, dn, v.draft_tokens.cpu().numpy(), v.T, "bf16", seed=v.seed, draft_len=dl,
+                           diagnostics=True)
+    sel = _np(sv.sv_verify_selected(v.target, v.draft, v.draft_tokens, v.T, lens, rl, n_rows, seed=v.seed,
+                                    want_amax=True))
+    rep = compare_verify(sel, o, tn, dn, "bf16", v.T, check=check, L=dl)
+    _say(f"report {rep}")
+
+
+def test_selected_verify_small_ragged_vocab(sv):
+    """Random small batches, vocabulary 9001 in rows padded to 9008 (a ragged last chunk),
+    budget allocation then sv_verify_selected, against the oracle on every request."""
+    rng = np.random.default_rng(11)
+    V, ld = 9001, 9008
+    for trial in range(4):
+        B, K = int(rng.integers(1, 6)), int(rng.integers(1, 6))
+        T = [0.9, 0.0, 1.3, 0.9][trial]
+        g = torch.Generator(device=DEV).manual_seed(60 + trial)
+        tt = torch.full((B, K + 1, ld), float("nan"), device=DEV, dtype=torch.bfloat16)
+        dd = torch.full((B, K, ld), float("nan"), device=DEV, dtype=torch.bfloat16)
+        t = 2.5 * torch.randn((B, K + 1, V), generator=g, device=DEV)
+        d = t[:, :K] + 0.7 * torch.randn((B, K, V), generator=g, device=DEV)
+        tt[..., :V] = t.to(torch.bfloat16)
+        dd[..., :V] = d.to(torch.bfloat16)
+        toks = torch.argmax(d, -1).to(torch.int32)
+        toks[:, 0] = torch.randint(0, V, (B,), generator=g, device=DEV, dtype=torch.int32)
+        conf = torch.as_tensor(rng.beta(5, 2, size=(B, K)).astype(np.float32), device=DEV)
+        N = int(rng.integers(0, B * K + 2))
+        lens, off, rl = sv.sv_alloc_verify_budget(conf, N)
+        n_rows = min(N, B * K)
+        _say(f"selected small trial {trial} B={B} K={K} N={N} T={T}")
+        ws = sv.Workspace(DEV)
+        out = _np(sv.sv_verify_selected(tt[..., :V], dd[..., :V], toks, T, lens, rl, n_rows, seed=5, step=trial,
+                                        want_amax=True, workspace=ws))
+        assert sv.sv_device_error(ws.get(B, K, V)) == 0
+        tn = workloads.to_oracle(tt[..., :V].contiguous())
+        dn = workloads.to_oracle(dd[..., :V].contiguous())
+        dl = lens.cpu().numpy()
+        o = svref.verify_batch(tn, dn, toks.cpu().numpy(), T, "bf16", seed=5, step=trial, draft_len=dl,
+                               diagnostics=True)
+        compare_verify(out, o, tn, dn, "bf16", T, L=dl)
+
+
 def test_e2e_small(sv):
     t, d, T = workloads.make_e2e_inputs(device=DEV, I=48, D=3)
     _say("e2e small")
