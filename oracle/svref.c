@@ -430,3 +430,57 @@ int svref_alloc_verify_budget(const float *conf, const int32_t *draft_len, int32
     free(cand);
     return 0;
 }
+
+int svref_dcut_budget(const float *conf, const int32_t *draft_len, int32_t B, int32_t K_max,
+                      const float *cost, int32_t n_cost, int32_t *n_chosen, double *utility,
+                      int32_t *lens, int32_t *row_off, int32_t *row_list) {
+    if (B < 0 || K_max < 0 || n_cost < 1 || !cost || !n_chosen || !utility) return 1;
+    size_t n = 0;
+    for (int32_t r = 0; r < B; ++r) {
+        const int32_t L_r = draft_len ? draft_len[r] : K_max;
+        if (L_r < 0 || L_r > K_max) return 1;
+        n += (size_t)L_r;
+    }
+    cand_t *cand = (cand_t *)malloc(sizeof(cand_t) * (n ? n : 1));
+    if (!cand) return 1;
+    size_t j = 0;
+    for (int32_t r = 0; r < B; ++r) {
+        const int32_t L_r = draft_len ? draft_len[r] : K_max;
+        volatile float C = 1.0f;
+        for (int32_t k = 0; k < L_r; ++k) {
+            float c = conf[(size_t)r * K_max + k];
+            C = (k == 0) ? c : (float)(C * c);
+            cand[j].c = C;
+            cand[j].r = r;
+            cand[j].k = k;
+            ++j;
+        }
+    }
+    qsort(cand, n, sizeof(cand_t), cand_cmp);
+    const size_t nmax = (size_t)(n_cost - 1) < n ? (size_t)(n_cost - 1) : n;
+    double P = 0.0;         /* sum of the first m candidates' C, in candidate order */
+    double best_ratio = 0.0;
+    int32_t best = -1;
+    double best_E = (double)B;
+    for (size_t m = 0; m <= nmax; ++m) {
+        const double E = (double)B + P;
+        const double cm = (double)cost[m];
+        if (isfinite(cm) && cm > 0.0) {
+            const double ratio = E / cm;
+            if (best < 0 || ratio > best_ratio) {
+                best = (int32_t)m;
+                best_ratio = ratio;
+                best_E = E;
+            }
+        }
+        if (m < n) P += (double)cand[m].c;
+    }
+    free(cand);
+    if (best < 0) {
+        best = 0;
+        best_E = (double)B;
+    }
+    *n_chosen = best;
+    *utility = best_E;
+    return svref_alloc_verify_budget(conf, draft_len, B, K_max, best, lens, row_off, row_list);
+}

@@ -117,6 +117,22 @@ int svref_alloc_verify_budget(const float *conf, const int32_t *draft_len, int32
                               int32_t K_max, int32_t budget_N, int32_t *lens, int32_t *row_off,
                               int32_t *row_list);
 
+/* D-cut: the total verification budget chosen from a cost table.  AngelSpec tutorial,
+ * section "Runtime adaptation: verification as a shared compute pool": verification is a
+ * pool shared across requests, spent on the prefixes with the highest expected benefit,
+ * and cut back when the load makes it dear.  Reading (the pages give no formula):
+ * verifying the best n candidates of the budget order (C desc, r asc, k asc) emits in
+ * expectation E(n) = B + (sum of their C), one correction/bonus token per request plus the
+ * expected accepted drafts of a prefix-closed selection; cost[n] (n = 0..n_cost-1) is the
+ * caller's measured cost of a step that verifies n positions.  The chosen n maximises
+ * E(n) / cost[n] over n <= min(n_cost - 1, sum_r L_r) among entries with a finite
+ * positive cost (the smallest such n on ties; 0 when no entry qualifies).  E is summed in
+ * binary64 in candidate order.  Outputs *n_chosen, *utility = E(n_chosen) and the
+ * allocation of svref_alloc_verify_budget with budget n_chosen. */
+int svref_dcut_budget(const float *conf, const int32_t *draft_len, int32_t B, int32_t K_max,
+                      const float *cost, int32_t n_cost, int32_t *n_chosen, double *utility,
+                      int32_t *lens, int32_t *row_off, int32_t *row_list);
+
 #ifdef __cplusplus
 }
 #endif

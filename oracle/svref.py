@@ -42,6 +42,7 @@ def lib():
         L.svref_e2e_from_alpha.restype = dbl
         L.svref_tv_e2e_loss.argtypes = [C.POINTER(Params), vp, vp, vp, vp]
         L.svref_alloc_verify_budget.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
+        L.svref_dcut_budget.argtypes = [vp, vp, i32, i32, vp, i32, C.POINTER(C.c_int32), C.POINTER(C.c_double), vp, vp, vp]
         _lib = L
     return _lib
 
@@ -177,6 +178,23 @@ def tv_e2e_loss(target, draft, T, dtype):
     if lib().svref_tv_e2e_loss(C.byref(prm), _ptr(target), _ptr(draft), _ptr(a), _ptr(loss)) != 0:
         raise ValueError("svref_tv_e2e_loss rejected its arguments")
     return float(loss[0]), a
+
+
+def dcut_budget(conf, cost, draft_len=None):
+    """D-cut budget choice: returns (n_chosen, utility, lens, row_off, row_list)."""
+    c = np.ascontiguousarray(conf, dtype=np.float32)
+    B, K = c.shape
+    dl = None if draft_len is None else np.ascontiguousarray(draft_len, dtype=np.int32)
+    cs = np.ascontiguousarray(cost, dtype=np.float32)
+    lens = np.zeros(B, np.int32)
+    off = np.zeros(B + 1, np.int32)
+    rl = np.zeros(max(B * K, 1), np.int32)
+    nc = C.c_int32(0)
+    ut = C.c_double(0.0)
+    if lib().svref_dcut_budget(_ptr(c), _ptr(dl), B, K, _ptr(cs), len(cs), C.byref(nc), C.byref(ut), _ptr(lens),
+                               _ptr(off), _ptr(rl)) != 0:
+        raise ValueError("svref_dcut_budget rejected its arguments")
+    return int(nc.value), float(ut.value), lens, off, rl[: int(off[-1])]
 
 
 def alloc_verify_budget(conf, budget_N, draft_len=None):

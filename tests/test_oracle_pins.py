@@ -344,3 +344,61 @@ def test_budget_binary32_cumprod_is_sequential():
         assert list(lens) == [k + 1, 0]
         lens, _, _ = svref.alloc_verify_budget(conf2, k + 2, draft_len=dl)
         assert list(lens) == [k + 1, 1] or k == 4
+
+
+# ---- D-cut budget choice from a cost table -------------------------------------------
+
+def test_dcut_hand_example():
+    # C = [[.9, .72, .36], [.6, .54, .486]]; E(n) = 2 + best n products; cost 1 + 0.2 n:
+    # E/cost = 2, 2.417, 2.586, 2.6375, 2.644, 2.623, 2.548 -> n = 4
+    conf = np.array([[0.9, 0.8, 0.5], [0.6, 0.9, 0.9]], np.float32)
+    cost = np.array([1.0, 1.2, 1.4, 1.6, 1.8, 2.0, 2.2], np.float32)
+    n, E, lens, off, rl = svref.dcut_budget(conf, cost)
+    assert n == 4
+    assert E == pytest.approx(2 + 0.9 + 0.72 + 0.6 + 0.54, abs=1e-6)
+    assert list(lens) == [2, 2] and list(rl) == [0, 1, 3, 4]
+
+
+@pytest.mark.parametrize("trial", range(20))
+def test_dcut_matches_brute_force(trial):
+    rng = np.random.default_rng(300 + trial)
+    B, K = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+    conf = rng.beta(5, 2, size=(B, K)).astype(np.float32)
+    C = np.multiply.accumulate(conf, axis=1, dtype=np.float32)
+    n_cost = int(rng.integers(1, B * K + 3))
+    cost = (1.0 + rng.random(n_cost) * 3).astype(np.float32)
+    cost[rng.random(n_cost) < 0.15] = [0.0, -1.0, np.inf, np.nan][trial % 4]   # never chosen
+    best, best_ratio, best_E = None, None, None
+    for n in range(0, min(n_cost - 1, B * K) + 1):
+        if not (np.isfinite(cost[n]) and cost[n] > 0):
+            continue
+        E = B + _brute_best(C, n)
+        ratio = E / float(cost[n])
+        if best is None or ratio > best_ratio * (1 + 1e-12):
+            best, best_ratio, best_E = n, ratio, E
+    if best is None:
+        best, best_E = 0, float(B)
+    n, E, lens, off, rl = svref.dcut_budget(conf, cost)
+    assert n == best
+    assert E == pytest.approx(best_E, abs=1e-9)
+    want_lens, _, _ = svref.alloc_verify_budget(conf, n)
+    assert np.array_equal(lens, want_lens)
+
+
+def test_dcut_special_cases():
+    conf = np.full((3, 4), 0.9, np.float32)
+    # a flat cost: every extra position adds expected tokens for free -> verify everything
+    n, E, lens, _, _ = svref.dcut_budget(conf, np.ones(100, np.float32))
+    assert n == 12 and list(lens) == [4, 4, 4]
+    # a table shorter than the candidates caps the choice
+    n, _, _, _, _ = svref.dcut_budget(conf, np.ones(6, np.float32))
+    assert n == 5
+    # cost growing faster than any gain: verify nothing (B tokens from the bonus rows)
+    n, E, lens, _, _ = svref.dcut_budget(conf, np.array([1.0] + [100.0] * 12, np.float32))
+    assert n == 0 and E == 3.0 and list(lens) == [0, 0, 0]
+    # no usable entry at all
+    n, E, _, _, _ = svref.dcut_budget(conf, np.array([0.0, np.nan, -2.0], np.float32))
+    assert n == 0 and E == 3.0
+    # draft_len bounds the candidates
+    n, _, lens, _, _ = svref.dcut_budget(conf, np.ones(100, np.float32), draft_len=np.array([1, 0, 2], np.int32))
+    assert n == 3 and list(lens) == [1, 0, 2]
