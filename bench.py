@@ -210,6 +210,14 @@ def bench_verify(args, sv, workloads, torch, name):
     if not args.no_cpu_baseline:
         what = {"dfly": "DFly", "mtp": "MTP chat", "budget": "budget-selected ragged"}[name]
         cpu = cpu_baseline_verify(base, T, base.seed, draft_len=state["lens"], what=what)
+    extra_t = {}
+    if conf is not None:
+        # the D-cut choice of the budget from a cost table (linear here: a fixed part plus a
+        # per-position part, in microseconds), timed on its own
+        cost = (40.0 + 0.05 * torch.arange(B * K + 1, device=dev, dtype=torch.float32)).contiguous()
+        t2 = Timed(torch, stream).run(lambda i: sv.sv_dcut_verify_budget(conf, cost), 5, 50)
+        n_c, _, _, _, _ = sv.sv_dcut_verify_budget(conf, cost)
+        extra_t = {"dcut_choice_us": round(t2.avg_launch_s * 1e6, 2), "dcut_chosen_n": int(n_c.item())}
     desc = {
         "dfly": f"DFly block verify: B={B} requests x block {K}, V={V}, bf16 logits",
         "mtp": f"MTP chat verify: B={B} requests x depth {K}, V={V}, bf16 logits",
@@ -223,7 +231,8 @@ def bench_verify(args, sv, workloads, torch, name):
         config={"workload": f"{desc}, {mode}; cache-cold ({len(copies)} rotating input copies)",
                 "B": B, "K": K, "V": V, "T": T, **({"budget_N": N} if N else {})},
         extra={"alpha_mean": round(float(state["out"]["alpha"].float().mean()), 4),
-               "tau_mean": round(sum(taus) / len(taus), 3), "n_full_accept_mean": sum(n_full) / len(n_full)})
+               "tau_mean": round(sum(taus) / len(taus), 3), "n_full_accept_mean": sum(n_full) / len(n_full),
+               **extra_t})
 
 
 def bench_e2e(args, sv, workloads, torch):

@@ -17,7 +17,7 @@ _STATUS = {0: "SV_OK", 1: "SV_EINVAL", 2: "SV_EUNSUPPORTED", 3: "SV_EHIP", 4: "S
 
 EXPORTS = [
     "sv_workspace_bytes", "sv_workspace_init", "sv_verify_batch", "sv_verify_selected", "sv_accept_len",
-    "sv_residual_sample", "sv_tv_e2e_loss", "sv_alloc_verify_budget", "sv_uniforms",
+    "sv_residual_sample", "sv_tv_e2e_loss", "sv_alloc_verify_budget", "sv_dcut_verify_budget", "sv_uniforms",
     "sv_device_error", "sv_status_string",
 ]
 
@@ -61,6 +61,7 @@ def lib():
         L.sv_residual_sample.argtypes = [P, vp, vp, vp, vp, vp, vp]
         L.sv_tv_e2e_loss.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
         L.sv_alloc_verify_budget.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp]
+        L.sv_dcut_verify_budget.argtypes = [vp, vp, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp]
         L.sv_uniforms.argtypes = [u64, vp, i32, vp, vp]
         L.sv_device_error.argtypes = [vp, vp, C.POINTER(C.c_uint32)]
         L.sv_status_string.argtypes = [C.c_int]
@@ -257,6 +258,25 @@ def sv_alloc_verify_budget(conf, budget_N, draft_len=None, want_row_list=True, s
     _check("sv_alloc_verify_budget", lib().sv_alloc_verify_budget(
         _p(conf), _p(draft_len), B, K, int(budget_N), _p(lens), _p(row_off), _p(row_list), _stream(stream)))
     return lens, row_off, row_list
+
+
+def sv_dcut_verify_budget(conf, cost, draft_len=None, want_row_list=True, stream=None):
+    """conf [B][K] float32, cost [n_cost] float32 (both on the GPU).  Returns (n_chosen [1]
+    int32, utility [1] float64, lens [B], row_off [B+1], row_list [B*K] or None), all device
+    tensors; row_list holds row_off[B] valid entries."""
+    B, K = conf.shape
+    dev = conf.device
+    if cost.dtype != torch.float32 or cost.dim() != 1 or not cost.is_contiguous():
+        raise ValueError("cost must be a contiguous float32 vector")
+    n_chosen = torch.empty((1,), dtype=torch.int32, device=dev)
+    utility = torch.empty((1,), dtype=torch.float64, device=dev)
+    lens = torch.empty((B,), dtype=torch.int32, device=dev)
+    row_off = torch.empty((B + 1,), dtype=torch.int32, device=dev)
+    row_list = torch.empty((max(B * K, 1),), dtype=torch.int32, device=dev) if want_row_list else None
+    _check("sv_dcut_verify_budget", lib().sv_dcut_verify_budget(
+        _p(conf), _p(draft_len), B, K, _p(cost), cost.numel(), _p(n_chosen), _p(utility), _p(lens), _p(row_off),
+        _p(row_list), _stream(stream)))
+    return n_chosen, utility, lens, row_off, row_list
 
 
 def sv_uniforms(seed, counters, stream=None):

@@ -318,10 +318,74 @@ __global__ __launch_bounds__(kReduceThreads) void e2e_reduce_kernel(const float 
 // ---------------------------------------------------------------------------------------
 // Batch verification budget
 // ---------------------------------------------------------------------------------------
+// D-cut choice of the budget (when cost != nullptr): among n = 0..min(n_cost - 1, total)
+// with a finite positive cost[n], the n maximising E(n) / cost[n], E(n) = B + the sum of the
+// first n candidates' C (binary64); the smallest n on ties, 0 if none qualifies.  The sum
+// runs as a block scan: each thread adds a contiguous run of candidates, then the run
+// totals are scanned.
+__device__ int dcut_choose(const uint64_t *keys, int total, int B, const float *cost, int n_cost, double *dscan,
+                           double *s_ratio, int *s_n, double *s_E, int32_t *n_chosen, double *utility) {
+    const int nmax = min(n_cost - 1, total);
+    const int count = nmax + 1;   // values of n
+    const int per = (count + kReduceThreads - 1) / kReduceThreads;
+    const int m0 = threadIdx.x * per, m1 = min(count, m0 + per);
+    auto Cof = [&](int m) { return (double)__uint_as_float(~(uint32_t)(keys[m] >> 32)); };
+    double run = 0.0;   // this thread's candidates m0..m1-1 that precede a later n
+    for (int m = m0; m < m1 && m < nmax; ++m) run += Cof(m);
+    // exclusive scan of the runs in thread order
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+    double incl = run;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const double y = __shfl_up(incl, d, kWave);
+        if (lane >= d) incl += y;
+    }
+    if (lane == kWave - 1) dscan[wv] = incl;
+    __syncthreads();
+    double before = 0.0;
+    for (int q = 0; q < wv; ++q) before += dscan[q];
+    double P = before + incl - run;
+    // this thread's best n
+    double best_r = -1.0, best_E = (double)B;
+    int best_n = 0x7fffffff;
+    for (int m = m0; m < m1; ++m) {
+        const double E = (double)B + P;
+        const double cm = (double)cost[m];
+        if (isfinite(cm) && cm > 0.0) {
+            const double ratio = E / cm;
+            if (ratio > best_r) { best_r = ratio; best_n = m; best_E = E; }
+        }
+        if (m < nmax) P += Cof(m);
+    }
+    // block argmax: larger ratio, then smaller n
+    for (int d = 32; d >= 1; d >>= 1) {
+        const double r2 = __shfl_xor(best_r, d, kWave);
+        const int n2 = __shfl_xor(best_n, d, kWave);
+        const double e2 = __shfl_xor(best_E, d, kWave);
+        if (r2 > best_r || (r2 == best_r && n2 < best_n)) { best_r = r2; best_n = n2; best_E = e2; }
+    }
+    __syncthreads();
+    if (lane == 0) { s_ratio[wv] = best_r; s_n[wv] = best_n; s_E[wv] = best_E; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double r = s_ratio[0], e = s_E[0];
+        int n = s_n[0];
+        for (int q = 1; q < kReduceThreads / kWave; ++q)
+            if (s_ratio[q] > r || (s_ratio[q] == r && s_n[q] < n)) { r = s_ratio[q]; n = s_n[q]; e = s_E[q]; }
+        if (n == 0x7fffffff) { n = 0; e = (double)B; }   // no usable cost entry
+        s_n[0] = n;
+        *n_chosen = n;
+        *utility = e;
+    }
+    __syncthreads();
+    return s_n[0];
+}
+
 __global__ __launch_bounds__(kReduceThreads) void budget_kernel(const float *conf, const int32_t *draft_len,
                                                                 int B, int K, int N, int32_t *lens,
                                                                 int32_t *row_off, int32_t *row_list,
-                                                                uint32_t *err) {
+                                                                uint32_t *err, const float *cost, int n_cost,
+                                                                int32_t *n_chosen, double *utility) {
     __shared__ uint64_t keys[SV_BUDGET_MAX];
     __shared__ int cnt[SV_BUDGET_MAX];
     __shared__ int scan[kReduceThreads];
@@ -396,7 +460,10 @@ __global__ __launch_bounds__(kReduceThreads) void budget_kernel(const float *con
             }
         }
     }
-    const int keep = min(N, s_total);
+    __shared__ double dscan[kReduceThreads / kWave], s_ratio[kReduceThreads / kWave], s_E[kReduceThreads / kWave];
+    __shared__ int s_n[kReduceThreads / kWave];
+    const int keep = cost ? dcut_choose(keys, s_total, B, cost, n_cost, dscan, s_ratio, s_n, s_E, n_chosen, utility)
+                          : min(N, s_total);
     for (int i = threadIdx.x; i < keep; i += kReduceThreads) {
         const int flat = (int)(keys[i] & 0xffffffffu);
         atomicAdd(&cnt[flat / K], 1);
@@ -683,7 +750,19 @@ int sv_alloc_verify_budget(const float *conf, const int32_t *draft_len, int32_t 
     if ((int64_t)B * K_max > SV_BUDGET_MAX || B > SV_BUDGET_MAX) return SV_EUNSUPPORTED;
     if (B > 0 && K_max > 0 && !conf) return SV_EINVAL;
     hipLaunchKernelGGL(budget_kernel, dim3(1), dim3(kReduceThreads), 0, (hipStream_t)stream, conf, draft_len, B,
-                       K_max, budget_N, lens, row_off, row_list, (uint32_t *)nullptr);
+                       K_max, budget_N, lens, row_off, row_list, (uint32_t *)nullptr, (const float *)nullptr, 0,
+                       (int32_t *)nullptr, (double *)nullptr);
+    return launch_status();
+}
+
+int sv_dcut_verify_budget(const float *conf, const int32_t *draft_len, int32_t B, int32_t K_max,
+                          const float *cost, int32_t n_cost, int32_t *n_chosen, double *utility, int32_t *lens,
+                          int32_t *row_off, int32_t *row_list, void *stream) {
+    if (B < 0 || K_max < 0 || n_cost < 1 || !cost || !n_chosen || !utility || !lens || !row_off) return SV_EINVAL;
+    if ((int64_t)B * K_max > SV_BUDGET_MAX || B > SV_BUDGET_MAX || n_cost > SV_BUDGET_MAX + 1) return SV_EUNSUPPORTED;
+    if (B > 0 && K_max > 0 && !conf) return SV_EINVAL;
+    hipLaunchKernelGGL(budget_kernel, dim3(1), dim3(kReduceThreads), 0, (hipStream_t)stream, conf, draft_len, B,
+                       K_max, 0, lens, row_off, row_list, (uint32_t *)nullptr, cost, n_cost, n_chosen, utility);
     return launch_status();
 }
 

@@ -167,6 +167,25 @@ int sv_alloc_verify_budget(const float *conf, const int32_t *draft_len, int32_t 
                            int32_t K_max, int32_t budget_N, int32_t *lens, int32_t *row_off,
                            int32_t *row_list, void *stream);
 
+/* D-cut budget choice [RT]: the total budget is picked from the caller's cost table, then
+ * allocated as by sv_alloc_verify_budget.  Reading (the pages give no formula): verifying
+ * the best n candidates of the budget order emits in expectation E(n) = B + (sum of their
+ * C), one correction/bonus token per request plus the expected accepted drafts.
+ *   cost [n_cost] float (device): the caller's measured cost of a step that verifies n
+ *                     positions, n = 0..n_cost-1, 1 <= n_cost <= SV_BUDGET_MAX + 1
+ *   n_chosen [1] int32 (device): the n maximising E(n) / cost[n] over n <= min(n_cost - 1,
+ *                     sum_r L_r) among entries with a finite positive cost (the smallest such
+ *                     n on ties; 0 if no entry qualifies)
+ *   utility [1] double (device): E(n_chosen)
+ *   lens, row_off, row_list: the allocation of sv_alloc_verify_budget with budget_N =
+ *                     n_chosen.
+ * E is summed in binary64 by a block scan, so on ratios equal to within ~1e-15 relative
+ * the choice may differ from a sequential sum's; any such choice is optimal to that
+ * precision.  B * K_max <= SV_BUDGET_MAX. */
+int sv_dcut_verify_budget(const float *conf, const int32_t *draft_len, int32_t B, int32_t K_max,
+                          const float *cost, int32_t n_cost, int32_t *n_chosen, double *utility,
+                          int32_t *lens, int32_t *row_off, int32_t *row_list, void *stream);
+
 /* The library's uniforms, for testing the generator: out[i] = U(seed; counters[i][0..3]). */
 int sv_uniforms(uint64_t seed, const uint64_t *counters, int32_t n, float *out, void *stream);
 

@@ -102,3 +102,20 @@ def test_verify_selected_host_validation(svlib):
     assert call(fake, nul, 2) == EINVAL            # rows without a list
     assert call(fake, nul, 0) == EWS               # zero rows is valid; then the workspace is missing
     assert call(fake, fake, 6) == EWS
+
+
+def test_dcut_host_validation(svlib):
+    EINVAL, EUNSUP = 1, 2
+    nul = None
+    fake = C.c_void_p(0x1000)
+    ok = [fake, nul, 4, 4, fake, 17, fake, fake, fake, fake, nul, nul]
+    bad_ncost = list(ok); bad_ncost[5] = 0
+    assert svlib.sv_dcut_verify_budget(*bad_ncost) == EINVAL
+    no_cost = list(ok); no_cost[4] = nul
+    assert svlib.sv_dcut_verify_budget(*no_cost) == EINVAL
+    no_out = list(ok); no_out[6] = nul
+    assert svlib.sv_dcut_verify_budget(*no_out) == EINVAL
+    big = list(ok); big[2], big[3] = 100, 100
+    assert svlib.sv_dcut_verify_budget(*big) == EUNSUP
+    long_table = list(ok); long_table[5] = 8194
+    assert svlib.sv_dcut_verify_budget(*long_table) == EUNSUP

@@ -272,6 +272,59 @@ def test_selected_verify_small_ragged_vocab(sv):
         compare_verify(out, o, tn, dn, "bf16", T, L=dl)
 
 
+def _dcut_ratios(conf, cost, draft_len=None):
+    """E(n) / cost[n] for every n, E summed in candidate order (binary64, sequential)."""
+    B, K = conf.shape
+    C = np.multiply.accumulate(conf, axis=1, dtype=np.float32)
+    L = np.full(B, K) if draft_len is None else draft_len
+    cand = [(-float(C[r, k]), r, k) for r in range(B) for k in range(L[r])]
+    cand.sort()
+    P = np.concatenate([[0.0], np.cumsum([-c for c, _, _ in cand])])
+    nmax = min(len(cost) - 1, len(cand))
+    out = {}
+    for n in range(nmax + 1):
+        if np.isfinite(cost[n]) and cost[n] > 0:
+            out[n] = (B + P[n]) / float(cost[n])
+    return out
+
+
+def test_dcut_matches_oracle(sv):
+    rng = np.random.default_rng(21)
+    cases = [(64, 16, 40.0 + 0.05 * np.arange(1025)), (64, 16, 1.0 + 0.002 * np.arange(1025) ** 1.3)]
+    for trial in range(30):
+        B, K = int(rng.integers(1, 40)), int(rng.integers(1, 40))
+        if B * K > 8192:
+            continue
+        n_cost = int(rng.integers(1, B * K + 3))
+        cost = (1.0 + np.sort(rng.random(n_cost)) * float(rng.integers(1, 5))).astype(np.float64)
+        if trial % 3 == 0:
+            cost[rng.random(n_cost) < 0.2] = [0.0, np.nan, -1.0][trial % 2]
+        cases.append((B, K, cost))
+    for i, (B, K, cost) in enumerate(cases):
+        conf = rng.beta(5, 2, size=(B, K)).astype(np.float32)
+        if i % 4 == 1:
+            conf[rng.random((B, K)) < 0.2] = 1.0   # ties in C
+        dl = rng.integers(0, K + 1, size=B).astype(np.int32) if i % 5 == 2 else None
+        cost = np.asarray(cost, np.float32)
+        _say(f"dcut case {i} B={B} K={K} n_cost={len(cost)}")
+        n_dev, u_dev, lens, off, rl = sv.sv_dcut_verify_budget(
+            torch.as_tensor(conf, device=DEV), torch.as_tensor(cost, device=DEV),
+            draft_len=None if dl is None else torch.as_tensor(dl, device=DEV))
+        torch.cuda.synchronize()
+        n_gpu, u_gpu = int(n_dev.item()), float(u_dev.item())
+        n_or, u_or, _, _, _ = svref.dcut_budget(conf, cost, draft_len=dl)
+        if n_gpu != n_or:
+            # only a tie within rounding of the two summation orders may differ
+            r = _dcut_ratios(conf, cost, dl)
+            assert n_gpu in r and abs(r[n_gpu] - r[n_or]) <= 1e-12 * abs(r[n_or]), (i, n_gpu, n_or)
+        else:
+            assert abs(u_gpu - u_or) <= 1e-12 * abs(u_or), (i, u_gpu, u_or)
+        want_lens, want_off, want_rl = svref.alloc_verify_budget(conf, n_gpu, draft_len=dl)
+        assert np.array_equal(lens.cpu().numpy(), want_lens), i
+        assert np.array_equal(off.cpu().numpy(), want_off), i
+        assert np.array_equal(rl.cpu().numpy()[: len(want_rl)], want_rl), i
+
+
 def test_e2e_small(sv):
     t, d, T = workloads.make_e2e_inputs(device=DEV, I=48, D=3)
     _say("e2e small")
