@@ -38,6 +38,7 @@ constexpr int kTeamChunk = kTeamThreads * kTeamE;   // logits of each row per me
 constexpr int kTeamSeg = 64 * kTeamE;               // one wave's contiguous range
 constexpr int kBonusSeg = 512;                      // segment of the single-row bonus draw
 constexpr int kXcds = 8;                            // accelerator complex dies of an MI355X
+constexpr int kAccWords = 8;                        // tagged words of a row's accept record
 
 enum TeamMode { kTeamStoch = 0, kTeamGreedy = 1, kTeamAlpha = 2 };
 
@@ -71,7 +72,8 @@ struct TeamArgs {
     // dir of a bonus slot: per wave range, sum 2^{z c - M_member}
     uint64_t *apart;   // [rows][S]   alpha share of each member (or the hand-over marker)
     uint64_t *dir;     // [rows][4 S] residual mass of each kTeamSeg-logit wave range
-    uint64_t *acc;     // [rows][4]   accept flag, L2t, L2d (from the member holding the token)
+    uint64_t *acc;     // [rows][kAccWords] accept flag and the two row normalisers, each as
+                       // hi, lo (t.hi, d.hi, t.lo, d.lo), from the member holding the token
     float *bonus;      // [B][2 nseg_b] scratch of the single-row bonus draw
     int64_t ld_t, ld_d;
     int32_t B, K, V, S, nseg, nseg_b;

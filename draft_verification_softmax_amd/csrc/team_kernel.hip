@@ -38,7 +38,7 @@ TeamLayout team_layout(int B, int slots, int V, size_t ws_bytes) {
     L.off_part = o;  o = al(o + sizeof(uint64_t) * 8 * (size_t)L.S * (size_t)L.rows);
     L.off_apart = o; o = al(o + sizeof(uint64_t) * (size_t)L.S * (size_t)L.rows);
     L.off_dir = o;   o = al(o + sizeof(uint64_t) * (size_t)L.nseg * (size_t)L.rows);
-    L.off_acc = o;   o = al(o + sizeof(uint64_t) * 4 * (size_t)L.rows);
+    L.off_acc = o;   o = al(o + sizeof(uint64_t) * kAccWords * (size_t)L.rows);
     L.off_bonus = o; o = al(o + sizeof(float) * 2 * (size_t)L.nseg_b * nB);
     L.off_alpha = o; o = al(o + sizeof(float) * (size_t)L.rows);
     const size_t tagged = o;
@@ -273,23 +273,61 @@ struct LaneRow {
     }
 };
 
-// sum_i min(p_i, q_i) with p = 2^{t c - L2t}, q = 2^{d c - L2d}: the same per-logit formula
-// as the inverse-CDF scan of the finalize kernel.
+// A row normaliser in base 2, log2 sum_v 2^{z_v c}, kept as an unevaluated sum hi + lo.
+// At low temperature it reaches several hundred, where one binary32 value would be off by
+// up to 2^-15 and so every probability by ~2e-5 relative; in two parts a probability is
+// 2^{fma(z, c, -hi) - lo}: the fma leaves a small argument, and lo (|lo| <= half an ulp
+// of hi) is applied after it.
+struct Norm2 {
+    float hi, lo;
+};
+
+// hi + lo = M + l exactly (Knuth's two-sum); lo = 0 when the sum is not finite.
+__device__ __forceinline__ Norm2 norm2(float M, float l) {
+    Norm2 n;
+    n.hi = M + l;
+    const float bv = n.hi - M;
+    const float e = (M - (n.hi - bv)) + (l - bv);
+    n.lo = __builtin_isfinite(n.hi) ? e : 0.f;
+    return n;
+}
+
+// log2 of the probability of logit z under the row normaliser n
+__device__ __forceinline__ float log2prob(float z, float c, Norm2 n) { return __builtin_fmaf(z, c, -n.hi) - n.lo; }
+
+// A low part this small moves a probability by at most 2^-20 ln 2 < 6.6e-7 relative; it is
+// always so when |hi| < 32 (half an ulp of hi).
+constexpr float kLoNegligible = 0x1p-20f;
+
+// sum_i min(p_i, q_i) with p = 2^{t c - Nt}, q = 2^{d c - Nd}, as
+// 2^{-Nt.lo} sum_i 2^{min(fma(t, c, -Nt.hi), fma(d, c, -Nd.hi) + Nt.lo - Nd.lo)} when `split`
+// (uniform), else with both low parts left out (each at most kLoNegligible).  The choice is
+// made per group of slots, after the group's words are refreshed, so both arms read the
+// same registers.
 template <int DTT, int DTD>
-__device__ __forceinline__ float min_sum(LaneRow<DTT> &t, LaneRow<DTD> &d, float c, float L2t, float L2d) {
+__device__ __forceinline__ float min_sum(LaneRow<DTT> &t, LaneRow<DTD> &d, float c, Norm2 nt, Norm2 nd, int split) {
+    const float dl = nt.lo - nd.lo;
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
     for (int g = 0; g < kTeamE; g += 8) {
         t.refresh8(g);
         d.refresh8(g);
+        if (split) {
 #pragma unroll
-        for (int i = g; i < g + 8; i += 2) {
-            a0 += exp2_fast(fminf(__builtin_fmaf(t.get(i), c, -L2t), __builtin_fmaf(d.get(i), c, -L2d)));
-            a1 += exp2_fast(fminf(__builtin_fmaf(t.get(i + 1), c, -L2t), __builtin_fmaf(d.get(i + 1), c, -L2d)));
+            for (int i = g; i < g + 8; i += 2) {
+                a0 += exp2_fast(fminf(__builtin_fmaf(t.get(i), c, -nt.hi), __builtin_fmaf(d.get(i), c, -nd.hi) + dl));
+                a1 += exp2_fast(fminf(__builtin_fmaf(t.get(i + 1), c, -nt.hi), __builtin_fmaf(d.get(i + 1), c, -nd.hi) + dl));
+            }
+        } else {
+#pragma unroll
+            for (int i = g; i < g + 8; i += 2) {
+                a0 += exp2_fast(fminf(__builtin_fmaf(t.get(i), c, -nt.hi), __builtin_fmaf(d.get(i), c, -nd.hi)));
+                a1 += exp2_fast(fminf(__builtin_fmaf(t.get(i + 1), c, -nt.hi), __builtin_fmaf(d.get(i + 1), c, -nd.hi)));
+            }
         }
         sched_fence();
     }
-    return a0 + a1;
+    return split ? (a0 + a1) * exp2_fast(-nt.lo) : a0 + a1;
 }
 
 // Pass 1 of a lane: base-2 log-sum-exp state (M = max * c, s = sum 2^{x c - M}) per row.
@@ -310,9 +348,12 @@ __device__ __forceinline__ ThreadStats pass1(LaneRow<DTT> &t, LaneRow<DTD> &d, f
 // Pass 2 of a lane: its share of alpha and of the residual mass sum max(p - q, 0).
 template <int DTT, int DTD>
 __device__ __forceinline__ void pass2(LaneRow<DTT> &t, LaneRow<DTD> &d, const ThreadStats &s, float c,
-                                      float L2t, float L2d, float &alpha, float &resid) {
-    alpha = min_sum(t, d, c, L2t, L2d);
-    const float P = (s.Mt == neg_inf()) ? 0.f : s.st * exp2_fast(s.Mt - L2t);   // this lane's target mass
+                                      Norm2 nt, Norm2 nd, float &alpha, float &resid) {
+    // the low parts matter only at large |hi| (low temperatures); the test is uniform
+    const int split = __builtin_amdgcn_readfirstlane(
+        (__builtin_fabsf(nt.lo) > kLoNegligible || __builtin_fabsf(nd.lo) > kLoNegligible) ? 1 : 0);
+    alpha = min_sum(t, d, c, nt, nd, split);
+    const float P = (s.Mt == neg_inf()) ? 0.f : s.st * exp2_fast((s.Mt - nt.hi) - nt.lo);   // this lane's target mass
     resid = P - alpha;
 }
 
@@ -348,12 +389,12 @@ __device__ int draw_from_row(const void *row, int V, float c, float u, float *se
     }
     float Md = neg_inf(), sd = 0.f;
     block_ms2(M, s, Md, sd, red);
-    const float L2 = M + log2f(s);
+    const Norm2 nb = norm2(M, log2f(s));
     __threadfence_block();
     __syncthreads();
     for (int q = threadIdx.x; q < nseg; q += kTeamThreads) {
         const float sM = seg[q], ss = seg[nseg + q];
-        seg[q] = (sM == neg_inf()) ? 0.f : ss * exp2_fast(sM - L2);
+        seg[q] = (sM == neg_inf()) ? 0.f : ss * exp2_fast((sM - nb.hi) - nb.lo);
     }
     __threadfence_block();
     __syncthreads();
@@ -372,7 +413,7 @@ __device__ int draw_from_row(const void *row, int V, float c, float u, float *se
             const int e0 = sidx * kBonusSeg;
             const int n = min(kBonusSeg, V - e0);
             double ex2;
-            const int k = wave_find([&](int q) { return exp2_fast(__builtin_fmaf(load1<DT>(row, e0 + q), c, -L2)); }, n,
+            const int k = wave_find([&](int q) { return exp2_fast(log2prob(load1<DT>(row, e0 + q), c, nb)); }, n,
                                     t - ex, &ex2);
             tok = k < 0 ? e0 : e0 + k;
         }
@@ -403,7 +444,7 @@ __device__ int row_argmax(const void *row, int V, TeamRed &red) {
 // The total R of the range masses is summed in binary64 in range order and the target is
 // u * R; -1 when every mass is zero.
 template <int DTT, int DTD, bool RESID>
-__device__ int draw_ranges(const void *trow, const void *drow, int V, float c, float L2t, float L2d,
+__device__ int draw_ranges(const void *trow, const void *drow, int V, float c, Norm2 nt, Norm2 nd,
                            const float *dirv, int nseg, float u, TeamRed &red) {
     __shared__ int s_seg;
     __shared__ double s_ex;
@@ -453,9 +494,9 @@ __device__ int draw_ranges(const void *trow, const void *drow, int V, float c, f
         if constexpr (RESID) load8<DTD>(drow, e0 + e8, vend, zd);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float p = exp2_fast(__builtin_fmaf(zt[e], c, -L2t));
+            const float p = exp2_fast(log2prob(zt[e], c, nt));
             if constexpr (RESID) {
-                const float q = exp2_fast(__builtin_fmaf(zd[e], c, -L2d));
+                const float q = exp2_fast(log2prob(zd[e], c, nd));
                 wt[e8 + e] = p - fminf(p, q);
             } else {
                 wt[e8 + e] = p;
@@ -508,15 +549,31 @@ __device__ int draw_ranges(const void *trow, const void *drow, int V, float c, f
 // Row normalisers (base 2) from the S member partials, in member order.  The stream
 // kernel and the finalize kernel both call this on the same payloads, so they agree bit
 // for bit.
-__device__ __forceinline__ void team_totals(const uint32_t *pay, int S, float &L2t, float &L2d) {
+__device__ __forceinline__ void team_totals(const uint32_t *pay, int S, Norm2 &nt, Norm2 &nd) {
     float Tt = neg_inf(), Ts = 0.f, Dt = neg_inf(), Ds = 0.f;
 #pragma unroll 1
     for (int q = 0; q < S; ++q) {   // not unrolled: it runs beside a chunk held in registers
         ms_merge(Tt, Ts, __uint_as_float(pay[q]), __uint_as_float(pay[S + q]));
         ms_merge(Dt, Ds, __uint_as_float(pay[2 * S + q]), __uint_as_float(pay[3 * S + q]));
     }
-    L2t = Tt + log2f(Ts);
-    L2d = Dt + log2f(Ds);
+    nt = norm2(Tt, log2f(Ts));
+    nd = norm2(Dt, log2f(Ds));
+}
+
+// Row normalisers in LDS words 1..4 of a row's accept record (the layout the stream
+// kernel publishes: flag, t.hi, d.hi, t.lo, d.lo).
+__device__ __forceinline__ void put_norms(uint32_t *w, Norm2 nt, Norm2 nd) {
+    w[1] = __float_as_uint(nt.hi); w[2] = __float_as_uint(nd.hi);
+    w[3] = __float_as_uint(nt.lo); w[4] = __float_as_uint(nd.lo);
+}
+__device__ __forceinline__ void get_norms(const uint32_t *w, Norm2 &nt, Norm2 &nd) {
+    nt = Norm2{__uint_as_float(w[1]), __uint_as_float(w[3])};
+    nd = Norm2{__uint_as_float(w[2]), __uint_as_float(w[4])};
+}
+// natural log-sum-exp of z / T from the base-2 normaliser
+__device__ __forceinline__ float ln_of(Norm2 n) {
+    constexpr float kLn2 = 0.69314718055994531f;
+    return __builtin_fmaf(n.hi, kLn2, n.lo * kLn2);
 }
 
 __device__ __forceinline__ int row_limit(const TeamArgs &a, int r) {
@@ -530,10 +587,10 @@ __device__ __forceinline__ const void *row_ptr(const void *base, int64_t row, in
 }
 
 // Accept iff u * q(x) < p(x), i.e. u < 2^{log2 p(x) - log2 q(x)}.
-__device__ __forceinline__ int accept_test(float zt, float zd, float c, float L2t, float L2d, uint64_t seed, int r,
+__device__ __forceinline__ int accept_test(float zt, float zd, float c, Norm2 nt, Norm2 nd, uint64_t seed, int r,
                                            int k, uint64_t step) {
-    const float lpt = __builtin_fmaf(zt, c, -L2t);
-    const float lpd = __builtin_fmaf(zd, c, -L2d);
+    const float lpt = log2prob(zt, c, nt);
+    const float lpd = log2prob(zd, c, nd);
     const float u = uniform24(seed, (uint64_t)r, (uint64_t)k, kPurposeAccept, step);
     return u < exp2f(lpt - lpd) ? 1 : 0;
 }
@@ -564,7 +621,7 @@ __device__ __forceinline__ void publish_partials(uint64_t *part, int S, int j, c
 template <int DTT, int DTD, int MODE>
 __device__ __forceinline__ void finish_row(const TeamArgs &a, int64_t row, int j, int r, int k, LaneRow<DTT> &tr,
                                            LaneRow<DTD> &dr, const ThreadStats &ts, bool owner, float zx_t,
-                                           float zx_d, uint32_t tag, TeamRed &red, uint32_t *pay, float *s_tot,
+                                           float zx_d, uint32_t tag, TeamRed &red, uint32_t *pay, Norm2 *s_tot,
                                            int *s_ok) {
     const int S = a.S;
     const float c = a.c;
@@ -582,9 +639,9 @@ __device__ __forceinline__ void finish_row(const TeamArgs &a, int64_t row, int j
         if (threadIdx.x == 0) put(a.apart + row * S + j, kGaveUp, tag);   // the finalize takes over
         return;
     }
-    const float L2t = s_tot[0], L2d = s_tot[1];
+    const Norm2 nt = s_tot[0], nd = s_tot[1];
     float al, rs;
-    pass2(tr, dr, ts, c, L2t, L2d, al, rs);
+    pass2(tr, dr, ts, c, nt, nd, al, rs);
     if constexpr (MODE == kTeamStoch) {
         rs = fmaxf(wave_sum(rs), 0.f);
         if (lane_id() == 0) putf(a.dir + row * a.nseg + j * kTeamWaves + w, rs, tag);
@@ -593,9 +650,12 @@ __device__ __forceinline__ void finish_row(const TeamArgs &a, int64_t row, int j
     if (threadIdx.x == 0) {
         putf(a.apart + row * S + j, al, tag);
         if (MODE == kTeamStoch && owner) {   // accept test and the row normalisers of this row
-            put(a.acc + 4 * row, (uint32_t)accept_test(zx_t, zx_d, c, L2t, L2d, a.seed, r, k, a.step), tag);
-            putf(a.acc + 4 * row + 1, L2t, tag);
-            putf(a.acc + 4 * row + 2, L2d, tag);
+            uint64_t *ac = a.acc + kAccWords * row;
+            put(ac, (uint32_t)accept_test(zx_t, zx_d, c, nt, nd, a.seed, r, k, a.step), tag);
+            putf(ac + 1, nt.hi, tag);
+            putf(ac + 2, nd.hi, tag);
+            putf(ac + 3, nt.lo, tag);
+            putf(ac + 4, nd.lo, tag);
         }
     }
 }
@@ -615,7 +675,7 @@ __device__ __forceinline__ void token_logits(const void *trow, const void *drow,
 // the row.
 template <int DTT, int DTD, int MODE, bool AMAX, bool FULL>
 __device__ __forceinline__ void row_member(const TeamArgs &a, int j, int64_t row, int r, int k, TeamRed &red,
-                                           uint32_t *pay, float *s_tot, int *s_ok) {
+                                           uint32_t *pay, Norm2 *s_tot, int *s_ok) {
     const int S = a.S;
     const int K = a.K;
     const int V = a.V;
@@ -740,7 +800,7 @@ template <int DTT, int DTD, int MODE, bool AMAX>
 __global__ __launch_bounds__(kTeamThreads) __attribute__((amdgpu_waves_per_eu(5))) void stream_kernel(TeamArgs a) {
     __shared__ TeamRed red;
     __shared__ uint32_t pay[4 * 128];
-    __shared__ float s_tot[2];
+    __shared__ Norm2 s_tot[2];
     __shared__ int s_ok;
 
     // The S members of a team are consecutive workgroups: round-robin dispatch spreads them
@@ -785,7 +845,7 @@ namespace {
 // Recompute member j's share of a row (alpha, and residual directory entries) from HBM;
 // used only when that member handed its share over.  Whole workgroup.
 template <int DTT, int DTD>
-__device__ float recompute_share(const TeamArgs &a, const void *trow, const void *drow, int j, float L2t, float L2d,
+__device__ float recompute_share(const TeamArgs &a, const void *trow, const void *drow, int j, Norm2 nt, Norm2 nd,
                                  int64_t row, uint32_t tag, TeamRed &red, bool publish_dir) {
     LaneRow<DTT> tr;
     LaneRow<DTD> dr;
@@ -795,7 +855,7 @@ __device__ float recompute_share(const TeamArgs &a, const void *trow, const void
     dr.template load<false>(drow, base, a.V);
     const ThreadStats s = pass1(tr, dr, tr.max(), dr.max(), a.c);
     float al, rs;
-    pass2(tr, dr, s, a.c, L2t, L2d, al, rs);
+    pass2(tr, dr, s, a.c, nt, nd, al, rs);
     rs = fmaxf(wave_sum(rs), 0.f);
     if (publish_dir && lane_id() == 0) putf(a.dir + row * a.nseg + j * kTeamWaves + w, rs, tag);
     return block_sumf(al, red);
@@ -840,9 +900,9 @@ __global__ __launch_bounds__(kTeamThreads) void finalize_kernel(TeamArgs a) {
     __shared__ uint32_t pay[8 * 128 + 512 + 8];
     __shared__ float s_mass[512 + 8];
     __shared__ int s_tau, s_tok, s_flags;
-    __shared__ float s_L2[2];
+    __shared__ Norm2 s_n[2];   // normalisers of the row the draw uses (target, drafter)
     __shared__ int s_at;
-    __shared__ float s_rt[kTeamThreads], s_rd[kTeamThreads];
+    __shared__ Norm2 s_rt[kTeamThreads], s_rd[kTeamThreads];
     __shared__ int s_ra[kTeamThreads];
     __shared__ float s_u[kTeamThreads];   // correction/bonus uniform for each candidate tau
 
@@ -864,14 +924,14 @@ __global__ __launch_bounds__(kTeamThreads) void finalize_kernel(TeamArgs a) {
     auto tau_u = [&](int t) {
         return pre_u ? s_u[t] : uniform24(a.seed, (uint64_t)r, (uint64_t)t, kPurposeCorrection, a.step);
     };
-    if (threadIdx.x == 0) { s_tau = L; s_at = 0; s_L2[0] = s_L2[1] = 0.f; }
+    if (threadIdx.x == 0) { s_tau = L; s_at = 0; s_n[0] = s_n[1] = Norm2{0.f, 0.f}; }
     if (pre_u && L == 0 && threadIdx.x <= K)
         s_u[threadIdx.x] = uniform24(a.seed, (uint64_t)r, (uint64_t)threadIdx.x, kPurposeCorrection, a.step);
     __syncthreads();
 
-    // rows are staged in batches: acc [nb][4] | shares [nb][S] | directory [nb][4S] |
+    // rows are staged in batches: acc [nb][kAccWords] | shares [nb][S] | directory [nb][4S] |
     // argmax words [nb][4S], all in one gather
-    const int nA = (MODE == kTeamStoch) ? 4 : 0;
+    const int nA = (MODE == kTeamStoch) ? kAccWords : 0;
     const int nB = (MODE != kTeamGreedy) ? S : 0;
     const int nC = (MODE == kTeamStoch) ? nseg : 0;
     const int nD = want_amax ? 4 * S : 0;
@@ -879,7 +939,7 @@ __global__ __launch_bounds__(kTeamThreads) void finalize_kernel(TeamArgs a) {
     const int batch = max(1, min(kTeamThreads, kFinWords / max(per_row, 1)));
     for (int k0 = 0; k0 < L; k0 += batch) {
         const int nb = min(batch, L - k0);
-        uint32_t *sx = stage;                // [nb][4]
+        uint32_t *sx = stage;                // [nb][kAccWords]
         uint32_t *sa = sx + nb * nA;         // [nb][S]
         uint32_t *sd = sa + nb * nB;         // [nb][4S]
         uint32_t *sm = sd + nb * nC;         // [nb][4S]
@@ -897,7 +957,7 @@ __global__ __launch_bounds__(kTeamThreads) void finalize_kernel(TeamArgs a) {
                     miss[u] = 0xffffffffu;
                     if (i < n) {
                         if (i < nb * nA) {
-                            src = a.acc + 4 * (row0 + k0) + i;
+                            src = a.acc + kAccWords * (row0 + k0) + i;
                         } else if ((i -= nb * nA) < nb * nB) {
                             src = a.apart + (row0 + k0) * S + i;
                             miss[u] = kGaveUp;
@@ -929,7 +989,7 @@ __global__ __launch_bounds__(kTeamThreads) void finalize_kernel(TeamArgs a) {
         {
             int f = 0;
             if (MODE == kTeamStoch)
-                for (int q = threadIdx.x; q < nb; q += kTeamThreads) f |= (sx[q * 4 + 1] == 0xffffffffu) ? 1 : 0;
+                for (int q = threadIdx.x; q < nb; q += kTeamThreads) f |= (sx[q * kAccWords + 1] == 0xffffffffu) ? 1 : 0;
             if (MODE != kTeamGreedy)
                 for (int q = threadIdx.x; q < nb * S; q += kTeamThreads) f |= (sa[q] == kGaveUp) ? 2 : 0;
             if (f) atomicOr(&s_flags, f);
@@ -940,15 +1000,14 @@ __global__ __launch_bounds__(kTeamThreads) void finalize_kernel(TeamArgs a) {
         // token is out of range): reduce the partials here
         if (MODE == kTeamStoch && (flags & 1)) {
             for (int q = 0; q < nb; ++q) {
-                if (sx[q * 4 + 1] != 0xffffffffu) continue;
+                if (sx[q * kAccWords + 1] != 0xffffffffu) continue;
                 const int missing = load_tagged(a.part + (row0 + k0 + q) * 8 * S, 4 * S, tag, pay, 0u);
                 if (missing && threadIdx.x == 0) atomicOr(a.err, SV_DEVERR_DRAFT_LEN);   // the row was never streamed
                 __syncthreads();
                 if (threadIdx.x == 0) {
-                    float L2t, L2d;
-                    team_totals(pay, S, L2t, L2d);
-                    sx[q * 4 + 1] = __float_as_uint(L2t);
-                    sx[q * 4 + 2] = __float_as_uint(L2d);
+                    Norm2 nt, nd;
+                    team_totals(pay, S, nt, nd);
+                    put_norms(sx + q * kAccWords, nt, nd);
                 }
                 __syncthreads();
             }
@@ -958,19 +1017,18 @@ __global__ __launch_bounds__(kTeamThreads) void finalize_kernel(TeamArgs a) {
             for (int q = 0; q < nb; ++q) {
                 for (int m = 0; m < S; ++m) {
                     if (sa[q * S + m] != kGaveUp) continue;
-                    float L2t, L2d;
+                    Norm2 nt, nd;
                     if (MODE == kTeamStoch) {
-                        L2t = __uint_as_float(sx[q * 4 + 1]);
-                        L2d = __uint_as_float(sx[q * 4 + 2]);
+                        get_norms(sx + q * kAccWords, nt, nd);
                     } else {
                         load_tagged(a.part + (row0 + k0 + q) * 8 * S, 4 * S, tag, pay, 0u);
                         __syncthreads();
-                        team_totals(pay, S, L2t, L2d);
+                        team_totals(pay, S, nt, nd);
                     }
                     const int k = k0 + q;
                     const void *trow = row_ptr<DTT>(a.target, (int64_t)r * a.trows + k, a.ld_t);
                     const void *drow = row_ptr<DTD>(a.draft, (int64_t)r * K + k, a.ld_d);
-                    const float sh = recompute_share<DTT, DTD>(a, trow, drow, m, L2t, L2d, row0 + k, tag, red,
+                    const float sh = recompute_share<DTT, DTD>(a, trow, drow, m, nt, nd, row0 + k, tag, red,
                                                                MODE == kTeamStoch);
                     __syncthreads();
                     if (threadIdx.x == 0) sa[q * S + m] = __float_as_uint(sh);
@@ -1003,7 +1061,8 @@ __global__ __launch_bounds__(kTeamThreads) void finalize_kernel(TeamArgs a) {
             const int x = x_mine;
             const bool okx = x >= 0 && x < a.V;
             if (!okx) atomicOr(a.err, SV_DEVERR_TOKEN);
-            float alpha, L2t = 0.f, L2d = 0.f;
+            float alpha;
+            Norm2 nt{0.f, 0.f}, nd{0.f, 0.f};
             int acc;
             if constexpr (MODE == kTeamGreedy) {
                 alpha = (at == ad) ? 1.f : 0.f;
@@ -1012,27 +1071,26 @@ __global__ __launch_bounds__(kTeamThreads) void finalize_kernel(TeamArgs a) {
                 double sum = 0.0;
                 for (int m = 0; m < S; ++m) sum += (double)__uint_as_float(sa[q * S + m]);
                 alpha = (float)sum;
-                L2t = __uint_as_float(sx[q * 4 + 1]);
-                L2d = __uint_as_float(sx[q * 4 + 2]);
-                if (sx[q * 4] != 0xffffffffu) {
-                    acc = (int)sx[q * 4];
+                get_norms(sx + q * kAccWords, nt, nd);
+                if (sx[q * kAccWords] != 0xffffffffu) {
+                    acc = (int)sx[q * kAccWords];
                 } else if (okx) {   // the owner member handed over: run the test here
                     const float zt = load1<DTT>(row_ptr<DTT>(a.target, (int64_t)r * a.trows + k, a.ld_t), x);
                     const float zd = load1<DTD>(row_ptr<DTD>(a.draft, (int64_t)r * K + k, a.ld_d), x);
-                    acc = accept_test(zt, zd, c, L2t, L2d, a.seed, r, k, a.step);
+                    acc = accept_test(zt, zd, c, nt, nd, a.seed, r, k, a.step);
                 } else {
                     acc = 0;
                 }
             }
             a.alpha[i] = alpha;
             a.accept[i] = (uint8_t)acc;
-            if (a.lse_t) a.lse_t[i] = (MODE == kTeamStoch) ? L2t * 0.69314718055994531f : 0.f;
-            if (a.lse_d) a.lse_d[i] = (MODE == kTeamStoch) ? L2d * 0.69314718055994531f : 0.f;
+            if (a.lse_t) a.lse_t[i] = (MODE == kTeamStoch) ? ln_of(nt) : 0.f;
+            if (a.lse_d) a.lse_d[i] = (MODE == kTeamStoch) ? ln_of(nd) : 0.f;
             if (a.amax_t) a.amax_t[i] = want_amax ? at : -1;
             if (a.amax_d) a.amax_d[i] = want_amax ? ad : -1;
             if (!acc) atomicMin(&s_tau, k);
-            s_rt[q] = L2t;
-            s_rd[q] = L2d;
+            s_rt[q] = nt;
+            s_rd[q] = nd;
             s_ra[q] = at;
         }
         __syncthreads();
@@ -1040,8 +1098,8 @@ __global__ __launch_bounds__(kTeamThreads) void finalize_kernel(TeamArgs a) {
         if (tau >= k0 && tau < k0 + nb) {
             // keep what the draw after the rejection at tau needs
             if (threadIdx.x == 0) {
-                s_L2[0] = s_rt[tau - k0];
-                s_L2[1] = s_rd[tau - k0];
+                s_n[0] = s_rt[tau - k0];
+                s_n[1] = s_rd[tau - k0];
                 s_at = s_ra[tau - k0];
             }
             if (MODE == kTeamStoch)
@@ -1086,16 +1144,16 @@ __global__ __launch_bounds__(kTeamThreads) void finalize_kernel(TeamArgs a) {
                     ms_merge(M, sm, __uint_as_float(pay[m]), sj);
                 }
                 wave_ms(M, sm);
-                if (threadIdx.x == 0) s_L2[0] = M + log2f(sm);
+                if (threadIdx.x == 0) s_n[0] = norm2(M, log2f(sm));
             }
             __syncthreads();
-            const float L2 = s_L2[0];
+            const Norm2 nb = s_n[0];
             for (int q = threadIdx.x; q < nseg; q += kTeamThreads) {
                 const float Mq = __uint_as_float(pay[q / kTeamWaves]);
-                s_mass[q] = (Mq == neg_inf()) ? 0.f : __uint_as_float(pay[S + q]) * exp2_fast(Mq - L2);
+                s_mass[q] = (Mq == neg_inf()) ? 0.f : __uint_as_float(pay[S + q]) * exp2_fast((Mq - nb.hi) - nb.lo);
             }
             __syncthreads();
-            tok = draw_ranges<DTT, DTD, false>(trow, nullptr, a.V, c, L2, 0.f, s_mass, nseg, tau_u(tau), red);
+            tok = draw_ranges<DTT, DTD, false>(trow, nullptr, a.V, c, nb, Norm2{0.f, 0.f}, s_mass, nseg, tau_u(tau), red);
             if (tok < 0) tok = 0;
         }
     } else if constexpr (MODE == kTeamGreedy) {
@@ -1106,7 +1164,7 @@ __global__ __launch_bounds__(kTeamThreads) void finalize_kernel(TeamArgs a) {
         bool done = false;
         {
             const void *drow = row_ptr<DTD>(a.draft, (int64_t)r * K + tau, a.ld_d);
-            const int t = draw_ranges<DTT, DTD, true>(trow, drow, a.V, c, s_L2[0], s_L2[1], s_mass, nseg, u, red);
+            const int t = draw_ranges<DTT, DTD, true>(trow, drow, a.V, c, s_n[0], s_n[1], s_mass, nseg, u, red);
             if (t >= 0) { tok = t; done = true; }
         }
         __syncthreads();
@@ -1171,13 +1229,13 @@ __global__ __launch_bounds__(kTeamThreads) void e2e_alpha_kernel(TeamArgs a) {
         const int64_t rr = (int64_t)blockIdx.x * kTeamThreads + s_list[q];
         load_tagged(a.part + rr * 8 * S, 4 * S, tag, pay, 0u);
         __syncthreads();
-        float L2t, L2d;
-        team_totals(pay, S, L2t, L2d);
+        Norm2 nt, nd;
+        team_totals(pay, S, nt, nd);
         const int ri = (int)(rr / a.K), ki = (int)(rr % a.K);
         const void *trow = row_ptr<DTT>(a.target, (int64_t)ri * a.trows + ki, a.ld_t);
         const void *drow = row_ptr<DTD>(a.draft, rr, a.ld_d);
         double t = 0.0;
-        for (int m = 0; m < S; ++m) t += (double)recompute_share<DTT, DTD>(a, trow, drow, m, L2t, L2d, rr, tag, red, false);
+        for (int m = 0; m < S; ++m) t += (double)recompute_share<DTT, DTD>(a, trow, drow, m, nt, nd, rr, tag, red, false);
         if (threadIdx.x == 0) a.alpha[rr] = (float)t;
         __syncthreads();
     }

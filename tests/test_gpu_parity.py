@@ -408,3 +408,109 @@ def test_all_accepted_bonus_token(sv, T):
     dl = np.array([16, 0, 5, 1, 16, 9], np.int32)
     g2, o2, rep2 = _run_pair(sv, w, T, draft_len=dl)
     assert (o2["accept_len"] == dl).all()
+
+
+# ---- edge cases ----------------------------------------------------------------------
+
+def _custom(t, d, toks, T, name, seed=13):
+    return workloads.VerifyInputs(t.contiguous(), d.contiguous(), toks.to(torch.int32).contiguous(), T, seed, name)
+
+
+@pytest.mark.parametrize("T", [0.9, 0.0])
+def test_no_drafts_only_bonus(sv, T):
+    """K_max = 0: nothing to verify, every request emits its bonus token from target row 0."""
+    g = torch.Generator(device=DEV).manual_seed(31)
+    B, V = 5, 3000
+    t = (2.0 * torch.randn((B, 1, V), generator=g, device=DEV)).to(torch.bfloat16)
+    d = torch.empty((B, 0, V), dtype=torch.bfloat16, device=DEV)
+    toks = torch.empty((B, 0), dtype=torch.int32, device=DEV)
+    _, o, _ = _run_pair(sv, _custom(t, d, toks, T, "K=0"), T)
+    assert (o["accept_len"] == 0).all()
+
+
+@pytest.mark.parametrize("V", [1, 7, 8, 4095, 4097])
+def test_tiny_and_boundary_vocabularies(sv, V):
+    """A single token, fewer logits than one 8-wide load, and sizes around a wave range."""
+    g = torch.Generator(device=DEV).manual_seed(V)
+    B, K = 3, 4
+    ld = (V + 7) // 8 * 8
+    tt = torch.full((B, K + 1, ld), float("nan"), device=DEV, dtype=torch.float32)
+    dd = torch.full((B, K, ld), float("nan"), device=DEV, dtype=torch.float32)
+    tt[..., :V] = 1.5 * torch.randn((B, K + 1, V), generator=g, device=DEV)
+    dd[..., :V] = tt[:, :K, :V] + 0.8 * torch.randn((B, K, V), generator=g, device=DEV)
+    toks = torch.randint(0, V, (B, K), generator=g, device=DEV, dtype=torch.int32)
+    for T in (1.0, 0.0):
+        _say(f"vocab V={V} T={T}")
+        out = _np(sv.sv_verify_batch(tt[..., :V], dd[..., :V], toks, T, seed=2, want_amax=True))
+        tn, dn = workloads.to_oracle(tt[..., :V].contiguous()), workloads.to_oracle(dd[..., :V].contiguous())
+        o = svref.verify_batch(tn, dn, toks.cpu().numpy(), T, "f32", seed=2, diagnostics=True)
+        compare_verify(out, o, tn, dn, "f32", T)
+        if V == 1:
+            assert (o["accept_len"] == K).all() and np.allclose(o["alpha"], 1.0)
+
+
+def test_largest_vocabulary(sv):
+    """V = SV_V_MAX (2^20): 64 members per row."""
+    g = torch.Generator(device=DEV).manual_seed(77)
+    B, K, V = 2, 2, 1 << 20
+    t = (3.0 * torch.randn((B, K + 1, V), generator=g, device=DEV)).to(torch.bfloat16)
+    d = (t[:, :K].float() + torch.randn((B, K, V), generator=g, device=DEV)).to(torch.bfloat16)
+    toks = torch.argmax(d.float(), -1).to(torch.int32)
+    toks[:, 1] = torch.randint(0, V, (B,), generator=g, device=DEV, dtype=torch.int32)
+    for T in (0.9, 0.0):
+        _run_pair(sv, _custom(t, d, toks, T, "V=2^20"), T)
+
+
+def test_masked_logits(sv):
+    """-inf logits (masked vocabulary): p or q is exactly 0 there; drafted tokens inside the
+    target's mask are always rejected, and no emitted token is a masked one."""
+    g = torch.Generator(device=DEV).manual_seed(5)
+    B, K, V = 4, 5, 20000
+    t = 2.0 * torch.randn((B, K + 1, V), generator=g, device=DEV)
+    d = t[:, :K] + torch.randn((B, K, V), generator=g, device=DEV)
+    t[..., 5000:9000] = float("-inf")
+    d[..., 8000:12000] = float("-inf")
+    t[:, :, 15000] = float("-inf")
+    t, d = t.to(torch.bfloat16), d.to(torch.bfloat16)
+    toks = torch.randint(0, V, (B, K), generator=g, device=DEV, dtype=torch.int32)
+    toks[:, 0] = 6000            # masked in the target only: p = 0 -> reject
+    toks[:, 2] = 8500            # masked in both
+    for T in (0.9, 0.0):
+        gg, o, _ = _run_pair(sv, _custom(t, d, toks, T, "masked"), T)
+        emitted = [gg["out_tokens"][r, gg["accept_len"][r]] for r in range(B)]
+        assert all(not (5000 <= x < 9000) and x != 15000 for x in emitted)
+        if T > 0:
+            assert (gg["accept"][:, 0] == 0).all()
+
+
+@pytest.mark.parametrize("T", [0.005, 0.02, 25.0])
+def test_extreme_temperatures(sv, T):
+    """Very low temperatures (base-2 normalisers of several hundred to a few thousand, past
+    what one binary32 value holds to 1e-5, and sums far from the provisional reference: the
+    exact-maximum fallback) and a very high one (nearly uniform rows)."""
+    v = _move(workloads.make_verify_inputs("mtp", device="cpu", T=T, B=4, K=3, V=50000))
+    _run_pair(sv, v, T)
+
+
+def test_argmax_ties_lowest_index(sv):
+    """Greedy: equal maxima in a row resolve to the lowest index on both sides."""
+    g = torch.Generator(device=DEV).manual_seed(3)
+    B, K, V = 3, 4, 40000
+    t = torch.randn((B, K + 1, V), generator=g, device=DEV)
+    d = t[:, :K].clone()
+    for r in range(B):
+        for k in range(K + 1):
+            t[r, k, [777 + 5000 * k, 39999, 20000]] = 9.0      # three-way tie
+        for k in range(K):
+            d[r, k, [300, 31000]] = 9.0
+    t, d = t.to(torch.bfloat16), d.to(torch.bfloat16)
+    toks = torch.full((B, K), 777, dtype=torch.int32, device=DEV)
+    gg, o, _ = _run_pair(sv, _custom(t, d, toks, 0.0, "ties"), 0.0)
+    assert (gg["amax_t"][:, 0] == 777).all() and (gg["amax_d"] == 300).all()
+
+
+def test_many_requests_short_drafts(sv):
+    """B = 300 requests of one draft each (grid mapping over many requests)."""
+    v = _move(workloads.make_verify_inputs("mtp", device="cpu", T=0.9, B=300, K=1, V=5000))
+    for T in (0.9, 0.0):
+        _run_pair(sv, v, T)
