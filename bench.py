@@ -261,8 +261,8 @@ def bench_e2e(args, sv, workloads, torch):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--mode", choices=["stoch", "greedy"], default="stoch")
     ap.add_argument("--workload", choices=["dfly", "mtp", "budget", "e2e"], default="dfly",
                     help="dfly (default: the headline line), mtp, budget (allocation + ragged verify) or e2e")
