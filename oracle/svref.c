@@ -367,6 +367,77 @@ int svref_tv_e2e_loss(const svref_params *p, const void *target, const void *dra
     return 0;
 }
 
+/* Gradient of L_e2e with respect to the draft logits: what the second training stage
+ * descends when it switches to the end-to-end TV objective.  The pages give the loss and
+ * the two-stage schedule [AngelSpec tutorial, section "From KL to an end-to-end TV loss",
+ * L_e2e equation and the paragraph after it] but not the derivative, so it is written out
+ * here by the chain rule, in the plain order of the definition:
+ *   dL/dalpha_{i,k} = -(1/(|I| D)) sum_{m=k}^{D-1} prod_{j<=m, j!=k} alpha_{i,j}
+ *   dalpha_{i,k}/dz^d_v = (1/T) q_v ([q_v < p_v] - sum_{w: q_w < p_w} q_w)
+ * since alpha = sum_w min(p_w, q_w) moves with q_w at slope [q_w < p_w] (at a tie q_w = p_w
+ * the one-sided slope 0 is taken) and dq_w/dz^d_v = (1/T) q_w ([w = v] - q_v).  The
+ * products over j != k are formed directly, never by dividing by alpha_{i,k}. */
+int svref_tv_e2e_backward(const svref_params *p, const void *target, const void *draft, double grad_loss,
+                          double *grad, double *alpha, double *loss, double *log_ratio) {
+    if (check_params(p) || !(p->temperature > 0.0) || p->B <= 0 || p->K_max <= 0 || !target ||
+        !draft || !grad)
+        return 1;
+    const int32_t I = p->B, D = p->K_max, V = p->V;
+    const double T = p->temperature;
+    const size_t et = p->dtype_t == SVREF_F32 ? 4 : 2, ed = p->dtype_d == SVREF_F32 ? 4 : 2;
+    double *a = alpha ? alpha : (double *)malloc(sizeof(double) * (size_t)I * D);
+    double *pp = (double *)malloc(sizeof(double) * (size_t)V);
+    double *qq = (double *)malloc(sizeof(double) * (size_t)V);
+    if (!a || !pp || !qq) {
+        if (!alpha) free(a);
+        free(pp);
+        free(qq);
+        return 1;
+    }
+    /* the overlaps of every row first: each row's weight needs those of its sequence */
+    for (int32_t i = 0; i < I; ++i)
+        for (int32_t k = 0; k < D; ++k) {
+            const size_t row = (size_t)i * D + k;
+            a[row] = svref_alpha((const char *)target + row * (size_t)p->ld_t * et, p->dtype_t,
+                                 (const char *)draft + row * (size_t)p->ld_d * ed, p->dtype_d, V, T);
+        }
+    if (loss) *loss = svref_e2e_from_alpha(a, I, D);
+    for (int32_t i = 0; i < I; ++i)
+        for (int32_t k = 0; k < D; ++k) {
+            const size_t row = (size_t)i * D + k;
+            double w = 0.0; /* sum_{m>=k} prod_{j<=m, j!=k} alpha_{i,j} */
+            for (int32_t m = k; m < D; ++m) {
+                double prod = 1.0;
+                for (int32_t j = 0; j <= m; ++j)
+                    if (j != k) prod *= a[(size_t)i * D + j];
+                w += prod;
+            }
+            const double dL_dalpha = -w / ((double)I * (double)D);
+            const void *trow = (const char *)target + row * (size_t)p->ld_t * et;
+            const void *drow = (const char *)draft + row * (size_t)p->ld_d * ed;
+            row_probs(trow, p->dtype_t, V, T, pp);
+            row_probs(drow, p->dtype_d, V, T, qq);
+            double beta = 0.0; /* sum of q over the tokens where q < p */
+            for (int32_t v = 0; v < V; ++v)
+                if (qq[v] < pp[v]) beta += qq[v];
+            for (int32_t v = 0; v < V; ++v) {
+                const double slope = (qq[v] < pp[v] ? 1.0 : 0.0) - beta;
+                grad[row * (size_t)V + v] = grad_loss * dL_dalpha * qq[v] * slope / T;
+            }
+            if (log_ratio) {
+                const double Lt = svref_row_lse(trow, p->dtype_t, V, T);
+                const double Ld = svref_row_lse(drow, p->dtype_d, V, T);
+                for (int32_t v = 0; v < V; ++v)
+                    log_ratio[row * (size_t)V + v] = (svref_logit(trow, p->dtype_t, v) / T - Lt) -
+                                                     (svref_logit(drow, p->dtype_d, v) / T - Ld);
+            }
+        }
+    if (!alpha) free(a);
+    free(pp);
+    free(qq);
+    return 0;
+}
+
 /* ------------------------------------------------------------------------------------ */
 /* Batch-level verification budget                                                       */
 /* ------------------------------------------------------------------------------------ */

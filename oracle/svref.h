@@ -12,7 +12,8 @@
  *   - serial acceptance: a rejection voids every later draft
  *       [same section, paragraph after the overlap equation]
  *   - L_e2e = 1 - (1/(|I| D)) sum_i sum_{m<D} prod_{k<=m} alpha_{i,k}
- *       [same section, L_e2e equation]
+ *       [same section, L_e2e equation]; its gradient in the draft logits, for the
+ *       stage that fine-tunes on it [same section, paragraph after the equation]
  *   - greedy (T=0) and stochastic (T=0.9) decoding modes
  *       [same section, MTP results paragraph]
  *   - verification as a batch-level budget given to high-confidence prefixes
@@ -108,6 +109,13 @@ double svref_e2e_from_alpha(const double *alpha, int32_t I, int32_t D);
  * p->B = |I|, p->K_max = D, temperature > 0.  alpha [I][D] may be NULL. */
 int svref_tv_e2e_loss(const svref_params *p, const void *target, const void *draft,
                       double *alpha, double *loss);
+
+/* Gradient of L_e2e with respect to the draft logits z^d (rows as for svref_tv_e2e_loss):
+ * grad [I][D][V] = grad_loss * dL_e2e/dz^d, with the slope of min(p, q) in q taken as
+ * [q < p] (0 at a tie).  alpha [I][D], loss and log_ratio [I][D][V] = ln p_v - ln q_v may be
+ * NULL. */
+int svref_tv_e2e_backward(const svref_params *p, const void *target, const void *draft, double grad_loss,
+                          double *grad, double *alpha, double *loss, double *log_ratio);
 
 /* Batch verification budget: C_{r,k} = prod_{j<=k} conf_{r,j} in binary32, sequential;
  * keep the first min(N, sum_r L_r) candidates (r, k < L_r) ordered by (C desc, r asc,

@@ -41,6 +41,7 @@ def lib():
         L.svref_e2e_from_alpha.argtypes = [vp, i32, i32]
         L.svref_e2e_from_alpha.restype = dbl
         L.svref_tv_e2e_loss.argtypes = [C.POINTER(Params), vp, vp, vp, vp]
+        L.svref_tv_e2e_backward.argtypes = [C.POINTER(Params), vp, vp, dbl, vp, vp, vp, vp]
         L.svref_alloc_verify_budget.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
         L.svref_dcut_budget.argtypes = [vp, vp, i32, i32, vp, i32, C.POINTER(C.c_int32), C.POINTER(C.c_double), vp, vp, vp]
         _lib = L
@@ -178,6 +179,23 @@ def tv_e2e_loss(target, draft, T, dtype):
     if lib().svref_tv_e2e_loss(C.byref(prm), _ptr(target), _ptr(draft), _ptr(a), _ptr(loss)) != 0:
         raise ValueError("svref_tv_e2e_loss rejected its arguments")
     return float(loss[0]), a
+
+
+def tv_e2e_backward(target, draft, T, dtype, grad_loss=1.0, want_log_ratio=False):
+    """target, draft [I][D][V]; returns (grad [I][D][V], alpha [I][D], loss) and, if asked,
+    log_ratio [I][D][V] = ln p - ln q."""
+    target, draft = _logits(target, dtype), _logits(draft, dtype)
+    I, D, V = target.shape
+    assert draft.shape == (I, D, V)
+    prm = make_params(I, D, V, dtype, T)
+    g = np.zeros((I, D, V))
+    a = np.zeros((I, D))
+    loss = np.zeros(1)
+    lr = np.zeros((I, D, V)) if want_log_ratio else None
+    if lib().svref_tv_e2e_backward(C.byref(prm), _ptr(target), _ptr(draft), float(grad_loss), _ptr(g), _ptr(a),
+                                   _ptr(loss), _ptr(lr)) != 0:
+        raise ValueError("svref_tv_e2e_backward rejected its arguments")
+    return (g, a, float(loss[0]), lr) if want_log_ratio else (g, a, float(loss[0]))
 
 
 def dcut_budget(conf, cost, draft_len=None):

@@ -278,6 +278,80 @@ def test_e2e_special_cases():
 
 
 # ---------------------------------------------------------------------------------------
+# L_e2e gradient in the draft logits: central differences of the forward oracle, a
+# two-token closed form, and the shift invariance of the softmax
+# ---------------------------------------------------------------------------------------
+
+def _kink_free_case(I, D, V, T, seed, margin=0.05):
+    """Logits on a 2^-6 grid with every |ln p - ln q| above `margin`, so that no small
+    perturbation of a drafter logit flips a comparison inside min(p, q)."""
+    for s in range(seed, seed + 500):
+        rng = np.random.default_rng(s)
+        t = (np.round(rng.normal(scale=1.5, size=(I, D, V)) * 64) / 64).astype(np.float32)
+        d = (np.round(rng.normal(scale=1.5, size=(I, D, V)) * 64) / 64).astype(np.float32)
+        lr = svref.tv_e2e_backward(t, d, T, "f32", want_log_ratio=True)[3]
+        if np.abs(lr).min() > margin:
+            return t, d
+    raise AssertionError("no kink-free case found")
+
+
+@pytest.mark.parametrize("T,seed", [(0.7, 0), (1.3, 100)])
+def test_e2e_grad_matches_central_differences(T, seed):
+    I, D, V = 2, 3, 6
+    t, d = _kink_free_case(I, D, V, T, seed)
+    g, _, loss = svref.tv_e2e_backward(t, d, T, "f32", grad_loss=2.5)
+    assert loss == pytest.approx(svref.tv_e2e_loss(t, d, T, "f32")[0], abs=1e-15)
+    h = 2.0 ** -10   # exact on the 2^-6 grid; moves ln q by < 0.005, far below the margin
+    fd = np.zeros_like(g)
+    for idx in itertools.product(range(I), range(D), range(V)):
+        dp, dm = d.copy(), d.copy()
+        dp[idx] += h
+        dm[idx] -= h
+        fd[idx] = (svref.tv_e2e_loss(t, dp, T, "f32")[0] - svref.tv_e2e_loss(t, dm, T, "f32")[0]) / (2 * h)
+    # central differences: error ~ h^2 / 6 times the third derivative
+    np.testing.assert_allclose(g, 2.5 * fd, rtol=1e-5, atol=2e-7)
+
+
+@pytest.mark.parametrize("T", [0.5, 1.0, 2.0])
+def test_e2e_grad_two_tokens_closed_form(T):
+    # V = 2, one position: L = 1 - alpha = |p_0 - q_0|, so dL/dz^d_0 = sign(q_0 - p_0) q_0 q_1 / T
+    rng = np.random.default_rng(7)
+    for _ in range(20):
+        t = rng.normal(size=(1, 1, 2)).astype(np.float32)
+        d = rng.normal(size=(1, 1, 2)).astype(np.float32)
+        p = special.softmax(t[0, 0].astype(np.float64) / T)
+        q = special.softmax(d[0, 0].astype(np.float64) / T)
+        g, a, loss = svref.tv_e2e_backward(t, d, T, "f32")
+        assert loss == pytest.approx(abs(p[0] - q[0]), abs=1e-15)
+        want = np.sign(q[0] - p[0]) * q[0] * q[1] / T
+        assert g[0, 0, 0] == pytest.approx(want, rel=1e-12, abs=1e-300)
+        assert g[0, 0, 1] == pytest.approx(-want, rel=1e-12, abs=1e-300)
+
+
+def test_e2e_grad_rows_sum_to_zero():
+    # adding a constant to a drafter row leaves q, hence the loss, unchanged
+    t = _logits((3, 4, 1000))
+    d = _logits((3, 4, 1000))
+    g, _, _ = svref.tv_e2e_backward(t, d, 0.9, "f32")
+    assert np.abs(g.sum(-1)).max() <= 1e-14 * np.abs(g).sum(-1).max()
+    assert np.abs(g).max() > 0
+
+
+def test_e2e_grad_zero_weight_after_a_certain_reject():
+    # alpha_{i,0} = 0 (disjoint supports) gives positions k >= 1 of that sequence zero weight
+    V = 8
+    t = np.full((1, 3, V), -np.inf, np.float32)
+    d = np.full((1, 3, V), -np.inf, np.float32)
+    t[0, 0, :4] = _logits(4)
+    d[0, 0, 4:] = _logits(4)
+    t[0, 1:] = _logits((2, V))
+    d[0, 1:] = _logits((2, V))
+    g, a, _ = svref.tv_e2e_backward(t, d, 1.0, "f32")
+    assert a[0, 0] == 0.0
+    assert np.all(g[0, 1:] == 0.0)
+
+
+# ---------------------------------------------------------------------------------------
 # Batch-level budget: the greedy selection is the best prefix allocation (brute force)
 # ---------------------------------------------------------------------------------------
 
