@@ -17,7 +17,7 @@ _STATUS = {0: "SV_OK", 1: "SV_EINVAL", 2: "SV_EUNSUPPORTED", 3: "SV_EHIP", 4: "S
 
 EXPORTS = [
     "sv_workspace_bytes", "sv_workspace_init", "sv_verify_batch", "sv_verify_selected", "sv_accept_len",
-    "sv_residual_sample", "sv_tv_e2e_loss", "sv_alloc_verify_budget", "sv_dcut_verify_budget", "sv_uniforms",
+    "sv_residual_sample", "sv_tv_e2e_loss", "sv_tv_e2e_backward", "sv_alloc_verify_budget", "sv_dcut_verify_budget", "sv_uniforms",
     "sv_device_error", "sv_status_string",
 ]
 
@@ -60,6 +60,7 @@ def lib():
         L.sv_accept_len.argtypes = [vp, vp, i32, i32, vp, vp]
         L.sv_residual_sample.argtypes = [P, vp, vp, vp, vp, vp, vp]
         L.sv_tv_e2e_loss.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
+        L.sv_tv_e2e_backward.argtypes = [P, vp, vp, vp, vp, vp, i32, C.c_int64, vp, sz, vp]
         L.sv_alloc_verify_budget.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp]
         L.sv_dcut_verify_budget.argtypes = [vp, vp, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp]
         L.sv_uniforms.argtypes = [u64, vp, i32, vp, vp]
@@ -245,6 +246,33 @@ def sv_tv_e2e_loss(target, draft, T=1.0, alpha=None, workspace=None, stream=None
     _check("sv_tv_e2e_loss", lib().sv_tv_e2e_loss(C.byref(prm), _p(target), _p(draft), _p(alpha), _p(loss),
                                                   _p(ws), ws.numel(), _stream(stream)))
     return loss, alpha
+
+
+def sv_tv_e2e_backward(target, draft, alpha, T=1.0, grad_loss=None, grad_dtype=None, grad=None, workspace=None,
+                       stream=None):
+    """Gradient of L_e2e in the drafter logits.  target, draft [I][D][V]; alpha [I][D] float32
+    (the overlaps of the same inputs, e.g. from sv_tv_e2e_loss); grad_loss: float32 [1] on the
+    GPU or None (1).  Returns grad [I][D][V] of grad_dtype (default: the drafter's dtype)."""
+    I, D, V = target.shape
+    if draft.shape != (I, D, V):
+        raise ValueError("target and draft must have the same shape")
+    if alpha.shape != (I, D) or alpha.dtype != torch.float32 or not alpha.is_contiguous():
+        raise ValueError("alpha must be a contiguous float32 [I][D] tensor")
+    _check_rows(target, D)
+    _check_rows(draft, D)
+    dev = target.device
+    if grad is None:   # rows padded to a 16-byte stride
+        ld = (V + 7) // 8 * 8
+        grad = torch.empty((I, D, ld), dtype=grad_dtype or draft.dtype, device=dev)[:, :, :V]
+    elif grad.shape != (I, D, V):
+        raise ValueError("grad must be [I][D][V]")
+    _check_rows(grad, D)
+    ws = workspace if isinstance(workspace, torch.Tensor) else (workspace or Workspace(dev)).get(I, D, V, stream)
+    prm = _params(I, D, V, target, draft, T, 0, 0)
+    _check("sv_tv_e2e_backward", lib().sv_tv_e2e_backward(
+        C.byref(prm), _p(target), _p(draft), _p(alpha), _p(grad_loss), _p(grad), _dtype_code(grad), _rows_ld(grad),
+        _p(ws), ws.numel(), _stream(stream)))
+    return grad
 
 
 def sv_alloc_verify_budget(conf, budget_N, draft_len=None, want_row_list=True, stream=None):

@@ -21,6 +21,7 @@
 #include "sv_device.hpp"
 #include "specverify.h"
 #include "team.hpp"
+#include "team_grad.hpp"
 
 namespace sv {
 
@@ -740,6 +741,38 @@ int sv_tv_e2e_loss(const sv_params *p, const void *target, const void *draft, fl
     if (e != hipSuccess) return SV_EHIP;
     hipLaunchKernelGGL(e2e_reduce_kernel, dim3(1), dim3(kReduceThreads), 0, (hipStream_t)stream, alpha_buf, p->B,
                        p->K_max, loss, a.epoch);
+    return launch_status();
+}
+
+int sv_tv_e2e_backward(const sv_params *p, const void *target, const void *draft, const float *alpha,
+                       const float *grad_loss, void *grad, int32_t dtype_g, int64_t ld_g, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    if (!p || p->B <= 0 || p->K_max <= 0 || p->V <= 0 || !alpha) return SV_EINVAL;
+    if (p->V > SV_V_MAX) return SV_EUNSUPPORTED;
+    if (!(p->temperature > 0.f) || !isfinite(p->temperature)) return SV_EINVAL;
+    int st = check_logits(target, p->dtype_t, p->ld_t, p->V);
+    if (st) return st;
+    st = check_logits(draft, p->dtype_d, p->ld_d, p->V);
+    if (st) return st;
+    st = check_logits(grad, dtype_g, ld_g, p->V);
+    if (st) return st;
+    const TeamLayout L = team_layout(p->B, p->K_max, p->V, workspace_bytes);
+    if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return SV_EWORKSPACE;
+    const uint64_t grid64 = (uint64_t)L.rows * (uint64_t)L.S;
+    if (grid64 > 0x7fffffffull) return SV_EINVAL;
+    TeamArgs a{};
+    fill_team_args(a, p, L, (char *)workspace);
+    a.target = target; a.draft = draft;
+    a.trows = p->K_max;
+    a.slots = p->K_max;
+    GradArgs g{};
+    g.grad = grad;
+    g.ld_g = ld_g;
+    g.alpha = alpha;
+    g.grad_loss = grad_loss;
+    g.scale = (float *)((char *)workspace + L.off_alpha);
+    g.inv_idt = 1.0 / ((double)p->B * (double)p->K_max * (double)p->temperature);
+    if (team_launch_grad(a, g, p->dtype_t, p->dtype_d, dtype_g, (hipStream_t)stream) != hipSuccess) return SV_EHIP;
     return launch_status();
 }
 

@@ -1,0 +1,383 @@
+// team_device.hpp -- device helpers shared by the kernels in which a team of workgroups
+// shares one row pair (verification, L_e2e and its gradient): tagged-word exchange, fixed-
+// order workgroup reductions, a member's register-resident chunk of a row pair and its
+// passes, and the row normalisers reduced from the members' partials.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "sv_device.hpp"
+#include "team.hpp"
+
+namespace sv {
+namespace {
+
+constexpr uint32_t kGaveUp = 0xffffffffu;  // share payload of a member that did not finish
+
+// ---- tagged words --------------------------------------------------------------------
+__device__ __forceinline__ void put(uint64_t *p, uint32_t payload, uint32_t tag) {
+    __hip_atomic_store(p, ((uint64_t)tag << 32) | payload, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void putf(uint64_t *p, float v, uint32_t tag) { put(p, __float_as_uint(v), tag); }
+__device__ __forceinline__ uint64_t peek(const uint64_t *p) {
+    return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One wave waits until words p[0..n) carry `tag` (n <= 2048), copying their payloads to
+// dst[0..n).  Bounded by `limit` 10-ns ticks; returns false on timeout.  Every lane of the
+// wave must call it.
+__device__ inline bool wave_poll(const uint64_t *p, int n, uint32_t tag, uint32_t *dst, int64_t limit) {
+    const int l = lane_id();
+    uint32_t missing = 0;
+    for (int i = l, b = 0; i < n; i += kWave, ++b) missing |= 1u << b;
+    const uint64_t t0 = wall_clock64();
+    while (true) {
+        for (int i = l, b = 0; i < n; i += kWave, ++b) {
+            if ((missing >> b) & 1u) {
+                const uint64_t w = peek(p + i);
+                if ((uint32_t)(w >> 32) == tag) {
+                    dst[i] = (uint32_t)w;
+                    missing &= ~(1u << b);
+                }
+            }
+        }
+        if (__all(missing == 0)) return true;
+        if ((int64_t)(wall_clock64() - t0) > limit) return false;
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+__device__ __forceinline__ uint32_t read_epoch(const uint32_t *e) {
+    return __hip_atomic_load(const_cast<uint32_t *>(e), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Scalar load of a value that stays constant while the kernel runs (written, if at all, by
+// an earlier kernel on the stream), at a workgroup-uniform address.  It uses the scalar
+// counter, so waiting for it never waits for the vector loads of the chunk.
+template <class T>
+__device__ __forceinline__ T load_uniform(const T *p) {
+    return *(const __attribute__((address_space(4))) T *)(uintptr_t)p;
+}
+
+// ---- row chunk loads -----------------------------------------------------------------
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---- workgroup reductions (fixed order) ------------------------------------------------
+struct TeamRed {
+    float f[8][kTeamWaves];
+    int i[4][kTeamWaves];
+    double d[kTeamWaves];
+};
+
+// (M, s) pairs in base 2: s = sum 2^{x - M}
+__device__ __forceinline__ void ms_merge(float &M, float &s, float M2, float s2) { lse_merge(M, s, M2, s2, 1.0f); }
+
+__device__ __forceinline__ void wave_ms(float &M, float &s) { wave_lse(M, s, 1.0f); }
+
+__device__ inline void block_ms2(float &Mt, float &st, float &Md, float &sd, TeamRed &red) {
+    wave_ms(Mt, st);
+    wave_ms(Md, sd);
+    const int w = threadIdx.x / kWave;
+    if (lane_id() == 0) { red.f[0][w] = Mt; red.f[1][w] = st; red.f[2][w] = Md; red.f[3][w] = sd; }
+    __syncthreads();
+    Mt = red.f[0][0]; st = red.f[1][0]; Md = red.f[2][0]; sd = red.f[3][0];
+    for (int q = 1; q < kTeamWaves; ++q) { ms_merge(Mt, st, red.f[0][q], red.f[1][q]); ms_merge(Md, sd, red.f[2][q], red.f[3][q]); }
+    __syncthreads();
+}
+
+__device__ inline void block_amax2(float &vt, int &it, float &vd, int &id, TeamRed &red) {
+    wave_amax(vt, it);
+    wave_amax(vd, id);
+    const int w = threadIdx.x / kWave;
+    if (lane_id() == 0) { red.f[4][w] = vt; red.i[0][w] = it; red.f[5][w] = vd; red.i[1][w] = id; }
+    __syncthreads();
+    vt = red.f[4][0]; it = red.i[0][0]; vd = red.f[5][0]; id = red.i[1][0];
+    for (int q = 1; q < kTeamWaves; ++q) { amax_merge(vt, it, red.f[4][q], red.i[0][q]); amax_merge(vd, id, red.f[5][q], red.i[1][q]); }
+    __syncthreads();
+}
+
+__device__ inline float block_sumf(float x, TeamRed &red) {
+    x = wave_sum(x);
+    const int w = threadIdx.x / kWave;
+    if (lane_id() == 0) red.f[6][w] = x;
+    __syncthreads();
+    float t = red.f[6][0];
+    for (int q = 1; q < kTeamWaves; ++q) t += red.f[6][q];
+    __syncthreads();
+    return t;
+}
+
+// ---- one member's chunk, kept as loaded ----------------------------------------------
+// Lane l of wave w of member j holds logits base + g * 512 + l * 8 + (0..7), g < kTeamE / 8,
+// base = j * kTeamChunk + w * kTeamSeg: bfloat16 as packed pairs, binary32 as is.
+template <int DT>
+struct LaneRow {
+    static constexpr int kWords = DT == kDtBF16 ? kTeamE / 2 : kTeamE;
+    uint32_t w[kWords];
+
+    // Widen slot i (bfloat16: a shift or a mask of its packed word).
+    __device__ __forceinline__ float get(int i) const {
+        if constexpr (DT == kDtBF16) {
+            return (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]);
+        } else {
+            return __uint_as_float(w[i]);
+        }
+    }
+
+    // Called at the start of every pass over each group of slots: the packed words become
+    // opaque to the compiler, so each pass widens them afresh instead of the compiler keeping the
+    // widened values of an earlier pass live (which would double the registers the chunk
+    // occupies).  Emits no instruction.
+    // Per group of 8 slots (one 16-byte load of bfloat16), so that a pass can start on the
+    // first groups while later loads are still in flight.
+    __device__ __forceinline__ void refresh8(int i) {
+        constexpr int kPer8 = DT == kDtBF16 ? 4 : 8;
+#pragma unroll
+        for (int q = 0; q < kPer8; ++q) asm volatile("" : "+v"(w[(i / 8) * kPer8 + q]));
+    }
+
+    // FULL: the range lies inside the row.  Then no load sits under a condition, so the
+    // compiler can wait for each one on its own as the passes consume them.
+    template <bool FULL>
+    __device__ __forceinline__ void load(const void *row, int base, int V) {
+#pragma unroll
+        for (int g = 0; g < kTeamE / 8; ++g) {
+            const int v0 = base + g * 512 + lane_id() * 8;
+            if (FULL || v0 + 8 <= V) {
+                if constexpr (DT == kDtBF16) {
+                    const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row) + (v0 >> 3));
+                    w[g * 4 + 0] = q.x; w[g * 4 + 1] = q.y; w[g * 4 + 2] = q.z; w[g * 4 + 3] = q.w;
+                } else {
+                    const u32x4 *p = reinterpret_cast<const u32x4 *>(row) + (v0 >> 2);
+                    const u32x4 q0 = __builtin_nontemporal_load(p), q1 = __builtin_nontemporal_load(p + 1);
+                    w[g * 8 + 0] = q0.x; w[g * 8 + 1] = q0.y; w[g * 8 + 2] = q0.z; w[g * 8 + 3] = q0.w;
+                    w[g * 8 + 4] = q1.x; w[g * 8 + 5] = q1.y; w[g * 8 + 6] = q1.z; w[g * 8 + 7] = q1.w;
+                }
+            } else {
+                // ragged end of the row: -inf past V
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int v = v0 + e;
+                    if constexpr (DT == kDtBF16) {
+                        const uint32_t h = v < V ? (uint32_t) static_cast<const uint16_t *>(row)[v] : 0xff80u;
+                        if (e & 1) w[g * 4 + (e >> 1)] |= h << 16;
+                        else w[g * 4 + (e >> 1)] = h;
+                    } else {
+                        w[g * 8 + e] = v < V ? static_cast<const uint32_t *>(row)[v] : 0xff800000u;
+                    }
+                }
+            }
+        }
+    }
+
+    __device__ __forceinline__ float max() {
+        float m0 = neg_inf(), m1 = neg_inf();
+#pragma unroll
+        for (int g = 0; g < kTeamE; g += 8) {
+            refresh8(g);
+#pragma unroll
+            for (int i = g; i < g + 8; i += 2) {
+                m0 = fmaxf(m0, get(i));
+                m1 = fmaxf(m1, get(i + 1));
+            }
+            sched_fence();
+        }
+        return fmaxf(m0, m1);
+    }
+
+    // first slot (in vocabulary order) holding m; its vocabulary index
+    __device__ __forceinline__ int first_index(float m, int base) {
+        int idx = 0x7fffffff;
+#pragma unroll
+        for (int g = kTeamE - 8; g >= 0; g -= 8) {
+            refresh8(g);
+#pragma unroll
+            for (int i = g + 7; i >= g; --i)
+                if (get(i) == m) idx = base + (i >> 3) * 512 + lane_id() * 8 + (i & 7);
+            sched_fence();
+        }
+        return idx;
+    }
+
+    // (M, s) of this lane's logits in base 2 (s = sum_i 2^{x_i c - M}) without a pass for
+    // the maximum: the reference M is c times the largest of the first 8 logits.  Should a
+    // later logit lie so far above it that the sum leaves range (or the first 8 be -inf),
+    // the exact maximum is taken instead.
+    __device__ __forceinline__ void lane_ms(float c, float &M, float &s) {
+        refresh8(0);
+        const float m8 = fmaxf(fmaxf(fmaxf(get(0), get(1)), fmaxf(get(2), get(3))),
+                               fmaxf(fmaxf(get(4), get(5)), fmaxf(get(6), get(7))));
+        M = m8 * c;
+        s = exp_sum(c, M);
+        if (!(s < 0x1p100f)) {
+            const float m = max();
+            M = (m == neg_inf()) ? neg_inf() : m * c;
+            s = (m == neg_inf()) ? 0.f : exp_sum(c, M);
+        }
+    }
+
+    // sum_i 2^{x_i c - M}
+    __device__ __forceinline__ float exp_sum(float c, float M) {
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int g = 0; g < kTeamE; g += 8) {
+            refresh8(g);
+#pragma unroll
+            for (int i = g; i < g + 8; i += 2) {
+                a0 += exp2_fast(__builtin_fmaf(get(i), c, -M));
+                a1 += exp2_fast(__builtin_fmaf(get(i + 1), c, -M));
+            }
+            sched_fence();
+        }
+        return a0 + a1;
+    }
+};
+
+// A row normaliser in base 2, log2 sum_v 2^{z_v c}, kept as an unevaluated sum hi + lo.
+// At low temperature it reaches several hundred, where one binary32 value would be off by
+// up to 2^-15 and so every probability by ~2e-5 relative; in two parts a probability is
+// 2^{fma(z, c, -hi) - lo}: the fma leaves a small argument, and lo (|lo| <= half an ulp
+// of hi) is applied after it.
+struct Norm2 {
+    float hi, lo;
+};
+
+// hi + lo = M + l exactly (Knuth's two-sum); lo = 0 when the sum is not finite.
+__device__ __forceinline__ Norm2 norm2(float M, float l) {
+    Norm2 n;
+    n.hi = M + l;
+    const float bv = n.hi - M;
+    const float e = (M - (n.hi - bv)) + (l - bv);
+    n.lo = __builtin_isfinite(n.hi) ? e : 0.f;
+    return n;
+}
+
+// log2 of the probability of logit z under the row normaliser n
+__device__ __forceinline__ float log2prob(float z, float c, Norm2 n) { return __builtin_fmaf(z, c, -n.hi) - n.lo; }
+
+// A low part this small moves a probability by at most 2^-20 ln 2 < 6.6e-7 relative; it is
+// always so when |hi| < 32 (half an ulp of hi).
+constexpr float kLoNegligible = 0x1p-20f;
+
+// sum_i min(p_i, q_i) with p = 2^{t c - Nt}, q = 2^{d c - Nd}, as
+// 2^{-Nt.lo} sum_i 2^{min(fma(t, c, -Nt.hi), fma(d, c, -Nd.hi) + Nt.lo - Nd.lo)} when `split`
+// (uniform), else with both low parts left out (each at most kLoNegligible).  The choice is
+// made per group of slots, after the group's words are refreshed, so both arms read the
+// same registers.
+template <int DTT, int DTD>
+__device__ __forceinline__ float min_sum(LaneRow<DTT> &t, LaneRow<DTD> &d, float c, Norm2 nt, Norm2 nd, int split) {
+    const float dl = nt.lo - nd.lo;
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int g = 0; g < kTeamE; g += 8) {
+        t.refresh8(g);
+        d.refresh8(g);
+        if (split) {
+#pragma unroll
+            for (int i = g; i < g + 8; i += 2) {
+                a0 += exp2_fast(fminf(__builtin_fmaf(t.get(i), c, -nt.hi), __builtin_fmaf(d.get(i), c, -nd.hi) + dl));
+                a1 += exp2_fast(fminf(__builtin_fmaf(t.get(i + 1), c, -nt.hi), __builtin_fmaf(d.get(i + 1), c, -nd.hi) + dl));
+            }
+        } else {
+#pragma unroll
+            for (int i = g; i < g + 8; i += 2) {
+                a0 += exp2_fast(fminf(__builtin_fmaf(t.get(i), c, -nt.hi), __builtin_fmaf(d.get(i), c, -nd.hi)));
+                a1 += exp2_fast(fminf(__builtin_fmaf(t.get(i + 1), c, -nt.hi), __builtin_fmaf(d.get(i + 1), c, -nd.hi)));
+            }
+        }
+        sched_fence();
+    }
+    return split ? (a0 + a1) * exp2_fast(-nt.lo) : a0 + a1;
+}
+
+// Pass 1 of a lane: base-2 log-sum-exp state (M = max * c, s = sum 2^{x c - M}) per row.
+struct ThreadStats {
+    float Mt, st, Md, sd;
+};
+
+template <int DTT, int DTD>
+__device__ __forceinline__ ThreadStats pass1(LaneRow<DTT> &t, LaneRow<DTD> &d, float mt, float md, float c) {
+    ThreadStats s;
+    s.Mt = (mt == neg_inf()) ? neg_inf() : mt * c;
+    s.Md = (md == neg_inf()) ? neg_inf() : md * c;
+    s.st = (mt == neg_inf()) ? 0.f : t.exp_sum(c, s.Mt);
+    s.sd = (md == neg_inf()) ? 0.f : d.exp_sum(c, s.Md);
+    return s;
+}
+
+// Pass 2 of a lane: its share of alpha and of the residual mass sum max(p - q, 0).
+template <int DTT, int DTD>
+__device__ __forceinline__ void pass2(LaneRow<DTT> &t, LaneRow<DTD> &d, const ThreadStats &s, float c,
+                                      Norm2 nt, Norm2 nd, float &alpha, float &resid) {
+    // the low parts matter only at large |hi| (low temperatures); the test is uniform
+    const int split = __builtin_amdgcn_readfirstlane(
+        (__builtin_fabsf(nt.lo) > kLoNegligible || __builtin_fabsf(nd.lo) > kLoNegligible) ? 1 : 0);
+    alpha = min_sum(t, d, c, nt, nd, split);
+    const float P = (s.Mt == neg_inf()) ? 0.f : s.st * exp2_fast((s.Mt - nt.hi) - nt.lo);   // this lane's target mass
+    resid = P - alpha;
+}
+
+// Row normalisers (base 2) from the S member partials, in member order.  The stream
+// kernel and the finalize kernel both call this on the same payloads, so they agree bit
+// for bit.
+__device__ __forceinline__ void team_totals(const uint32_t *pay, int S, Norm2 &nt, Norm2 &nd) {
+    float Tt = neg_inf(), Ts = 0.f, Dt = neg_inf(), Ds = 0.f;
+#pragma unroll 1
+    for (int q = 0; q < S; ++q) {   // not unrolled: it runs beside a chunk held in registers
+        ms_merge(Tt, Ts, __uint_as_float(pay[q]), __uint_as_float(pay[S + q]));
+        ms_merge(Dt, Ds, __uint_as_float(pay[2 * S + q]), __uint_as_float(pay[3 * S + q]));
+    }
+    nt = norm2(Tt, log2f(Ts));
+    nd = norm2(Dt, log2f(Ds));
+}
+
+template <int DT>
+__device__ __forceinline__ const void *row_ptr(const void *base, int64_t row, int64_t ld) {
+    return static_cast<const char *>(base) + (size_t)(row * ld) * (DT == kDtBF16 ? 2 : 4);
+}
+
+// Workgroup-cooperative load of n tagged words into dst (payloads); returns the number of
+// words whose tag is not `tag` (their payload is replaced by `missing`).
+__device__ inline int load_tagged(const uint64_t *p, int n, uint32_t tag, uint32_t *dst, uint32_t missing) {
+    constexpr int U = 8;
+    int bad = 0;
+    for (int i0 = 0; i0 < n; i0 += U * kTeamThreads) {
+        uint64_t w[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * kTeamThreads + threadIdx.x;
+            w[u] = i < n ? peek(p + i) : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * kTeamThreads + threadIdx.x;
+            if (i < n) {
+                const bool ok = (uint32_t)(w[u] >> 32) == tag;
+                dst[i] = ok ? (uint32_t)w[u] : missing;
+                bad += ok ? 0 : 1;
+            }
+        }
+    }
+    return bad;
+}
+
+}  // namespace
+
+// Phase 1 of a row: the workgroup merges its lanes' (M, s) states of both rows and thread 0
+// publishes the member's partials.
+__device__ __forceinline__ void publish_partials(uint64_t *part, int S, int j, const ThreadStats &ts, uint32_t tag,
+                                                 TeamRed &red) {
+    float Mt = ts.Mt, st = ts.st, Md = ts.Md, sd = ts.sd;
+    block_ms2(Mt, st, Md, sd, red);
+    if (threadIdx.x == 0) {
+        putf(part + 0 * S + j, Mt, tag);
+        putf(part + 1 * S + j, st, tag);
+        putf(part + 2 * S + j, Md, tag);
+        putf(part + 3 * S + j, sd, tag);
+    }
+}
+
+}  // namespace sv

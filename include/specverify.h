@@ -157,6 +157,25 @@ int sv_tv_e2e_loss(const sv_params *params, const void *target, const void *draf
                    float *alpha, float *loss, void *workspace, size_t workspace_bytes,
                    void *stream);
 
+/* Gradient of the end-to-end TV objective in the drafter logits, for the training stage that
+ * fine-tunes on it [TV, L_e2e equation and the paragraph after it].  The pages do not write
+ * the derivative; by the chain rule
+ *   grad[i][k][v] = grad_loss * dL_e2e / dz^d_{i,k,v}
+ *                 = -grad_loss (w_{i,k} / (|I| D T)) q_v ([q_v < p_v] - sum_{w: q_w < p_w} q_w),
+ *   w_{i,k} = sum_{m=k}^{D-1} prod_{j<=m, j!=k} alpha_{i,j},
+ * reading the slope of min(p, q) in q as [q < p] (0 at a tie).  The target logits get no
+ * gradient (the target model is frozen).
+ * params, target, draft: as for sv_tv_e2e_loss.  alpha [|I|][D] float (device): the overlaps
+ * of the same inputs, e.g. the alpha output of sv_tv_e2e_loss.  grad_loss: one float (device),
+ * or NULL for 1.  grad: [|I|][D] rows of ld_g >= V elements of dtype_g (SV_F32, or SV_BF16
+ * rounded to nearest even), 16-byte aligned rows, not overlapping the logits; elements past V
+ * are not written.  workspace: sv_workspace_bytes(|I|, D, V) bytes, same rules as
+ * sv_tv_e2e_loss.  Errors: SV_EINVAL (sizes, pointers, alignment, T <= 0), SV_EUNSUPPORTED
+ * (dtype code, V > SV_V_MAX), SV_EWORKSPACE, SV_EHIP. */
+int sv_tv_e2e_backward(const sv_params *params, const void *target, const void *draft,
+                       const float *alpha, const float *grad_loss, void *grad, int32_t dtype_g,
+                       int64_t ld_g, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Batch-level verification budget [RT] [ABS]: C_{r,k} = prod_{j<=k} conf_{r,j} (binary32,
  * sequential in k); the first min(N, sum_r L_r) candidates (r, k < L_r) in the order
  * (C desc, r asc, k asc) are kept.  conf [B][K_max] float in [0, 1]; draft_len [B] or

@@ -6,7 +6,8 @@ Tolerances (from the stated goal for this path):
     threshold p(x)/q(x); such requests are counted and their tokens are not compared;
   * correction / bonus tokens: bit-exact unless the oracle's CDF target u*R lies within
     1e-6*R of every CDF boundary between the two tokens; counted;
-  * alpha, log-normalisers: 1e-5 relative (binary32 accumulation).
+  * alpha, log-normalisers: 1e-5 relative (binary32 accumulation);
+  * the L_e2e gradient: see compare_grad.
 """
 import numpy as np
 
@@ -68,3 +69,32 @@ def compare_verify(gpu, ora, target_np, draft_np, dtype, T, check=None, L=None):
         assert 0 <= gap <= CDF_BAND * R, f"token r={r}: gpu {tg} oracle {to}, gap {gap} R {R}"
         rep["near_token"] += 1
     return rep
+
+
+# ---- gradient of L_e2e in the drafter logits ------------------------------------------
+# An element is g = s q ([q < p] - beta).  Its own arithmetic (q = 2^x from one fma, the
+# products) is held to GRAD_RTOL relative.  beta is a sum over the whole row; its binary32
+# rounding (~1e-7 relative) reaches every element of the row as s q dbeta, bounded by
+# GRAD_ROW_ATOL times the row's largest |g|.  Where |ln p - ln q| < TIE_BAND the comparison
+# q < p may fall either way in binary32; those elements are counted, checked finite, and not
+# compared.  bfloat16 gradients add their rounding (half an ulp, 2^-9 relative).
+GRAD_RTOL = 1e-5
+GRAD_ROW_ATOL = 2e-6
+TIE_BAND = 1e-4
+
+
+def compare_grad(gpu, ora, log_ratio, rtol=GRAD_RTOL, bf16=False):
+    """gpu, ora, log_ratio: [..., V] arrays.  Returns a report; raises AssertionError."""
+    g = np.asarray(gpu, np.float64)
+    o = np.asarray(ora, np.float64)
+    ties = np.abs(log_ratio) < TIE_BAND
+    assert np.isfinite(g).all(), "non-finite gradient"
+    row_max = np.abs(o).max(-1, keepdims=True)
+    tol = (rtol + (2.0 ** -8 if bf16 else 0.0)) * np.abs(o) + GRAD_ROW_ATOL * row_max
+    bad = (np.abs(g - o) > tol) & ~ties
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError(f"gradient mismatch at {tuple(i)}: gpu {g[tuple(i)]!r} oracle {o[tuple(i)]!r} "
+                             f"({int(bad.sum())} elements)")
+    rel = np.abs(g - o)[~ties] / np.maximum(np.abs(o)[~ties], 1e-300)
+    return {"elements": int(o.size), "ties": int(ties.sum()), "max_rel": float(rel.max()) if rel.size else 0.0}

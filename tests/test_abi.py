@@ -24,7 +24,7 @@ def svlib():
 
 def test_header_declares_the_boundary():
     names = _declared()
-    for n in ["sv_verify_batch", "sv_accept_len", "sv_residual_sample", "sv_tv_e2e_loss",
+    for n in ["sv_verify_batch", "sv_accept_len", "sv_residual_sample", "sv_tv_e2e_loss", "sv_tv_e2e_backward",
               "sv_alloc_verify_budget", "sv_workspace_bytes", "sv_status_string"]:
         assert n in names
 
@@ -119,3 +119,24 @@ def test_dcut_host_validation(svlib):
     assert svlib.sv_dcut_verify_budget(*big) == EUNSUP
     long_table = list(ok); long_table[5] = 8194
     assert svlib.sv_dcut_verify_budget(*long_table) == EUNSUP
+
+
+def test_e2e_backward_host_validation(svlib):
+    from draft_verification_softmax_amd.binding import Params
+    EINVAL, EUNSUP, EWS = 1, 2, 4
+    nul = None
+    fake = C.c_void_p(0x1000)
+    odd = C.c_void_p(0x1004)
+
+    def call(prm, alpha=fake, grad=fake, dg=1, ld_g=96, ws=nul, wsb=0):
+        return svlib.sv_tv_e2e_backward(C.byref(prm), fake, fake, alpha, nul, grad, dg, ld_g, ws, wsb, nul)
+    ok = Params(2, 3, 96, 1, 1, 1.0, 0, 0, 96, 96)
+    assert call(Params(2, 3, 96, 1, 1, 0.0, 0, 0, 96, 96)) == EINVAL     # T = 0
+    assert call(Params(0, 3, 96, 1, 1, 1.0, 0, 0, 96, 96)) == EINVAL     # |I| = 0
+    assert call(ok, alpha=nul) == EINVAL                                  # no alpha
+    assert call(ok, grad=nul) == EINVAL                                   # no gradient
+    assert call(ok, grad=odd) == EINVAL                                   # misaligned gradient rows
+    assert call(ok, ld_g=100) == EINVAL                                   # stride not 16-byte aligned
+    assert call(ok, ld_g=90) == EINVAL                                    # stride below V
+    assert call(ok, dg=5) == EUNSUP                                       # gradient dtype code
+    assert call(ok) == EWS                                                # everything valid but the workspace
