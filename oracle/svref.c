@@ -439,6 +439,63 @@ int svref_tv_e2e_backward(const svref_params *p, const void *target, const void 
 }
 
 /* ------------------------------------------------------------------------------------ */
+/* Draft tokens and confidences                                                          */
+/* ------------------------------------------------------------------------------------ */
+
+/* The budget step ranks prefixes by an expected utility taken from the drafter's output
+ * distribution [AngelSpec tutorial, section "Runtime adaptation: verification as a shared
+ * pool", D-cut paragraph]; this is the step that produces what it ranks.  Reading: a
+ * drafted token is a sample of q = softmax(z^d / T) and its confidence is q(x).  The draw is
+ * the inverse CDF used for every other token here, at u = uniform(seed; r, k, DRAFT, step).
+ * T == 0 (greedy drafting): x = argmax, lowest index on ties, and the confidence is the
+ * drafter's own probability of it, softmax(z^d)(x) at T = 1 (q at T = 0 would be 1). */
+int svref_sample_drafts(const svref_params *p, const void *draft, int32_t *tokens, double *conf,
+                        double *u_out, double *R_out) {
+    if (check_params(p) || !(p->temperature >= 0.0) || !draft || !tokens || !conf) return 1;
+    const int32_t V = p->V;
+    double *q = (double *)malloc(sizeof(double) * (size_t)V);
+    if (!q) return 1;
+    for (int32_t r = 0; r < p->B; ++r)
+        for (int32_t k = 0; k < p->K_max; ++k) {
+            const size_t i = (size_t)r * p->K_max + k;
+            const void *drow = drow_ptr(p, draft, r, k);
+            int32_t x;
+            if (p->temperature > 0.0) {
+                row_probs(drow, p->dtype_d, V, p->temperature, q);
+                const double u = svref_uniform(p->seed, (uint64_t)r, (uint64_t)k, SVREF_PURPOSE_DRAFT, p->step);
+                double R, t;
+                x = inverse_cdf(q, V, u, &R, &t);
+                if (u_out) u_out[i] = u;
+                if (R_out) R_out[i] = R;
+            } else {
+                x = svref_row_argmax(drow, p->dtype_d, V);
+                row_probs(drow, p->dtype_d, V, 1.0, q);
+                if (u_out) u_out[i] = 0.0;
+                if (R_out) R_out[i] = 1.0;
+            }
+            if (x < 0) x = 0; /* q == 0 everywhere cannot happen for finite logits */
+            tokens[i] = x;
+            conf[i] = q[x];
+        }
+    free(q);
+    return 0;
+}
+
+/* sum_{j<=v} q_j of drafter row (r, k) at the params' temperature (T > 0). */
+double svref_draft_cdf(const svref_params *p, const void *draft, int32_t r, int32_t k, int32_t v) {
+    if (check_params(p) || !(p->temperature > 0.0) || r < 0 || r >= p->B || k < 0 || k >= p->K_max || v < -1 ||
+        v >= p->V)
+        return NAN;
+    double *q = (double *)malloc(sizeof(double) * (size_t)p->V);
+    if (!q) return NAN;
+    row_probs(drow_ptr(p, draft, r, k), p->dtype_d, p->V, p->temperature, q);
+    double c = 0.0;
+    for (int32_t j = 0; j <= v; ++j) c += q[j];
+    free(q);
+    return c;
+}
+
+/* ------------------------------------------------------------------------------------ */
 /* Batch-level verification budget                                                       */
 /* ------------------------------------------------------------------------------------ */
 

@@ -16,7 +16,8 @@
  *       stage that fine-tunes on it [same section, paragraph after the equation]
  *   - greedy (T=0) and stochastic (T=0.9) decoding modes
  *       [same section, MTP results paragraph]
- *   - verification as a batch-level budget given to high-confidence prefixes
+ *   - verification as a batch-level budget given to high-confidence prefixes, ranked by
+ *       what the drafter's distribution says of each prefix
  *       [AngelSpec tutorial, section "Runtime adaptation: verification as a shared pool"]
  *   - the target distribution is left unchanged
  *       [AngelSpec abstract, first sentence]
@@ -116,6 +117,16 @@ int svref_tv_e2e_loss(const svref_params *p, const void *target, const void *dra
  * NULL. */
 int svref_tv_e2e_backward(const svref_params *p, const void *target, const void *draft, double grad_loss,
                           double *grad, double *alpha, double *loss, double *log_ratio);
+
+/* Draft tokens and confidences for drafter rows [B][K_max][ld_d] (as svref_verify_batch's
+ * draft): T > 0: tokens[r][k] = inverse CDF of q = softmax(z/T) at u = uniform(seed; r, k,
+ * DRAFT, step), conf = q(token); T == 0: the argmax (lowest index) and its probability at
+ * T = 1.  u_out, R_out ([B][K_max], may be NULL): the draw's u and R = sum q. */
+int svref_sample_drafts(const svref_params *p, const void *draft, int32_t *tokens, double *conf,
+                        double *u_out, double *R_out);
+
+/* sum_{j<=v} q_j of drafter row (r, k) at temperature T > 0 (v = -1 gives 0). */
+double svref_draft_cdf(const svref_params *p, const void *draft, int32_t r, int32_t k, int32_t v);
 
 /* Batch verification budget: C_{r,k} = prod_{j<=k} conf_{r,j} in binary32, sequential;
  * keep the first min(N, sum_r L_r) candidates (r, k < L_r) ordered by (C desc, r asc,

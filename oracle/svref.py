@@ -42,6 +42,9 @@ def lib():
         L.svref_e2e_from_alpha.restype = dbl
         L.svref_tv_e2e_loss.argtypes = [C.POINTER(Params), vp, vp, vp, vp]
         L.svref_tv_e2e_backward.argtypes = [C.POINTER(Params), vp, vp, dbl, vp, vp, vp, vp]
+        L.svref_sample_drafts.argtypes = [C.POINTER(Params), vp, vp, vp, vp, vp]
+        L.svref_draft_cdf.argtypes = [C.POINTER(Params), vp, i32, i32, i32]
+        L.svref_draft_cdf.restype = dbl
         L.svref_alloc_verify_budget.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
         L.svref_dcut_budget.argtypes = [vp, vp, i32, i32, vp, i32, C.POINTER(C.c_int32), C.POINTER(C.c_double), vp, vp, vp]
         _lib = L
@@ -196,6 +199,25 @@ def tv_e2e_backward(target, draft, T, dtype, grad_loss=1.0, want_log_ratio=False
                                    _ptr(loss), _ptr(lr)) != 0:
         raise ValueError("svref_tv_e2e_backward rejected its arguments")
     return (g, a, float(loss[0]), lr) if want_log_ratio else (g, a, float(loss[0]))
+
+
+def sample_drafts(draft, T, dtype, seed=0, step=0):
+    """draft [B][K][V]; returns (tokens [B][K] int32, conf [B][K], u [B][K], R [B][K])."""
+    draft = _logits(draft, dtype)
+    B, K, V = draft.shape
+    prm = make_params(B, K, V, dtype, T, seed, step)
+    tok = np.zeros((B, K), np.int32)
+    conf, u, R = np.zeros((B, K)), np.zeros((B, K)), np.zeros((B, K))
+    if lib().svref_sample_drafts(C.byref(prm), _ptr(draft), _ptr(tok), _ptr(conf), _ptr(u), _ptr(R)) != 0:
+        raise ValueError("svref_sample_drafts rejected its arguments")
+    return tok, conf, u, R
+
+
+def draft_cdf(draft, T, dtype, r, k, v):
+    draft = _logits(draft, dtype)
+    B, K, V = draft.shape
+    prm = make_params(B, K, V, dtype, T)
+    return lib().svref_draft_cdf(C.byref(prm), _ptr(draft), r, k, v)
 
 
 def dcut_budget(conf, cost, draft_len=None):

@@ -352,6 +352,65 @@ def test_e2e_grad_zero_weight_after_a_certain_reject():
 
 
 # ---------------------------------------------------------------------------------------
+# Draft tokens and confidences: the draw follows q, the confidence is q(x), the draw is a
+# searchsorted inverse CDF keyed by the DRAFT counter, greedy takes the first maximum
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [0.7, 1.0])
+def test_draft_tokens_follow_q(T):
+    """Rows of identical logits draw independent uniforms (r, k differ): counts follow q."""
+    B, K, V = 50_000, 2, 6
+    z = _logits(V, rng=np.random.default_rng(31))
+    d = np.broadcast_to(z, (B, K, V)).astype(np.float32).copy()
+    tok, conf, _, _ = svref.sample_drafts(d, T, "f32", seed=4, step=2)
+    q = special.softmax(z.astype(np.float64) / T)
+    for k in range(K):
+        counts = np.bincount(tok[:, k], minlength=V).astype(np.float64)
+        ok, pval = _chi2_ok(counts, q)
+        assert ok, (k, pval)
+    np.testing.assert_allclose(conf, q[tok], rtol=1e-14)
+
+
+@pytest.mark.parametrize("T", [0.0, 0.5, 1.3])
+def test_draft_confidence_is_softmax_of_token(T):
+    d = _logits((3, 4, 50), rng=np.random.default_rng(32))
+    tok, conf, _, _ = svref.sample_drafts(d, T, "f32", seed=1, step=0)
+    q = special.softmax(d.astype(np.float64) / (T if T > 0 else 1.0), axis=-1)
+    want = np.take_along_axis(q, tok[..., None].astype(np.int64), -1)[..., 0]
+    np.testing.assert_allclose(conf, want, rtol=1e-13)
+    if T == 0:
+        np.testing.assert_array_equal(tok, d.argmax(-1))
+
+
+def test_draft_draw_is_searchsorted_on_the_draft_counter():
+    B, K, V, T, seed, step = 8, 5, 40, 0.9, 123, 7
+    d = _logits((B, K, V), rng=np.random.default_rng(33))
+    tok, _, u, R = svref.sample_drafts(d, T, "f32", seed=seed, step=step)
+    q = special.softmax(d.astype(np.float64) / T, axis=-1)
+    for r in range(B):
+        for k in range(K):
+            assert u[r, k] == svref.uniform(seed, r, k, 2, step)      # purpose word 2
+            assert u[r, k] != svref.uniform(seed, r, k, 1, step)
+            cq = np.cumsum(q[r, k])
+            assert R[r, k] == pytest.approx(1.0, abs=1e-12)
+            assert tok[r, k] == int(np.searchsorted(cq, u[r, k] * R[r, k], side="right"))
+            assert svref.draft_cdf(d, T, "f32", r, k, int(tok[r, k])) == pytest.approx(cq[tok[r, k]], abs=1e-13)
+
+
+def test_draft_greedy_ties_take_lowest_index():
+    d = np.zeros((1, 2, 9), np.float32)
+    d[0, 0, [2, 5, 7]] = 3.0
+    d[0, 1, [8, 1]] = -1.0
+    d[0, 1, 4] = -1.0
+    d[0, 1] -= 5.0
+    d[0, 1, [1, 4, 8]] = 0.5
+    tok, conf, _, _ = svref.sample_drafts(d, 0.0, "f32")
+    assert tok.tolist() == [[2, 1]]
+    q0 = special.softmax(d[0, 0].astype(np.float64))
+    assert conf[0, 0] == pytest.approx(q0[2], rel=1e-14)
+
+
+# ---------------------------------------------------------------------------------------
 # Batch-level budget: the greedy selection is the best prefix allocation (brute force)
 # ---------------------------------------------------------------------------------------
 
