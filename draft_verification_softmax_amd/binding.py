@@ -17,7 +17,7 @@ _STATUS = {0: "SV_OK", 1: "SV_EINVAL", 2: "SV_EUNSUPPORTED", 3: "SV_EHIP", 4: "S
 
 EXPORTS = [
     "sv_workspace_bytes", "sv_workspace_init", "sv_verify_batch", "sv_verify_selected", "sv_accept_len",
-    "sv_residual_sample", "sv_tv_e2e_loss", "sv_tv_e2e_backward", "sv_alloc_verify_budget", "sv_dcut_verify_budget", "sv_uniforms",
+    "sv_residual_sample", "sv_tv_e2e_loss", "sv_tv_e2e_backward", "sv_sample_drafts", "sv_alloc_verify_budget", "sv_dcut_verify_budget", "sv_uniforms",
     "sv_device_error", "sv_status_string",
 ]
 
@@ -61,6 +61,7 @@ def lib():
         L.sv_residual_sample.argtypes = [P, vp, vp, vp, vp, vp, vp]
         L.sv_tv_e2e_loss.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
         L.sv_tv_e2e_backward.argtypes = [P, vp, vp, vp, vp, vp, i32, C.c_int64, vp, sz, vp]
+        L.sv_sample_drafts.argtypes = [P, vp, vp, vp, vp, sz, vp]
         L.sv_alloc_verify_budget.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp]
         L.sv_dcut_verify_budget.argtypes = [vp, vp, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp]
         L.sv_uniforms.argtypes = [u64, vp, i32, vp, vp]
@@ -273,6 +274,24 @@ def sv_tv_e2e_backward(target, draft, alpha, T=1.0, grad_loss=None, grad_dtype=N
         C.byref(prm), _p(target), _p(draft), _p(alpha), _p(grad_loss), _p(grad), _dtype_code(grad), _rows_ld(grad),
         _p(ws), ws.numel(), _stream(stream)))
     return grad
+
+
+def sv_sample_drafts(draft, T, seed=0, step=0, workspace=None, stream=None):
+    """draft [B][K][V] (GPU).  Returns (tokens [B][K] int32, conf [B][K] float32): a sample of
+    softmax(draft / T) per row and its probability (T = 0: the argmax and its probability at
+    T = 1)."""
+    B, K, V = draft.shape
+    dev = draft.device
+    tokens = torch.empty((B, K), dtype=torch.int32, device=dev)
+    conf = torch.empty((B, K), dtype=torch.float32, device=dev)
+    if B == 0 or K == 0:
+        return tokens, conf
+    _check_rows(draft, K)
+    ws = workspace if isinstance(workspace, torch.Tensor) else (workspace or Workspace(dev)).get(B, K, V, stream)
+    prm = Params(B, K, V, _dtype_code(draft), _dtype_code(draft), float(T), seed, step, _rows_ld(draft), _rows_ld(draft))
+    _check("sv_sample_drafts", lib().sv_sample_drafts(C.byref(prm), _p(draft), _p(tokens), _p(conf), _p(ws),
+                                                      ws.numel(), _stream(stream)))
+    return tokens, conf
 
 
 def sv_alloc_verify_budget(conf, budget_N, draft_len=None, want_row_list=True, stream=None):

@@ -10,7 +10,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libspecverify.so")
-SOURCES = ["specverify.hip", "team_kernel.hip", "team_grad.hip"]
+SOURCES = ["specverify.hip", "team_kernel.hip", "team_grad.hip", "team_sample.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 

@@ -22,6 +22,7 @@
 #include "specverify.h"
 #include "team.hpp"
 #include "team_grad.hpp"
+#include "team_sample.hpp"
 
 namespace sv {
 
@@ -773,6 +774,28 @@ int sv_tv_e2e_backward(const sv_params *p, const void *target, const void *draft
     g.scale = (float *)((char *)workspace + L.off_alpha);
     g.inv_idt = 1.0 / ((double)p->B * (double)p->K_max * (double)p->temperature);
     if (team_launch_grad(a, g, p->dtype_t, p->dtype_d, dtype_g, (hipStream_t)stream) != hipSuccess) return SV_EHIP;
+    return launch_status();
+}
+
+int sv_sample_drafts(const sv_params *p, const void *draft, int32_t *tokens, float *conf, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+    if (!p || p->B < 0 || p->K_max < 0 || p->V <= 0) return SV_EINVAL;
+    if (p->V > SV_V_MAX) return SV_EUNSUPPORTED;
+    if (!(p->temperature >= 0.f) || !isfinite(p->temperature)) return SV_EINVAL;
+    if (p->B == 0 || p->K_max == 0) return SV_OK;
+    const int st = check_logits(draft, p->dtype_d, p->ld_d, p->V);
+    if (st) return st;
+    if (!tokens || !conf) return SV_EINVAL;
+    const TeamLayout L = team_layout(p->B, p->K_max, p->V, workspace_bytes);
+    if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return SV_EWORKSPACE;
+    const uint64_t grid64 = (uint64_t)L.rows * (uint64_t)L.S;
+    if (grid64 > 0x7fffffffull) return SV_EINVAL;
+    TeamArgs a{};
+    fill_team_args(a, p, L, (char *)workspace);
+    a.draft = draft;
+    a.trows = p->K_max;
+    a.slots = p->K_max;
+    if (team_launch_sample(a, p->dtype_d, tokens, conf, (hipStream_t)stream) != hipSuccess) return SV_EHIP;
     return launch_status();
 }
 

@@ -84,6 +84,7 @@ __device__ __forceinline__ float uniform24(uint64_t seed, uint64_t c0, uint64_t 
 
 constexpr uint64_t kPurposeAccept = 0;
 constexpr uint64_t kPurposeCorrection = 1;
+constexpr uint64_t kPurposeDraft = 2;
 
 // ---------------------------------------------------------------------------------------
 // Log-sum-exp state in base 2: (m, s) stands for sum_v 2^{(z_v - m) c}; c = log2(e) / T.

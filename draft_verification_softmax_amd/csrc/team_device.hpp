@@ -364,6 +364,115 @@ __device__ inline int load_tagged(const uint64_t *p, int n, uint32_t tag, uint32
     return bad;
 }
 
+// Token drawn by inverse CDF at target t over weights w: the residual max(p - q, 0) after
+// a rejection (RESID), else p (the bonus token).  The per-range masses (one per
+// kTeamSeg-logit wave range) pick the range; the workgroup re-reads that range and scans
+// it in binary64.
+// The total R of the range masses is summed in binary64 in range order and the target is
+// u * R; -1 when every mass is zero.
+template <int DTT, int DTD, bool RESID>
+__device__ int draw_ranges(const void *trow, const void *drow, int V, float c, Norm2 nt, Norm2 nd,
+                           const float *dirv, int nseg, float u, TeamRed &red) {
+    __shared__ int s_seg;
+    __shared__ double s_ex;
+    __shared__ double s_scan[kTeamThreads];
+    __shared__ int s_tok;
+    const int w = threadIdx.x / kWave;
+    if (w == 0) {
+        const int lane = lane_id();
+        double ex = 0.0;
+        int sidx = -1;
+        if (nseg <= kWave) {
+            // one pass: the inclusive scan gives R at its last lane and the crossing at once
+            const double x = lane < nseg ? (double)dirv[lane] : 0.0;
+            const double incl = wave_incl_scan(x);
+            const double t = (double)u * __shfl(incl, kWave - 1, kWave);
+            const uint64_t hit = __ballot(incl > t);
+            const uint64_t pos = __ballot(x > 0.0);
+            const int l = hit ? __builtin_ctzll(hit) : (pos ? 63 - __builtin_clzll(pos) : 0);
+            ex = __shfl(incl - x, l, kWave);
+            sidx = (hit || pos) ? l : -1;
+            if (lane == 0) s_ex = t - ex;
+        } else {
+            double part = 0.0;
+            for (int q = lane; q < nseg; q += kWave) part += (double)dirv[q];
+            // fixed order: lane partials summed in lane order
+            const double R = __shfl(wave_incl_scan(part), kWave - 1, kWave);
+            const double t = (double)u * R;
+            sidx = wave_find([&](int q) { return dirv[q]; }, nseg, t, &ex);
+            if (lane == 0) s_ex = t - ex;
+        }
+        if (lane == 0) s_seg = sidx;
+    }
+    __syncthreads();
+    const int sidx = s_seg;
+    if (sidx < 0) return -1;
+    const double rem = s_ex;
+    // the range's kTeamSeg logits, kPer consecutive ones per thread
+    constexpr int kPer = kTeamSeg / kTeamThreads;
+    const int e0 = sidx * kTeamSeg + threadIdx.x * kPer;
+    const int vend = min(V, (sidx + 1) * kTeamSeg);
+    float wt[kPer];
+    double my = 0.0;
+#pragma unroll
+    for (int e8 = 0; e8 < kPer; e8 += 8) {
+        float zt[8], zd[8];
+        load8<DTT>(trow, e0 + e8, vend, zt);
+        if constexpr (RESID) load8<DTD>(drow, e0 + e8, vend, zd);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float p = exp2_fast(log2prob(zt[e], c, nt));
+            if constexpr (RESID) {
+                const float q = exp2_fast(log2prob(zd[e], c, nd));
+                wt[e8 + e] = p - fminf(p, q);
+            } else {
+                wt[e8 + e] = p;
+            }
+            my += (double)wt[e8 + e];
+        }
+    }
+    // inclusive scan of per-thread sums in thread order
+    double incl = wave_incl_scan(my);
+    if (lane_id() == kWave - 1) s_scan[w] = incl;
+    __syncthreads();
+    double off = 0.0;
+    for (int q = 0; q < w; ++q) off += s_scan[q];
+    incl += off;
+    __syncthreads();
+    if (threadIdx.x == 0) s_tok = 0x7fffffff;
+    __syncthreads();
+    if (incl > rem && incl - my <= rem) {
+        // this thread's 8 logits hold the crossing
+        double run = incl - my;
+        int k = kPer - 1;
+        for (int e = 0; e < kPer; ++e) {
+            run += (double)wt[e];
+            if (run > rem) { k = e; break; }
+        }
+        atomicMin(&s_tok, e0 + k);
+    }
+    __syncthreads();
+    int tok = s_tok;
+    if (tok == 0x7fffffff) {
+        // rounding ran past the range: the last logit of the range with positive weight
+        int last = -1;
+        for (int e = kPer - 1; e >= 0; --e)
+            if (wt[e] > 0.f) { last = e0 + e; break; }
+        s_scan[threadIdx.x] = (double)last;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int best = min(sidx * kTeamSeg, V - 1);
+            for (int q = kTeamThreads - 1; q >= 0; --q)
+                if (s_scan[q] >= 0.0) { best = (int)s_scan[q]; break; }
+            s_tok = best;
+        }
+        __syncthreads();
+        tok = s_tok;
+    }
+    __syncthreads();
+    return tok;
+}
+
 }  // namespace
 
 // Phase 1 of a row: the workgroup merges its lanes' (M, s) states of both rows and thread 0

@@ -176,6 +176,18 @@ int sv_tv_e2e_backward(const sv_params *params, const void *target, const void *
                        const float *alpha, const float *grad_loss, void *grad, int32_t dtype_g,
                        int64_t ld_g, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Draft tokens and their confidences, the input of the batch-level budget [RT]: the pool
+ * ranks prefixes by what the drafter's output distribution says of them.  For each drafter
+ * row (r, k < K_max): T > 0: tokens[r][k] ~ q = softmax(z^d / T), drawn by inverse CDF (the
+ * smallest x with sum_{j<=x} q_j > u R, R = sum q) at u = U(Philox(seed; r, k, 2, step)), and
+ * conf[r][k] = q(x).  T == 0: the first argmax, with conf = its probability at T = 1.
+ * params: B, K_max, V, dtype_d, ld_d, temperature >= 0, seed, step (the target fields are
+ * unused).  draft [B][K_max] rows as for sv_verify_batch; tokens int32 [B][K_max], conf float
+ * [B][K_max] (device).  workspace: sv_workspace_bytes(B, K_max, V) bytes, same rules as
+ * sv_verify_batch.  Errors: SV_EINVAL, SV_EUNSUPPORTED, SV_EWORKSPACE, SV_EHIP. */
+int sv_sample_drafts(const sv_params *params, const void *draft, int32_t *tokens, float *conf,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
 /* Batch-level verification budget [RT] [ABS]: C_{r,k} = prod_{j<=k} conf_{r,j} (binary32,
  * sequential in k); the first min(N, sum_r L_r) candidates (r, k < L_r) in the order
  * (C desc, r asc, k asc) are kept.  conf [B][K_max] float in [0, 1]; draft_len [B] or

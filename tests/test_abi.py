@@ -140,3 +140,21 @@ def test_e2e_backward_host_validation(svlib):
     assert call(ok, ld_g=90) == EINVAL                                    # stride below V
     assert call(ok, dg=5) == EUNSUP                                       # gradient dtype code
     assert call(ok) == EWS                                                # everything valid but the workspace
+
+
+def test_sample_drafts_host_validation(svlib):
+    from draft_verification_softmax_amd.binding import Params
+    EINVAL, EUNSUP, EWS = 1, 2, 4
+    nul = None
+    fake = C.c_void_p(0x1000)
+
+    def call(prm, draft=fake, tok=fake, conf=fake):
+        return svlib.sv_sample_drafts(C.byref(prm), draft, tok, conf, nul, 0, nul)
+    assert call(Params(2, 3, 96, 1, 1, -1.0, 0, 0, 96, 96)) == EINVAL             # T < 0
+    assert call(Params(2, 3, 96, 1, 1, float("inf"), 0, 0, 96, 96)) == EINVAL     # T infinite
+    assert call(Params(2, 3, (1 << 20) + 8, 1, 1, 1.0, 0, 0, 96, (1 << 20) + 8)) == EUNSUP
+    assert call(Params(2, 3, 96, 1, 1, 1.0, 0, 0, 96, 90)) == EINVAL              # stride below V
+    assert call(Params(2, 3, 96, 1, 1, 1.0, 0, 0, 96, 96), tok=nul) == EINVAL
+    assert call(Params(2, 3, 96, 1, 1, 1.0, 0, 0, 96, 96), conf=nul) == EINVAL
+    assert call(Params(0, 3, 96, 1, 1, 1.0, 0, 0, 96, 96)) == 0                   # nothing to draw
+    assert call(Params(2, 3, 96, 1, 1, 0.0, 0, 0, 96, 96)) == EWS                 # greedy, no workspace
