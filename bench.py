@@ -6,9 +6,10 @@ A step is one sv_verify_batch call over the DFly block workload (B=64 requests, 
 16 drafts, V=131072, bfloat16 logits, T=0.9): temperature softmax of both rows, alpha,
 accept test, first-reject scan and correction/bonus draw, all in the HIP kernels.  Inputs
 are resident in HBM before timing starts and rotate through two copies (1.1 GB > 2x the
-256 MB Infinity Cache) so every step reads from HBM.  --workload mtp | budget | e2e measure
-the other workloads (MTP chat verify, budget allocation + ragged verify, the L_e2e objective)
-the same way.
+256 MB Infinity Cache) so every step reads from HBM.  --workload mtp | budget | e2e | e2e_bwd
+| sample measure the other workloads (MTP chat verify, budget allocation + ragged verify, the
+L_e2e objective and its gradient in the drafter logits, draft tokens and confidences) the
+same way.
 
 Prints one JSON line (rank 0).  `value` is verified draft positions per second.  The
 `roofline` object divides the algorithmic bytes of one launch (2 * V * 2 bytes per
@@ -132,6 +133,32 @@ def cpu_baseline_e2e(target, draft, T, n_i=256):
                       f"{dt:.1f} s single-threaded"}
 
 
+def cpu_baseline_e2e_bwd(target, draft, T, n_i=64):
+    """The oracle's L_e2e gradient on the first n_i sequences (all D depths), single thread."""
+    import workloads
+    from oracle import svref
+
+    tn, dn = workloads.to_oracle(target[:n_i]), workloads.to_oracle(draft[:n_i])
+    D = target.shape[1]
+    dt = _oracle_time(lambda: svref.tv_e2e_backward(tn, dn, T, "bf16"))
+    return {"value": n_i * D / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n_i} of {target.shape[0]} sequences x D={D}, V={target.shape[2]}, "
+                      f"{dt:.1f} s single-threaded"}
+
+
+def cpu_baseline_sample(draft, T, seed, n_rows=256):
+    """The oracle's draft sampling on the first n_rows drafter rows, single thread."""
+    import workloads
+    from oracle import svref
+
+    B, K, V = draft.shape
+    nb = max(1, n_rows // K)
+    dn = workloads.to_oracle(draft[:nb])
+    dt = _oracle_time(lambda: svref.sample_drafts(dn, T, "bf16", seed=seed))
+    return {"value": nb * K / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {nb} of {B} requests x {K} drafter rows, V={V}, {dt:.1f} s single-threaded"}
+
+
 class Timed:
     """Times `step(i)` over n launches with HIP events on the launch stream."""
 
@@ -140,6 +167,7 @@ class Timed:
 
     def run(self, step, warmup, n):
         torch = self.torch
+        self.warmup = warmup
         for i in range(warmup):
             step(i)
         torch.cuda.synchronize()
@@ -258,14 +286,69 @@ def bench_e2e(args, sv, workloads, torch):
                 extra={"loss": float(state["loss"].item()), "alpha_mean": round(float(alpha.mean()), 4)})
 
 
+def bench_e2e_bwd(args, sv, workloads, torch):
+    """sv_tv_e2e_backward on the L_e2e set (alpha from one untimed forward), bf16 gradient."""
+    dev = "cuda"
+    target, draft, T = workloads.make_e2e_inputs(device=dev)
+    I, D, V = target.shape
+    ws = sv.Workspace(dev).get(I, D, V)
+    loss, alpha = sv.sv_tv_e2e_loss(target, draft, T, workspace=ws)
+    grad = torch.empty((I, D, V), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        sv.sv_tv_e2e_backward(target, draft, alpha, T, grad=grad, workspace=ws)
+
+    tm = Timed(torch, torch.cuda.current_stream()).run(step, min(args.warmup, 3), min(args.steps, 10))
+    npos = I * D
+    alg_bytes = npos * V * (2 + 2 + 2)   # read both logit rows, write the gradient row (bf16)
+    cpu = None if args.no_cpu_baseline else cpu_baseline_e2e_bwd(target, draft, T)
+    gs = grad[:64].float()
+    return dict(positions=npos, tm=tm, alg_bytes=alg_bytes, achieved=alg_bytes / tm.avg_launch_s / 1e9, cpu=cpu,
+                key="e2e_backward",
+                config={"workload": f"L_e2e gradient in the drafter logits: |I|={I} x D={D}, V={V}, bf16 logits "
+                                    f"and gradient, T={T} ({alg_bytes / 1e9:.1f} GB moved per call)",
+                        "I": I, "D": D, "V": V, "T": T},
+                extra={"loss": float(loss.item()), "grad_abs_mean_first64": float(gs.abs().mean()),
+                       "grad_row_sum_max_first64": float(gs.sum(-1).abs().max())})
+
+
+def bench_sample(args, sv, workloads, torch):
+    """sv_sample_drafts over the DFly drafter rows (B=64 x 16, V=131072, bf16)."""
+    dev = "cuda"
+    T = 0.9 if args.mode == "stoch" else 0.0
+    base = workloads.make_verify_inputs("dfly", device=dev, T=T)
+    B, K, V = base.draft.shape
+    ncopy = args.copies if args.copies else 2
+    copies = [base.draft] + [base.draft.clone() for _ in range(ncopy - 1)]
+    ws = sv.Workspace(dev).get(B, K, V)
+    state = {}
+
+    def step(i):
+        state["tok"], state["conf"] = sv.sv_sample_drafts(copies[i % len(copies)], T, seed=base.seed, step=i,
+                                                          workspace=ws)
+
+    tm = Timed(torch, torch.cuda.current_stream()).run(step, args.warmup, args.steps)
+    npos = B * K
+    alg_bytes = npos * V * 2
+    cpu = None if args.no_cpu_baseline else cpu_baseline_sample(base.draft, T, base.seed)
+    mode = "T=0.9 stochastic" if T > 0 else "T=0 greedy"
+    return dict(positions=npos, tm=tm, alg_bytes=alg_bytes, achieved=alg_bytes / tm.avg_launch_s / 1e9, cpu=cpu,
+                key=f"sample_{args.mode}",
+                config={"workload": f"draft tokens and confidences: B={B} requests x {K} drafter rows, V={V}, "
+                                    f"bf16 logits, {mode}; cache-cold ({ncopy} rotating input copies)",
+                        "B": B, "K": K, "V": V, "T": T},
+                extra={"conf_mean": round(float(state["conf"].mean()), 4)})
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--mode", choices=["stoch", "greedy"], default="stoch")
-    ap.add_argument("--workload", choices=["dfly", "mtp", "budget", "e2e"], default="dfly",
-                    help="dfly (default: the headline line), mtp, budget (allocation + ragged verify) or e2e")
+    ap.add_argument("--workload", choices=["dfly", "mtp", "budget", "e2e", "e2e_bwd", "sample"], default="dfly",
+                    help="dfly (default: the headline line), mtp, budget (allocation + ragged verify), e2e "
+                         "(L_e2e forward), e2e_bwd (its gradient) or sample (draft tokens and confidences)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copies", type=int, default=0, help="rotating input copies (0: per-workload default)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -293,6 +376,10 @@ def main():
 
     if args.workload == "e2e":
         r = bench_e2e(args, sv, workloads, torch)
+    elif args.workload == "e2e_bwd":
+        r = bench_e2e_bwd(args, sv, workloads, torch)
+    elif args.workload == "sample":
+        r = bench_sample(args, sv, workloads, torch)
     else:
         r = bench_verify(args, sv, workloads, torch, args.workload)
     tm = r["tm"]
@@ -304,7 +391,7 @@ def main():
         "unit": "positions/s",
         "n_gpus": 1,
         "steps": n,
-        "warmup": args.warmup,
+        "warmup": tm.warmup,
         "ms_per_step": tm.total_ms / n,
         "higher_is_better": True,
         "scaling": "weak",

@@ -369,10 +369,11 @@ __device__ inline int load_tagged(const uint64_t *p, int n, uint32_t tag, uint32
 // kTeamSeg-logit wave range) pick the range; the workgroup re-reads that range and scans
 // it in binary64.
 // The total R of the range masses is summed in binary64 in range order and the target is
-// u * R; -1 when every mass is zero.
+// u * R; -1 when every mass is zero.  w_sel (LDS, optional, set beforehand by the caller):
+// receives the weight of the token drawn.
 template <int DTT, int DTD, bool RESID>
 __device__ int draw_ranges(const void *trow, const void *drow, int V, float c, Norm2 nt, Norm2 nd,
-                           const float *dirv, int nseg, float u, TeamRed &red) {
+                           const float *dirv, int nseg, float u, TeamRed &red, float *w_sel = nullptr) {
     __shared__ int s_seg;
     __shared__ double s_ex;
     __shared__ double s_scan[kTeamThreads];
@@ -468,6 +469,11 @@ __device__ int draw_ranges(const void *trow, const void *drow, int V, float c, N
         }
         __syncthreads();
         tok = s_tok;
+    }
+    if (w_sel) {   // the weight of the token drawn, from the thread that holds it (w_sel: LDS)
+#pragma unroll
+        for (int e = 0; e < kPer; ++e)
+            if (e0 + e == tok) *w_sel = wt[e];
     }
     __syncthreads();
     return tok;

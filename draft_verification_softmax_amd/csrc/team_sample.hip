@@ -14,8 +14,8 @@
 //                       maximum and its first index, and the chunk's (M, s) at T = 1.
 // sample_finalize_kernel one workgroup per row: merges the published words in member order,
 //                       picks the range holding u R and re-reads it (the same inverse-CDF
-//                       draw as the bonus token of verification), then the confidence from the
-//                       row normaliser.  The last workgroup advances the call epoch.
+//                       draw as the bonus token of verification); the confidence is the drawn
+//                       token's weight.  The last workgroup advances the call epoch.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -98,6 +98,7 @@ __global__ __launch_bounds__(kTeamThreads) void sample_finalize_kernel(TeamArgs 
     __shared__ uint32_t pay[8 * 64 + 8];        // 4S <= 256 published words, then nseg <= 256
     __shared__ float s_mass[4 * 64 + 8];
     __shared__ Norm2 s_n;
+    __shared__ float s_conf;
     const int S = a.S;
     const int nseg = a.nseg;
     const int64_t row = blockIdx.x;
@@ -112,6 +113,7 @@ __global__ __launch_bounds__(kTeamThreads) void sample_finalize_kernel(TeamArgs 
         else got = wave_poll(part, S, tag, pay, 0) && wave_poll(a.dir + row * nseg, nseg, tag, pay + S, 0);
         if (!got && threadIdx.x == 0) atomicOr(a.err, SV_DEVERR_TIMEOUT);
     }
+    if (threadIdx.x == 0) s_conf = 0.f;
     __syncthreads();
     float cf = 0.f;
     int tok = 0;
@@ -146,9 +148,10 @@ __global__ __launch_bounds__(kTeamThreads) void sample_finalize_kernel(TeamArgs 
         }
         __syncthreads();
         const float u = uniform24(a.seed, (uint64_t)r, (uint64_t)k, kPurposeDraft, a.step);
-        tok = draw_ranges<DT, DT, false>(drow, nullptr, a.V, a.c, nb, Norm2{0.f, 0.f}, s_mass, nseg, u, red);
+        // the confidence is the weight of the token drawn, from the thread that holds it
+        tok = draw_ranges<DT, DT, false>(drow, nullptr, a.V, a.c, nb, Norm2{0.f, 0.f}, s_mass, nseg, u, red, &s_conf);
         if (tok < 0) tok = 0;
-        if (threadIdx.x == 0) cf = exp2_fast(log2prob(load1<DT>(drow, tok), a.c, nb));
+        cf = s_conf;
     }
     if (threadIdx.x == 0) {
         tokens[row] = tok;
