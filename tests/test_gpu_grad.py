@@ -136,6 +136,21 @@ def test_backward_workspace_reuse(sv):
     assert sv.sv_device_error(buf) == 0
 
 
+def test_backward_low_temperature(sv):
+    """T = 0.02: base-2 normalisers of several hundred (kept as hi + lo); most of q lies below
+    the binary32 normal range, where the floor of the comparison applies."""
+    I, D, V, T = 3, 4, 40000, 0.02
+    t, d = _inputs(I, D, V, torch.bfloat16, torch.bfloat16, seed=12)
+    og, oa, oloss, lr = _oracle(t, d, T)
+    _say(f"backward low temperature I={I} D={D} V={V} T={T}")
+    loss, alpha = sv.sv_tv_e2e_loss(t, d, T)
+    g = sv.sv_tv_e2e_backward(t, d, alpha, T, grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(alpha.cpu().numpy(), oa, rtol=1e-5)
+    rep = compare_grad(g.cpu().numpy(), og, lr, rtol=D * 1e-5)
+    _say(f"report {rep}")
+
+
 def test_backward_full_size_sampled(sv):
     """|I| = 8192, D = 3, V = 131072, bfloat16 logits and gradient (the benchmarked launch),
     forward alpha from the GPU; four sequences recomputed by the oracle, whose per-sequence
