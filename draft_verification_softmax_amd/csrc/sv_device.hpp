@@ -157,6 +157,17 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
+__device__ __forceinline__ float wave_max(float x) {
+    sched_fence();
+    x = fmaxf(x, dpp_f<0xB1>(x));
+    x = fmaxf(x, dpp_f<0x4E>(x));
+    x = fmaxf(x, dpp_f<0x141>(x));
+    x = fmaxf(x, dpp_f<0x140>(x));
+    x = fmaxf(fmaxf(readlane_f(x, 0), readlane_f(x, 16)), fmaxf(readlane_f(x, 32), readlane_f(x, 48)));
+    sched_fence();
+    return x;
+}
+
 template <int CTRL>
 __device__ __forceinline__ void lse_step(float &m, float &s, float c) {
     const float m2 = dpp_f<CTRL>(m), s2 = dpp_f<CTRL>(s);

@@ -75,17 +75,32 @@ struct TeamRed {
 // (M, s) pairs in base 2: s = sum 2^{x - M}
 __device__ __forceinline__ void ms_merge(float &M, float &s, float M2, float s2) { lse_merge(M, s, M2, s2, 1.0f); }
 
+// (M, s) pairs whose references differ from lane to lane
 __device__ __forceinline__ void wave_ms(float &M, float &s) { wave_lse(M, s, 1.0f); }
 
-__device__ inline void block_ms2(float &Mt, float &st, float &Md, float &sd, TeamRed &red) {
-    wave_ms(Mt, st);
-    wave_ms(Md, sd);
+// The four waves' (M, s) of both rows merged in wave order, into every thread.
+__device__ inline void block_merge2(float &Mt, float &st, float &Md, float &sd, TeamRed &red) {
     const int w = threadIdx.x / kWave;
     if (lane_id() == 0) { red.f[0][w] = Mt; red.f[1][w] = st; red.f[2][w] = Md; red.f[3][w] = sd; }
     __syncthreads();
     Mt = red.f[0][0]; st = red.f[1][0]; Md = red.f[2][0]; sd = red.f[3][0];
     for (int q = 1; q < kTeamWaves; ++q) { ms_merge(Mt, st, red.f[0][q], red.f[1][q]); ms_merge(Md, sd, red.f[2][q], red.f[3][q]); }
     __syncthreads();
+}
+
+// Workgroup (M, s) of both rows from lane states whose reference M is uniform across each
+// wave: the lane sums add up without rescaling.
+__device__ inline void block_ms2(float &Mt, float &st, float &Md, float &sd, TeamRed &red) {
+    st = wave_sum(st);
+    sd = wave_sum(sd);
+    block_merge2(Mt, st, Md, sd, red);
+}
+
+// The same from lane states with a reference per lane.
+__device__ inline void block_ms2_lanes(float &Mt, float &st, float &Md, float &sd, TeamRed &red) {
+    wave_ms(Mt, st);
+    wave_ms(Md, sd);
+    block_merge2(Mt, st, Md, sd, red);
 }
 
 __device__ inline void block_amax2(float &vt, int &it, float &vd, int &id, TeamRed &red) {
@@ -203,17 +218,19 @@ struct LaneRow {
     }
 
     // (M, s) of this lane's logits in base 2 (s = sum_i 2^{x_i c - M}) without a pass for
-    // the maximum: the reference M is c times the largest of the first 8 logits.  Should a
-    // later logit lie so far above it that the sum leaves range (or the first 8 be -inf),
-    // the exact maximum is taken instead.
+    // the maximum.  The reference M is the same for the whole wave, c times the largest of
+    // the lanes' first 8 logits, so the wave's sums add up without rescaling.  Should a
+    // logit lie so far above it that some lane's sum leaves range (or every first 8 be
+    // -inf), the wave takes its exact maximum instead.  Every lane of the wave must call it.
     __device__ __forceinline__ void lane_ms(float c, float &M, float &s) {
         refresh8(0);
         const float m8 = fmaxf(fmaxf(fmaxf(get(0), get(1)), fmaxf(get(2), get(3))),
                                fmaxf(fmaxf(get(4), get(5)), fmaxf(get(6), get(7))));
-        M = m8 * c;
-        s = exp_sum(c, M);
-        if (!(s < 0x1p100f)) {
-            const float m = max();
+        const float mw = wave_max(m8);
+        M = (mw == neg_inf()) ? neg_inf() : mw * c;
+        s = (mw == neg_inf()) ? 0.f : exp_sum(c, M);
+        if (__ballot(mw == neg_inf() || !(s < 0x1p100f))) {   // wave-uniform
+            const float m = wave_max(max());
             M = (m == neg_inf()) ? neg_inf() : m * c;
             s = (m == neg_inf()) ? 0.f : exp_sum(c, M);
         }
@@ -293,13 +310,17 @@ __device__ __forceinline__ float min_sum(LaneRow<DTT> &t, LaneRow<DTD> &d, float
     return split ? (a0 + a1) * exp2_fast(-nt.lo) : a0 + a1;
 }
 
-// Pass 1 of a lane: base-2 log-sum-exp state (M = max * c, s = sum 2^{x c - M}) per row.
+// Pass 1 of a lane: base-2 log-sum-exp state (M, s = sum 2^{x c - M}) per row, M uniform
+// across the wave.
 struct ThreadStats {
     float Mt, st, Md, sd;
 };
 
+// From the lane maxima mt, md: the wave's maxima are the references.
 template <int DTT, int DTD>
 __device__ __forceinline__ ThreadStats pass1(LaneRow<DTT> &t, LaneRow<DTD> &d, float mt, float md, float c) {
+    mt = wave_max(mt);
+    md = wave_max(md);
     ThreadStats s;
     s.Mt = (mt == neg_inf()) ? neg_inf() : mt * c;
     s.Md = (md == neg_inf()) ? neg_inf() : md * c;
@@ -481,8 +502,8 @@ __device__ int draw_ranges(const void *trow, const void *drow, int V, float c, N
 
 }  // namespace
 
-// Phase 1 of a row: the workgroup merges its lanes' (M, s) states of both rows and thread 0
-// publishes the member's partials.
+// Phase 1 of a row: the workgroup merges its lanes' (M, s) states of both rows (references
+// uniform across each wave) and thread 0 publishes the member's partials.
 __device__ __forceinline__ void publish_partials(uint64_t *part, int S, int j, const ThreadStats &ts, uint32_t tag,
                                                  TeamRed &red) {
     float Mt = ts.Mt, st = ts.st, Md = ts.Md, sd = ts.sd;

@@ -84,7 +84,7 @@ __device__ int draw_from_row(const void *row, int V, float c, float u, float *se
         }
     }
     float Md = neg_inf(), sd = 0.f;
-    block_ms2(M, s, Md, sd, red);
+    block_ms2_lanes(M, s, Md, sd, red);
     const Norm2 nb = norm2(M, log2f(s));
     __threadfence_block();
     __syncthreads();
@@ -326,7 +326,7 @@ __device__ __forceinline__ void bonus_member(const TeamArgs &a, int j, int64_t r
         // wave maximum), so the finalize needs one directory word per range
         float M, sm;
         br.lane_ms(c, M, sm);
-        wave_ms(M, sm);
+        sm = wave_sum(sm);   // M is the wave's
         if (lane_id() == 0) red.f[0][w] = M;
         __syncthreads();
         float Mj = red.f[0][0];

@@ -54,9 +54,10 @@ __device__ __forceinline__ void sample_member(const TeamArgs &a, int j, int64_t 
         float fm = wm, fz = neg_inf();
         int iz = 0x7fffffff;
         block_amax2(fm, im, fz, iz, red);   // its lowest index
-        // (M, s) at T = 1 against the lane maximum, for the confidence
-        float M = (m == neg_inf()) ? neg_inf() : m * kLog2eF;
-        float s = (m == neg_inf()) ? 0.f : dr.exp_sum(kLog2eF, M);
+        // (M, s) at T = 1 against the wave maximum, for the confidence
+        const float mw = wave_max(m);
+        float M = (mw == neg_inf()) ? neg_inf() : mw * kLog2eF;
+        float s = (mw == neg_inf()) ? 0.f : dr.exp_sum(kLog2eF, M);
         float Mz = neg_inf(), sz = 0.f;
         block_ms2(M, s, Mz, sz, red);
         if (threadIdx.x == 0) {
@@ -68,7 +69,7 @@ __device__ __forceinline__ void sample_member(const TeamArgs &a, int j, int64_t 
     } else {
         float M, sm;
         dr.lane_ms(a.c, M, sm);
-        wave_ms(M, sm);
+        sm = wave_sum(sm);   // M is the wave's
         if (lane_id() == 0) red.f[0][w] = M;
         __syncthreads();
         float Mj = red.f[0][0];
