@@ -46,7 +46,7 @@ __device__ inline bool wave_poll(const uint64_t *p, int n, uint32_t tag, uint32_
         }
         if (__all(missing == 0)) return true;
         if ((int64_t)(wall_clock64() - t0) > limit) return false;
-        __builtin_amdgcn_s_sleep(1);
+        __builtin_amdgcn_s_sleep(4);   // ~256 cycles between sweeps
     }
 }
 
@@ -506,13 +506,20 @@ __device__ int draw_ranges(const void *trow, const void *drow, int V, float c, N
 // uniform across each wave) and thread 0 publishes the member's partials.
 __device__ __forceinline__ void publish_partials(uint64_t *part, int S, int j, const ThreadStats &ts, uint32_t tag,
                                                  TeamRed &red) {
-    float Mt = ts.Mt, st = ts.st, Md = ts.Md, sd = ts.sd;
-    block_ms2(Mt, st, Md, sd, red);
-    if (threadIdx.x == 0) {
+    const float st = wave_sum(ts.st), sd = wave_sum(ts.sd);
+    const int w = threadIdx.x / kWave;
+    if (lane_id() == 0) { red.f[0][w] = ts.Mt; red.f[1][w] = st; red.f[2][w] = ts.Md; red.f[3][w] = sd; }
+    __syncthreads();
+    if (threadIdx.x == 0) {   // only the publisher needs the merged values
+        float Mt = red.f[0][0], Tt = red.f[1][0], Md = red.f[2][0], Dd = red.f[3][0];
+        for (int q = 1; q < kTeamWaves; ++q) {
+            ms_merge(Mt, Tt, red.f[0][q], red.f[1][q]);
+            ms_merge(Md, Dd, red.f[2][q], red.f[3][q]);
+        }
         putf(part + 0 * S + j, Mt, tag);
-        putf(part + 1 * S + j, st, tag);
+        putf(part + 1 * S + j, Tt, tag);
         putf(part + 2 * S + j, Md, tag);
-        putf(part + 3 * S + j, sd, tag);
+        putf(part + 3 * S + j, Dd, tag);
     }
 }
 
