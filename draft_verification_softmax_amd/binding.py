@@ -17,8 +17,8 @@ _STATUS = {0: "SV_OK", 1: "SV_EINVAL", 2: "SV_EUNSUPPORTED", 3: "SV_EHIP", 4: "S
 
 EXPORTS = [
     "sv_workspace_bytes", "sv_workspace_init", "sv_verify_batch", "sv_verify_selected", "sv_accept_len",
-    "sv_residual_sample", "sv_tv_e2e_loss", "sv_tv_e2e_backward", "sv_sample_drafts", "sv_alloc_verify_budget", "sv_dcut_verify_budget", "sv_uniforms",
-    "sv_device_error", "sv_status_string",
+    "sv_residual_sample", "sv_tv_e2e_loss", "sv_tv_e2e_backward", "sv_sample_drafts", "sv_alloc_verify_budget",
+    "sv_dcut_verify_budget", "sv_uniforms", "sv_device_error", "sv_status_string", "sv_set_wait_bound",
 ]
 
 
@@ -66,6 +66,7 @@ def lib():
         L.sv_dcut_verify_budget.argtypes = [vp, vp, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp]
         L.sv_uniforms.argtypes = [u64, vp, i32, vp, vp]
         L.sv_device_error.argtypes = [vp, vp, C.POINTER(C.c_uint32)]
+        L.sv_set_wait_bound.argtypes = [C.c_int64]
         L.sv_status_string.argtypes = [C.c_int]
         L.sv_status_string.restype = C.c_char_p
         for name in EXPORTS:
@@ -73,6 +74,11 @@ def lib():
                 getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
+
+
+def sv_set_wait_bound(ns: int):
+    """Bound (ns) of the in-kernel wait for teammates' partials; 0 forces every hand-over."""
+    _check("sv_set_wait_bound", lib().sv_set_wait_bound(int(ns)))
 
 
 def sv_status_string(code: int) -> str:

@@ -571,6 +571,9 @@ struct ResidualLauncher {
 
 const double kLog2e = 1.4426950408889634;
 
+// Bound of a member's wait for its teammates' partials, in 10-ns ticks (sv_set_wait_bound).
+int64_t g_wait_ticks = 20000;   // 200 us
+
 void fill_team_args(TeamArgs &a, const sv_params *p, const TeamLayout &L, char *ws) {
     a.err = (uint32_t *)(ws + L.off_err);
     a.epoch = (uint32_t *)(ws + L.off_epoch);
@@ -591,7 +594,7 @@ void fill_team_args(TeamArgs &a, const sv_params *p, const TeamLayout &L, char *
     a.c = p->temperature > 0.f ? (float)(kLog2e / (double)p->temperature) : 0.f;
     a.seed = p->seed;
     a.step = p->step;
-    a.spin_ticks = 20000;  // 200 us: then a member hands its share to the finalize kernel
+    a.spin_ticks = g_wait_ticks;  // then a member hands its share over (to the finalize kernel)
     a.rows = L.rows;
 }
 
@@ -602,6 +605,12 @@ extern "C" {
 size_t sv_workspace_bytes(int32_t B, int32_t K_max, int32_t V) {
     if (B < 0 || K_max < 0 || V <= 0) return 0;
     return team_layout(B, K_max + 1, V).total;   // K_max + 1 slots also cover L_e2e with D = K_max
+}
+
+int sv_set_wait_bound(int64_t ns) {
+    if (ns < 0) return SV_EINVAL;
+    g_wait_ticks = ns / 10;
+    return SV_OK;
 }
 
 int sv_workspace_init(void *workspace, size_t workspace_bytes, void *stream) {

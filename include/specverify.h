@@ -87,6 +87,15 @@ typedef struct sv_params {
  * that share a workspace must not overlap (same stream, or ordered by events). */
 size_t sv_workspace_bytes(int32_t B, int32_t K_max, int32_t V);
 
+/* Bound, in nanoseconds, of the wait inside a verification, L_e2e or gradient launch for the
+ * partial results of the other workgroups that share a row (default 200000).  A workgroup
+ * that reaches it hands its share over: a later kernel of the same call recomputes it from
+ * the logits, so results do not depend on the bound; only time does.  0 makes every
+ * workgroup hand over at once unless its partners have already published (for tests of the
+ * hand-over path).  Applies to calls issued after it returns; it is process-wide and not
+ * synchronised with calls being issued from other host threads.  Errors: SV_EINVAL (ns < 0). */
+int sv_set_wait_bound(int64_t ns);
+
 /* Zero-fill a workspace (a fill kernel on `stream`; no host synchronisation). */
 int sv_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
 

@@ -158,3 +158,9 @@ def test_sample_drafts_host_validation(svlib):
     assert call(Params(2, 3, 96, 1, 1, 1.0, 0, 0, 96, 96), conf=nul) == EINVAL
     assert call(Params(0, 3, 96, 1, 1, 1.0, 0, 0, 96, 96)) == 0                   # nothing to draw
     assert call(Params(2, 3, 96, 1, 1, 0.0, 0, 0, 96, 96)) == EWS                 # greedy, no workspace
+
+
+def test_wait_bound_validation(svlib):
+    assert svlib.sv_set_wait_bound(-1) == 1
+    assert svlib.sv_set_wait_bound(0) == 0
+    assert svlib.sv_set_wait_bound(200000) == 0   # back to the default
