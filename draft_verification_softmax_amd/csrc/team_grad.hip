@@ -137,7 +137,7 @@ __device__ __forceinline__ void grad_member(const TeamArgs &a, const GradArgs &g
     sched_fence();
     const uint32_t tag = epoch + 1;
 
-    // ---- round 1: the row normalisers ----
+    // ---- first exchange: the row normalisers ----
     ThreadStats ts;
     tr.lane_ms(c, ts.Mt, ts.st);
     dr.lane_ms(c, ts.Md, ts.sd);
@@ -156,7 +156,7 @@ __device__ __forceinline__ void grad_member(const TeamArgs &a, const GradArgs &g
     }
     const Norm2 nt = s_tot[0], nd = s_tot[1];
 
-    // ---- round 2: beta ----
+    // ---- second exchange: beta ----
     const float b = block_sumf(beta_sum(tr, dr, c, nt, nd), red);
     if (threadIdx.x == 0) putf(a.apart + row * S + j, b, tag);
     if (threadIdx.x < kWave) {
