@@ -578,6 +578,7 @@ void fill_team_args(TeamArgs &a, const sv_params *p, const TeamLayout &L, char *
     a.err = (uint32_t *)(ws + L.off_err);
     a.epoch = (uint32_t *)(ws + L.off_epoch);
     a.gdone = (int32_t *)(ws + L.off_gdone);
+    a.arrive = (int32_t *)(ws + L.off_arrive);
     a.part = (uint64_t *)(ws + L.off_part);
     a.apart = (uint64_t *)(ws + L.off_apart);
     a.dir = (uint64_t *)(ws + L.off_dir);

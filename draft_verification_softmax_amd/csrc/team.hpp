@@ -39,11 +39,13 @@ constexpr int kTeamSeg = 64 * kTeamE;               // one wave's contiguous ran
 constexpr int kBonusSeg = 512;                      // segment of the single-row bonus draw
 constexpr int kXcds = 8;                            // accelerator complex dies of an MI355X
 constexpr int kAccWords = 8;                        // tagged words of a row's accept record
+constexpr int kArriveSlots = 32;                    // first-level arrival counters of a call
+constexpr int kArriveStride = 32;                   // int32 words between them (128 bytes)
 
 enum TeamMode { kTeamStoch = 0, kTeamGreedy = 1, kTeamAlpha = 2 };
 
 struct TeamLayout {
-    size_t off_err, off_epoch, off_gdone;
+    size_t off_err, off_epoch, off_gdone, off_arrive;
     size_t off_part, off_apart, off_dir, off_acc, off_bonus, off_alpha, total;
     int S, nseg, nseg_b;
     int64_t rows;
@@ -66,7 +68,8 @@ struct TeamArgs {
     int32_t *amax_t, *amax_d;
     int32_t *accept_len, *out_tokens, *n_out;
     uint32_t *err, *epoch;
-    int32_t *gdone;
+    int32_t *gdone;    // second-level arrival counter
+    int32_t *arrive;   // [kArriveSlots][kArriveStride] first-level arrival counters
     uint64_t *part;    // [rows][8][S]: M_t, s_t, M_d, s_d, argmax value/index of both rows;
                        // bonus slots: the member's base-2 reference (stochastic)
     // dir of a bonus slot: per wave range, sum 2^{z c - M_member}

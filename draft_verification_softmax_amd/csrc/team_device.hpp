@@ -54,6 +54,24 @@ __device__ __forceinline__ uint32_t read_epoch(const uint32_t *e) {
     return __hip_atomic_load(const_cast<uint32_t *>(e), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Arrival of unit i of n (one call of one thread per unit) at the end of a call; true for
+// exactly one unit, whose arrival completes the call.  Units land on kArriveSlots counters (i
+// modulo the slot count); the arrival that fills a slot moves on to the single second-level
+// counter.  So at most about n / kArriveSlots + kArriveSlots returning atomics queue on one
+// address, where one counter for all n would queue n of them; each counter is back at zero
+// once it is full.
+__device__ inline bool last_arrival(const TeamArgs &a, int64_t i, int64_t n) {
+    const int slot = (int)(i % kArriveSlots);
+    const int in_slot = (int)((n - 1 - slot) / kArriveSlots) + 1;   // units i < n on this slot
+    const int slots = (int)(n < kArriveSlots ? n : kArriveSlots);
+    int32_t *c = a.arrive + slot * kArriveStride;
+    if (atomicAdd(c, 1) != in_slot - 1) return false;
+    __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (atomicAdd(a.gdone, 1) != slots - 1) return false;
+    __hip_atomic_store(a.gdone, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+}
+
 // Scalar load of a value that stays constant while the kernel runs (written, if at all, by
 // an earlier kernel on the stream), at a workgroup-uniform address.  It uses the scalar
 // counter, so waiting for it never waits for the vector loads of the chunk.

@@ -278,10 +278,7 @@ __global__ __launch_bounds__(kTeamThreads) void fixup_kernel(TeamArgs a, GradArg
     }
     if (threadIdx.x == 0) {
         // the last workgroup of the call advances the epoch for the next call
-        if (atomicAdd(a.gdone, 1) == (int)gridDim.x - 1) {
-            __hip_atomic_store(a.gdone, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(a.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        if (last_arrival(a, blockIdx.x, gridDim.x)) __hip_atomic_store(a.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

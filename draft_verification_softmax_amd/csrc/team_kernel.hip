@@ -33,7 +33,8 @@ TeamLayout team_layout(int B, int slots, int V, size_t ws_bytes) {
     L.off_err = 0;
     L.off_epoch = 64;
     L.off_gdone = 128;
-    const size_t counters = 256;
+    L.off_arrive = 256;
+    const size_t counters = 256 + sizeof(int32_t) * kArriveSlots * kArriveStride;
     // tagged words and scratch, relative to their own base
     size_t o = 0;
     L.off_part = o;  o = al(o + sizeof(uint64_t) * 8 * (size_t)L.S * (size_t)L.rows);
@@ -720,10 +721,7 @@ __global__ __launch_bounds__(kTeamThreads) void finalize_kernel(TeamArgs a) {
         a.accept_len[r] = tau;
         a.n_out[r] = tau + 1;
         // the last request of the call advances the epoch for the next call
-        if (atomicAdd(a.gdone, 1) == a.B - 1) {
-            __hip_atomic_store(a.gdone, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(a.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        if (last_arrival(a, r, a.B)) __hip_atomic_store(a.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

@@ -12,10 +12,11 @@
 //                       mass of each 4096-logit wave range against the member's reference
 //                       (its largest wave maximum) and that reference; greedy, the chunk's
 //                       maximum and its first index, and the chunk's (M, s) at T = 1.
-// sample_finalize_kernel one workgroup per row: merges the published words in member order,
-//                       picks the range holding u R and re-reads it (the same inverse-CDF
-//                       draw as the bonus token of verification); the confidence is the drawn
-//                       token's weight.  The last workgroup advances the call epoch.
+// sample_finalize_kernel one wave per row: merges the published words in member order, picks
+//                       the range holding u R and re-reads it, 64 consecutive logits per lane
+//                       (the inverse-CDF draw of the verification's bonus token, laid out for
+//                       one wave); the confidence is the drawn token's weight.  The last row
+//                       advances the call epoch.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -93,89 +94,190 @@ __global__ __launch_bounds__(kTeamThreads) void sample_stream_kernel(TeamArgs a)
     else sample_member<DT, GREEDY, false>(a, j, row, red);
 }
 
+namespace {
+
+// Orders this wave's LDS writes before its later LDS reads by other lanes.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+constexpr int kRowsPerFinalize = kTeamThreads / kWave;   // one wave per row
+constexpr int kGatherMax = 5;                             // words per lane: S + nseg <= 5 * 64
+
+// Words p0[0..n0) then p1[0..n1) (n0 + n1 <= kGatherMax * 64), written by an earlier kernel on
+// the stream, to dst[0..n0 + n1) in one pass whose loads all issue before any returns.
+// Returns false (every lane) when any of them lacks the tag.
+__device__ bool wave_gather(const uint64_t *p0, int n0, const uint64_t *p1, int n1, uint32_t tag, uint32_t *dst) {
+    const int lane = lane_id();
+    const int n = n0 + n1;
+    uint64_t w[kGatherMax];
+#pragma unroll
+    for (int b = 0; b < kGatherMax; ++b) {
+        const int i = lane + b * kWave;
+        w[b] = i < n0 ? p0[i] : (i < n ? p1[i - n0] : 0);
+    }
+    bool ok = true;
+#pragma unroll
+    for (int b = 0; b < kGatherMax; ++b) {
+        const int i = lane + b * kWave;
+        if (i < n) {
+            dst[i] = (uint32_t)w[b];
+            ok = ok && (uint32_t)(w[b] >> 32) == tag;
+        }
+    }
+    return __all(ok);
+}
+constexpr int kFinLane = kTeamSeg / kWave;              // logits of a range per lane (64)
+
+// Token of the range sidx of a row at target rem inside the range, by one wave: lane l holds
+// kFinLane consecutive logits; their weights sum in order, the lane sums scan in lane order,
+// and the lane holding the crossing scans its weights.  If rounding runs past the range, the
+// last logit with positive weight.  Returns the token (every lane); *w: its weight.
+template <int DT>
+__device__ int wave_draw_range(const void *row, int V, float c, Norm2 nb, int sidx, double rem, float *w) {
+    const int lane = lane_id();
+    const int e0 = sidx * kTeamSeg + lane * kFinLane;
+    const int vend = min(V, (sidx + 1) * kTeamSeg);
+    float wt[kFinLane];
+    double my = 0.0;
+#pragma unroll
+    for (int e8 = 0; e8 < kFinLane; e8 += 8) {
+        float z[8];
+        load8<DT>(row, e0 + e8, vend, z);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            wt[e8 + e] = exp2_fast(log2prob(z[e], c, nb));
+            my += (double)wt[e8 + e];
+        }
+    }
+    const double incl = wave_incl_scan(my);
+    const uint64_t hit = __ballot(incl > rem && my > 0.0);
+    int tok = -1;
+    float wsel = 0.f;
+    if (hit) {
+        const int l = __builtin_ctzll(hit);
+        if (lane == l) {
+            double run = incl - my;
+            int k = kFinLane - 1;
+            for (int e = 0; e < kFinLane; ++e) {
+                run += (double)wt[e];
+                if (run > rem) { k = e; break; }
+            }
+            tok = e0 + k;
+#pragma unroll
+            for (int e = 0; e < kFinLane; ++e)
+                if (e == k) wsel = wt[e];
+        }
+        tok = __shfl(tok, l, kWave);
+        wsel = __shfl(wsel, l, kWave);
+    } else {
+        // the last logit of the range with positive weight
+        int last = -1;
+        for (int e = kFinLane - 1; e >= 0; --e)
+            if (wt[e] > 0.f) { last = e; break; }
+        const uint64_t pos = __ballot(last >= 0);
+        if (pos) {
+            const int l = 63 - __builtin_clzll(pos);
+            if (lane == l) {
+                tok = e0 + last;
+#pragma unroll
+                for (int e = 0; e < kFinLane; ++e)
+                    if (e == last) wsel = wt[e];
+            }
+            tok = __shfl(tok, l, kWave);
+            wsel = __shfl(wsel, l, kWave);
+        } else {
+            tok = min(sidx * kTeamSeg, V - 1);
+        }
+    }
+    *w = wsel;
+    return tok;
+}
+
+}  // namespace
+
+// One wave per row (kRowsPerFinalize rows per workgroup, no workgroup barrier): merges the
+// row's published words in member order, picks the range holding u R, and re-reads it.
 template <int DT, bool GREEDY>
 __global__ __launch_bounds__(kTeamThreads) void sample_finalize_kernel(TeamArgs a, int32_t *tokens, float *conf) {
-    __shared__ TeamRed red;
-    __shared__ uint32_t pay[8 * 64 + 8];        // 4S <= 256 published words, then nseg <= 256
-    __shared__ float s_mass[4 * 64 + 8];
-    __shared__ Norm2 s_n;
-    __shared__ float s_conf;
+    __shared__ uint32_t pay_all[kRowsPerFinalize][5 * 64 + 8];   // S + nseg <= 320 words, or 4S <= 256
+    __shared__ float mass_all[kRowsPerFinalize][4 * 64 + 8];
+    const int w = threadIdx.x / kWave;
+    const int lane = lane_id();
+    const int64_t row = (int64_t)blockIdx.x * kRowsPerFinalize + w;
+    if (row >= a.rows) return;
+    uint32_t *pay = pay_all[w];
+    float *mass = mass_all[w];
     const int S = a.S;
     const int nseg = a.nseg;
-    const int64_t row = blockIdx.x;
     const int r = (int)(row / a.K), k = (int)(row % a.K);
     const uint32_t tag = read_epoch(a.epoch) + 1;
     const uint64_t *part = a.part + row * (int64_t)(8 * S);
     const void *drow = row_ptr<DT>(a.draft, row, a.ld_d);
     // the stream kernel has completed: every word is there, so one pass reads them
-    if (threadIdx.x < kWave) {
-        bool got;
-        if constexpr (GREEDY) got = wave_poll(part, 2 * S, tag, pay, 0) && wave_poll(part + 4 * S, 2 * S, tag, pay + 2 * S, 0);
-        else got = wave_poll(part, S, tag, pay, 0) && wave_poll(a.dir + row * nseg, nseg, tag, pay + S, 0);
-        if (!got && threadIdx.x == 0) atomicOr(a.err, SV_DEVERR_TIMEOUT);
-    }
-    if (threadIdx.x == 0) s_conf = 0.f;
-    __syncthreads();
-    float cf = 0.f;
+    bool got;
+    if constexpr (GREEDY) got = wave_gather(part, 2 * S, part + 4 * S, 2 * S, tag, pay);
+    else got = wave_gather(part, S, a.dir + row * nseg, nseg, tag, pay);
+    if (!got && lane == 0) atomicOr(a.err, SV_DEVERR_TIMEOUT);
+    wave_sync();
     int tok = 0;
+    float cf = 0.f;
     if constexpr (GREEDY) {
-        if (threadIdx.x == 0) {
-            float bv = neg_inf(), M = neg_inf(), s = 0.f;
-            int bi = 0x7fffffff;
-            for (int m = 0; m < S; ++m) {
-                amax_merge(bv, bi, __uint_as_float(pay[2 * S + m]), (int)pay[3 * S + m]);
-                ms_merge(M, s, __uint_as_float(pay[m]), __uint_as_float(pay[S + m]));
-            }
-            tok = bi == 0x7fffffff ? 0 : bi;
-            cf = exp2_fast(log2prob(load1<DT>(drow, tok), kLog2eF, norm2(M, log2f(s))));
+        float bv = neg_inf(), M = neg_inf(), s = 0.f;
+        int bi = 0x7fffffff;
+        for (int m = 0; m < S; ++m) {   // every lane, the same order
+            amax_merge(bv, bi, __uint_as_float(pay[2 * S + m]), (int)pay[3 * S + m]);
+            ms_merge(M, s, __uint_as_float(pay[m]), __uint_as_float(pay[S + m]));
         }
+        tok = bi == 0x7fffffff ? 0 : bi;
+        cf = exp2_fast(log2prob(load1<DT>(drow, tok), kLog2eF, norm2(M, log2f(s))));
     } else {
         // pay[0..S): member references Mj; pay[S + j * W + w]: range masses against Mj
-        if (threadIdx.x < kWave) {
-            float M = neg_inf(), sm = 0.f;
-            for (int m = threadIdx.x; m < S; m += kWave) {
-                float sj = 0.f;
-                for (int w = 0; w < kTeamWaves; ++w) sj += __uint_as_float(pay[S + m * kTeamWaves + w]);
-                ms_merge(M, sm, __uint_as_float(pay[m]), sj);
-            }
-            wave_ms(M, sm);
-            if (threadIdx.x == 0) s_n = norm2(M, log2f(sm));
+        float M = neg_inf(), sm = 0.f;
+        for (int m = lane; m < S; m += kWave) {
+            float sj = 0.f;
+            for (int q = 0; q < kTeamWaves; ++q) sj += __uint_as_float(pay[S + m * kTeamWaves + q]);
+            ms_merge(M, sm, __uint_as_float(pay[m]), sj);
         }
-        __syncthreads();
-        const Norm2 nb = s_n;
-        for (int q = threadIdx.x; q < nseg; q += kTeamThreads) {
+        wave_ms(M, sm);
+        const Norm2 nb = norm2(M, log2f(sm));
+        double part_sum = 0.0;
+        for (int q = lane; q < nseg; q += kWave) {
             const float Mq = __uint_as_float(pay[q / kTeamWaves]);
-            s_mass[q] = (Mq == neg_inf()) ? 0.f : __uint_as_float(pay[S + q]) * exp2_fast((Mq - nb.hi) - nb.lo);
+            mass[q] = (Mq == neg_inf()) ? 0.f : __uint_as_float(pay[S + q]) * exp2_fast((Mq - nb.hi) - nb.lo);
+            part_sum += (double)mass[q];
         }
-        __syncthreads();
+        wave_sync();
+        // R: lane partials summed in lane order; the range by inverse CDF in range order
+        const double R = __shfl(wave_incl_scan(part_sum), kWave - 1, kWave);
         const float u = uniform24(a.seed, (uint64_t)r, (uint64_t)k, kPurposeDraft, a.step);
-        // the confidence is the weight of the token drawn, from the thread that holds it
-        tok = draw_ranges<DT, DT, false>(drow, nullptr, a.V, a.c, nb, Norm2{0.f, 0.f}, s_mass, nseg, u, red, &s_conf);
-        if (tok < 0) tok = 0;
-        cf = s_conf;
+        const double t = (double)u * R;
+        double ex = 0.0;
+        const int sidx = wave_find([&](int q) { return mass[q]; }, nseg, t, &ex);
+        if (sidx >= 0) tok = wave_draw_range<DT>(drow, a.V, a.c, nb, sidx, t - ex, &cf);
     }
-    if (threadIdx.x == 0) {
+    if (lane == 0) {
         tokens[row] = tok;
         conf[row] = cf;
-        // the last workgroup of the call advances the epoch for the next call
-        if (atomicAdd(a.gdone, 1) == (int)gridDim.x - 1) {
-            __hip_atomic_store(a.gdone, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(a.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        // the last row of the call advances the epoch for the next call
+        if (last_arrival(a, row, a.rows)) __hip_atomic_store(a.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
 template <int DT>
 static hipError_t launch_sample_t(const TeamArgs &a, int32_t *tokens, float *conf, hipStream_t s) {
     const unsigned grid = (unsigned)((uint64_t)a.rows * (uint64_t)a.S);
+    const unsigned fblocks = (unsigned)((a.rows + kRowsPerFinalize - 1) / kRowsPerFinalize);
     if (a.c == 0.f) {
         hipLaunchKernelGGL((sample_stream_kernel<DT, true>), dim3(grid), dim3(kTeamThreads), 0, s, a);
-        hipLaunchKernelGGL((sample_finalize_kernel<DT, true>), dim3((unsigned)a.rows), dim3(kTeamThreads), 0, s, a,
-                           tokens, conf);
+        hipLaunchKernelGGL((sample_finalize_kernel<DT, true>), dim3(fblocks), dim3(kTeamThreads), 0, s, a, tokens,
+                           conf);
     } else {
         hipLaunchKernelGGL((sample_stream_kernel<DT, false>), dim3(grid), dim3(kTeamThreads), 0, s, a);
-        hipLaunchKernelGGL((sample_finalize_kernel<DT, false>), dim3((unsigned)a.rows), dim3(kTeamThreads), 0, s, a,
-                           tokens, conf);
+        hipLaunchKernelGGL((sample_finalize_kernel<DT, false>), dim3(fblocks), dim3(kTeamThreads), 0, s, a, tokens,
+                           conf);
     }
     return hipGetLastError();
 }
