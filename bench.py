@@ -33,8 +33,8 @@ METRIC = "verified draft positions/s + HBM GB/s (% peak), B=64 block16 V=131072 
 def _source_digest():
     h = hashlib.sha256()
     # the sources of the verification kernels (stream + finalize) and their launch code
-    for rel in ["draft_verification_softmax_amd/csrc/sv_device.hpp", "draft_verification_softmax_amd/csrc/team_kernel.hip",
-                "draft_verification_softmax_amd/csrc/team.hpp"]:
+    for rel in ["draft_verification_softmax_amd/csrc/sv_device.hpp", "draft_verification_softmax_amd/csrc/team_device.hpp",
+                "draft_verification_softmax_amd/csrc/team_kernel.hip", "draft_verification_softmax_amd/csrc/team.hpp"]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
