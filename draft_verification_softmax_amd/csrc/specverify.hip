@@ -573,6 +573,7 @@ const double kLog2e = 1.4426950408889634;
 
 // Bound of a member's wait for its teammates' partials, in 10-ns ticks (sv_set_wait_bound).
 int64_t g_wait_ticks = 20000;   // 200 us
+const int64_t kFinalizeWaitTicks = 2000000;   // 20 ms beyond it
 
 void fill_team_args(TeamArgs &a, const sv_params *p, const TeamLayout &L, char *ws) {
     a.err = (uint32_t *)(ws + L.off_err);
@@ -595,7 +596,10 @@ void fill_team_args(TeamArgs &a, const sv_params *p, const TeamLayout &L, char *
     a.c = p->temperature > 0.f ? (float)(kLog2e / (double)p->temperature) : 0.f;
     a.seed = p->seed;
     a.step = p->step;
-    a.spin_ticks = g_wait_ticks;  // then a member hands its share over (to the finalize kernel)
+    a.spin_ticks = g_wait_ticks;  // then a member hands its share over (to the finalize)
+    // A finalize workgroup waits for members that are still running: longer than any member
+    // can take to publish after its own bounded wait.
+    a.fin_ticks = g_wait_ticks + kFinalizeWaitTicks;
     a.rows = L.rows;
 }
 
@@ -646,7 +650,7 @@ static int verify_impl(const sv_params *p, const void *target, const void *draft
     if (!accept_len || !out_tokens || !n_out) return SV_EINVAL;
     const TeamLayout L = team_layout(p->B, p->K_max + 1, p->V, workspace_bytes);
     if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return SV_EWORKSPACE;
-    const uint64_t grid64 = (uint64_t)L.rows * (uint64_t)L.S;
+    const uint64_t grid64 = (uint64_t)L.rows * (uint64_t)L.S + (uint64_t)p->B;
     if (grid64 > 0x7fffffffull) return SV_EINVAL;
 
     TeamArgs a{};
@@ -662,8 +666,7 @@ static int verify_impl(const sv_params *p, const void *target, const void *draft
     a.row_list = row_list;
     a.n_rows = n_rows;
     const int mode = p->temperature == 0.f ? kTeamGreedy : kTeamStoch;
-    hipError_t e = team_launch_stream(a, p->dtype_t, p->dtype_d, mode, (hipStream_t)stream);
-    if (e == hipSuccess) e = team_launch_finalize(a, p->dtype_t, p->dtype_d, mode, (hipStream_t)stream);
+    const hipError_t e = team_launch_stream(a, p->dtype_t, p->dtype_d, mode, (hipStream_t)stream);
     return e == hipSuccess ? SV_OK : SV_EHIP;
 }
 
@@ -738,7 +741,7 @@ int sv_tv_e2e_loss(const sv_params *p, const void *target, const void *draft, fl
     if (st) return st;
     const TeamLayout L = team_layout(p->B, p->K_max, p->V, workspace_bytes);
     if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return SV_EWORKSPACE;
-    const uint64_t grid64 = (uint64_t)L.rows * (uint64_t)L.S;
+    const uint64_t grid64 = (uint64_t)L.rows * (uint64_t)L.S + (uint64_t)p->B;
     if (grid64 > 0x7fffffffull) return SV_EINVAL;
     float *alpha_buf = alpha ? alpha : (float *)((char *)workspace + L.off_alpha);
     TeamArgs a{};
@@ -769,7 +772,7 @@ int sv_tv_e2e_backward(const sv_params *p, const void *target, const void *draft
     if (st) return st;
     const TeamLayout L = team_layout(p->B, p->K_max, p->V, workspace_bytes);
     if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return SV_EWORKSPACE;
-    const uint64_t grid64 = (uint64_t)L.rows * (uint64_t)L.S;
+    const uint64_t grid64 = (uint64_t)L.rows * (uint64_t)L.S + (uint64_t)p->B;
     if (grid64 > 0x7fffffffull) return SV_EINVAL;
     TeamArgs a{};
     fill_team_args(a, p, L, (char *)workspace);
@@ -798,7 +801,7 @@ int sv_sample_drafts(const sv_params *p, const void *draft, int32_t *tokens, flo
     if (!tokens || !conf) return SV_EINVAL;
     const TeamLayout L = team_layout(p->B, p->K_max, p->V, workspace_bytes);
     if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return SV_EWORKSPACE;
-    const uint64_t grid64 = (uint64_t)L.rows * (uint64_t)L.S;
+    const uint64_t grid64 = (uint64_t)L.rows * (uint64_t)L.S + (uint64_t)p->B;
     if (grid64 > 0x7fffffffull) return SV_EINVAL;
     TeamArgs a{};
     fill_team_args(a, p, L, (char *)workspace);

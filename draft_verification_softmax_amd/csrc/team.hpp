@@ -19,10 +19,12 @@
 // and publish per-wave-range masses against a per-member reference (argmax in greedy
 // mode) without waiting.
 //
-// Finalize kernel (one workgroup per request, after the stream kernel): sums the shares
-// in member order, recomputes handed-over shares from HBM, and runs the first-reject scan
-// and the correction / bonus draw (one range of the row re-read, found by inverse CDF
-// over the published per-range masses).
+// Finalize (verification: the last B workgroups of the same grid, one per request,
+// dispatched after every member): gathers its rows' tagged words as they are published
+// (bounded wait), sums the shares in member order, recomputes handed-over shares from HBM,
+// and runs the first-reject scan and the correction / bonus draw (one range of the row
+// re-read, found by inverse CDF over the published per-range masses), beside the tail of
+// the grid rather than after it.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -39,6 +41,7 @@ constexpr int kTeamSeg = 64 * kTeamE;               // one wave's contiguous ran
 constexpr int kBonusSeg = 512;                      // segment of the single-row bonus draw
 constexpr int kXcds = 8;                            // accelerator complex dies of an MI355X
 constexpr int kAccWords = 8;                        // tagged words of a row's accept record
+constexpr int kArriveSingle = 256;                  // calls of this many units arrive on one counter
 constexpr int kArriveSlots = 32;                    // first-level arrival counters of a call
 constexpr int kArriveStride = 32;                   // int32 words between them (128 bytes)
 
@@ -90,11 +93,13 @@ struct TeamArgs {
     const int32_t *row_list;  //    (0: every row k < L_r)
     int32_t n_rows;
     int64_t spin_ticks;  // bounded wait for teammates' partials (10 ns ticks)
+    int64_t fin_ticks;   // bounded wait of a finalize workgroup for its request's words
 };
 
-// Grid sizes are derived from a (rows * S workgroups at most; the caller checks they fit).
+// Grid sizes are derived from a (rows * S + B workgroups at most; the caller checks they fit).
+// Verification (kTeamStoch, kTeamGreedy) launches the whole call: members, bonus slots and
+// the B finalize workgroups.  kTeamAlpha launches the members of the L_e2e rows only.
 hipError_t team_launch_stream(const TeamArgs &a, int dtype_t, int dtype_d, int mode, hipStream_t s);
-hipError_t team_launch_finalize(const TeamArgs &a, int dtype_t, int dtype_d, int mode, hipStream_t s);
 // L_e2e: alpha per row from the shares (one thread per row).
 hipError_t team_launch_e2e_alpha(const TeamArgs &a, int dtype_t, int dtype_d, hipStream_t s);
 

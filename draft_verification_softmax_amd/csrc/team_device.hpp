@@ -55,12 +55,17 @@ __device__ __forceinline__ uint32_t read_epoch(const uint32_t *e) {
 }
 
 // Arrival of unit i of n (one call of one thread per unit) at the end of a call; true for
-// exactly one unit, whose arrival completes the call.  Units land on kArriveSlots counters (i
-// modulo the slot count); the arrival that fills a slot moves on to the single second-level
-// counter.  So at most about n / kArriveSlots + kArriveSlots returning atomics queue on one
-// address, where one counter for all n would queue n of them; each counter is back at zero
-// once it is full.
+// exactly one unit, whose arrival completes the call.  Up to kArriveSingle units share the
+// second-level counter directly (one returning atomic on the last unit's path).  More land on
+// kArriveSlots counters (i modulo the slot count) and the arrival that fills a slot moves on
+// to the second-level counter, so at most about n / kArriveSlots + kArriveSlots returning
+// atomics queue on one address.  Each counter is back at zero once it is full.
 __device__ inline bool last_arrival(const TeamArgs &a, int64_t i, int64_t n) {
+    if (n <= kArriveSingle) {
+        if (atomicAdd(a.gdone, 1) != (int)n - 1) return false;
+        __hip_atomic_store(a.gdone, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return true;
+    }
     const int slot = (int)(i % kArriveSlots);
     const int in_slot = (int)((n - 1 - slot) / kArriveSlots) + 1;   // units i < n on this slot
     const int slots = (int)(n < kArriveSlots ? n : kArriveSlots);
@@ -403,6 +408,14 @@ __device__ inline int load_tagged(const uint64_t *p, int n, uint32_t tag, uint32
     return bad;
 }
 
+// LDS scratch of draw_ranges (part of the caller's shared block, so that kernels which
+// run other work in other workgroups can overlay it).
+struct DrawShared {
+    double scan[kTeamThreads];
+    double ex;
+    int seg, tok;
+};
+
 // Token drawn by inverse CDF at target t over weights w: the residual max(p - q, 0) after
 // a rejection (RESID), else p (the bonus token).  The per-range masses (one per
 // kTeamSeg-logit wave range) pick the range; the workgroup re-reads that range and scans
@@ -412,11 +425,11 @@ __device__ inline int load_tagged(const uint64_t *p, int n, uint32_t tag, uint32
 // receives the weight of the token drawn.
 template <int DTT, int DTD, bool RESID>
 __device__ int draw_ranges(const void *trow, const void *drow, int V, float c, Norm2 nt, Norm2 nd,
-                           const float *dirv, int nseg, float u, TeamRed &red, float *w_sel = nullptr) {
-    __shared__ int s_seg;
-    __shared__ double s_ex;
-    __shared__ double s_scan[kTeamThreads];
-    __shared__ int s_tok;
+                           const float *dirv, int nseg, float u, DrawShared &ds, float *w_sel = nullptr) {
+    int &s_seg = ds.seg;
+    double &s_ex = ds.ex;
+    double *s_scan = ds.scan;
+    int &s_tok = ds.tok;
     const int w = threadIdx.x / kWave;
     if (w == 0) {
         const int lane = lane_id();

@@ -60,7 +60,7 @@ namespace {
 // keeps (max, sum) of every 512-logit segment in `seg` (workspace, this workgroup only),
 // then a wave finds the segment and re-reads it.
 template <int DT>
-__device__ int draw_from_row(const void *row, int V, float c, float u, float *seg, int nseg, TeamRed &red) {
+__device__ __forceinline__ int draw_from_row(const void *row, int V, float c, float u, float *seg, int nseg, TeamRed &red, int &s_tok) {
     const int w = threadIdx.x / kWave;
     float M = neg_inf(), s = 0.f;
     int it = 0;
@@ -95,7 +95,6 @@ __device__ int draw_from_row(const void *row, int V, float c, float u, float *se
     }
     __threadfence_block();
     __syncthreads();
-    __shared__ int s_tok;
     if (w == 0) {
         double part = 0.0;
         for (int q = lane_id(); q < nseg; q += kWave) part += (double)seg[q];
@@ -349,28 +348,467 @@ __device__ __forceinline__ int request_limit(const TeamArgs &a, int r, bool repo
     return L;
 }
 
+namespace {
+
+// Recompute member j's share of a row (alpha, and the residual directory entries of its
+// wave ranges when dir_row is given) from HBM, once the row normalisers are known: one
+// streaming pass over the member's chunk in the member layout, 8 logits of each row at a
+// time.  Used only when that member handed its share over, so it keeps few registers live
+// rather than the chunk (it runs inside the verification kernel, under its register bound).
+template <int DTT, int DTD>
+__device__ __forceinline__ float recompute_share(const void *trow, const void *drow, int V, float c, int j, Norm2 nt,
+                                                 Norm2 nd, uint64_t *dir_row, uint32_t tag, TeamRed &red) {
+    const int w = threadIdx.x / kWave;
+    const int base = j * kTeamChunk + w * kTeamSeg + lane_id() * 8;
+    float al = 0.f, rs = 0.f;
+#pragma unroll 1
+    for (int g = 0; g < kTeamE / 8; ++g) {
+        float zt[8], zd[8];
+        load8<DTT>(trow, base + g * 512, V, zt);
+        load8<DTD>(drow, base + g * 512, V, zd);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float p = exp2_fast(log2prob(zt[e], c, nt));
+            const float m = fminf(p, exp2_fast(log2prob(zd[e], c, nd)));
+            al += m;
+            rs += p - m;
+        }
+    }
+    rs = wave_sum(rs);
+    if (dir_row && lane_id() == 0) putf(dir_row + j * kTeamWaves + w, rs, tag);
+    return block_sumf(al, red);
+}
+
+constexpr int kMaxS = (SV_V_MAX + kTeamChunk - 1) / kTeamChunk;   // members per row at most
+constexpr int kFinWords = 4096;     // LDS words staged per batch of rows
+constexpr int kAccUsed = 5;         // words of an accept record: flag, t.hi, d.hi, t.lo, d.lo
+constexpr uint32_t kAbsent = 0xfffffffeu;   // staged payload of a word not published (yet)
+
+// LDS of a member workgroup (one row pair's chunk)
+struct MemberShared {
+    TeamRed red;
+    uint32_t pay[4 * kMaxS];
+    Norm2 tot[2];
+    int ok;
+};
+
+// LDS of a request's finalize workgroup
+struct FinShared {
+    TeamRed red;
+    DrawShared draw;
+    uint32_t stage[kFinWords];
+    uint32_t pay[6 * kMaxS + 8];
+    float mass[4 * kMaxS + 8];
+    float u[kTeamThreads];     // correction/bonus uniform for each candidate tau
+    int x[kTeamThreads];       // drafted tokens of the rows of a batch
+    Norm2 n[2];                // normalisers of the row the draw uses (target, drafter)
+    int tau, tok, flags, at;
+};
+
+// Members and finalize workgroups run the same kernel: their LDS overlays.
+union TeamShared {
+    MemberShared m;
+    FinShared f;
+};
+
+// One wave (every lane) waits for words p[0..n) with the call's tag; on timeout it flags
+// the call.
+__device__ __forceinline__ bool wave_wait(const TeamArgs &a, const uint64_t *p, int n, uint32_t tag, uint32_t *dst) {
+    const bool got = wave_poll(p, n, tag, dst, a.fin_ticks);
+    if (!got && lane_id() == 0) atomicOr(a.err, SV_DEVERR_TIMEOUT);
+    return got;
+}
+
+}  // namespace
+
+// =======================================================================================
+// Finalize: the last B workgroups of the verification grid, one per request
+// =======================================================================================
+// Request r's workgroup is dispatched after every member workgroup of the call.  It gathers
+// its rows' tagged words as they are published (bounded wait), sums the shares in member
+// order, recomputes handed-over shares from HBM, and runs the first-reject scan and the
+// correction / bonus draw while the rest of the grid is still streaming.  Before it arrives
+// at the call's end it has seen the final word of every workgroup of its request that read
+// the call epoch (the shares of its rows, or their argmax words, and the bonus slot's
+// references), so the epoch advances only once no workgroup of the call still has to read
+// it.
+template <int DTT, int DTD, int MODE>
+__device__ __forceinline__ void finalize_request(const TeamArgs &a, int r, FinShared &sh) {
+    TeamRed &red = sh.red;
+    const int K = a.K;
+    const int S = a.S;
+    const int nseg = a.nseg;
+    const int L = row_limit(a, r);
+    const uint32_t tag = read_epoch(a.epoch) + 1;
+    const int64_t row0 = (int64_t)r * a.slots;
+    const int64_t brow = row0 + K;   // the bonus slot
+    const float c = a.c;
+    const bool want_amax = (MODE == kTeamGreedy) || a.want_amax;
+
+    // The uniform of the draw after the scan, for every candidate tau <= K: computed up front
+    // if K + 1 <= kTeamThreads (the request's rows are usually still streaming), else on
+    // demand.
+    const bool pre_u = MODE == kTeamStoch && K + 1 <= kTeamThreads;
+    auto tau_u = [&](int t) {
+        return pre_u ? sh.u[t] : uniform24(a.seed, (uint64_t)r, (uint64_t)t, kPurposeCorrection, a.step);
+    };
+    if (threadIdx.x == 0) { sh.tau = L; sh.at = 0; sh.n[0] = sh.n[1] = Norm2{0.f, 0.f}; }
+    if (pre_u && threadIdx.x <= K)
+        sh.u[threadIdx.x] = uniform24(a.seed, (uint64_t)r, (uint64_t)threadIdx.x, kPurposeCorrection, a.step);
+    __syncthreads();
+
+    // Rows are staged in batches: acc [nb][kAccUsed] | shares [nb][S] | directory [nb][nseg] |
+    // argmax words [nb][4S].
+    const int nA = (MODE == kTeamStoch) ? kAccUsed : 0;
+    const int nB = (MODE != kTeamGreedy) ? S : 0;
+    const int nC = (MODE == kTeamStoch) ? nseg : 0;
+    const int nD = want_amax ? 4 * S : 0;
+    // The last batch also stages the bonus slot's final words (its members' references,
+    // greedy: their argmax indices), which must be seen before the arrival below.
+    const int per_row = nA + nB + nC + nD;
+    const int batch = max(1, min(kTeamThreads, (kFinWords - S) / max(per_row, 1)));
+    const uint64_t *bonus_final = a.part + brow * 8 * S + (MODE == kTeamGreedy ? 5 * S : 0);
+    for (int k0 = 0; k0 < L; k0 += batch) {
+        const int nb = min(batch, L - k0);
+        uint32_t *sx = sh.stage;             // [nb][kAccUsed]
+        uint32_t *sa = sx + nb * nA;         // [nb][S]
+        uint32_t *sd = sa + nb * nB;         // [nb][nseg]
+        uint32_t *sm = sd + nb * nC;         // [nb][4S]
+        const int n = nb * per_row + (k0 + nb == L ? S : 0);   // + [S] bonus final words
+        if (threadIdx.x < nb) sh.x[threadIdx.x] = a.tokens[(size_t)r * K + k0 + threadIdx.x];
+
+        auto src = [&](int i) -> const uint64_t * {
+            if (i < nb * nA) return a.acc + kAccWords * (row0 + k0 + i / kAccUsed) + i % kAccUsed;
+            i -= nb * nA;
+            if (i < nb * nB) return a.apart + (row0 + k0) * S + i;
+            i -= nb * nB;
+            if (i < nb * nC) return a.dir + (row0 + k0) * nseg + i;
+            i -= nb * nC;
+            if (i < nb * nD) return a.part + (row0 + k0 + i / (4 * S)) * 8 * S + 4 * S + i % (4 * S);
+            return bonus_final + (i - nb * nD);
+        };
+        // A staged word is settled once published, or once it is known not to come: the
+        // directory words of a member that handed its share over, and the accept record of a
+        // row whose token is out of range or whose owner member handed over.
+        auto settled = [&](int i) -> bool {
+            if (sh.stage[i] != kAbsent) return true;
+            if (i < nb * nA) {
+                const int q = i / kAccUsed;
+                const int x = sh.x[q];
+                return x < 0 || x >= a.V || sa[q * S + x / kTeamChunk] == kGaveUp;
+            }
+            i -= nb * nA;
+            if (i < nb * nB) return false;
+            i -= nb * nB;
+            if (i < nb * nC) return sa[(i / nseg) * S + (i % nseg) / kTeamWaves] == kGaveUp;
+            return false;
+        };
+
+        // Sweeps until every word is settled: each thread owns words threadIdx.x + u * 256
+        // (u < 16) and re-reads those still pending.
+        uint32_t pend = 0;
+        for (int u = 0; u * kTeamThreads + (int)threadIdx.x < n; ++u) pend |= 1u << u;
+        const uint64_t t0 = wall_clock64();
+        while (true) {
+            for (int u0 = 0; u0 < kFinWords / kTeamThreads; u0 += 4) {
+                if (!(pend >> u0)) break;
+                uint64_t wv[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    wv[u] = ((pend >> (u0 + u)) & 1u) ? peek(src((u0 + u) * kTeamThreads + threadIdx.x)) : 0;
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if ((pend >> (u0 + u)) & 1u)
+                        sh.stage[(u0 + u) * kTeamThreads + threadIdx.x] =
+                            (uint32_t)(wv[u] >> 32) == tag ? (uint32_t)wv[u] : kAbsent;
+            }
+            __syncthreads();
+            for (int u = 0; u < kFinWords / kTeamThreads; ++u)
+                if (((pend >> u) & 1u) && settled(u * kTeamThreads + threadIdx.x)) pend &= ~(1u << u);
+            if (!__syncthreads_or(pend != 0)) break;
+            if ((int64_t)(wall_clock64() - t0) > a.fin_ticks) {
+                // Not published within the bound: shares (and the shares of members whose
+                // directory words are missing) are recomputed here; an incomplete accept
+                // record sends the row to the partials below.
+                if (threadIdx.x == 0) atomicOr(a.err, SV_DEVERR_TIMEOUT);
+                for (int u = 0; u < kFinWords / kTeamThreads; ++u) {
+                    if (!((pend >> u) & 1u)) continue;
+                    int i = u * kTeamThreads + (int)threadIdx.x - nb * nA;
+                    if (i >= 0 && i < nb * nB) sa[i] = kGaveUp;
+                    i -= nb * nB;
+                    if (i >= 0 && i < nb * nC) sa[(i / nseg) * S + (i % nseg) / kTeamWaves] = kGaveUp;
+                }
+                __syncthreads();
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+
+        // any row whose accept record is incomplete, or any handed-over share?
+        if (threadIdx.x == 0) sh.flags = 0;
+        __syncthreads();
+        {
+            int f = 0;
+            if (MODE == kTeamStoch)
+                for (int q = threadIdx.x; q < nb * kAccUsed; q += kTeamThreads) f |= (sx[q] == kAbsent) ? 1 : 0;
+            if (MODE != kTeamGreedy)
+                for (int q = threadIdx.x; q < nb * S; q += kTeamThreads) f |= (sa[q] == kGaveUp) ? 2 : 0;
+            if (f) atomicOr(&sh.flags, f);
+        }
+        __syncthreads();
+        const int flags = sh.flags;
+        // rows whose accept record is incomplete (a member handed over, or the drafted token
+        // is out of range): the normalisers from the partials, the accept test below
+        if (MODE == kTeamStoch && (flags & 1)) {
+            for (int q = 0; q < nb; ++q) {
+                bool whole = true;
+                for (int e = 0; e < kAccUsed; ++e) whole = whole && sx[q * kAccUsed + e] != kAbsent;
+                if (whole) continue;
+                if (threadIdx.x < kWave) {
+                    const bool got = wave_poll(a.part + (row0 + k0 + q) * 8 * S, 4 * S, tag, sh.pay, a.fin_ticks);
+                    if (!got && threadIdx.x == 0) atomicOr(a.err, SV_DEVERR_DRAFT_LEN);   // the row was never streamed
+                }
+                __syncthreads();
+                if (threadIdx.x == 0) {
+                    Norm2 nt, nd;
+                    team_totals(sh.pay, S, nt, nd);
+                    sx[q * kAccUsed] = kAbsent;   // the test runs here
+                    put_norms(sx + q * kAccUsed, nt, nd);
+                }
+                __syncthreads();
+            }
+        }
+        // handed-over shares: recompute them (and their directory entries) from HBM
+        if (MODE != kTeamGreedy && (flags & 2)) {
+            for (int q = 0; q < nb; ++q) {
+                for (int m = 0; m < S; ++m) {
+                    if (sa[q * S + m] != kGaveUp) continue;
+                    Norm2 nt, nd;
+                    if (MODE == kTeamStoch) {
+                        get_norms(sx + q * kAccUsed, nt, nd);
+                    } else {
+                        if (threadIdx.x < kWave) wave_wait(a, a.part + (row0 + k0 + q) * 8 * S, 4 * S, tag, sh.pay);
+                        __syncthreads();
+                        team_totals(sh.pay, S, nt, nd);
+                    }
+                    const int k = k0 + q;
+                    const void *trow = row_ptr<DTT>(a.target, (int64_t)r * a.trows + k, a.ld_t);
+                    const void *drow = row_ptr<DTD>(a.draft, (int64_t)r * K + k, a.ld_d);
+                    const float share = recompute_share<DTT, DTD>(
+                        trow, drow, a.V, c, m, nt, nd, MODE == kTeamStoch ? a.dir + (row0 + k) * nseg : nullptr, tag, red);
+                    __syncthreads();
+                    if (threadIdx.x == 0) sa[q * S + m] = __float_as_uint(share);
+                    if (MODE == kTeamStoch) {   // the fresh directory entries of this member
+                        load_tagged(a.dir + (row0 + k) * nseg + m * kTeamWaves, kTeamWaves, tag,
+                                    sd + q * nseg + m * kTeamWaves, 0u);
+                    }
+                    __syncthreads();
+                }
+            }
+        }
+
+        // one thread per row of the batch
+        Norm2 nt{0.f, 0.f}, nd{0.f, 0.f};
+        int at = 0;
+        if (threadIdx.x < nb) {
+            const int q = threadIdx.x;
+            const int k = k0 + q;
+            const size_t i = (size_t)r * K + k;
+            int ad = 0;
+            if (want_amax) {
+                const uint32_t *pp = sm + q * 4 * S;
+                float bv = neg_inf(), bd = neg_inf();
+                int bi = 0x7fffffff, bj = 0x7fffffff;
+                for (int m = 0; m < S; ++m) {
+                    amax_merge(bv, bi, __uint_as_float(pp[m]), (int)pp[S + m]);
+                    amax_merge(bd, bj, __uint_as_float(pp[2 * S + m]), (int)pp[3 * S + m]);
+                }
+                at = bi == 0x7fffffff ? 0 : bi;
+                ad = bj == 0x7fffffff ? 0 : bj;
+            }
+            const int x = sh.x[q];
+            const bool okx = x >= 0 && x < a.V;
+            if (!okx) atomicOr(a.err, SV_DEVERR_TOKEN);
+            float alpha;
+            int acc;
+            if constexpr (MODE == kTeamGreedy) {
+                alpha = (at == ad) ? 1.f : 0.f;
+                acc = okx && x == at;
+            } else {
+                double sum = 0.0;
+                for (int m = 0; m < S; ++m) sum += (double)__uint_as_float(sa[q * S + m]);
+                alpha = (float)sum;
+                get_norms(sx + q * kAccUsed, nt, nd);
+                if (sx[q * kAccUsed] != kAbsent) {
+                    acc = (int)sx[q * kAccUsed];
+                } else if (okx) {   // the owner member handed over: run the test here
+                    const float zt = load1<DTT>(row_ptr<DTT>(a.target, (int64_t)r * a.trows + k, a.ld_t), x);
+                    const float zd = load1<DTD>(row_ptr<DTD>(a.draft, (int64_t)r * K + k, a.ld_d), x);
+                    acc = accept_test(zt, zd, c, nt, nd, a.seed, r, k, a.step);
+                } else {
+                    acc = 0;
+                }
+            }
+            a.alpha[i] = alpha;
+            a.accept[i] = (uint8_t)acc;
+            if (a.lse_t) a.lse_t[i] = (MODE == kTeamStoch) ? ln_of(nt) : 0.f;
+            if (a.lse_d) a.lse_d[i] = (MODE == kTeamStoch) ? ln_of(nd) : 0.f;
+            if (a.amax_t) a.amax_t[i] = want_amax ? at : -1;
+            if (a.amax_d) a.amax_d[i] = want_amax ? ad : -1;
+            if (!acc) atomicMin(&sh.tau, k);
+        }
+        __syncthreads();
+        const int tau = sh.tau;
+        if (tau >= k0 && tau < k0 + nb) {
+            // keep what the draw after the rejection at tau needs
+            if (threadIdx.x == tau - k0) {
+                sh.n[0] = nt;
+                sh.n[1] = nd;
+                sh.at = at;
+            }
+            if (MODE == kTeamStoch)
+                for (int q = threadIdx.x; q < nseg; q += kTeamThreads) sh.mass[q] = __uint_as_float(sd[(tau - k0) * nseg + q]);
+        }
+        __syncthreads();
+    }
+
+    // The bonus slot's members read the epoch too: see their final words (staged with the
+    // last batch of rows when there were rows).  After that no workgroup of the call still
+    // reads the epoch, so the request arrives now, and the last arrival advances it while
+    // the draws still run.
+    if (L == 0 && threadIdx.x < kWave) wave_wait(a, bonus_final, S, tag, sh.pay);
+    if (threadIdx.x == 0 && last_arrival(a, r, a.B))
+        __hip_atomic_store(a.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    const int tau = sh.tau;
+    int tok = 0;
+    const void *trow = row_ptr<DTT>(a.target, (int64_t)r * a.trows + tau, a.ld_t);
+    if (tau == L) {
+        // every draft accepted: the bonus token from the bonus slot's published states
+        if (threadIdx.x < kWave) {
+            // greedy: argmax words 4S..6S only
+            if (MODE == kTeamGreedy) wave_wait(a, a.part + brow * 8 * S + 4 * S, 2 * S, tag, sh.pay + 4 * S);
+            else wave_wait(a, a.part + brow * 8 * S, S, tag, sh.pay);
+        }
+        __syncthreads();
+        if constexpr (MODE == kTeamGreedy) {
+            if (threadIdx.x == 0) {
+                float bv = neg_inf();
+                int bi = 0x7fffffff;
+                for (int m = 0; m < S; ++m) amax_merge(bv, bi, __uint_as_float(sh.pay[4 * S + m]), (int)sh.pay[5 * S + m]);
+                sh.at = bi == 0x7fffffff ? 0 : bi;
+            }
+            __syncthreads();
+            tok = sh.at;
+        } else {
+            if (threadIdx.x < kWave) wave_wait(a, a.dir + brow * nseg, nseg, tag, sh.pay + S);
+            __syncthreads();
+            // pay[0..S): member references Mj; pay[S + j * W + w]: range sums against Mj
+            if (threadIdx.x < kWave) {
+                float M = neg_inf(), sm = 0.f;
+                for (int m = threadIdx.x; m < S; m += kWave) {
+                    float sj = 0.f;
+                    for (int w = 0; w < kTeamWaves; ++w) sj += __uint_as_float(sh.pay[S + m * kTeamWaves + w]);
+                    ms_merge(M, sm, __uint_as_float(sh.pay[m]), sj);
+                }
+                wave_ms(M, sm);
+                if (threadIdx.x == 0) sh.n[0] = norm2(M, log2f(sm));
+            }
+            __syncthreads();
+            const Norm2 nb = sh.n[0];
+            for (int q = threadIdx.x; q < nseg; q += kTeamThreads) {
+                const float Mq = __uint_as_float(sh.pay[q / kTeamWaves]);
+                sh.mass[q] = (Mq == neg_inf()) ? 0.f : __uint_as_float(sh.pay[S + q]) * exp2_fast((Mq - nb.hi) - nb.lo);
+            }
+            __syncthreads();
+            tok = draw_ranges<DTT, DTD, false>(trow, nullptr, a.V, c, nb, Norm2{0.f, 0.f}, sh.mass, nseg, tau_u(tau),
+                                               sh.draw);
+            if (tok < 0) tok = 0;
+        }
+    } else if constexpr (MODE == kTeamGreedy) {
+        tok = sh.at;
+    } else {
+        // rejection at tau: the residual max(p - q, 0) of row tau
+        const float u = tau_u(tau);
+        bool done = false;
+        {
+            const void *drow = row_ptr<DTD>(a.draft, (int64_t)r * K + tau, a.ld_d);
+            const int t = draw_ranges<DTT, DTD, true>(trow, drow, a.V, c, sh.n[0], sh.n[1], sh.mass, nseg, u, sh.draw);
+            if (t >= 0) { tok = t; done = true; }
+        }
+        __syncthreads();
+        // an empty residual (p == q everywhere in binary32): draw from p_tau
+        if (!done)
+            tok = draw_from_row<DTT>(trow, a.V, c, u, a.bonus + (size_t)r * 2 * a.nseg_b, a.nseg_b, red, sh.tok);
+    }
+    if (threadIdx.x == 0) sh.tok = tok;
+    __syncthreads();
+    tok = sh.tok;
+
+    int32_t *o = a.out_tokens + (size_t)r * (K + 1);
+    for (int q = threadIdx.x; q <= K; q += kTeamThreads)
+        o[q] = q < tau ? a.tokens[(size_t)r * K + q] : (q == tau ? tok : -1);
+    for (int k = L + threadIdx.x; k < K; k += kTeamThreads) {
+        const size_t i = (size_t)r * K + k;
+        a.alpha[i] = 0.f;
+        a.accept[i] = 0;
+        if (a.lse_t) a.lse_t[i] = 0.f;
+        if (a.lse_d) a.lse_d[i] = 0.f;
+        if (a.amax_t) a.amax_t[i] = -1;
+        if (a.amax_d) a.amax_d[i] = -1;
+    }
+    if (threadIdx.x == 0) {
+        a.accept_len[r] = tau;
+        a.n_out[r] = tau + 1;
+    }
+}
+
+// The kernel's argument block (its one parameter, at the start of the kernarg segment)
+// through a pointer the compiler cannot see through: reads through it are scalar loads of
+// their own (the pointer still carries the constant address space the loads need).
+__device__ __forceinline__ const TeamArgs &opaque_args() {
+    auto kp = (const __attribute__((address_space(4))) TeamArgs *)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(kp));
+    return *(const TeamArgs *)kp;
+}
+
+// =======================================================================================
+// Verification grid: one member workgroup per (row pair, vocabulary chunk), then the
+// bonus slots, then one finalize workgroup per request
+// =======================================================================================
 // AMAX: also publish the argmax partials (always in greedy mode; on request otherwise).
 // At most 96 registers per lane, so five waves share each SIMD.
 template <int DTT, int DTD, int MODE, bool AMAX>
 __global__ __launch_bounds__(kTeamThreads) __attribute__((amdgpu_waves_per_eu(5))) void stream_kernel(TeamArgs a) {
-    __shared__ TeamRed red;
-    __shared__ uint32_t pay[4 * 128];
-    __shared__ Norm2 s_tot[2];
-    __shared__ int s_ok;
+    __shared__ TeamShared sh;
 
     // The S members of a team are consecutive workgroups: round-robin dispatch spreads them
     // over the XCDs, whose dispatchers start them at nearly the same time.
     // Work items in grid order: the verified rows (r, k < K) request by request, then every
     // request's bonus slot, so the short bonus workgroups are dispatched last and fill the
-    // tail of the grid.  (Divisions by runtime values are done on the vector unit:
-    // readfirstlane returns the uniform results to scalar registers.)
+    // tail of the grid, then (verification) the finalize workgroups, which run their
+    // requests' scans and draws beside the tail.  (Divisions by runtime values are done on
+    // the vector unit: readfirstlane returns the uniform results to scalar registers.)
     const int S = a.S;
-    const int j = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % (unsigned)S));
-    const int item = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / (unsigned)S));
     const int K = a.K;
     const int slots = a.slots;
     // With a row list, the verified items are the listed rows only.
     const int nv = a.selected ? a.n_rows : a.B * K;
+    if constexpr (MODE != kTeamAlpha) {
+        const unsigned members = (unsigned)(nv + a.B) * (unsigned)S;
+        if (blockIdx.x >= members) {
+            // The finalize reads the arguments through an opaque pointer to the kernel's own
+            // argument block (the one parameter sits at its start), so none of its scalar
+            // loads is merged with the members' and hoisted above the branch, where they would
+            // stay live, and spill, through the member path.
+            const TeamArgs &fa = opaque_args();
+            finalize_request<DTT, DTD, MODE>(fa, (int)(blockIdx.x - members), sh.f);
+            return;
+        }
+    }
+    MemberShared &ms = sh.m;
+    const int j = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % (unsigned)S));
+    const int item = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / (unsigned)S));
     int r = item - nv, k = K;
     if (item < nv) {
         const int f = a.selected ? load_uniform(a.row_list + item) : item;
@@ -388,341 +826,13 @@ __global__ __launch_bounds__(kTeamThreads) __attribute__((amdgpu_waves_per_eu(5)
     const int L = (MODE != kTeamAlpha) ? request_limit(a, r, bonus && j == 0 && threadIdx.x == 0) : K;
     if (!bonus && k >= L) return;
     if (bonus) {
-        bonus_member<DTT, MODE>(a, j, row, r, L, red);
+        bonus_member<DTT, MODE>(a, j, row, r, L, ms.red);
         return;
     }
-    if ((j + 1) * kTeamChunk <= a.V) row_member<DTT, DTD, MODE, AMAX, true>(a, j, row, r, k, red, pay, s_tot, &s_ok);
-    else row_member<DTT, DTD, MODE, AMAX, false>(a, j, row, r, k, red, pay, s_tot, &s_ok);
-}
-
-namespace {
-
-// Recompute member j's share of a row (alpha, and residual directory entries) from HBM;
-// used only when that member handed its share over.  Whole workgroup.
-template <int DTT, int DTD>
-__device__ float recompute_share(const TeamArgs &a, const void *trow, const void *drow, int j, Norm2 nt, Norm2 nd,
-                                 int64_t row, uint32_t tag, TeamRed &red, bool publish_dir) {
-    LaneRow<DTT> tr;
-    LaneRow<DTD> dr;
-    const int w = threadIdx.x / kWave;
-    const int base = j * kTeamChunk + w * kTeamSeg;
-    tr.template load<false>(trow, base, a.V);
-    dr.template load<false>(drow, base, a.V);
-    const ThreadStats s = pass1(tr, dr, tr.max(), dr.max(), a.c);
-    float al, rs;
-    pass2(tr, dr, s, a.c, nt, nd, al, rs);
-    rs = fmaxf(wave_sum(rs), 0.f);
-    if (publish_dir && lane_id() == 0) putf(a.dir + row * a.nseg + j * kTeamWaves + w, rs, tag);
-    return block_sumf(al, red);
-}
-
-constexpr int kFinWords = 8192;   // LDS words staged per batch of rows
-
-}  // namespace
-
-// =======================================================================================
-// Finalize kernel: one workgroup per request
-// =======================================================================================
-template <int DTT, int DTD, int MODE>
-__global__ __launch_bounds__(kTeamThreads) void finalize_kernel(TeamArgs a) {
-    __shared__ TeamRed red;
-    __shared__ uint32_t stage[kFinWords];
-    __shared__ uint32_t pay[8 * 128 + 512 + 8];
-    __shared__ float s_mass[512 + 8];
-    __shared__ int s_tau, s_tok, s_flags;
-    __shared__ Norm2 s_n[2];   // normalisers of the row the draw uses (target, drafter)
-    __shared__ int s_at;
-    __shared__ Norm2 s_rt[kTeamThreads], s_rd[kTeamThreads];
-    __shared__ int s_ra[kTeamThreads];
-    __shared__ float s_u[kTeamThreads];   // correction/bonus uniform for each candidate tau
-
-    const int r = blockIdx.x;
-    const int K = a.K;
-    const int S = a.S;
-    const int nseg = a.nseg;
-    const int L = row_limit(a, r);
-    const uint32_t tag = read_epoch(a.epoch) + 1;
-    const int64_t row0 = (int64_t)r * a.slots;
-    const int64_t brow = row0 + K;   // the bonus slot
-    const float c = a.c;
-    const bool want_amax = (MODE == kTeamGreedy) || a.want_amax;
-
-    // The uniform of the draw after the scan, for every candidate tau <= K: computed while
-    // the first gather is in flight (here when there is no gather) if K + 1 <= kTeamThreads,
-    // else on demand.
-    const bool pre_u = MODE == kTeamStoch && K + 1 <= kTeamThreads;
-    auto tau_u = [&](int t) {
-        return pre_u ? s_u[t] : uniform24(a.seed, (uint64_t)r, (uint64_t)t, kPurposeCorrection, a.step);
-    };
-    if (threadIdx.x == 0) { s_tau = L; s_at = 0; s_n[0] = s_n[1] = Norm2{0.f, 0.f}; }
-    if (pre_u && L == 0 && threadIdx.x <= K)
-        s_u[threadIdx.x] = uniform24(a.seed, (uint64_t)r, (uint64_t)threadIdx.x, kPurposeCorrection, a.step);
-    __syncthreads();
-
-    // rows are staged in batches: acc [nb][kAccWords] | shares [nb][S] | directory [nb][4S] |
-    // argmax words [nb][4S], all in one gather
-    const int nA = (MODE == kTeamStoch) ? kAccWords : 0;
-    const int nB = (MODE != kTeamGreedy) ? S : 0;
-    const int nC = (MODE == kTeamStoch) ? nseg : 0;
-    const int nD = want_amax ? 4 * S : 0;
-    const int per_row = nA + nB + nC + nD;
-    const int batch = max(1, min(kTeamThreads, kFinWords / max(per_row, 1)));
-    for (int k0 = 0; k0 < L; k0 += batch) {
-        const int nb = min(batch, L - k0);
-        uint32_t *sx = stage;                // [nb][kAccWords]
-        uint32_t *sa = sx + nb * nA;         // [nb][S]
-        uint32_t *sd = sa + nb * nB;         // [nb][4S]
-        uint32_t *sm = sd + nb * nC;         // [nb][4S]
-        const int x_mine = threadIdx.x < nb ? a.tokens[(size_t)r * K + k0 + threadIdx.x] : 0;
-        {
-            const int n = nb * per_row;
-            constexpr int U = 8;
-            for (int i0 = 0; i0 < n; i0 += U * kTeamThreads) {
-                uint64_t wv[U];
-                uint32_t miss[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    int i = i0 + u * kTeamThreads + threadIdx.x;
-                    const uint64_t *src = nullptr;
-                    miss[u] = 0xffffffffu;
-                    if (i < n) {
-                        if (i < nb * nA) {
-                            src = a.acc + kAccWords * (row0 + k0) + i;
-                        } else if ((i -= nb * nA) < nb * nB) {
-                            src = a.apart + (row0 + k0) * S + i;
-                            miss[u] = kGaveUp;
-                        } else if ((i -= nb * nB) < nb * nC) {
-                            src = a.dir + (row0 + k0) * nseg + i;
-                            miss[u] = 0u;
-                        } else {
-                            i -= nb * nC;
-                            src = a.part + (row0 + k0 + i / (4 * S)) * 8 * S + 4 * S + i % (4 * S);
-                            miss[u] = 0x7fffffffu;
-                        }
-                    }
-                    wv[u] = src ? peek(src) : 0;
-                }
-                if (pre_u && k0 == 0 && i0 == 0 && threadIdx.x <= K)
-                    s_u[threadIdx.x] = uniform24(a.seed, (uint64_t)r, (uint64_t)threadIdx.x, kPurposeCorrection, a.step);
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int i = i0 + u * kTeamThreads + threadIdx.x;
-                    if (i < n) stage[i] = (uint32_t)(wv[u] >> 32) == tag ? (uint32_t)wv[u] : miss[u];
-                }
-            }
-        }
-        __syncthreads();
-
-        // any row whose normalisers were not published, or any handed-over share?
-        if (threadIdx.x == 0) s_flags = 0;
-        __syncthreads();
-        {
-            int f = 0;
-            if (MODE == kTeamStoch)
-                for (int q = threadIdx.x; q < nb; q += kTeamThreads) f |= (sx[q * kAccWords + 1] == 0xffffffffu) ? 1 : 0;
-            if (MODE != kTeamGreedy)
-                for (int q = threadIdx.x; q < nb * S; q += kTeamThreads) f |= (sa[q] == kGaveUp) ? 2 : 0;
-            if (f) atomicOr(&s_flags, f);
-        }
-        __syncthreads();
-        const int flags = s_flags;
-        // rows whose normalisers were not published (a member handed over, or the drafted
-        // token is out of range): reduce the partials here
-        if (MODE == kTeamStoch && (flags & 1)) {
-            for (int q = 0; q < nb; ++q) {
-                if (sx[q * kAccWords + 1] != 0xffffffffu) continue;
-                const int missing = load_tagged(a.part + (row0 + k0 + q) * 8 * S, 4 * S, tag, pay, 0u);
-                if (missing && threadIdx.x == 0) atomicOr(a.err, SV_DEVERR_DRAFT_LEN);   // the row was never streamed
-                __syncthreads();
-                if (threadIdx.x == 0) {
-                    Norm2 nt, nd;
-                    team_totals(pay, S, nt, nd);
-                    put_norms(sx + q * kAccWords, nt, nd);
-                }
-                __syncthreads();
-            }
-        }
-        // handed-over shares: recompute them (and their directory entries) from HBM
-        if (MODE != kTeamGreedy && (flags & 2)) {
-            for (int q = 0; q < nb; ++q) {
-                for (int m = 0; m < S; ++m) {
-                    if (sa[q * S + m] != kGaveUp) continue;
-                    Norm2 nt, nd;
-                    if (MODE == kTeamStoch) {
-                        get_norms(sx + q * kAccWords, nt, nd);
-                    } else {
-                        load_tagged(a.part + (row0 + k0 + q) * 8 * S, 4 * S, tag, pay, 0u);
-                        __syncthreads();
-                        team_totals(pay, S, nt, nd);
-                    }
-                    const int k = k0 + q;
-                    const void *trow = row_ptr<DTT>(a.target, (int64_t)r * a.trows + k, a.ld_t);
-                    const void *drow = row_ptr<DTD>(a.draft, (int64_t)r * K + k, a.ld_d);
-                    const float sh = recompute_share<DTT, DTD>(a, trow, drow, m, nt, nd, row0 + k, tag, red,
-                                                               MODE == kTeamStoch);
-                    __syncthreads();
-                    if (threadIdx.x == 0) sa[q * S + m] = __float_as_uint(sh);
-                    if (MODE == kTeamStoch) {   // the fresh directory entries of this member
-                        load_tagged(a.dir + (row0 + k) * nseg + m * kTeamWaves, kTeamWaves, tag,
-                                    sd + q * nseg + m * kTeamWaves, 0u);
-                    }
-                    __syncthreads();
-                }
-            }
-        }
-
-        // one thread per row of the batch
-        if (threadIdx.x < nb) {
-            const int q = threadIdx.x;
-            const int k = k0 + q;
-            const size_t i = (size_t)r * K + k;
-            int at = 0, ad = 0;
-            if (want_amax) {
-                const uint32_t *pp = sm + q * 4 * S;
-                float bv = neg_inf(), bd = neg_inf();
-                int bi = 0x7fffffff, bj = 0x7fffffff;
-                for (int m = 0; m < S; ++m) {
-                    amax_merge(bv, bi, __uint_as_float(pp[m]), (int)pp[S + m]);
-                    amax_merge(bd, bj, __uint_as_float(pp[2 * S + m]), (int)pp[3 * S + m]);
-                }
-                at = bi == 0x7fffffff ? 0 : bi;
-                ad = bj == 0x7fffffff ? 0 : bj;
-            }
-            const int x = x_mine;
-            const bool okx = x >= 0 && x < a.V;
-            if (!okx) atomicOr(a.err, SV_DEVERR_TOKEN);
-            float alpha;
-            Norm2 nt{0.f, 0.f}, nd{0.f, 0.f};
-            int acc;
-            if constexpr (MODE == kTeamGreedy) {
-                alpha = (at == ad) ? 1.f : 0.f;
-                acc = okx && x == at;
-            } else {
-                double sum = 0.0;
-                for (int m = 0; m < S; ++m) sum += (double)__uint_as_float(sa[q * S + m]);
-                alpha = (float)sum;
-                get_norms(sx + q * kAccWords, nt, nd);
-                if (sx[q * kAccWords] != 0xffffffffu) {
-                    acc = (int)sx[q * kAccWords];
-                } else if (okx) {   // the owner member handed over: run the test here
-                    const float zt = load1<DTT>(row_ptr<DTT>(a.target, (int64_t)r * a.trows + k, a.ld_t), x);
-                    const float zd = load1<DTD>(row_ptr<DTD>(a.draft, (int64_t)r * K + k, a.ld_d), x);
-                    acc = accept_test(zt, zd, c, nt, nd, a.seed, r, k, a.step);
-                } else {
-                    acc = 0;
-                }
-            }
-            a.alpha[i] = alpha;
-            a.accept[i] = (uint8_t)acc;
-            if (a.lse_t) a.lse_t[i] = (MODE == kTeamStoch) ? ln_of(nt) : 0.f;
-            if (a.lse_d) a.lse_d[i] = (MODE == kTeamStoch) ? ln_of(nd) : 0.f;
-            if (a.amax_t) a.amax_t[i] = want_amax ? at : -1;
-            if (a.amax_d) a.amax_d[i] = want_amax ? ad : -1;
-            if (!acc) atomicMin(&s_tau, k);
-            s_rt[q] = nt;
-            s_rd[q] = nd;
-            s_ra[q] = at;
-        }
-        __syncthreads();
-        const int tau = s_tau;
-        if (tau >= k0 && tau < k0 + nb) {
-            // keep what the draw after the rejection at tau needs
-            if (threadIdx.x == 0) {
-                s_n[0] = s_rt[tau - k0];
-                s_n[1] = s_rd[tau - k0];
-                s_at = s_ra[tau - k0];
-            }
-            if (MODE == kTeamStoch)
-                for (int q = threadIdx.x; q < nseg; q += kTeamThreads) s_mass[q] = __uint_as_float(sd[(tau - k0) * nseg + q]);
-        }
-        __syncthreads();
-    }
-
-    const int tau = s_tau;
-    int tok = 0;
-    const void *trow = row_ptr<DTT>(a.target, (int64_t)r * a.trows + tau, a.ld_t);
-    if (tau == L) {
-        // every draft accepted: the bonus token from the bonus slot's published states
-        if (threadIdx.x < kWave) {
-            // one pass: the stream kernel has written them (greedy: argmax words 4S..6S only)
-            const bool got = MODE == kTeamGreedy ? wave_poll(a.part + brow * 8 * S + 4 * S, 2 * S, tag, pay + 4 * S, 0)
-                                                 : wave_poll(a.part + brow * 8 * S, S, tag, pay, 0);
-            if (!got && threadIdx.x == 0) atomicOr(a.err, SV_DEVERR_TIMEOUT);
-        }
-        __syncthreads();
-        if constexpr (MODE == kTeamGreedy) {
-            if (threadIdx.x == 0) {
-                float bv = neg_inf();
-                int bi = 0x7fffffff;
-                for (int m = 0; m < S; ++m) amax_merge(bv, bi, __uint_as_float(pay[4 * S + m]), (int)pay[5 * S + m]);
-                s_at = bi == 0x7fffffff ? 0 : bi;
-            }
-            __syncthreads();
-            tok = s_at;
-        } else {
-            if (threadIdx.x < kWave) {
-                const bool got = wave_poll(a.dir + brow * nseg, nseg, tag, pay + S, 0);
-                if (!got && threadIdx.x == 0) atomicOr(a.err, SV_DEVERR_TIMEOUT);
-            }
-            __syncthreads();
-            // pay[0..S): member references Mj; pay[S + j * W + w]: range sums against Mj
-            if (threadIdx.x < kWave) {
-                float M = neg_inf(), sm = 0.f;
-                for (int m = threadIdx.x; m < S; m += kWave) {
-                    float sj = 0.f;
-                    for (int w = 0; w < kTeamWaves; ++w) sj += __uint_as_float(pay[S + m * kTeamWaves + w]);
-                    ms_merge(M, sm, __uint_as_float(pay[m]), sj);
-                }
-                wave_ms(M, sm);
-                if (threadIdx.x == 0) s_n[0] = norm2(M, log2f(sm));
-            }
-            __syncthreads();
-            const Norm2 nb = s_n[0];
-            for (int q = threadIdx.x; q < nseg; q += kTeamThreads) {
-                const float Mq = __uint_as_float(pay[q / kTeamWaves]);
-                s_mass[q] = (Mq == neg_inf()) ? 0.f : __uint_as_float(pay[S + q]) * exp2_fast((Mq - nb.hi) - nb.lo);
-            }
-            __syncthreads();
-            tok = draw_ranges<DTT, DTD, false>(trow, nullptr, a.V, c, nb, Norm2{0.f, 0.f}, s_mass, nseg, tau_u(tau), red);
-            if (tok < 0) tok = 0;
-        }
-    } else if constexpr (MODE == kTeamGreedy) {
-        tok = s_at;
-    } else {
-        // rejection at tau: the residual max(p - q, 0) of row tau
-        const float u = tau_u(tau);
-        bool done = false;
-        {
-            const void *drow = row_ptr<DTD>(a.draft, (int64_t)r * K + tau, a.ld_d);
-            const int t = draw_ranges<DTT, DTD, true>(trow, drow, a.V, c, s_n[0], s_n[1], s_mass, nseg, u, red);
-            if (t >= 0) { tok = t; done = true; }
-        }
-        __syncthreads();
-        // an empty residual (p == q everywhere in binary32): draw from p_tau
-        if (!done) tok = draw_from_row<DTT>(trow, a.V, c, u, a.bonus + (size_t)r * 2 * a.nseg_b, a.nseg_b, red);
-    }
-    if (threadIdx.x == 0) s_tok = tok;
-    __syncthreads();
-    tok = s_tok;
-
-    int32_t *o = a.out_tokens + (size_t)r * (K + 1);
-    for (int q = threadIdx.x; q <= K; q += kTeamThreads)
-        o[q] = q < tau ? a.tokens[(size_t)r * K + q] : (q == tau ? tok : -1);
-    for (int k = L + threadIdx.x; k < K; k += kTeamThreads) {
-        const size_t i = (size_t)r * K + k;
-        a.alpha[i] = 0.f;
-        a.accept[i] = 0;
-        if (a.lse_t) a.lse_t[i] = 0.f;
-        if (a.lse_d) a.lse_d[i] = 0.f;
-        if (a.amax_t) a.amax_t[i] = -1;
-        if (a.amax_d) a.amax_d[i] = -1;
-    }
-    if (threadIdx.x == 0) {
-        a.accept_len[r] = tau;
-        a.n_out[r] = tau + 1;
-        // the last request of the call advances the epoch for the next call
-        if (last_arrival(a, r, a.B)) __hip_atomic_store(a.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if ((j + 1) * kTeamChunk <= a.V)
+        row_member<DTT, DTD, MODE, AMAX, true>(a, j, row, r, k, ms.red, ms.pay, ms.tot, &ms.ok);
+    else
+        row_member<DTT, DTD, MODE, AMAX, false>(a, j, row, r, k, ms.red, ms.pay, ms.tot, &ms.ok);
 }
 
 // =======================================================================================
@@ -762,7 +872,8 @@ __global__ __launch_bounds__(kTeamThreads) void e2e_alpha_kernel(TeamArgs a) {
         const void *trow = row_ptr<DTT>(a.target, (int64_t)ri * a.trows + ki, a.ld_t);
         const void *drow = row_ptr<DTD>(a.draft, rr, a.ld_d);
         double t = 0.0;
-        for (int m = 0; m < S; ++m) t += (double)recompute_share<DTT, DTD>(a, trow, drow, m, nt, nd, rr, tag, red, false);
+        for (int m = 0; m < S; ++m)
+            t += (double)recompute_share<DTT, DTD>(trow, drow, a.V, a.c, m, nt, nd, nullptr, tag, red);
         if (threadIdx.x == 0) a.alpha[rr] = (float)t;
         __syncthreads();
     }
@@ -770,8 +881,10 @@ __global__ __launch_bounds__(kTeamThreads) void e2e_alpha_kernel(TeamArgs a) {
 
 template <int DTT, int DTD>
 static hipError_t launch_stream_t(const TeamArgs &a, int mode, hipStream_t s) {
+    // verification: member workgroups of the verified rows and the bonus slots, then one
+    // finalize workgroup per request; L_e2e: member workgroups only
     const uint64_t items = a.selected ? (uint64_t)a.n_rows + (uint64_t)a.B : (uint64_t)a.rows;
-    const unsigned grid = (unsigned)(items * (uint64_t)a.S);
+    const unsigned grid = (unsigned)(items * (uint64_t)a.S + (mode == kTeamAlpha ? 0u : (uint64_t)a.B));
     if (grid == 0) return hipSuccess;
     if (mode == kTeamStoch && a.want_amax)
         hipLaunchKernelGGL((stream_kernel<DTT, DTD, kTeamStoch, true>), dim3(grid), dim3(kTeamThreads), 0, s, a);
@@ -781,13 +894,6 @@ static hipError_t launch_stream_t(const TeamArgs &a, int mode, hipStream_t s) {
         hipLaunchKernelGGL((stream_kernel<DTT, DTD, kTeamGreedy, true>), dim3(grid), dim3(kTeamThreads), 0, s, a);
     else
         hipLaunchKernelGGL((stream_kernel<DTT, DTD, kTeamAlpha, false>), dim3(grid), dim3(kTeamThreads), 0, s, a);
-    return hipGetLastError();
-}
-
-template <int DTT, int DTD>
-static hipError_t launch_finalize_t(const TeamArgs &a, int mode, hipStream_t s) {
-    if (mode == kTeamStoch) hipLaunchKernelGGL((finalize_kernel<DTT, DTD, kTeamStoch>), dim3(a.B), dim3(kTeamThreads), 0, s, a);
-    else hipLaunchKernelGGL((finalize_kernel<DTT, DTD, kTeamGreedy>), dim3(a.B), dim3(kTeamThreads), 0, s, a);
     return hipGetLastError();
 }
 
@@ -807,9 +913,6 @@ static hipError_t launch_e2e_t(const TeamArgs &a, hipStream_t s) {
 
 hipError_t team_launch_stream(const TeamArgs &a, int dt, int dd, int mode, hipStream_t s) {
     SV_DISPATCH(launch_stream_t, a, mode, s)
-}
-hipError_t team_launch_finalize(const TeamArgs &a, int dt, int dd, int mode, hipStream_t s) {
-    SV_DISPATCH(launch_finalize_t, a, mode, s)
 }
 hipError_t team_launch_e2e_alpha(const TeamArgs &a, int dt, int dd, hipStream_t s) { SV_DISPATCH(launch_e2e_t, a, s) }
 
