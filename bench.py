@@ -32,7 +32,7 @@ METRIC = "verified draft positions/s + HBM GB/s (% peak), B=64 block16 V=131072 
 
 def _source_digest():
     h = hashlib.sha256()
-    # the sources of the verification kernels (stream + finalize) and their launch code
+    # the sources of the verification kernel (members and finalize workgroups) and its launch code
     for rel in ["draft_verification_softmax_amd/csrc/sv_device.hpp", "draft_verification_softmax_amd/csrc/team_device.hpp",
                 "draft_verification_softmax_amd/csrc/team_kernel.hip", "draft_verification_softmax_amd/csrc/team.hpp"]:
         with open(os.path.join(ROOT, rel), "rb") as f:
@@ -81,8 +81,8 @@ def write_traffic(mode, fetch, write, copy_fetch, copy_write):
     """Fold two counter runs of bench.py (FETCH_SIZE, WRITE_SIZE) and two of
     --copy-calibration into profiles/verify_dfly_traffic.json (no GPU needed)."""
     from draft_verification_softmax_amd import profiling
-    t = profiling.traffic(fetch, write, copy_fetch, copy_write, COPY_BYTES, ["stream_kernel", "finalize_kernel"])
-    per = {k: t[k] for k in ["stream_kernel", "finalize_kernel"]}
+    t = profiling.traffic(fetch, write, copy_fetch, copy_write, COPY_BYTES, ["stream_kernel"])
+    per = {k: t[k] for k in ["stream_kernel"]}
     total = sum(v["fetch_bytes"] + v["write_bytes"] for v in per.values())
     try:
         d = json.load(open(TRAFFIC_JSON))
