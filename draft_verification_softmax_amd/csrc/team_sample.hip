@@ -7,16 +7,18 @@
 // conf = q(x).  At T = 0 the token is the first argmax and the confidence is the drafter's
 // probability of it at T = 1.
 //
-// sample_stream_kernel  rows x S members.  Member j streams its 16384-logit chunk of the row
-//                       once into registers and publishes, without waiting: stochastic, the
-//                       mass of each 4096-logit wave range against the member's reference
-//                       (its largest wave maximum) and that reference; greedy, the chunk's
-//                       maximum and its first index, and the chunk's (M, s) at T = 1.
-// sample_finalize_kernel one wave per row: merges the published words in member order, picks
-//                       the range holding u R and re-reads it, 64 consecutive logits per lane
-//                       (the inverse-CDF draw of the verification's bonus token, laid out for
-//                       one wave); the confidence is the drawn token's weight.  The last row
-//                       advances the call epoch.
+// sample_kernel, one launch per call:
+//   rows x S members.  Member j streams its 16384-logit chunk of the row once into registers
+//   and publishes, without waiting: stochastic, the mass of each 4096-logit wave range
+//   against the member's reference (its largest wave maximum) and that reference; greedy, the
+//   chunk's maximum and its first index, and the chunk's (M, s) at T = 1.
+//   then ceil(rows / 4) finalize workgroups, one wave per row, dispatched after every member:
+//   the wave gathers the row's published words as they arrive (bounded wait), merges them in
+//   member order, picks the range holding u R and re-reads it, 64 consecutive logits per lane
+//   (the inverse-CDF draw of the verification's bonus token, laid out for one wave); the
+//   confidence is the drawn token's weight.  Once a row's words are all in, no workgroup
+//   that writes them still has to read the call epoch: the row arrives, and the last
+//   arrival advances the epoch.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -84,16 +86,6 @@ __device__ __forceinline__ void sample_member(const TeamArgs &a, int j, int64_t 
 
 }  // namespace
 
-template <int DT, bool GREEDY>
-__global__ __launch_bounds__(kTeamThreads) void sample_stream_kernel(TeamArgs a) {
-    __shared__ TeamRed red;
-    const int S = a.S;
-    const int j = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % (unsigned)S));
-    const int64_t row = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / (unsigned)S));
-    if ((j + 1) * kTeamChunk <= a.V) sample_member<DT, GREEDY, true>(a, j, row, red);
-    else sample_member<DT, GREEDY, false>(a, j, row, red);
-}
-
 namespace {
 
 // Orders this wave's LDS writes before its later LDS reads by other lanes.
@@ -106,121 +98,149 @@ __device__ __forceinline__ void wave_sync() {
 constexpr int kRowsPerFinalize = kTeamThreads / kWave;   // one wave per row
 constexpr int kGatherMax = 5;                             // words per lane: S + nseg <= 5 * 64
 
-// Words p0[0..n0) then p1[0..n1) (n0 + n1 <= kGatherMax * 64), written by an earlier kernel on
-// the stream, to dst[0..n0 + n1) in one pass whose loads all issue before any returns.
-// Returns false (every lane) when any of them lacks the tag.
-__device__ bool wave_gather(const uint64_t *p0, int n0, const uint64_t *p1, int n1, uint32_t tag, uint32_t *dst) {
+// Words p0[0..n0) then p1[0..n1) (n0 + n1 <= kGatherMax * 64) to dst[0..n0 + n1), by one wave,
+// as they are published: each sweep re-reads the words still without the tag, all its loads
+// issued before any returns.  Bounded by `limit` 10-ns ticks; false (every lane) on timeout.
+__device__ bool wave_gather(const uint64_t *p0, int n0, const uint64_t *p1, int n1, uint32_t tag, uint32_t *dst,
+                            int64_t limit) {
     const int lane = lane_id();
     const int n = n0 + n1;
-    uint64_t w[kGatherMax];
+    uint32_t pend = 0;
 #pragma unroll
-    for (int b = 0; b < kGatherMax; ++b) {
-        const int i = lane + b * kWave;
-        w[b] = i < n0 ? p0[i] : (i < n ? p1[i - n0] : 0);
-    }
-    bool ok = true;
+    for (int b = 0; b < kGatherMax; ++b)
+        if (lane + b * kWave < n) pend |= 1u << b;
+    const uint64_t t0 = wall_clock64();
+    while (true) {
+        uint64_t w[kGatherMax];
 #pragma unroll
-    for (int b = 0; b < kGatherMax; ++b) {
-        const int i = lane + b * kWave;
-        if (i < n) {
-            dst[i] = (uint32_t)w[b];
-            ok = ok && (uint32_t)(w[b] >> 32) == tag;
+        for (int b = 0; b < kGatherMax; ++b) {
+            const int i = lane + b * kWave;
+            w[b] = ((pend >> b) & 1u) ? peek(i < n0 ? p0 + i : p1 + (i - n0)) : 0;
         }
+#pragma unroll
+        for (int b = 0; b < kGatherMax; ++b) {
+            if (((pend >> b) & 1u) && (uint32_t)(w[b] >> 32) == tag) {
+                dst[lane + b * kWave] = (uint32_t)w[b];
+                pend &= ~(1u << b);
+            }
+        }
+        if (__all(pend == 0)) return true;
+        if ((int64_t)(wall_clock64() - t0) > limit) return false;
+        __builtin_amdgcn_s_sleep(2);
     }
-    return __all(ok);
 }
 constexpr int kFinLane = kTeamSeg / kWave;              // logits of a range per lane (64)
 
-// Token of the range sidx of a row at target rem inside the range, by one wave: lane l holds
-// kFinLane consecutive logits; their weights sum in order, the lane sums scan in lane order,
-// and the lane holding the crossing scans its weights.  If rounding runs past the range, the
-// last logit with positive weight.  Returns the token (every lane); *w: its weight.
+// Weight of one logit of the range: both passes of the draw below compute it with this one
+// function, so they see the same binary32 values.
+__device__ __forceinline__ float range_weight(float z, float c, Norm2 nb) { return exp2_fast(log2prob(z, c, nb)); }
+
+// Token of the range sidx of a row at target rem inside the range, by one wave: lane l sums
+// the weights of its kFinLane consecutive logits in order and the lane sums scan in lane
+// order; then the wave reads the logits of the lane holding the crossing again (from cache),
+// one per lane, and scans their weights in binary64.  If rounding runs past the range, the
+// last logit with positive weight.  Returns the token (every lane); *w: its weight.  No
+// lane keeps its weights between the passes, so the draw fits the member workgroups'
+// register budget of the kernel it runs in.
 template <int DT>
 __device__ int wave_draw_range(const void *row, int V, float c, Norm2 nb, int sidx, double rem, float *w) {
     const int lane = lane_id();
-    const int e0 = sidx * kTeamSeg + lane * kFinLane;
     const int vend = min(V, (sidx + 1) * kTeamSeg);
-    float wt[kFinLane];
     double my = 0.0;
+    const int e0 = sidx * kTeamSeg + lane * kFinLane;
+    if (DT == kDtBF16 && e0 + kFinLane <= vend) {
+        // all 8 loads in flight at once, kept packed (bfloat16 pairs, element 2i low)
+        u32x4 q[kFinLane / 8];
+        const u32x4 *p = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(row) + e0);
 #pragma unroll
-    for (int e8 = 0; e8 < kFinLane; e8 += 8) {
-        float z[8];
-        load8<DT>(row, e0 + e8, vend, z);
+        for (int g = 0; g < kFinLane / 8; ++g) q[g] = p[g];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            wt[e8 + e] = exp2_fast(log2prob(z[e], c, nb));
-            my += (double)wt[e8 + e];
+        for (int g = 0; g < kFinLane / 8; ++g) {
+            const uint32_t ws[4] = {q[g].x, q[g].y, q[g].z, q[g].w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                my += (double)range_weight(bf16_lo(ws[h]), c, nb);
+                my += (double)range_weight(bf16_hi(ws[h]), c, nb);
+            }
+        }
+    } else {
+#pragma unroll 2
+        for (int e8 = 0; e8 < kFinLane; e8 += 8) {
+            float z[8];
+            load8<DT>(row, e0 + e8, vend, z);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) my += (double)range_weight(z[e], c, nb);
         }
     }
     const double incl = wave_incl_scan(my);
     const uint64_t hit = __ballot(incl > rem && my > 0.0);
-    int tok = -1;
-    float wsel = 0.f;
-    if (hit) {
-        const int l = __builtin_ctzll(hit);
-        if (lane == l) {
-            double run = incl - my;
-            int k = kFinLane - 1;
-            for (int e = 0; e < kFinLane; ++e) {
-                run += (double)wt[e];
-                if (run > rem) { k = e; break; }
-            }
-            tok = e0 + k;
-#pragma unroll
-            for (int e = 0; e < kFinLane; ++e)
-                if (e == k) wsel = wt[e];
-        }
-        tok = __shfl(tok, l, kWave);
-        wsel = __shfl(wsel, l, kWave);
-    } else {
-        // the last logit of the range with positive weight
-        int last = -1;
-        for (int e = kFinLane - 1; e >= 0; --e)
-            if (wt[e] > 0.f) { last = e; break; }
-        const uint64_t pos = __ballot(last >= 0);
-        if (pos) {
-            const int l = 63 - __builtin_clzll(pos);
-            if (lane == l) {
-                tok = e0 + last;
-#pragma unroll
-                for (int e = 0; e < kFinLane; ++e)
-                    if (e == last) wsel = wt[e];
-            }
-            tok = __shfl(tok, l, kWave);
-            wsel = __shfl(wsel, l, kWave);
-        } else {
-            tok = min(sidx * kTeamSeg, V - 1);
-        }
+    const uint64_t pos = __ballot(my > 0.0);
+    if (!pos) {
+        *w = 0.f;
+        return min(sidx * kTeamSeg, V - 1);
     }
-    *w = wsel;
-    return tok;
+    // the lane whose logits hold the token: the crossing, else the last with positive weight
+    const int l = hit ? __builtin_ctzll(hit) : 63 - __builtin_clzll(pos);
+    const int base = sidx * kTeamSeg + l * kFinLane;
+    const int v = base + lane;
+    const float x = range_weight(v < vend ? load1<DT>(row, v) : neg_inf(), c, nb);
+    int k;
+    if (hit) {
+        const double before = __shfl(incl - my, l, kWave);
+        const uint64_t h = __ballot(before + wave_incl_scan((double)x) > rem);
+        k = h ? __builtin_ctzll(h) : kFinLane - 1;   // rounding ran past the lane's logits: its last
+    } else {
+        k = 63 - __builtin_clzll(__ballot(x > 0.f) | 1ull);
+    }
+    *w = __shfl(x, k, kWave);
+    return base + k;
 }
 
-}  // namespace
+// LDS of a finalize workgroup: one slice per wave (row)
+struct SampleFinShared {
+    uint32_t pay[kRowsPerFinalize][5 * 64 + 8];   // S + nseg <= 320 words, or 4S <= 256
+    float mass[kRowsPerFinalize][4 * 64 + 8];
+};
+union SampleShared {
+    TeamRed red;
+    SampleFinShared f;
+};
 
-// One wave per row (kRowsPerFinalize rows per workgroup, no workgroup barrier): merges the
-// row's published words in member order, picks the range holding u R, and re-reads it.
+// The kernel's argument block through a pointer the compiler cannot see through (see the
+// verification kernel): the finalize's scalar loads are not hoisted above its branch.
+__device__ __forceinline__ const TeamArgs &sample_opaque_args() {
+    auto kp = (const __attribute__((address_space(4))) TeamArgs *)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(kp));
+    return *(const TeamArgs *)kp;
+}
+
+// One wave per row (kRowsPerFinalize rows per workgroup, no workgroup barrier): gathers the
+// row's published words, merges them in member order, picks the range holding u R, and
+// re-reads it.
 template <int DT, bool GREEDY>
-__global__ __launch_bounds__(kTeamThreads) void sample_finalize_kernel(TeamArgs a, int32_t *tokens, float *conf) {
-    __shared__ uint32_t pay_all[kRowsPerFinalize][5 * 64 + 8];   // S + nseg <= 320 words, or 4S <= 256
-    __shared__ float mass_all[kRowsPerFinalize][4 * 64 + 8];
+__device__ __forceinline__ void sample_finalize(const TeamArgs &a, int fb, SampleFinShared &sh, int32_t *tokens,
+                                                float *conf) {
     const int w = threadIdx.x / kWave;
     const int lane = lane_id();
-    const int64_t row = (int64_t)blockIdx.x * kRowsPerFinalize + w;
+    const int64_t row = (int64_t)fb * kRowsPerFinalize + w;
     if (row >= a.rows) return;
-    uint32_t *pay = pay_all[w];
-    float *mass = mass_all[w];
+    uint32_t *pay = sh.pay[w];
+    float *mass = sh.mass[w];
     const int S = a.S;
     const int nseg = a.nseg;
     const int r = (int)(row / a.K), k = (int)(row % a.K);
     const uint32_t tag = read_epoch(a.epoch) + 1;
     const uint64_t *part = a.part + row * (int64_t)(8 * S);
     const void *drow = row_ptr<DT>(a.draft, row, a.ld_d);
-    // the stream kernel has completed: every word is there, so one pass reads them
     bool got;
-    if constexpr (GREEDY) got = wave_gather(part, 2 * S, part + 4 * S, 2 * S, tag, pay);
-    else got = wave_gather(part, S, a.dir + row * nseg, nseg, tag, pay);
-    if (!got && lane == 0) atomicOr(a.err, SV_DEVERR_TIMEOUT);
+    if constexpr (GREEDY) got = wave_gather(part, 2 * S, part + 4 * S, 2 * S, tag, pay, a.fin_ticks);
+    else got = wave_gather(part, S, a.dir + row * nseg, nseg, tag, pay, a.fin_ticks);
+    if (lane == 0) {
+        if (!got) atomicOr(a.err, SV_DEVERR_TIMEOUT);
+        // every member of the row has published: the row arrives, the last one advancing the
+        // epoch while the draws still run
+        if (last_arrival(a, row, a.rows)) __hip_atomic_store(a.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     wave_sync();
     int tok = 0;
     float cf = 0.f;
@@ -261,24 +281,37 @@ __global__ __launch_bounds__(kTeamThreads) void sample_finalize_kernel(TeamArgs 
     if (lane == 0) {
         tokens[row] = tok;
         conf[row] = cf;
-        // the last row of the call advances the epoch for the next call
-        if (last_arrival(a, row, a.rows)) __hip_atomic_store(a.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+}
+
+}  // namespace
+
+// Members (rows x S workgroups), then the finalize workgroups.  bfloat16: at most 64
+// registers per lane, so eight waves share each SIMD (binary32 chunks take 64 on their own).
+template <int DT, bool GREEDY>
+__global__ __launch_bounds__(kTeamThreads) __attribute__((amdgpu_waves_per_eu(DT == kDtBF16 ? 8 : 5))) void sample_kernel(
+    TeamArgs a, int32_t *tokens, float *conf) {
+    __shared__ SampleShared sh;
+    const int S = a.S;
+    const unsigned members = (unsigned)a.rows * (unsigned)S;
+    if (blockIdx.x >= members) {
+        sample_finalize<DT, GREEDY>(sample_opaque_args(), (int)(blockIdx.x - members), sh.f, tokens, conf);
+        return;
+    }
+    const int j = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % (unsigned)S));
+    const int64_t row = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / (unsigned)S));
+    if ((j + 1) * kTeamChunk <= a.V) sample_member<DT, GREEDY, true>(a, j, row, sh.red);
+    else sample_member<DT, GREEDY, false>(a, j, row, sh.red);
 }
 
 template <int DT>
 static hipError_t launch_sample_t(const TeamArgs &a, int32_t *tokens, float *conf, hipStream_t s) {
-    const unsigned grid = (unsigned)((uint64_t)a.rows * (uint64_t)a.S);
     const unsigned fblocks = (unsigned)((a.rows + kRowsPerFinalize - 1) / kRowsPerFinalize);
-    if (a.c == 0.f) {
-        hipLaunchKernelGGL((sample_stream_kernel<DT, true>), dim3(grid), dim3(kTeamThreads), 0, s, a);
-        hipLaunchKernelGGL((sample_finalize_kernel<DT, true>), dim3(fblocks), dim3(kTeamThreads), 0, s, a, tokens,
-                           conf);
-    } else {
-        hipLaunchKernelGGL((sample_stream_kernel<DT, false>), dim3(grid), dim3(kTeamThreads), 0, s, a);
-        hipLaunchKernelGGL((sample_finalize_kernel<DT, false>), dim3(fblocks), dim3(kTeamThreads), 0, s, a, tokens,
-                           conf);
-    }
+    const unsigned grid = (unsigned)((uint64_t)a.rows * (uint64_t)a.S + fblocks);
+    if (a.c == 0.f)
+        hipLaunchKernelGGL((sample_kernel<DT, true>), dim3(grid), dim3(kTeamThreads), 0, s, a, tokens, conf);
+    else
+        hipLaunchKernelGGL((sample_kernel<DT, false>), dim3(grid), dim3(kTeamThreads), 0, s, a, tokens, conf);
     return hipGetLastError();
 }
 

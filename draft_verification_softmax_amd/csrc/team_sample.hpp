@@ -1,5 +1,6 @@
 // team_sample.hpp -- draft tokens and their confidences from the drafter rows, computed by
-// teams of workgroups (one team per drafter row) and one finalize workgroup per row.
+// teams of workgroups (one team per drafter row) and, in the same launch, one finalize wave
+// per row.
 #pragma once
 
 #include <hip/hip_runtime.h>
