@@ -364,9 +364,9 @@ __device__ __forceinline__ void pass2(LaneRow<DTT> &t, LaneRow<DTD> &d, const Th
     resid = P - alpha;
 }
 
-// Row normalisers (base 2) from the S member partials, in member order.  The stream
-// kernel and the finalize kernel both call this on the same payloads, so they agree bit
-// for bit.
+// Row normalisers (base 2) from the S member partials, in member order.  The members and
+// the finalize (which recomputes them when a member handed over) both call this on the same
+// payloads, so they agree bit for bit.
 __device__ __forceinline__ void team_totals(const uint32_t *pay, int S, Norm2 &nt, Norm2 &nd) {
     float Tt = neg_inf(), Ts = 0.f, Dt = neg_inf(), Ds = 0.f;
 #pragma unroll 1

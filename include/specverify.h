@@ -65,7 +65,9 @@ enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 };
 #define SV_DEVERR_TOKEN 1u     /* a draft token outside [0, V) */
 #define SV_DEVERR_DRAFT_LEN 2u /* a draft_len entry outside [0, K_max], or a row list that does not
                                   match its lengths (sv_verify_selected) */
-#define SV_DEVERR_TIMEOUT 4u   /* an internal wait for already-issued stores exceeded its bound */
+#define SV_DEVERR_TIMEOUT 4u   /* an internal wait for other workgroups' stores of the same call
+                                  exceeded its bound (the member wait bound plus 20 ms); the call
+                                  recomputed what was missing */
 
 typedef struct sv_params {
     int32_t B;          /* requests (or |I| for sv_tv_e2e_loss) */
@@ -89,8 +91,9 @@ size_t sv_workspace_bytes(int32_t B, int32_t K_max, int32_t V);
 
 /* Bound, in nanoseconds, of the wait inside a verification, L_e2e or gradient launch for the
  * partial results of the other workgroups that share a row (default 200000).  A workgroup
- * that reaches it hands its share over: a later kernel of the same call recomputes it from
- * the logits, so results do not depend on the bound; only time does.  0 makes every
+ * that reaches it hands its share over: a later workgroup (verification) or kernel (L_e2e,
+ * gradient) of the same call recomputes it from the logits, so results do not depend on the
+ * bound; only time does.  0 makes every
  * workgroup hand over at once unless its partners have already published (for tests of the
  * hand-over path).  Applies to calls issued after it returns; it is process-wide and not
  * synchronised with calls being issued from other host threads.  Errors: SV_EINVAL (ns < 0). */
