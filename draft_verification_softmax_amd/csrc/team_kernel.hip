@@ -119,20 +119,6 @@ __device__ __forceinline__ int draw_from_row(const void *row, int V, float c, fl
     return s_tok;
 }
 
-template <int DT>
-__device__ int row_argmax(const void *row, int V, TeamRed &red) {
-    float v = neg_inf(), vd = neg_inf();
-    int i = 0x7fffffff, id = 0x7fffffff;
-    for (int base = 0; base < V; base += kTeamThreads * 8) {
-        const int e = base + threadIdx.x * 8;
-        float z[8];
-        load8<DT>(row, e, V, z);
-        amax_update8(v, i, z, e);
-    }
-    block_amax2(v, i, vd, id, red);
-    return i == 0x7fffffff ? 0 : i;
-}
-
 // Row normalisers in LDS words 1..4 of a row's accept record (the layout the stream
 // kernel publishes: flag, t.hi, d.hi, t.lo, d.lo).
 __device__ __forceinline__ void put_norms(uint32_t *w, Norm2 nt, Norm2 nd) {
@@ -405,11 +391,22 @@ struct FinShared {
     int tau, tok, flags, at;
 };
 
-// Members and finalize workgroups run the same kernel: their LDS overlays.
+// Members and finalize workgroups run the same kernel: their LDS overlays.  The L_e2e grid
+// has members only.
 union TeamShared {
     MemberShared m;
     FinShared f;
 };
+template <int MODE>
+struct KernelShared {
+    using type = TeamShared;
+};
+template <>
+struct KernelShared<kTeamAlpha> {
+    using type = MemberShared;
+};
+__device__ __forceinline__ MemberShared &member_lds(TeamShared &u) { return u.m; }
+__device__ __forceinline__ MemberShared &member_lds(MemberShared &m) { return m; }
 
 // One wave (every lane) waits for words p[0..n) with the call's tag; on timeout it flags
 // the call.
@@ -780,7 +777,7 @@ __device__ __forceinline__ const TeamArgs &opaque_args() {
 // At most 96 registers per lane, so five waves share each SIMD.
 template <int DTT, int DTD, int MODE, bool AMAX>
 __global__ __launch_bounds__(kTeamThreads) __attribute__((amdgpu_waves_per_eu(5))) void stream_kernel(TeamArgs a) {
-    __shared__ TeamShared sh;
+    __shared__ typename KernelShared<MODE>::type sh;
 
     // The S members of a team are consecutive workgroups: round-robin dispatch spreads them
     // over the XCDs, whose dispatchers start them at nearly the same time.
@@ -806,7 +803,7 @@ __global__ __launch_bounds__(kTeamThreads) __attribute__((amdgpu_waves_per_eu(5)
             return;
         }
     }
-    MemberShared &ms = sh.m;
+    MemberShared &ms = member_lds(sh);
     const int j = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % (unsigned)S));
     const int item = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / (unsigned)S));
     int r = item - nv, k = K;
