@@ -364,6 +364,34 @@ def test_device_error_flag_for_bad_token(sv):
     assert sv.sv_device_error(buf) == 0
 
 
+def test_selected_row_left_out_is_flagged(sv):
+    """A row list that leaves out a row its lengths include: that row is never streamed, so
+    the request's finalize workgroup waits out its bound (about 20 ms per wait, two waits)
+    and flags the call.  The next call on the same workspace is unaffected."""
+    v = workloads.make_verify_inputs("dfly", device=DEV, T=0.9, B=4, K=4, V=20000)
+    B, K = 4, 4
+    lens = torch.tensor([3, 1, 4, 2], dtype=torch.int32, device=DEV)
+    full = [r * K + k for r in range(B) for k in range(int(lens[r]))]
+    ws = sv.Workspace(DEV)
+    buf = ws.get(B, K, 20000)
+    left = [f for f in full if f != 2 * K + 1]   # request 2 loses its row 1
+    rl = torch.tensor(left, dtype=torch.int32, device=DEV)
+    _say("selected verify, one row left out")
+    sv.sv_verify_selected(v.target, v.draft, v.draft_tokens, 0.9, lens, rl, len(left), seed=3, workspace=buf)
+    flags = sv.sv_device_error(buf)
+    assert flags & 2, flags
+    rl = torch.tensor(full, dtype=torch.int32, device=DEV)
+    _say("selected verify, full list, same workspace")
+    a = _np(sv.sv_verify_selected(v.target, v.draft, v.draft_tokens, 0.9, lens, rl, len(full), seed=3,
+                                  want_amax=True, workspace=buf))
+    b = _np(sv.sv_verify_selected(v.target, v.draft, v.draft_tokens, 0.9, lens, rl, len(full), seed=3,
+                                  want_amax=True))
+    for k in a:
+        if a[k] is not None:
+            assert np.array_equal(a[k], b[k]), k
+    assert sv.sv_device_error(buf) == 0
+
+
 def test_workspace_reuse_across_calls_and_modes(sv):
     """One workspace, many calls (the per-call epoch advances inside the kernel): every
     call equals the same call on a fresh workspace."""
@@ -372,13 +400,19 @@ def test_workspace_reuse_across_calls_and_modes(sv):
     ws = sv.Workspace(DEV)
     buf = ws.get(64, 16, 131072)
     plan = [(0.9, None, 0), (0.0, None, 1), (0.9, [3, 0, 16, 1, 7, 2], 2), ("e2e", None, 0), (1.3, None, 3),
-            (0.9, [16, 16, 0, 0, 5, 9], 4), (0.0, [2, 0, 1, 16, 16, 3], 5), ("e2e", None, 0), (0.9, None, 0)]
+            ("sample", 0.9, 6), (0.9, [16, 16, 0, 0, 5, 9], 4), ("sample", 0.0, 7), (0.0, [2, 0, 1, 16, 16, 3], 5),
+            ("e2e", None, 0), (0.9, None, 0)]
     for i, (T, dl, step) in enumerate(plan):
         _say(f"reuse call {i}: T={T} dl={dl}")
         if T == "e2e":
             l1, a1 = sv.sv_tv_e2e_loss(t2, d2, 1.0, workspace=buf)
             l2, a2 = sv.sv_tv_e2e_loss(t2, d2, 1.0)
             assert torch.equal(a1, a2) and torch.equal(l1, l2)
+            continue
+        if T == "sample":   # the draft sampler on the same workspace (its own one-kernel call)
+            x1, c1 = sv.sv_sample_drafts(v.draft, dl, seed=7, step=step, workspace=buf)
+            x2, c2 = sv.sv_sample_drafts(v.draft, dl, seed=7, step=step)
+            assert torch.equal(x1, x2) and torch.equal(c1, c2)
             continue
         dlt = None if dl is None else torch.tensor(dl, dtype=torch.int32, device=DEV)
         a = _np(sv.sv_verify_batch(v.target, v.draft, v.draft_tokens, T, seed=7, step=step, draft_len=dlt,
