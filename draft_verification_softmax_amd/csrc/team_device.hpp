@@ -364,18 +364,30 @@ __device__ __forceinline__ void pass2(LaneRow<DTT> &t, LaneRow<DTD> &d, const Th
     resid = P - alpha;
 }
 
-// Row normalisers (base 2) from the S member partials, in member order.  The members and
-// the finalize (which recomputes them when a member handed over) both call this on the same
-// payloads, so they agree bit for bit.
+// Orders this wave's LDS writes before its lanes' later LDS reads of each other's words.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Row normalisers (base 2) from the S member partials (S <= 64) in pay, by one whole wave:
+// lane q takes member q; the maxima and then the rescaled sums reduce in a fixed tree order.
+// The members and the finalize (which recomputes them when a member handed over) both call
+// this on the same payloads, so they agree bit for bit.  Every lane of the wave must call it;
+// every lane gets the result.
 __device__ __forceinline__ void team_totals(const uint32_t *pay, int S, Norm2 &nt, Norm2 &nd) {
-    float Tt = neg_inf(), Ts = 0.f, Dt = neg_inf(), Ds = 0.f;
-#pragma unroll 1
-    for (int q = 0; q < S; ++q) {   // not unrolled: it runs beside a chunk held in registers
-        ms_merge(Tt, Ts, __uint_as_float(pay[q]), __uint_as_float(pay[S + q]));
-        ms_merge(Dt, Ds, __uint_as_float(pay[2 * S + q]), __uint_as_float(pay[3 * S + q]));
-    }
-    nt = norm2(Tt, log2f(Ts));
-    nd = norm2(Dt, log2f(Ds));
+    wave_lds_sync();
+    const int q = lane_id();
+    const float mt = q < S ? __uint_as_float(pay[q]) : neg_inf();
+    const float st = q < S ? __uint_as_float(pay[S + q]) : 0.f;
+    const float md = q < S ? __uint_as_float(pay[2 * S + q]) : neg_inf();
+    const float sd = q < S ? __uint_as_float(pay[3 * S + q]) : 0.f;
+    const float Mt = wave_max(mt), Md = wave_max(md);
+    const float Ts = wave_sum(mt == neg_inf() ? 0.f : st * exp2_fast(mt - Mt));
+    const float Ds = wave_sum(md == neg_inf() ? 0.f : sd * exp2_fast(md - Md));
+    nt = norm2(Mt, log2f(Ts));
+    nd = norm2(Md, log2f(Ds));
 }
 
 template <int DT>

@@ -143,11 +143,13 @@ __device__ __forceinline__ void grad_member(const TeamArgs &a, const GradArgs &g
     dr.lane_ms(c, ts.Md, ts.sd);
     publish_partials(part, S, j, ts, tag, red);
     if (threadIdx.x < kWave) {
-        const bool got = wave_poll(part, 4 * S, tag, pay, a.spin_ticks);
-        if (threadIdx.x == 0) {
-            *s_ok = got ? 1 : 0;
-            if (got) team_totals(pay, S, s_tot[0], s_tot[1]);
+        const bool got = wave_poll(part, 4 * S, tag, pay, a.spin_ticks);   // wave-uniform
+        if (got) {
+            Norm2 nt, nd;
+            team_totals(pay, S, nt, nd);
+            if (threadIdx.x == 0) { s_tot[0] = nt; s_tot[1] = nd; }
         }
+        if (threadIdx.x == 0) *s_ok = got ? 1 : 0;
     }
     __syncthreads();
     if (!*s_ok) {   // no share from this member: its teammates write nothing either

@@ -168,11 +168,13 @@ __device__ __forceinline__ void finish_row(const TeamArgs &a, int64_t row, int j
     const int w = threadIdx.x / kWave;
     const uint64_t *part = a.part + row * (int64_t)(8 * S);
     if (threadIdx.x < kWave) {
-        const bool got = wave_poll(part, 4 * S, tag, pay, a.spin_ticks);
-        if (threadIdx.x == 0) {
-            *s_ok = got ? 1 : 0;
-            if (got) team_totals(pay, S, s_tot[0], s_tot[1]);
+        const bool got = wave_poll(part, 4 * S, tag, pay, a.spin_ticks);   // wave-uniform
+        if (got) {
+            Norm2 nt, nd;
+            team_totals(pay, S, nt, nd);
+            if (threadIdx.x == 0) { s_tot[0] = nt; s_tot[1] = nd; }
         }
+        if (threadIdx.x == 0) *s_ok = got ? 1 : 0;
     }
     __syncthreads();
     if (!*s_ok) {
@@ -566,11 +568,13 @@ __device__ __forceinline__ void finalize_request(const TeamArgs &a, int r, FinSh
                     if (!got && threadIdx.x == 0) atomicOr(a.err, SV_DEVERR_DRAFT_LEN);   // the row was never streamed
                 }
                 __syncthreads();
-                if (threadIdx.x == 0) {
+                if (threadIdx.x < kWave) {
                     Norm2 nt, nd;
                     team_totals(sh.pay, S, nt, nd);
-                    sx[q * kAccUsed] = kAbsent;   // the test runs here
-                    put_norms(sx + q * kAccUsed, nt, nd);
+                    if (threadIdx.x == 0) {
+                        sx[q * kAccUsed] = kAbsent;   // the test runs here
+                        put_norms(sx + q * kAccUsed, nt, nd);
+                    }
                 }
                 __syncthreads();
             }
