@@ -553,16 +553,26 @@ __device__ __forceinline__ void publish_partials(uint64_t *part, int S, int j, c
     const int w = threadIdx.x / kWave;
     if (lane_id() == 0) { red.f[0][w] = ts.Mt; red.f[1][w] = st; red.f[2][w] = ts.Md; red.f[3][w] = sd; }
     __syncthreads();
-    if (threadIdx.x == 0) {   // only the publisher needs the merged values
-        float Mt = red.f[0][0], Tt = red.f[1][0], Md = red.f[2][0], Dd = red.f[3][0];
-        for (int q = 1; q < kTeamWaves; ++q) {
-            ms_merge(Mt, Tt, red.f[0][q], red.f[1][q]);
-            ms_merge(Md, Dd, red.f[2][q], red.f[3][q]);
+    if (threadIdx.x < kWave) {   // only the publisher needs the merged values
+        // lane q < 4 takes wave q: the maxima, then the rescaled sums, over the quad
+        const int q = lane_id();
+        const float mt = q < kTeamWaves ? red.f[0][q] : neg_inf(), tt = q < kTeamWaves ? red.f[1][q] : 0.f;
+        const float md = q < kTeamWaves ? red.f[2][q] : neg_inf(), dd = q < kTeamWaves ? red.f[3][q] : 0.f;
+        float Mt = fmaxf(mt, dpp_f<0xB1>(mt)), Md = fmaxf(md, dpp_f<0xB1>(md));
+        Mt = fmaxf(Mt, dpp_f<0x4E>(Mt));
+        Md = fmaxf(Md, dpp_f<0x4E>(Md));
+        float Tt = (mt == neg_inf()) ? 0.f : tt * exp2_fast(mt - Mt);
+        float Dd = (md == neg_inf()) ? 0.f : dd * exp2_fast(md - Md);
+        Tt += dpp_f<0xB1>(Tt);
+        Dd += dpp_f<0xB1>(Dd);
+        Tt += dpp_f<0x4E>(Tt);
+        Dd += dpp_f<0x4E>(Dd);
+        if (q == 0) {
+            putf(part + 0 * S + j, Mt, tag);
+            putf(part + 1 * S + j, Tt, tag);
+            putf(part + 2 * S + j, Md, tag);
+            putf(part + 3 * S + j, Dd, tag);
         }
-        putf(part + 0 * S + j, Mt, tag);
-        putf(part + 1 * S + j, Tt, tag);
-        putf(part + 2 * S + j, Md, tag);
-        putf(part + 3 * S + j, Dd, tag);
     }
 }
 
