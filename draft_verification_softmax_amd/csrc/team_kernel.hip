@@ -141,12 +141,14 @@ __device__ __forceinline__ int row_limit(const TeamArgs &a, int r) {
 }
 
 // Accept iff u * q(x) < p(x), i.e. u < 2^{log2 p(x) - log2 q(x)}.
-__device__ __forceinline__ int accept_test(float zt, float zd, float c, Norm2 nt, Norm2 nd, uint64_t seed, int r,
-                                           int k, uint64_t step) {
+// u: the accept uniform of the row, accept_uniform(seed, r, k, step).
+__device__ __forceinline__ int accept_test(float zt, float zd, float c, Norm2 nt, Norm2 nd, float u) {
     const float lpt = log2prob(zt, c, nt);
     const float lpd = log2prob(zd, c, nd);
-    const float u = uniform24(seed, (uint64_t)r, (uint64_t)k, kPurposeAccept, step);
     return u < exp2f(lpt - lpd) ? 1 : 0;
+}
+__device__ __forceinline__ float accept_uniform(uint64_t seed, int r, int k, uint64_t step) {
+    return uniform24(seed, (uint64_t)r, (uint64_t)k, kPurposeAccept, step);
 }
 
 }  // namespace
@@ -159,10 +161,10 @@ __device__ __forceinline__ int accept_test(float zt, float zd, float c, Norm2 nt
 // directory entries and (member holding the drafted token) the accept flag.  s_tot[2] and
 // s_ok are this row's own LDS slots.
 template <int DTT, int DTD, int MODE>
-__device__ __forceinline__ void finish_row(const TeamArgs &a, int64_t row, int j, int r, int k, LaneRow<DTT> &tr,
+__device__ __forceinline__ void finish_row(const TeamArgs &a, int64_t row, int j, LaneRow<DTT> &tr,
                                            LaneRow<DTD> &dr, const ThreadStats &ts, bool owner, float zx_t,
-                                           float zx_d, uint32_t tag, TeamRed &red, uint32_t *pay, Norm2 *s_tot,
-                                           int *s_ok) {
+                                           float zx_d, float ua, uint32_t tag, TeamRed &red, uint32_t *pay,
+                                           Norm2 *s_tot, int *s_ok) {
     const int S = a.S;
     const float c = a.c;
     const int w = threadIdx.x / kWave;
@@ -193,7 +195,7 @@ __device__ __forceinline__ void finish_row(const TeamArgs &a, int64_t row, int j
         putf(a.apart + row * S + j, al, tag);
         if (MODE == kTeamStoch && owner) {   // accept test and the row normalisers of this row
             uint64_t *ac = a.acc + kAccWords * row;
-            put(ac, (uint32_t)accept_test(zx_t, zx_d, c, nt, nd, a.seed, r, k, a.step), tag);
+            put(ac, (uint32_t)accept_test(zx_t, zx_d, c, nt, nd, ua), tag);
             putf(ac + 1, nt.hi, tag);
             putf(ac + 2, nd.hi, tag);
             putf(ac + 3, nt.lo, tag);
@@ -243,7 +245,13 @@ __device__ __forceinline__ void row_member(const TeamArgs &a, int j, int64_t row
 
     float zx_t = 0.f, zx_d = 0.f;
     bool owner = false;
-    if constexpr (MODE == kTeamStoch) token_logits<DTT, DTD>(trow, drow, x, V, j, zx_t, zx_d, owner);
+    // The accept uniform depends on the row alone: the member holding the token draws it now,
+    // while its chunk loads are in flight, rather than after pass 2.
+    float ua = 0.f;
+    if constexpr (MODE == kTeamStoch) {
+        token_logits<DTT, DTD>(trow, drow, x, V, j, zx_t, zx_d, owner);
+        if (x >= 0 && x < V && x / kTeamChunk == j) ua = accept_uniform(a.seed, r, k, a.step);
+    }
 
     constexpr bool want_amax = MODE == kTeamGreedy || AMAX;
     float mt = 0.f, md = 0.f;
@@ -277,7 +285,7 @@ __device__ __forceinline__ void row_member(const TeamArgs &a, int j, int64_t row
     }
     publish_partials(part, S, j, ts, tag, red);
     // ---- phase 2 ----
-    finish_row<DTT, DTD, MODE>(a, row, j, r, k, tr, dr, ts, owner, zx_t, zx_d, tag, red, pay, s_tot, s_ok);
+    finish_row<DTT, DTD, MODE>(a, row, j, tr, dr, ts, owner, zx_t, zx_d, ua, tag, red, pay, s_tot, s_ok);
 }
 
 // Bonus slot of request r (target row L): per-wave-range masses against the member's
@@ -645,7 +653,7 @@ __device__ __forceinline__ void finalize_request(const TeamArgs &a, int r, FinSh
                 } else if (okx) {   // the owner member handed over: run the test here
                     const float zt = load1<DTT>(row_ptr<DTT>(a.target, (int64_t)r * a.trows + k, a.ld_t), x);
                     const float zd = load1<DTD>(row_ptr<DTD>(a.draft, (int64_t)r * K + k, a.ld_d), x);
-                    acc = accept_test(zt, zd, c, nt, nd, a.seed, r, k, a.step);
+                    acc = accept_test(zt, zd, c, nt, nd, accept_uniform(a.seed, r, k, a.step));
                 } else {
                     acc = 0;
                 }

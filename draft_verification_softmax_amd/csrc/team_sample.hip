@@ -232,6 +232,8 @@ __device__ __forceinline__ void sample_finalize(const TeamArgs &a, int fb, Sampl
     const uint32_t tag = read_epoch(a.epoch) + 1;
     const uint64_t *part = a.part + row * (int64_t)(8 * S);
     const void *drow = row_ptr<DT>(a.draft, row, a.ld_d);
+    // the draw's uniform depends on the row alone: drawn before the wait for the members
+    const float u = GREEDY ? 0.f : uniform24(a.seed, (uint64_t)r, (uint64_t)k, kPurposeDraft, a.step);
     bool got;
     if constexpr (GREEDY) got = wave_gather(part, 2 * S, part + 4 * S, 2 * S, tag, pay, a.fin_ticks);
     else got = wave_gather(part, S, a.dir + row * nseg, nseg, tag, pay, a.fin_ticks);
@@ -272,7 +274,6 @@ __device__ __forceinline__ void sample_finalize(const TeamArgs &a, int fb, Sampl
         wave_sync();
         // R: lane partials summed in lane order; the range by inverse CDF in range order
         const double R = __shfl(wave_incl_scan(part_sum), kWave - 1, kWave);
-        const float u = uniform24(a.seed, (uint64_t)r, (uint64_t)k, kPurposeDraft, a.step);
         const double t = (double)u * R;
         double ex = 0.0;
         const int sidx = wave_find([&](int q) { return mass[q]; }, nseg, t, &ex);
