@@ -188,6 +188,12 @@ class Timed:
         self.avg_launch_s = sum(self.per_launch_ms) / n / 1e3
         return self
 
+    def percentiles_us(self):
+        """p10 / median / p90 of the per-launch event times, in microseconds."""
+        xs = sorted(self.per_launch_ms)
+        pick = lambda f: round(xs[min(len(xs) - 1, int(f * (len(xs) - 1) + 0.5))] * 1e3, 2)
+        return {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9)}
+
 
 def bench_verify(args, sv, workloads, torch, name):
     """dfly | mtp | budget: sv_verify_batch (after sv_alloc_verify_budget for budget)."""
@@ -412,7 +418,7 @@ def main():
         },
         "cpu_baseline": r["cpu"],
         "extra": {"hbm_gbs": round(r["achieved"], 1), **r["extra"], "wall_s_timed_region": round(tm.wall, 4),
-                  "source_digest": digest},
+                  "launch_us": tm.percentiles_us(), "source_digest": digest},
     }
     print(json.dumps(line), flush=True)
 

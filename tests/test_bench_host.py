@@ -39,3 +39,14 @@ def test_traffic_calibration(tmp_path):
     assert t["stream_kernel"]["fetch_bytes"] == 1024 * 2048.0
     assert t["stream_kernel"]["write_bytes"] == 10 * 1024.0
     assert t["stream_kernel"]["dispatches"] == 2
+
+
+def test_launch_percentiles():
+    """p10 / median / p90 of the per-launch times: nearest rank on the sorted times, in us."""
+    import bench
+
+    t = bench.Timed(None, None)
+    t.per_launch_ms = [0.1 + 0.001 * i for i in range(401)][::-1]   # 100..500 us, unsorted
+    assert t.percentiles_us() == {"p10": 140.0, "p50": 300.0, "p90": 460.0}
+    t.per_launch_ms = [0.25]
+    assert t.percentiles_us() == {"p10": 250.0, "p50": 250.0, "p90": 250.0}
