@@ -210,13 +210,34 @@ __device__ __forceinline__ void wave_amax(float &v, int &i) {
     sched_fence();
 }
 
+// A double from the lane DPP control CTRL selects, 0 where there is none (rows outside
+// ROW_MASK also read 0).
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ double dpp_d(double x) {
+    const uint64_t b = (uint64_t)__double_as_longlong(x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, ROW_MASK, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, ROW_MASK, 0xF, false);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// A double from lane l, l the same in every lane of the wave (two scalar reads).
+__device__ __forceinline__ double readlane_d(double x, int l) {
+    const uint64_t b = (uint64_t)__double_as_longlong(x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Inclusive scan over the wave in lane order, in registers: shifts by 1, 2, 4 and 8 inside
+// each row of 16 lanes, then the last lane of row 0 (2) is added to row 1 (3), and the last
+// lane of row 1 to rows 2 and 3.  Every lane of the wave must call it.
 __device__ __forceinline__ double wave_incl_scan(double x) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const double y = __shfl_up(x, d, kWave);
-        if (lane >= d) x += y;
-    }
+    x += dpp_d<0x111>(x);        // row_shr:1
+    x += dpp_d<0x112>(x);        // row_shr:2
+    x += dpp_d<0x114>(x);        // row_shr:4
+    x += dpp_d<0x118>(x);        // row_shr:8
+    x += dpp_d<0x142, 0xA>(x);   // row_bcast:15 into rows 1 and 3
+    x += dpp_d<0x143, 0xC>(x);   // row_bcast:31 into rows 2 and 3
     return x;
 }
 
@@ -238,7 +259,7 @@ __device__ int wave_find(F weight, int n, double t, double *excl) {
         const uint64_t hit = __ballot(incl > t);
         if (hit) {
             const int l = __builtin_ctzll(hit);
-            const double e = __shfl(incl - x, l, kWave);
+            const double e = readlane_d(incl - x, l);
             *excl = e;
             return b + l;
         }
@@ -246,9 +267,9 @@ __device__ int wave_find(F weight, int n, double t, double *excl) {
         if (pos) {
             const int l = 63 - __builtin_clzll(pos);
             last_pos = b + l;
-            last_pos_excl = __shfl(incl - x, l, kWave);
+            last_pos_excl = readlane_d(incl - x, l);
         }
-        base = __shfl(incl, kWave - 1, kWave);
+        base = readlane_d(incl, kWave - 1);
     }
     *excl = last_pos_excl;
     return last_pos;

@@ -451,18 +451,18 @@ __device__ int draw_ranges(const void *trow, const void *drow, int V, float c, N
             // one pass: the inclusive scan gives R at its last lane and the crossing at once
             const double x = lane < nseg ? (double)dirv[lane] : 0.0;
             const double incl = wave_incl_scan(x);
-            const double t = (double)u * __shfl(incl, kWave - 1, kWave);
+            const double t = (double)u * readlane_d(incl, kWave - 1);
             const uint64_t hit = __ballot(incl > t);
             const uint64_t pos = __ballot(x > 0.0);
             const int l = hit ? __builtin_ctzll(hit) : (pos ? 63 - __builtin_clzll(pos) : 0);
-            ex = __shfl(incl - x, l, kWave);
+            ex = readlane_d(incl - x, l);
             sidx = (hit || pos) ? l : -1;
             if (lane == 0) s_ex = t - ex;
         } else {
             double part = 0.0;
             for (int q = lane; q < nseg; q += kWave) part += (double)dirv[q];
             // fixed order: lane partials summed in lane order
-            const double R = __shfl(wave_incl_scan(part), kWave - 1, kWave);
+            const double R = readlane_d(wave_incl_scan(part), kWave - 1);
             const double t = (double)u * R;
             sidx = wave_find([&](int q) { return dirv[q]; }, nseg, t, &ex);
             if (lane == 0) s_ex = t - ex;

@@ -186,13 +186,13 @@ __device__ int wave_draw_range(const void *row, int V, float c, Norm2 nb, int si
     const float x = range_weight(v < vend ? load1<DT>(row, v) : neg_inf(), c, nb);
     int k;
     if (hit) {
-        const double before = __shfl(incl - my, l, kWave);
+        const double before = readlane_d(incl - my, l);
         const uint64_t h = __ballot(before + wave_incl_scan((double)x) > rem);
         k = h ? __builtin_ctzll(h) : kFinLane - 1;   // rounding ran past the lane's logits: its last
     } else {
         k = 63 - __builtin_clzll(__ballot(x > 0.f) | 1ull);
     }
-    *w = __shfl(x, k, kWave);
+    *w = readlane_f(x, k);
     return base + k;
 }
 
@@ -273,7 +273,7 @@ __device__ __forceinline__ void sample_finalize(const TeamArgs &a, int fb, Sampl
         }
         wave_sync();
         // R: lane partials summed in lane order; the range by inverse CDF in range order
-        const double R = __shfl(wave_incl_scan(part_sum), kWave - 1, kWave);
+        const double R = readlane_d(wave_incl_scan(part_sum), kWave - 1);
         const double t = (double)u * R;
         double ex = 0.0;
         const int sidx = wave_find([&](int q) { return mass[q]; }, nseg, t, &ex);
