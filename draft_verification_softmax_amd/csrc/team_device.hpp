@@ -226,18 +226,28 @@ struct LaneRow {
         return fmaxf(m0, m1);
     }
 
-    // first slot (in vocabulary order) holding m; its vocabulary index
-    __device__ __forceinline__ int first_index(float m, int base) {
-        int idx = 0x7fffffff;
+    // The lane's maximum and the vocabulary index of its first occurrence (0x7fffffff when
+    // every logit is -inf), in one pass.  Two running maxima over the even and the odd slots
+    // keep the dependency chains short; each keeps the first slot of its maximum (slots are
+    // visited in vocabulary order), and equal maxima resolve to the lower slot.
+    __device__ __forceinline__ void max_first(int base, float &m, int &idx) {
+        float m0 = neg_inf(), m1 = neg_inf();
+        int s0 = -1, s1 = -1;
 #pragma unroll
-        for (int g = kTeamE - 8; g >= 0; g -= 8) {
+        for (int g = 0; g < kTeamE; g += 8) {
             refresh8(g);
 #pragma unroll
-            for (int i = g + 7; i >= g; --i)
-                if (get(i) == m) idx = base + (i >> 3) * 512 + lane_id() * 8 + (i & 7);
+            for (int i = g; i < g + 8; i += 2) {
+                const float z0 = get(i), z1 = get(i + 1);
+                if (z0 > m0) { m0 = z0; s0 = i; }
+                if (z1 > m1) { m1 = z1; s1 = i + 1; }
+            }
             sched_fence();
         }
-        return idx;
+        const bool take1 = m1 > m0 || (m1 == m0 && s1 >= 0 && s1 < s0);
+        m = take1 ? m1 : m0;
+        const int sl = take1 ? s1 : s0;
+        idx = sl < 0 ? 0x7fffffff : base + (sl >> 3) * 512 + lane_id() * 8 + (sl & 7);
     }
 
     // (M, s) of this lane's logits in base 2 (s = sum_i 2^{x_i c - M}) without a pass for

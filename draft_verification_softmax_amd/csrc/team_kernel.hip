@@ -255,17 +255,13 @@ __device__ __forceinline__ void row_member(const TeamArgs &a, int j, int64_t row
 
     constexpr bool want_amax = MODE == kTeamGreedy || AMAX;
     float mt = 0.f, md = 0.f;
-    // ---- argmax partials: chunk maximum, then the first index holding it ----
+    // ---- argmax partials: chunk maximum and the first index holding it ----
     if constexpr (want_amax) {
-        mt = tr.max();
-        md = dr.max();
+        int it, id;
+        tr.max_first(base, mt, it);
+        dr.max_first(base, md, id);
         float wt = mt, wd = md;
-        int i0 = 0, i1 = 0;
-        block_amax2(wt, i0, wd, i1, red);   // chunk maxima
-        int it = (mt == wt && mt != neg_inf()) ? tr.first_index(mt, base) : 0x7fffffff;
-        int id = (md == wd && md != neg_inf()) ? dr.first_index(md, base) : 0x7fffffff;
-        float ft = wt, fd = wd;
-        block_amax2(ft, it, fd, id, red);   // equal values: lowest index
+        block_amax2(wt, it, wd, id, red);   // larger value; equal values: lowest index
         if (threadIdx.x == 0) {
             putf(part + 4 * S + j, wt, tag);
             put(part + 5 * S + j, (uint32_t)it, tag);
@@ -305,14 +301,12 @@ __device__ __forceinline__ void bonus_member(const TeamArgs &a, int j, int64_t r
     sched_fence();
     const uint32_t tag = epoch + 1;
     if constexpr (MODE == kTeamGreedy) {
-        const float mb = br.max();
-        float wb = mb, wz = neg_inf();
-        int i0 = 0, i1 = 0;
-        block_amax2(wb, i0, wz, i1, red);
-        int ib = (mb == wb && mb != neg_inf()) ? br.first_index(mb, base) : 0x7fffffff;
-        float fb = wb, fz = neg_inf();
+        float wb;
+        int ib;
+        br.max_first(base, wb, ib);
+        float wz = neg_inf();
         int iz = 0x7fffffff;
-        block_amax2(fb, ib, fz, iz, red);
+        block_amax2(wb, ib, wz, iz, red);   // larger value; equal values: lowest index
         if (threadIdx.x == 0) {
             putf(part + 4 * S + j, wb, tag);
             put(part + 5 * S + j, (uint32_t)ib, tag);

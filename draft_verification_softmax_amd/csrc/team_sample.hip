@@ -49,14 +49,12 @@ __device__ __forceinline__ void sample_member(const TeamArgs &a, int j, int64_t 
     sched_fence();
     const uint32_t tag = epoch + 1;
     if constexpr (GREEDY) {
-        const float m = dr.max();
+        float m;
+        int im;
+        dr.max_first(base, m, im);
         float wm = m, wz = neg_inf();
-        int i0 = 0, i1 = 0;
-        block_amax2(wm, i0, wz, i1, red);   // chunk maximum
-        int im = (m == wm && m != neg_inf()) ? dr.first_index(m, base) : 0x7fffffff;
-        float fm = wm, fz = neg_inf();
         int iz = 0x7fffffff;
-        block_amax2(fm, im, fz, iz, red);   // its lowest index
+        block_amax2(wm, im, wz, iz, red);   // chunk maximum; equal values: lowest index
         // (M, s) at T = 1 against the wave maximum, for the confidence
         const float mw = wave_max(m);
         float M = (mw == neg_inf()) ? neg_inf() : mw * kLog2eF;
