@@ -77,6 +77,18 @@ __device__ inline bool last_arrival(const TeamArgs &a, int64_t i, int64_t n) {
     return true;
 }
 
+// The kernel's argument block (a TeamArgs, the kernel's first parameter, at the start of the
+// kernarg segment) through a pointer the compiler cannot see through: reads through it are
+// scalar loads of their own (the pointer still carries the constant address space the loads
+// need).  A kernel whose workgroups take one of two paths gives one path this view, so the
+// compiler does not merge the two paths' argument loads and hoist them above the branch,
+// where they would stay live, and spill, through the other path.
+__device__ __forceinline__ const TeamArgs &opaque_args() {
+    auto kp = (const __attribute__((address_space(4))) TeamArgs *)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(kp));
+    return *(const TeamArgs *)kp;
+}
+
 // Scalar load of a value that stays constant while the kernel runs (written, if at all, by
 // an earlier kernel on the stream), at a workgroup-uniform address.  It uses the scalar
 // counter, so waiting for it never waits for the vector loads of the chunk.

@@ -766,15 +766,6 @@ __device__ __forceinline__ void finalize_request(const TeamArgs &a, int r, FinSh
     }
 }
 
-// The kernel's argument block (its one parameter, at the start of the kernarg segment)
-// through a pointer the compiler cannot see through: reads through it are scalar loads of
-// their own (the pointer still carries the constant address space the loads need).
-__device__ __forceinline__ const TeamArgs &opaque_args() {
-    auto kp = (const __attribute__((address_space(4))) TeamArgs *)__builtin_amdgcn_kernarg_segment_ptr();
-    asm volatile("" : "+s"(kp));
-    return *(const TeamArgs *)kp;
-}
-
 // =======================================================================================
 // Verification grid: one member workgroup per (row pair, vocabulary chunk), then the
 // bonus slots, then one finalize workgroup per request

@@ -86,13 +86,6 @@ __device__ __forceinline__ void sample_member(const TeamArgs &a, int j, int64_t 
 
 namespace {
 
-// Orders this wave's LDS writes before its later LDS reads by other lanes.
-__device__ __forceinline__ void wave_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 constexpr int kRowsPerFinalize = kTeamThreads / kWave;   // one wave per row
 constexpr int kGatherMax = 5;                             // words per lane: S + nseg <= 5 * 64
 
@@ -204,13 +197,6 @@ union SampleShared {
     SampleFinShared f;
 };
 
-// The kernel's argument block through a pointer the compiler cannot see through (see the
-// verification kernel): the finalize's scalar loads are not hoisted above its branch.
-__device__ __forceinline__ const TeamArgs &sample_opaque_args() {
-    auto kp = (const __attribute__((address_space(4))) TeamArgs *)__builtin_amdgcn_kernarg_segment_ptr();
-    asm volatile("" : "+s"(kp));
-    return *(const TeamArgs *)kp;
-}
 
 // One wave per row (kRowsPerFinalize rows per workgroup, no workgroup barrier): gathers the
 // row's published words, merges them in member order, picks the range holding u R, and
@@ -241,7 +227,7 @@ __device__ __forceinline__ void sample_finalize(const TeamArgs &a, int fb, Sampl
         // epoch while the draws still run
         if (last_arrival(a, row, a.rows)) __hip_atomic_store(a.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    wave_sync();
+    wave_lds_sync();
     int tok = 0;
     float cf = 0.f;
     if constexpr (GREEDY) {
@@ -269,7 +255,7 @@ __device__ __forceinline__ void sample_finalize(const TeamArgs &a, int fb, Sampl
             mass[q] = (Mq == neg_inf()) ? 0.f : __uint_as_float(pay[S + q]) * exp2_fast((Mq - nb.hi) - nb.lo);
             part_sum += (double)mass[q];
         }
-        wave_sync();
+        wave_lds_sync();
         // R: lane partials summed in lane order; the range by inverse CDF in range order
         const double R = readlane_d(wave_incl_scan(part_sum), kWave - 1);
         const double t = (double)u * R;
@@ -294,7 +280,7 @@ __global__ __launch_bounds__(kTeamThreads) __attribute__((amdgpu_waves_per_eu(DT
     const int S = a.S;
     const unsigned members = (unsigned)a.rows * (unsigned)S;
     if (blockIdx.x >= members) {
-        sample_finalize<DT, GREEDY>(sample_opaque_args(), (int)(blockIdx.x - members), sh.f, tokens, conf);
+        sample_finalize<DT, GREEDY>(opaque_args(), (int)(blockIdx.x - members), sh.f, tokens, conf);
         return;
     }
     const int j = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % (unsigned)S));
