@@ -1,9 +1,10 @@
 // team_kernel.hip -- fused batched verification, one team of workgroups per row pair.
 //
-// Grid: (row slots) x S members; member j of row (r, k) owns logits
-// [j * 8192, (j + 1) * 8192) of target row (r, k) and drafter row (r, k).  Wave w of a member
-// owns the contiguous range [j * 8192 + w * 2048, +2048); lane l of that wave holds
-// logits base + g * 512 + l * 8 + (0..7), g = 0..3, in registers (16-byte non-temporal loads).
+// Grid: (row slots) x S members, then (verification) one finalize workgroup per request.
+// Member j of row (r, k) owns logits [j * 16384, (j + 1) * 16384) of target row (r, k) and
+// drafter row (r, k).  Wave w of a member owns the contiguous range [j * 16384 + w * 4096,
+// +4096); lane l of that wave holds logits base + g * 512 + l * 8 + (0..7), g = 0..7, in
+// registers (16-byte non-temporal loads).
 //
 // Definitions (AngelSpec tutorial page, section "From KL to an end-to-end TV loss"): the
 // overlap alpha = sum_v min(p_v, q_v); a rejected draft voids the later ones; the L_e2e
