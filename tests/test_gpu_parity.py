@@ -364,6 +364,25 @@ def test_device_error_flag_for_bad_token(sv):
     assert sv.sv_device_error(buf) == 0
 
 
+@pytest.mark.parametrize("T", [0.9, 0.0])
+def test_selected_with_zero_budget(sv, T):
+    """A budget of 0 selects no row: every request gets its bonus token from target row 0,
+    the same as dense verification with every draft length 0 (the grid holds only the bonus
+    slots and the finalize workgroups)."""
+    v, conf, _ = workloads.make_budget_inputs(device=DEV, T=T)
+    B, K = conf.shape
+    lens, off, rl = sv.sv_alloc_verify_budget(conf, 0)
+    assert int(lens.sum().item()) == 0 and int(off[-1].item()) == 0
+    _say(f"selected verify with no rows, T={T}")
+    sel = _np(sv.sv_verify_selected(v.target, v.draft, v.draft_tokens, T, lens, rl, 0, seed=v.seed, want_amax=True))
+    bat = _np(sv.sv_verify_batch(v.target, v.draft, v.draft_tokens, T, seed=v.seed, draft_len=lens, want_amax=True))
+    for key in bat:
+        if bat[key] is not None:
+            assert np.array_equal(sel[key], bat[key]), key
+    assert (sel["accept_len"] == 0).all() and (sel["n_out"] == 1).all()
+    assert ((sel["out_tokens"][:, 0] >= 0) & (sel["out_tokens"][:, 0] < v.target.shape[2])).all()
+
+
 def test_selected_row_left_out_is_flagged(sv):
     """A row list that leaves out a row its lengths include: that row is never streamed, so
     the request's finalize workgroup waits out its bound (about 20 ms per wait, two waits)
