@@ -383,6 +383,41 @@ def test_selected_with_zero_budget(sv, T):
     assert ((sel["out_tokens"][:, 0] >= 0) & (sel["out_tokens"][:, 0] < v.target.shape[2])).all()
 
 
+def test_graph_replay_matches_eager(sv):
+    """One verification call captured in a HIP graph and replayed: the call epoch lives on the
+    device, so every replay tags its words afresh.  Each replay (outputs cleared first) equals
+    the eager call, with other eager calls on the same workspace and synchronizations between
+    the replays."""
+    v = workloads.make_verify_inputs("dfly", device=DEV, T=0.9, B=8)
+    B, K, V = 8, 16, v.target.shape[2]
+    ref = _np(sv.sv_verify_batch(v.target, v.draft, v.draft_tokens, 0.9, seed=5, step=3, want_amax=True))
+    ws = sv.Workspace(DEV)
+    buf = ws.get(B, K, V)
+    out = sv.sv_verify_batch(v.target, v.draft, v.draft_tokens, 0.9, seed=5, step=3, workspace=buf, want_amax=True)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sv.sv_verify_batch(v.target, v.draft, v.draft_tokens, 0.9, seed=5, step=3, workspace=buf, out=out,
+                           want_amax=True)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        _say(f"graph replay {rep}")
+        for t in out.values():
+            if t is not None:
+                t.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        got = _np(out)
+        for key in ref:
+            if ref[key] is not None:
+                assert np.array_equal(got[key], ref[key]), (rep, key)
+        # eager work on the same workspace between the replays
+        sv.sv_verify_batch(v.target, v.draft, v.draft_tokens, 0.0 if rep % 2 else 0.9, seed=9, step=rep + 10,
+                           workspace=buf)
+        torch.cuda.synchronize()
+    assert sv.sv_device_error(buf) == 0
+
+
 def test_selected_row_left_out_is_flagged(sv):
     """A row list that leaves out a row its lengths include: that row is never streamed, so
     the request's finalize workgroup waits out its bound (about 20 ms per wait, two waits)
