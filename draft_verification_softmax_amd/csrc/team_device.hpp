@@ -281,6 +281,44 @@ struct LaneRow {
         }
     }
 
+    // sum_i 2^{x_i c - M}, each term kept in e[i] (M = -inf: every logit is -inf, every term 0).
+    __device__ __forceinline__ float exp_keep(float c, float M, float (&e)[kTeamE]) {
+        const float Mf = M == neg_inf() ? 0.f : M;
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int g = 0; g < kTeamE; g += 8) {
+            refresh8(g);
+#pragma unroll
+            for (int i = g; i < g + 8; i += 2) {
+                e[i] = exp2_fast(__builtin_fmaf(get(i), c, -Mf));
+                e[i + 1] = exp2_fast(__builtin_fmaf(get(i + 1), c, -Mf));
+                a0 += e[i];
+                a1 += e[i + 1];
+            }
+            sched_fence();
+        }
+        return a0 + a1;
+    }
+
+    // lane_ms with the terms kept in e.  The packed words are dead once e holds the terms:
+    // should the first-8 reference fail, the chunk is read again from the row.
+    template <bool FULL>
+    __device__ __forceinline__ void lane_ms_keep(float c, float &M, float &s, float (&e)[kTeamE], const void *row,
+                                                 int base, int V) {
+        refresh8(0);
+        const float m8 = fmaxf(fmaxf(fmaxf(get(0), get(1)), fmaxf(get(2), get(3))),
+                               fmaxf(fmaxf(get(4), get(5)), fmaxf(get(6), get(7))));
+        const float mw = wave_max(m8);
+        M = (mw == neg_inf()) ? neg_inf() : mw * c;
+        s = exp_keep(c, M, e);
+        if (__ballot(mw == neg_inf() || !(s < 0x1p100f))) {   // wave-uniform
+            load<FULL>(row, base, V);
+            const float m = wave_max(max());
+            M = (m == neg_inf()) ? neg_inf() : m * c;
+            s = exp_keep(c, M, e);
+        }
+    }
+
     // sum_i 2^{x_i c - M}
     __device__ __forceinline__ float exp_sum(float c, float M) {
         float a0 = 0.f, a1 = 0.f;
@@ -383,6 +421,55 @@ __device__ __forceinline__ void pass2(LaneRow<DTT> &t, LaneRow<DTD> &d, const Th
         (__builtin_fabsf(nt.lo) > kLoNegligible || __builtin_fabsf(nd.lo) > kLoNegligible) ? 1 : 0);
     alpha = min_sum(t, d, c, nt, nd, split);
     const float P = (s.Mt == neg_inf()) ? 0.f : s.st * exp2_fast((s.Mt - nt.hi) - nt.lo);   // this lane's target mass
+    resid = P - alpha;
+}
+
+// Pass 1 from the lane maxima, the terms kept in et, ed.
+template <int DTT, int DTD>
+__device__ __forceinline__ ThreadStats pass1_keep(LaneRow<DTT> &t, LaneRow<DTD> &d, float mt, float md, float c,
+                                                  float (&et)[kTeamE], float (&ed)[kTeamE]) {
+    mt = wave_max(mt);
+    md = wave_max(md);
+    ThreadStats s;
+    s.Mt = (mt == neg_inf()) ? neg_inf() : mt * c;
+    s.Md = (md == neg_inf()) ? neg_inf() : md * c;
+    s.st = t.exp_keep(c, s.Mt, et);
+    s.sd = d.exp_keep(c, s.Md, ed);
+    return s;
+}
+
+// Pass 2 over the kept terms.  With p_i = et_i A and q_i = ed_i B (A = 2^{Mt - Nt},
+// B = 2^{Md - Nd}, both uniform over the wave), sum min(p_i, q_i) is taken as
+// A sum min(et_i, ed_i B/A) when A >= B, else B sum min(et_i A/B, ed_i): one multiply, a
+// min and an add per pair, and the ratio is at most 1, so no product overflows.
+__device__ __forceinline__ void pass2_keep(const float (&et)[kTeamE], const float (&ed)[kTeamE], const ThreadStats &s,
+                                           Norm2 nt, Norm2 nd, float &alpha, float &resid) {
+    const float lA = __uint_as_float(__builtin_amdgcn_readfirstlane(
+        __float_as_uint(s.Mt == neg_inf() ? neg_inf() : (s.Mt - nt.hi) - nt.lo)));
+    const float lB = __uint_as_float(__builtin_amdgcn_readfirstlane(
+        __float_as_uint(s.Md == neg_inf() ? neg_inf() : (s.Md - nd.hi) - nd.lo)));
+    float a0 = 0.f, a1 = 0.f;
+    alpha = 0.f;
+    if (lA == neg_inf() || lB == neg_inf()) {
+        // one of the rows has no mass in this wave's range: no overlap
+    } else if (lA >= lB) {
+        const float R = exp2_fast(lB - lA);
+#pragma unroll
+        for (int i = 0; i < kTeamE; i += 2) {
+            a0 += fminf(et[i], ed[i] * R);
+            a1 += fminf(et[i + 1], ed[i + 1] * R);
+        }
+        alpha = (a0 + a1) * exp2_fast(lA);
+    } else {
+        const float R = exp2_fast(lA - lB);
+#pragma unroll
+        for (int i = 0; i < kTeamE; i += 2) {
+            a0 += fminf(et[i] * R, ed[i]);
+            a1 += fminf(et[i + 1] * R, ed[i + 1]);
+        }
+        alpha = (a0 + a1) * exp2_fast(lB);
+    }
+    const float P = (s.Mt == neg_inf()) ? 0.f : s.st * exp2_fast(lA);   // this lane's target mass
     resid = P - alpha;
 }
 

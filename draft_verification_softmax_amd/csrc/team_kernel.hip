@@ -1,6 +1,8 @@
 // team_kernel.hip -- fused batched verification, one team of workgroups per row pair.
 //
 // Grid: (row slots) x S members, then (verification) one finalize workgroup per request.
+// A grid that fits on the device at once runs a variant whose lanes keep pass 1's terms in
+// binary32 for pass 2 (fewer instructions, fewer waves per SIMD).
 // Member j of row (r, k) owns logits [j * 16384, (j + 1) * 16384) of target row (r, k) and
 // drafter row (r, k).  Wave w of a member owns the contiguous range [j * 16384 + w * 4096,
 // +4096); lane l of that wave holds logits base + g * 512 + l * 8 + (0..7), g = 0..7, in
@@ -14,6 +16,8 @@
 
 #include <math.h>
 #include <stdint.h>
+
+#include <atomic>
 
 #include "specverify.h"
 #include "sv_device.hpp"
@@ -54,6 +58,11 @@ TeamLayout team_layout(int B, int slots, int V, size_t ws_bytes) {
 }
 
 namespace {
+
+// A grid of at most this many workgroups per compute unit runs with the kept terms (three
+// waves per SIMD, one wave of each workgroup on each SIMD).
+constexpr int kKeepWgPerCu = 3;
+constexpr int kMaxDevices = 64;
 
 // ---- request-level helpers --------------------------------------------------------------
 
@@ -160,10 +169,12 @@ __device__ __forceinline__ float accept_uniform(uint64_t seed, int r, int k, uin
 // Phase 2 of a row: wait (bounded) for the team's partials, reduce them in member order to
 // the row normalisers, then publish this member's share of alpha, its residual-mass
 // directory entries and (member holding the drafted token) the accept flag.  s_tot[2] and
-// s_ok are this row's own LDS slots.
-template <int DTT, int DTD, int MODE>
+// s_ok are this row's own LDS slots.  KEEP: pass 2 runs over the terms pass 1 kept in et, ed
+// instead of the packed words.
+template <int DTT, int DTD, int MODE, bool KEEP>
 __device__ __forceinline__ void finish_row(const TeamArgs &a, int64_t row, int j, LaneRow<DTT> &tr,
-                                           LaneRow<DTD> &dr, const ThreadStats &ts, bool owner, float zx_t,
+                                           LaneRow<DTD> &dr, const float (&et)[kTeamE],
+                                           const float (&ed)[kTeamE], const ThreadStats &ts, bool owner, float zx_t,
                                            float zx_d, float ua, uint32_t tag, TeamRed &red, uint32_t *pay,
                                            Norm2 *s_tot, int *s_ok) {
     const int S = a.S;
@@ -186,7 +197,8 @@ __device__ __forceinline__ void finish_row(const TeamArgs &a, int64_t row, int j
     }
     const Norm2 nt = s_tot[0], nd = s_tot[1];
     float al, rs;
-    pass2(tr, dr, ts, c, nt, nd, al, rs);
+    if constexpr (KEEP) pass2_keep(et, ed, ts, nt, nd, al, rs);
+    else pass2(tr, dr, ts, c, nt, nd, al, rs);
     if constexpr (MODE == kTeamStoch) {
         rs = fmaxf(wave_sum(rs), 0.f);
         if (lane_id() == 0) putf(a.dir + row * a.nseg + j * kTeamWaves + w, rs, tag);
@@ -217,8 +229,8 @@ __device__ __forceinline__ void token_logits(const void *trow, const void *drow,
 }
 
 // One member's work on a verified row pair (not a bonus slot).  FULL: its chunk lies inside
-// the row.
-template <int DTT, int DTD, int MODE, bool AMAX, bool FULL>
+// the row.  KEEP: pass 1 keeps its terms for pass 2 (more registers per lane, less issue).
+template <int DTT, int DTD, int MODE, bool AMAX, bool FULL, bool KEEP>
 __device__ __forceinline__ void row_member(const TeamArgs &a, int j, int64_t row, int r, int k, TeamRed &red,
                                            uint32_t *pay, Norm2 *s_tot, int *s_ok) {
     const int S = a.S;
@@ -274,7 +286,15 @@ __device__ __forceinline__ void row_member(const TeamArgs &a, int j, int64_t row
 
     // ---- phase 1 (the exact maxima serve as the references when they were needed anyway) ----
     ThreadStats ts;
-    if constexpr (want_amax) {
+    float et[kTeamE], ed[kTeamE];
+    if constexpr (KEEP) {
+        if constexpr (want_amax) {
+            ts = pass1_keep(tr, dr, mt, md, c, et, ed);
+        } else {
+            tr.template lane_ms_keep<FULL>(c, ts.Mt, ts.st, et, trow, base, V);
+            dr.template lane_ms_keep<FULL>(c, ts.Md, ts.sd, ed, drow, base, V);
+        }
+    } else if constexpr (want_amax) {
         ts = pass1(tr, dr, mt, md, c);
     } else {
         tr.lane_ms(c, ts.Mt, ts.st);
@@ -282,7 +302,8 @@ __device__ __forceinline__ void row_member(const TeamArgs &a, int j, int64_t row
     }
     publish_partials(part, S, j, ts, tag, red);
     // ---- phase 2 ----
-    finish_row<DTT, DTD, MODE>(a, row, j, tr, dr, ts, owner, zx_t, zx_d, ua, tag, red, pay, s_tot, s_ok);
+    finish_row<DTT, DTD, MODE, KEEP>(a, row, j, tr, dr, et, ed, ts, owner, zx_t, zx_d, ua, tag, red, pay, s_tot,
+                                     s_ok);
 }
 
 // Bonus slot of request r (target row L): per-wave-range masses against the member's
@@ -772,9 +793,14 @@ __device__ __forceinline__ void finalize_request(const TeamArgs &a, int r, FinSh
 // bonus slots, then one finalize workgroup per request
 // =======================================================================================
 // AMAX: also publish the argmax partials (always in greedy mode; on request otherwise).
-// At most 96 registers per lane, so five waves share each SIMD.
-template <int DTT, int DTD, int MODE, bool AMAX>
-__global__ __launch_bounds__(kTeamThreads) __attribute__((amdgpu_waves_per_eu(5))) void stream_kernel(TeamArgs a) {
+// At most 96 registers per lane, so five waves share each SIMD.  KEEP (not greedy): each lane
+// keeps pass 1's terms in binary32 for pass 2, which then costs a multiply, a min and an add per
+// logit pair instead of two widenings, two FMAs, a min, an exponential and an add; the terms
+// take ~160 registers, so three waves share a SIMD.  The launch takes it only for a grid that
+// fits on the device at once at that occupancy, where fewer waves per SIMD cost nothing.
+template <int DTT, int DTD, int MODE, bool AMAX, bool KEEP>
+__global__ __launch_bounds__(kTeamThreads) __attribute__((amdgpu_waves_per_eu(KEEP ? 3 : 5))) void stream_kernel(
+    TeamArgs a) {
     __shared__ typename KernelShared<MODE>::type sh;
 
     // The S members of a team are consecutive workgroups: round-robin dispatch spreads them
@@ -825,9 +851,9 @@ __global__ __launch_bounds__(kTeamThreads) __attribute__((amdgpu_waves_per_eu(5)
         return;
     }
     if ((j + 1) * kTeamChunk <= a.V)
-        row_member<DTT, DTD, MODE, AMAX, true>(a, j, row, r, k, ms.red, ms.pay, ms.tot, &ms.ok);
+        row_member<DTT, DTD, MODE, AMAX, true, KEEP>(a, j, row, r, k, ms.red, ms.pay, ms.tot, &ms.ok);
     else
-        row_member<DTT, DTD, MODE, AMAX, false>(a, j, row, r, k, ms.red, ms.pay, ms.tot, &ms.ok);
+        row_member<DTT, DTD, MODE, AMAX, false, KEEP>(a, j, row, r, k, ms.red, ms.pay, ms.tot, &ms.ok);
 }
 
 // =======================================================================================
@@ -874,6 +900,27 @@ __global__ __launch_bounds__(kTeamThreads) void e2e_alpha_kernel(TeamArgs a) {
     }
 }
 
+// Compute units of the current device, read once per device (0 when unknown).
+static int device_cus() {
+    static std::atomic<int> cached[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+        cached[dev].store(n, std::memory_order_relaxed);
+    return n > 0 ? n : 0;
+}
+
+template <int DTT, int DTD, bool KEEP>
+static void launch_stream_k(const TeamArgs &a, int mode, unsigned grid, hipStream_t s) {
+    if (mode == kTeamStoch && a.want_amax)
+        hipLaunchKernelGGL((stream_kernel<DTT, DTD, kTeamStoch, true, KEEP>), dim3(grid), dim3(kTeamThreads), 0, s, a);
+    else if (mode == kTeamStoch)
+        hipLaunchKernelGGL((stream_kernel<DTT, DTD, kTeamStoch, false, KEEP>), dim3(grid), dim3(kTeamThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((stream_kernel<DTT, DTD, kTeamAlpha, false, KEEP>), dim3(grid), dim3(kTeamThreads), 0, s, a);
+}
+
 template <int DTT, int DTD>
 static hipError_t launch_stream_t(const TeamArgs &a, int mode, hipStream_t s) {
     // verification: member workgroups of the verified rows and the bonus slots, then one
@@ -881,14 +928,14 @@ static hipError_t launch_stream_t(const TeamArgs &a, int mode, hipStream_t s) {
     const uint64_t items = a.selected ? (uint64_t)a.n_rows + (uint64_t)a.B : (uint64_t)a.rows;
     const unsigned grid = (unsigned)(items * (uint64_t)a.S + (mode == kTeamAlpha ? 0u : (uint64_t)a.B));
     if (grid == 0) return hipSuccess;
-    if (mode == kTeamStoch && a.want_amax)
-        hipLaunchKernelGGL((stream_kernel<DTT, DTD, kTeamStoch, true>), dim3(grid), dim3(kTeamThreads), 0, s, a);
-    else if (mode == kTeamStoch)
-        hipLaunchKernelGGL((stream_kernel<DTT, DTD, kTeamStoch, false>), dim3(grid), dim3(kTeamThreads), 0, s, a);
-    else if (mode == kTeamGreedy)
-        hipLaunchKernelGGL((stream_kernel<DTT, DTD, kTeamGreedy, true>), dim3(grid), dim3(kTeamThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL((stream_kernel<DTT, DTD, kTeamAlpha, false>), dim3(grid), dim3(kTeamThreads), 0, s, a);
+    if (mode == kTeamGreedy) {
+        hipLaunchKernelGGL((stream_kernel<DTT, DTD, kTeamGreedy, true, false>), dim3(grid), dim3(kTeamThreads), 0, s,
+                           a);
+    } else if ((uint64_t)grid <= (uint64_t)kKeepWgPerCu * (uint64_t)device_cus()) {
+        launch_stream_k<DTT, DTD, true>(a, mode, grid, s);   // every workgroup resident at once
+    } else {
+        launch_stream_k<DTT, DTD, false>(a, mode, grid, s);
+    }
     return hipGetLastError();
 }
 

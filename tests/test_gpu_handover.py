@@ -29,8 +29,8 @@ def sv():
         m.sv_set_wait_bound(200000)
 
 
-def _verify_case(sv, T, selected=False):
-    v = workloads.make_verify_inputs("mtp", device="cpu", T=T)
+def _verify_case(sv, T, selected=False, name="mtp", B=None):
+    v = workloads.make_verify_inputs(name, device="cpu", T=T, B=B)
     t, d, x = v.target.to(DEV), v.draft.to(DEV), v.draft_tokens.to(DEV)
     B, K = v.draft_tokens.shape
     ws = sv.Workspace(DEV)
@@ -57,6 +57,14 @@ def _verify_case(sv, T, selected=False):
 def test_verify_with_every_share_handed_over(sv, T):
     _say(f"hand-over verify MTP T={T}")
     _say(f"report {_verify_case(sv, T)}")
+
+
+def test_verify_large_grid_with_every_share_handed_over(sv):
+    # 8 requests x 16 drafts: 1096 workgroups, more than fit on the device at once at three
+    # per compute unit, so the variant without kept terms runs (the MTP case above runs the
+    # other one at T = 0.9)
+    _say("hand-over verify DFly B=8 T=0.9")
+    _say(f"report {_verify_case(sv, 0.9, name='dfly', B=8)}")
 
 
 def test_selected_verify_with_every_share_handed_over(sv):

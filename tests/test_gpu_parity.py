@@ -383,6 +383,37 @@ def test_selected_with_zero_budget(sv, T):
     assert ((sel["out_tokens"][:, 0] >= 0) & (sel["out_tokens"][:, 0] < v.target.shape[2])).all()
 
 
+def _keep_limit():
+    # workgroups of a verification grid that runs with the kept binary32 terms: three per CU
+    return 3 * torch.cuda.get_device_properties(0).multi_processor_count
+
+
+@pytest.mark.parametrize("T", [0.9, 0.3])
+def test_both_stream_variants_on_one_batch(sv, T):
+    """The same requests in a grid that fits on the device at once (kept terms) and in a larger
+    one (terms recomputed): both against the oracle, and equal to each other where the result
+    is discrete."""
+    big = workloads.make_verify_inputs("mtp", device="cpu", T=T, B=40)
+    B, K = big.draft_tokens.shape
+    S = (big.target.shape[-1] + 16383) // 16384
+    n_small, n_big = 16, B
+    assert (n_small * K + n_small) * S + n_small <= _keep_limit() < (n_big * K + n_big) * S + n_big
+    t, d, x = big.target.to(DEV), big.draft.to(DEV), big.draft_tokens.to(DEV)
+    _say(f"both variants T={T}: B={n_big} and its first {n_small} requests")
+    full = _np(sv.sv_verify_batch(t, d, x, T, seed=big.seed, want_amax=True))
+    part = _np(sv.sv_verify_batch(t[:n_small].contiguous(), d[:n_small].contiguous(), x[:n_small].contiguous(), T,
+                                  seed=big.seed, want_amax=True))
+    tn, dn = workloads.to_oracle(big.target), workloads.to_oracle(big.draft)
+    o = svref.verify_batch(tn, dn, big.draft_tokens.numpy(), T, "bf16", seed=big.seed, diagnostics=True)
+    compare_verify(full, o, tn, dn, "bf16", T)
+    os_ = svref.verify_batch(tn[:n_small], dn[:n_small], big.draft_tokens.numpy()[:n_small], T, "bf16",
+                             seed=big.seed, diagnostics=True)
+    compare_verify(part, os_, tn[:n_small], dn[:n_small], "bf16", T)
+    np.testing.assert_allclose(part["alpha"], full["alpha"][:n_small], rtol=1e-5, atol=1e-9)
+    for key in ("amax_t", "amax_d"):
+        assert np.array_equal(part[key], full[key][:n_small])
+
+
 def test_graph_replay_matches_eager(sv):
     """One verification call captured in a HIP graph and replayed: the call epoch lives on the
     device, so every replay tags its words afresh.  Each replay (outputs cleared first) equals
