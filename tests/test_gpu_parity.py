@@ -414,6 +414,34 @@ def test_both_stream_variants_on_one_batch(sv, T):
         assert np.array_equal(part[key], full[key][:n_small])
 
 
+@pytest.mark.parametrize("tdt,ddt,T,want_amax", [("f32", "f32", 0.9, False), ("f32", "f32", 1.7, True),
+                                                  ("bf16", "f32", 0.9, True), ("f32", "bf16", 0.9, False)])
+def test_fp32_and_mixed_logits_large_grid(sv, tdt, ddt, T, want_amax):
+    """binary32 and mixed-dtype logits in a grid above the kept-term threshold (64 x 16 rows of
+    a ragged vocabulary 9001 in rows padded to 9008), so the 96-register instances run; the
+    small fp32 cases elsewhere run the kept-term ones."""
+    B, K, V, ld = 64, 16, 9001, 9008
+    assert (B * K + B) * 1 + B > _keep_limit()
+    g = torch.Generator(device=DEV).manual_seed(23)
+    tt_ = torch.bfloat16 if tdt == "bf16" else torch.float32
+    dt_ = torch.bfloat16 if ddt == "bf16" else torch.float32
+    tt = torch.full((B, K + 1, ld), float("nan"), device=DEV, dtype=tt_)
+    dd = torch.full((B, K, ld), float("nan"), device=DEV, dtype=dt_)
+    t = 2.5 * torch.randn((B, K + 1, V), generator=g, device=DEV)
+    d = t[:, :K] + 0.8 * torch.randn((B, K, V), generator=g, device=DEV)
+    tt[..., :V] = t.to(tt_)
+    dd[..., :V] = d.to(dt_)
+    toks = torch.argmax(d, -1).to(torch.int32)
+    toks[:, 2] = torch.randint(0, V, (B,), generator=g, device=DEV, dtype=torch.int32)
+    _say(f"large-grid {tdt}/{ddt} T={T} amax={want_amax}")
+    out = _np(sv.sv_verify_batch(tt[..., :V], dd[..., :V], toks, T, seed=4, step=2, want_amax=want_amax))
+    # bfloat16 values are exact in binary32: the oracle takes both rows as binary32
+    tn = tt[..., :V].float().cpu().numpy()
+    dn = dd[..., :V].float().cpu().numpy()
+    o = svref.verify_batch(tn, dn, toks.cpu().numpy(), T, "f32", seed=4, step=2, diagnostics=True)
+    _say(f"report {compare_verify(out, o, tn, dn, 'f32', T)}")
+
+
 def test_graph_replay_matches_eager(sv):
     """One verification call captured in a HIP graph and replayed: the call epoch lives on the
     device, so every replay tags its words afresh.  Each replay (outputs cleared first) equals
