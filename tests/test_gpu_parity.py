@@ -608,11 +608,22 @@ def test_largest_vocabulary(sv):
         _run_pair(sv, _custom(t, d, toks, T, "V=2^20"), T)
 
 
-def test_masked_logits(sv):
+def _grid(B, K, V):
+    """Workgroups of a dense verification grid: members of every row and bonus slot, then the
+    finalize workgroups."""
+    return (B * K + B) * ((V + 16383) // 16384) + B
+
+
+@pytest.mark.parametrize("B", [4, 64])
+def test_masked_logits(sv, B):
     """-inf logits (masked vocabulary): p or q is exactly 0 there; drafted tokens inside the
-    target's mask are always rejected, and no emitted token is a masked one."""
+    target's mask are always rejected, and no emitted token is a masked one.  B = 4 runs the
+    kept-term instance, B = 64 (832 workgroups) the other; in both, the drafter's wave range
+    [8192, 12288) starts with 512 masked logits, so every lane's first 8 are -inf, its
+    provisional reference is -inf and the exact-maximum fallback runs."""
     g = torch.Generator(device=DEV).manual_seed(5)
-    B, K, V = 4, 5, 20000
+    K, V = 5, 20000
+    assert (_grid(B, K, V) > _keep_limit()) == (B == 64)
     t = 2.0 * torch.randn((B, K + 1, V), generator=g, device=DEV)
     d = t[:, :K] + torch.randn((B, K, V), generator=g, device=DEV)
     t[..., 5000:9000] = float("-inf")
@@ -630,12 +641,14 @@ def test_masked_logits(sv):
             assert (gg["accept"][:, 0] == 0).all()
 
 
-@pytest.mark.parametrize("T", [0.005, 0.02, 25.0])
-def test_extreme_temperatures(sv, T):
+@pytest.mark.parametrize("T,B", [(0.005, 4), (0.02, 4), (25.0, 4), (0.005, 48), (0.02, 48)])
+def test_extreme_temperatures(sv, T, B):
     """Very low temperatures (base-2 normalisers of several hundred to a few thousand, past
     what one binary32 value holds to 1e-5, and sums far from the provisional reference: the
-    exact-maximum fallback) and a very high one (nearly uniform rows)."""
-    v = _move(workloads.make_verify_inputs("mtp", device="cpu", T=T, B=4, K=3, V=50000))
+    exact-maximum fallback) and a very high one (nearly uniform rows).  B = 4 runs the
+    kept-term instance, B = 48 (816 workgroups) the other."""
+    assert (_grid(B, 3, 50000) > _keep_limit()) == (B == 48)
+    v = _move(workloads.make_verify_inputs("mtp", device="cpu", T=T, B=B, K=3, V=50000))
     _run_pair(sv, v, T)
 
 
