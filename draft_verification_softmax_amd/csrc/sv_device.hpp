@@ -157,13 +157,33 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
+// Order-preserving map of binary32 bit patterns (no NaN) to unsigned integers: positive
+// values get the top bit set, negative ones are complemented.  The unsigned maximum of keys
+// is the key of the floating maximum, and an integer maximum needs no NaN quieting of its
+// operands, so each exchange step is one DPP-fused instruction.
+__device__ __forceinline__ uint32_t fkey(float x) {
+    const uint32_t b = __float_as_uint(x);
+    return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
+}
+__device__ __forceinline__ float fkey_inv(uint32_t k) { return __uint_as_float(k ^ ((k >> 31) ? 0x80000000u : 0xffffffffu)); }
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t kmax_step(uint32_t k) {
+    const uint32_t o = (uint32_t)dpp_i<CTRL>((int)k);
+    return k > o ? k : o;
+}
+
 __device__ __forceinline__ float wave_max(float x) {
     sched_fence();
-    x = fmaxf(x, dpp_f<0xB1>(x));
-    x = fmaxf(x, dpp_f<0x4E>(x));
-    x = fmaxf(x, dpp_f<0x141>(x));
-    x = fmaxf(x, dpp_f<0x140>(x));
-    x = fmaxf(fmaxf(readlane_f(x, 0), readlane_f(x, 16)), fmaxf(readlane_f(x, 32), readlane_f(x, 48)));
+    uint32_t k = fkey(x);
+    k = kmax_step<0xB1>(k);
+    k = kmax_step<0x4E>(k);
+    k = kmax_step<0x141>(k);
+    k = kmax_step<0x140>(k);
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)k, 0), r1 = (uint32_t)__builtin_amdgcn_readlane((int)k, 16);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)k, 32), r3 = (uint32_t)__builtin_amdgcn_readlane((int)k, 48);
+    const uint32_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
+    x = fkey_inv(a > b ? a : b);
     sched_fence();
     return x;
 }
