@@ -1,8 +1,10 @@
 """ctypes binding of libspecverify.so: argument marshalling only.
 
-Tensors must live on the GPU; their ``data_ptr()`` and ``torch.cuda.current_stream()``
-are handed to the C entry points unchanged.  Output tensors are allocated here with torch
-(device memory plumbing) when the caller does not pass them.
+Tensors must live on the GPU; their ``data_ptr()`` and the launch stream (default
+``torch.cuda.current_stream()``) are handed to the C entry points unchanged.  Output tensors
+are allocated here with torch (device memory plumbing) when the caller does not pass them,
+and calls without a workspace share one per (device, launch stream).  ``PreparedVerify``
+marshals a verification call once for repeated launches.
 """
 import ctypes as C
 import os
@@ -130,8 +132,49 @@ class Workspace:
         need = sv_workspace_bytes(B, K_max, V)
         if self.buf is None or self.buf.numel() < need:
             self.buf = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
+            fs = _foreign(stream)
+            if fs is not None:   # allocated on the current stream, used on the launch stream
+                self.buf.record_stream(fs)
             sv_workspace_init(self.buf, stream)
         return self.buf
+
+
+_default_ws = {}
+
+
+def default_workspace(device=None, stream=None) -> Workspace:
+    """The workspace of calls that pass none: one per (device, launch stream), kept for the
+    life of the process, so such calls do not allocate and zero a workspace each time and
+    their device error flags stay readable (sv_device_error(default_workspace().buf))."""
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    key = (s.device.index, s.cuda_stream)
+    ws = _default_ws.get(key)
+    if ws is None:
+        ws = _default_ws[key] = Workspace(s.device)
+    return ws
+
+
+def _foreign(stream):
+    """The launch stream when it is not its device's current stream, else None.  Tensors
+    allocated here come from the current stream's pool; when another stream runs the kernel
+    that uses them they are recorded on it, so the caching allocator does not hand their
+    memory to a new tensor while that kernel may still use it."""
+    if stream is None:
+        return None
+    return None if torch.cuda.current_stream(stream.device).cuda_stream == stream.cuda_stream else stream
+
+
+def _ws_for(workspace, dev, B, K, V, stream):
+    if isinstance(workspace, torch.Tensor):
+        return workspace
+    return (workspace or default_workspace(dev, stream)).get(B, K, V, stream)
+
+
+def _record(fs, *tensors):
+    if fs is not None:
+        for t in tensors:
+            if t is not None:
+                t.record_stream(fs)
 
 
 def _rows_ld(t):
@@ -179,8 +222,10 @@ def sv_verify_selected(target, draft, draft_tokens, T, lens, row_list, n_rows, s
                    workspace, out, stream, selected=True)
 
 
-def _verify(target, draft, draft_tokens, T, seed, step, draft_len, row_list, n_rows, want_lse, want_amax, workspace,
-            out, stream, selected=False):
+def _prepare_verify(target, draft, draft_tokens, T, seed, step, draft_len, row_list, n_rows, want_lse, want_amax,
+                    workspace, out, stream, selected=False):
+    """Checks shapes and marshals one verification call: returns (entry point, argument
+    tuple, the Params it points to, outputs, the workspace)."""
     B, K1, V = target.shape
     K = K1 - 1
     if draft.shape != (B, K, V) or draft_tokens.shape != (B, K):
@@ -192,6 +237,7 @@ def _verify(target, draft, draft_tokens, T, seed, step, draft_len, row_list, n_r
     _check_rows(target, K + 1)
     _check_rows(draft, K)
     dev = target.device
+    fs = _foreign(stream)
     if out is None:
         out = dict(
             alpha=torch.empty((B, K), dtype=torch.float32, device=dev),
@@ -204,24 +250,67 @@ def _verify(target, draft, draft_tokens, T, seed, step, draft_len, row_list, n_r
             out_tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
             n_out=torch.empty((B,), dtype=torch.int32, device=dev),
         )
-    ws = workspace if isinstance(workspace, torch.Tensor) else (workspace or Workspace(dev)).get(B, K, V, stream)
+        _record(fs, *out.values())
+    ws = _ws_for(workspace, dev, B, K, V, stream)
     prm = _params(B, K, V, target, draft, T, seed, step)
     outs = (_p(out["alpha"]), _p(out["accept"]), _p(out["lse_t"]), _p(out["lse_d"]), _p(out["amax_t"]),
             _p(out["amax_d"]), _p(out["accept_len"]), _p(out["out_tokens"]), _p(out["n_out"]))
     if selected:
-        rc = lib().sv_verify_selected(C.byref(prm), _p(target), _p(draft), _p(draft_tokens), _p(draft_len),
-                                      _p(row_list), n_rows, *outs, _p(ws), ws.numel(), _stream(stream))
-        _check("sv_verify_selected", rc)
+        fn = lib().sv_verify_selected
+        args = (C.byref(prm), _p(target), _p(draft), _p(draft_tokens), _p(draft_len), _p(row_list), n_rows, *outs,
+                _p(ws), ws.numel(), _stream(stream))
     else:
-        rc = lib().sv_verify_batch(C.byref(prm), _p(target), _p(draft), _p(draft_tokens), _p(draft_len), *outs,
-                                   _p(ws), ws.numel(), _stream(stream))
-        _check("sv_verify_batch", rc)
+        fn = lib().sv_verify_batch
+        args = (C.byref(prm), _p(target), _p(draft), _p(draft_tokens), _p(draft_len), *outs, _p(ws), ws.numel(),
+                _stream(stream))
+    return fn, args, prm, out, ws
+
+
+def _verify(target, draft, draft_tokens, T, seed, step, draft_len, row_list, n_rows, want_lse, want_amax, workspace,
+            out, stream, selected=False):
+    fn, args, _, out, _ = _prepare_verify(target, draft, draft_tokens, T, seed, step, draft_len, row_list, n_rows,
+                                          want_lse, want_amax, workspace, out, stream, selected)
+    _check("sv_verify_selected" if selected else "sv_verify_batch", fn(*args))
     return out
+
+
+class PreparedVerify:
+    """One verification call (sv_verify_batch, or sv_verify_selected when row_list is given)
+    marshalled once for repeated launches on the same buffers, as a decoding loop issues
+    them: launch(step) writes the generator's step counter (and optionally the seed) into the
+    stored parameters and calls the entry point with the stored arguments.  The tensors
+    passed here (inputs, outputs, workspace) must stay alive and in place while it is used;
+    the launch stream is fixed here (default: the current stream)."""
+
+    def __init__(self, target, draft, draft_tokens, T, seed=0, draft_len=None, row_list=None, n_rows=None,
+                 want_lse=True, want_amax=False, workspace=None, out=None, stream=None):
+        selected = row_list is not None
+        if selected:
+            if draft_len is None or draft_len.dtype != torch.int32:
+                raise ValueError("a selected-row call needs lens (draft_len) as int32 [B]")
+            if row_list.dtype != torch.int32 or n_rows is None or row_list.numel() < int(n_rows):
+                raise ValueError("row_list must be int32 with at least n_rows entries")
+        self.stream = torch.cuda.current_stream(target.device) if stream is None else stream
+        self._fn, self._args, self._prm, self.out, self.workspace = _prepare_verify(
+            target, draft, draft_tokens, T, seed, 0, draft_len, row_list, int(n_rows or 0), want_lse, want_amax,
+            workspace, out, self.stream, selected)
+        self._keep = (target, draft, draft_tokens, draft_len, row_list)
+        self._name = "sv_verify_selected" if selected else "sv_verify_batch"
+
+    def launch(self, step, seed=None):
+        self._prm.step = step
+        if seed is not None:
+            self._prm.seed = seed
+        rc = self._fn(*self._args)
+        if rc:
+            raise SVError(self._name, rc)
+        return self.out
 
 
 def sv_accept_len(accept, draft_len=None, out=None, stream=None):
     B, K = accept.shape
     out = torch.empty((B,), dtype=torch.int32, device=accept.device) if out is None else out
+    _record(_foreign(stream), out)
     _check("sv_accept_len", lib().sv_accept_len(_p(accept), _p(draft_len), B, K, _p(out), _stream(stream)))
     return out
 
@@ -232,6 +321,7 @@ def sv_residual_sample(target, draft, accept_len, T, seed=0, step=0, draft_len=N
     _check_rows(target, K + 1)
     _check_rows(draft, K)
     out = torch.empty((B,), dtype=torch.int32, device=target.device) if out is None else out
+    _record(_foreign(stream), out)
     prm = _params(B, K, V, target, draft, T, seed, step)
     _check("sv_residual_sample", lib().sv_residual_sample(
         C.byref(prm), _p(target), _p(draft), _p(draft_len), _p(accept_len), _p(out), _stream(stream)))
@@ -248,7 +338,8 @@ def sv_tv_e2e_loss(target, draft, T=1.0, alpha=None, workspace=None, stream=None
     dev = target.device
     alpha = torch.empty((I, D), dtype=torch.float32, device=dev) if alpha is None else alpha
     loss = torch.empty((1,), dtype=torch.float32, device=dev)
-    ws = workspace if isinstance(workspace, torch.Tensor) else (workspace or Workspace(dev)).get(I, D, V, stream)
+    _record(_foreign(stream), alpha, loss)
+    ws = _ws_for(workspace, dev, I, D, V, stream)
     prm = _params(I, D, V, target, draft, T, 0, 0)
     _check("sv_tv_e2e_loss", lib().sv_tv_e2e_loss(C.byref(prm), _p(target), _p(draft), _p(alpha), _p(loss),
                                                   _p(ws), ws.numel(), _stream(stream)))
@@ -274,7 +365,8 @@ def sv_tv_e2e_backward(target, draft, alpha, T=1.0, grad_loss=None, grad_dtype=N
     elif grad.shape != (I, D, V):
         raise ValueError("grad must be [I][D][V]")
     _check_rows(grad, D)
-    ws = workspace if isinstance(workspace, torch.Tensor) else (workspace or Workspace(dev)).get(I, D, V, stream)
+    _record(_foreign(stream), grad)
+    ws = _ws_for(workspace, dev, I, D, V, stream)
     prm = _params(I, D, V, target, draft, T, 0, 0)
     _check("sv_tv_e2e_backward", lib().sv_tv_e2e_backward(
         C.byref(prm), _p(target), _p(draft), _p(alpha), _p(grad_loss), _p(grad), _dtype_code(grad), _rows_ld(grad),
@@ -293,7 +385,8 @@ def sv_sample_drafts(draft, T, seed=0, step=0, workspace=None, stream=None):
     if B == 0 or K == 0:
         return tokens, conf
     _check_rows(draft, K)
-    ws = workspace if isinstance(workspace, torch.Tensor) else (workspace or Workspace(dev)).get(B, K, V, stream)
+    _record(_foreign(stream), tokens, conf)
+    ws = _ws_for(workspace, dev, B, K, V, stream)
     prm = Params(B, K, V, _dtype_code(draft), _dtype_code(draft), float(T), seed, step, _rows_ld(draft), _rows_ld(draft))
     _check("sv_sample_drafts", lib().sv_sample_drafts(C.byref(prm), _p(draft), _p(tokens), _p(conf), _p(ws),
                                                       ws.numel(), _stream(stream)))
@@ -308,6 +401,7 @@ def sv_alloc_verify_budget(conf, budget_N, draft_len=None, want_row_list=True, s
     row_off = torch.empty((B + 1,), dtype=torch.int32, device=dev)
     n = min(int(budget_N), B * K)  # upper bound on the selected count
     row_list = torch.empty((max(n, 1),), dtype=torch.int32, device=dev) if want_row_list else None
+    _record(_foreign(stream), lens, row_off, row_list)
     _check("sv_alloc_verify_budget", lib().sv_alloc_verify_budget(
         _p(conf), _p(draft_len), B, K, int(budget_N), _p(lens), _p(row_off), _p(row_list), _stream(stream)))
     return lens, row_off, row_list
@@ -326,6 +420,7 @@ def sv_dcut_verify_budget(conf, cost, draft_len=None, want_row_list=True, stream
     lens = torch.empty((B,), dtype=torch.int32, device=dev)
     row_off = torch.empty((B + 1,), dtype=torch.int32, device=dev)
     row_list = torch.empty((max(B * K, 1),), dtype=torch.int32, device=dev) if want_row_list else None
+    _record(_foreign(stream), n_chosen, utility, lens, row_off, row_list)
     _check("sv_dcut_verify_budget", lib().sv_dcut_verify_budget(
         _p(conf), _p(draft_len), B, K, _p(cost), cost.numel(), _p(n_chosen), _p(utility), _p(lens), _p(row_off),
         _p(row_list), _stream(stream)))
@@ -336,6 +431,7 @@ def sv_uniforms(seed, counters, stream=None):
     """counters [n][4] uint64 (torch int64 on the GPU); returns float32 [n]."""
     n = counters.shape[0]
     out = torch.empty((n,), dtype=torch.float32, device=counters.device)
+    _record(_foreign(stream), out)
     _check("sv_uniforms", lib().sv_uniforms(C.c_uint64(seed), _p(counters), n, _p(out), _stream(stream)))
     return out
 

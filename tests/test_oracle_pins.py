@@ -198,6 +198,72 @@ def test_inverse_cdf_is_searchsorted():
         assert out["out_tokens"][r, tau] == int(np.searchsorted(cw, u * cw[-1], side="right"))
 
 
+def _widen_bf16(u16):
+    """bfloat16 bit patterns to float64 (the upper half of a binary32), independently of the
+    oracle's own widening."""
+    return (u16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [0.9, 1.7])
+def test_correction_cdf_is_cumsum_of_the_draw_weights(dtype, T):
+    """svref_correction_cdf (the parity checker's CDF-band test reads it) is the running sum
+    of the draw's weights: max(p_tau - q_tau, 0) after a rejection at tau < L_r, p at target
+    row L_r for the bonus token (the standard speculative-sampling rule that keeps the target
+    distribution).  Checked against scipy's softmax and numpy's cumsum at v = -1 (empty sum),
+    0, interior points and V - 1 (the total), for several rows, so a wrong row, wrong weights
+    (no clamp, q - p, p alone after a rejection) or an off-by-one in v fails."""
+    B, K, V = 3, 4, 257
+    rng = np.random.default_rng(71)
+    zt = (2.5 * rng.standard_normal((B, K + 1, V))).astype(np.float32)
+    zd = (zt[:, :K] + rng.standard_normal((B, K, V))).astype(np.float32)
+    zt[1, 2, 100:140] = -np.inf   # masked logits (p = 0 there)
+    if dtype == "bf16":
+        t16 = (zt.view(np.uint32) >> 16).astype(np.uint16)
+        d16 = (zd.view(np.uint32) >> 16).astype(np.uint16)
+        target, draft = t16, d16
+        zt64, zd64 = _widen_bf16(t16), _widen_bf16(d16)
+    else:
+        target, draft = zt, zd
+        zt64, zd64 = zt.astype(np.float64), zd.astype(np.float64)
+    p = special.softmax(zt64 / T, axis=-1)
+    q = special.softmax(zd64 / T, axis=-1)
+    for r, tau, L in [(0, 0, 4), (0, 3, 4), (1, 2, 4), (2, 1, 2), (0, 4, 4), (1, 2, 2), (2, 0, 0)]:
+        w = np.maximum(p[r, tau] - q[r, tau], 0.0) if tau < L else p[r, tau]
+        cw = np.cumsum(w)
+        for v in [-1, 0, 1, 57, 99, 120, 200, V - 2, V - 1]:
+            want = 0.0 if v < 0 else cw[v]
+            got = svref.correction_cdf(target, draft, T, dtype, r, tau, L, v)
+            assert got == pytest.approx(want, rel=1e-12, abs=1e-15), (r, tau, L, v)
+    # outside the domain: NaN
+    assert np.isnan(svref.correction_cdf(target, draft, T, dtype, 0, 3, 2, 0))     # tau > L_r
+    assert np.isnan(svref.correction_cdf(target, draft, T, dtype, 0, 0, 4, V))     # v >= V
+
+
+def test_correction_cdf_brackets_every_drawn_token():
+    """At every request of a verification, the drawn token x is the smallest v whose
+    cumulative weight exceeds the draw's target u R: cdf(x - 1) <= u R < cdf(x), with the
+    target and total mass the oracle reports (the band the parity checker uses)."""
+    B, K, V, T = 40, 3, 300, 0.9
+    rng = np.random.default_rng(72)
+    zt = (2.0 * rng.standard_normal((B, K + 1, V))).astype(np.float32)
+    zd = (zt[:, :K] + 1.2 * rng.standard_normal((B, K, V))).astype(np.float32)
+    qd = special.softmax(zd.astype(np.float64) / T, axis=-1)
+    toks = np.array([[rng.choice(V, p=qd[r, k]) for k in range(K)] for r in range(B)], np.int32)
+    out = svref.verify_batch(zt, zd, toks, T, "f32", seed=8, step=2, diagnostics=True)
+    p = special.softmax(zt.astype(np.float64) / T, axis=-1)
+    q = special.softmax(zd.astype(np.float64) / T, axis=-1)
+    for r in range(B):
+        tau = int(out["accept_len"][r])
+        x = int(out["out_tokens"][r, tau])
+        w = np.maximum(p[r, tau] - q[r, tau], 0.0) if tau < K else p[r, tau]
+        assert out["resid_mass"][r] == pytest.approx(w.sum(), rel=1e-12)
+        t = out["cdf_target"][r]
+        lo = svref.correction_cdf(zt, zd, T, "f32", r, tau, K, x - 1)
+        hi = svref.correction_cdf(zt, zd, T, "f32", r, tau, K, x)
+        assert lo <= t < hi, (r, tau, x, lo, t, hi)
+
+
 def test_greedy_accept_len_is_argmax_match_prefix():
     rng = np.random.default_rng(5)
     B, K, V = 300, 5, 40
