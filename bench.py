@@ -16,6 +16,15 @@ Prints one JSON line (rank 0).  `value` is verified draft positions per second. 
 verified position, plus V * 2 for the bonus row of each fully accepted request) by the
 launch's average duration: HIP events on the launch stream bracket the timed launches,
 which run back to back, and the region's time is divided by their number.
+
+Before the warm-up calls, the plain read-only streaming kernel (sv_stream_read) reads a
+4 GiB buffer STREAM_PASSES times: its bandwidth is reported as the achievable reference
+(`extra.stream_read`), and it leaves the device at its sustained clocks, so the timed calls
+measure the kernels rather than the power-management ramp of an idle device.  The timed
+region itself holds exactly --steps full calls.  Verification steps are issued through the
+binding's prepared call (arguments marshalled once); `extra.host_issue_us_per_step` is the
+host time of one issue.  The oracle leg (`cpu_baseline`) also compares one GPU call with the
+oracle on every request of the batch (`extra.parity`).
 """
 import argparse
 import hashlib
@@ -43,6 +52,8 @@ def _source_digest():
 
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "verify_dfly_traffic.json")
 COPY_BYTES = 1 << 30
+STREAM_BYTES = 4 << 30
+STREAM_PASSES = 12
 
 
 def _traffic(kernel_key, digest):
@@ -98,14 +109,76 @@ def write_traffic(mode, fetch, write, copy_fetch, copy_write):
     print(json.dumps(d[f"verify_rows_{mode}"]))
 
 
+def stream_reference(torch, sv, stream):
+    """Achieved bandwidth of the read-only streaming kernel over STREAM_BYTES (first two passes
+    untimed), timed with events on the launch stream."""
+    buf = torch.empty(STREAM_BYTES, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        sv.sv_stream_read(buf, sink, stream=stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(STREAM_PASSES):
+        sv.sv_stream_read(buf, sink, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) / 1e3 / STREAM_PASSES
+    del buf
+    return {"GB/s": round(STREAM_BYTES / s / 1e9, 1), "bytes": STREAM_BYTES, "passes": STREAM_PASSES,
+            "frac_of_peak": round(STREAM_BYTES / s / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def host_info():
+    """The host the oracle runs on: logical CPUs the process may use, and the CPU model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"cpu_count": os.cpu_count(), "usable_cpus": usable, "model": model}
+
+
+def parity_check(gpu_out, oracle_out, tn, dn, dtype, T, L=None):
+    """Every request of one GPU call against the oracle's call on the same inputs, seed and
+    step (the comparison the GPU tests make): counts of requests compared, near-threshold
+    cases and mismatches outside the bands."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import parity
+
+    g = {k: (None if v is None else v.cpu().numpy()) for k, v in gpu_out.items()}
+    B = oracle_out["alpha"].shape[0]
+    rep = {"requests": 0, "near_accept": 0, "near_token": 0, "mismatches": 0}
+    for r in range(B):
+        rep["requests"] += 1
+        try:
+            one = parity.compare_verify(g, oracle_out, tn, dn, dtype, T, check=[r], L=L, label="bench")
+        except AssertionError as e:
+            rep["mismatches"] += 1
+            rep.setdefault("first_mismatch", f"request {r}: {str(e)[:200]}")
+            continue
+        rep["near_accept"] += one["near_accept"]
+        rep["near_token"] += one["near_token"]
+    return rep
+
+
 def _oracle_time(fn):
     t0 = time.perf_counter()
     fn()
     return time.perf_counter() - t0
 
 
-def cpu_baseline_verify(inputs, T, seed, draft_len=None, what="DFly"):
-    """The oracle, as it stands, on the whole batch (single thread)."""
+def cpu_baseline_verify(inputs, T, seed, draft_len=None, what="DFly", gpu_call=None):
+    """The oracle, as it stands, on the whole batch (single thread); then, when gpu_call is
+    given (a function of (seed, step) returning the GPU outputs of the same inputs), one GPU
+    call at the oracle's seed and step compared with it request by request."""
     import workloads
     from oracle import svref
 
@@ -114,11 +187,18 @@ def cpu_baseline_verify(inputs, T, seed, draft_len=None, what="DFly"):
     dl = None if draft_len is None else draft_len.cpu().numpy()
     B, K = toks.shape
     dtype = "bf16" if inputs.target.dtype.__str__().endswith("bfloat16") else "f32"
-    dt = _oracle_time(lambda: svref.verify_batch(tn, dn, toks, T, dtype, seed=seed, draft_len=dl))
+    res = {}
+    dt = _oracle_time(lambda: res.update(o=svref.verify_batch(tn, dn, toks, T, dtype, seed=seed, draft_len=dl,
+                                                              diagnostics=True)))
     npos = int(dl.sum()) if dl is not None else B * K
-    return {"value": npos / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
-            "sample": f"whole {what} batch: {npos} verified positions of {B} requests, V={tn.shape[-1]}, T={T}, "
-                      f"one pass, {dt:.1f} s single-threaded"}
+    out = {"value": npos / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
+           "sample": f"whole {what} batch: {npos} verified positions of {B} requests, V={tn.shape[-1]}, T={T}, "
+                     f"one pass, {dt:.1f} s single-threaded",
+           "host": host_info()}
+    par = None
+    if gpu_call is not None:
+        par = parity_check(gpu_call(seed, 0), res["o"], tn, dn, dtype, T, L=dl)
+    return out, par
 
 
 def cpu_baseline_e2e(target, draft, T, n_i=256):
@@ -183,9 +263,11 @@ class Timed:
         t_all0.record(self.stream)
         for i in range(n):
             step(warmup + i)
+        issue1 = time.perf_counter()
         t_all1.record(self.stream)
         torch.cuda.synchronize()
         self.wall = time.perf_counter() - wall0
+        self.host_issue_us = (issue1 - wall0) / n * 1e6
         self.total_ms = t_all0.elapsed_time(t_all1)
         self.avg_launch_s = self.total_ms / n / 1e3
         m = min(n, 200)
@@ -222,46 +304,72 @@ def bench_verify(args, sv, workloads, torch, name):
                                               base.T, base.seed, base.name) for _ in range(ncopy - 1)]
     ws = sv.Workspace(dev).get(B, K, V)
     stream = torch.cuda.current_stream()
-    state = {"out": None, "lens": None}
+    out = None
+    alloc = None
+    if conf is not None:
+        # the allocation writes into fixed buffers, which the prepared selected-row calls read
+        alloc = sv.sv_alloc_verify_budget(conf, N)
+        n_rows = min(N, B * K)
+    preps = []
+    for c in copies:
+        if conf is not None:
+            p = sv.PreparedVerify(c.target, c.draft, c.draft_tokens, T, seed=c.seed, draft_len=alloc[0],
+                                  row_list=alloc[2], n_rows=n_rows, workspace=ws, out=out, stream=stream)
+        else:
+            p = sv.PreparedVerify(c.target, c.draft, c.draft_tokens, T, seed=c.seed, workspace=ws, out=out,
+                                  stream=stream)
+        out = p.out
+        preps.append(p)
 
     def step(i):
-        c = copies[i % len(copies)]
         if conf is not None:
             # allocation, then verification laid out over the selected rows only
-            lens, _, rl = sv.sv_alloc_verify_budget(conf, N)
-            state["lens"] = lens
-            state["out"] = sv.sv_verify_selected(c.target, c.draft, c.draft_tokens, T, lens, rl, min(N, B * K),
-                                                 seed=c.seed, step=i, workspace=ws, out=state["out"], want_lse=True)
-        else:
-            state["out"] = sv.sv_verify_batch(c.target, c.draft, c.draft_tokens, T, seed=c.seed, step=i,
-                                              workspace=ws, out=state["out"], want_lse=True)
+            sv.sv_alloc_verify_budget(conf, N, out=alloc, stream=stream)
+        preps[i % len(preps)].launch(i)
 
+    ref = stream_reference(torch, sv, stream)
     tm = Timed(torch, stream).run(step, args.warmup, args.steps)
     # the draws differ per step (the step counter keys the generator): replay the timed steps
     # untimed to count the fully accepted requests of each
     n_full = []
     taus = []
+    lens_h = alloc[0].cpu() if alloc is not None else torch.full((B,), K, dtype=torch.int32)
     for i in range(args.steps):
         step(args.warmup + i)
-        tau = state["out"]["accept_len"].cpu()
-        L = state["lens"].cpu() if state["lens"] is not None else torch.full((B,), K, dtype=torch.int32)
-        n_full.append(int((tau == L).sum()))
+        tau = out["accept_len"].cpu()
+        n_full.append(int((tau == lens_h).sum()))
         taus.append(float(tau.float().mean()))
-    npos = int(state["lens"].sum()) if state["lens"] is not None else B * K
+    npos = int(lens_h.sum())
     alg_bytes = npos * 2 * V * 2 + (sum(n_full) / len(n_full)) * V * 2
     achieved = alg_bytes / tm.avg_launch_s / 1e9
+    # warm cache: the same calls on one input copy (its rows partly still in the 256 MB
+    # Infinity Cache from the call before), reported apart from the cache-cold figure
+    warm = Timed(torch, stream).run(lambda i: preps[0].launch(i), args.warmup, args.steps)
+    extra_t = {"warm_cache": {"avg_launch_us": round(warm.avg_launch_s * 1e6, 2),
+                              "GB/s_algorithmic": round(alg_bytes / warm.avg_launch_s / 1e9, 1),
+                              "note": "one input copy reused by every call; not the headline"},
+               "stream_read": ref, "host_issue_us_per_step": round(tm.host_issue_us, 2)}
     cpu = None
     if not args.no_cpu_baseline:
         what = {"dfly": "DFly", "mtp": "MTP chat", "budget": "budget-selected ragged"}[name]
-        cpu = cpu_baseline_verify(base, T, base.seed, draft_len=state["lens"], what=what)
-    extra_t = {}
+
+        def gpu_call(seed, step_):
+            if conf is not None:
+                sv.sv_alloc_verify_budget(conf, N, out=alloc, stream=stream)
+            preps[0].launch(step_, seed=seed)
+            torch.cuda.synchronize()
+            return out
+
+        cpu, par = cpu_baseline_verify(base, T, base.seed, draft_len=alloc[0] if alloc is not None else None,
+                                       what=what, gpu_call=gpu_call)
+        extra_t["parity"] = par
     if conf is not None:
         # the D-cut choice of the budget from a cost table (linear here: a fixed part plus a
         # per-position part, in microseconds), timed on its own
         cost = (40.0 + 0.05 * torch.arange(B * K + 1, device=dev, dtype=torch.float32)).contiguous()
         t2 = Timed(torch, stream).run(lambda i: sv.sv_dcut_verify_budget(conf, cost), 5, 50)
         n_c, _, _, _, _ = sv.sv_dcut_verify_budget(conf, cost)
-        extra_t = {"dcut_choice_us": round(t2.avg_launch_s * 1e6, 2), "dcut_chosen_n": int(n_c.item())}
+        extra_t.update({"dcut_choice_us": round(t2.avg_launch_s * 1e6, 2), "dcut_chosen_n": int(n_c.item())})
     desc = {
         "dfly": f"DFly block verify: B={B} requests x block {K}, V={V}, bf16 logits",
         "mtp": f"MTP chat verify: B={B} requests x depth {K}, V={V}, bf16 logits",
@@ -274,7 +382,7 @@ def bench_verify(args, sv, workloads, torch, name):
         key=f"verify_rows_{args.mode}" if name == "dfly" else f"{name}_{args.mode}",
         config={"workload": f"{desc}, {mode}; cache-cold ({len(copies)} rotating input copies)",
                 "B": B, "K": K, "V": V, "T": T, **({"budget_N": N} if N else {})},
-        extra={"alpha_mean": round(float(state["out"]["alpha"].float().mean()), 4),
+        extra={"alpha_mean": round(float(out["alpha"].float().mean()), 4),
                "tau_mean": round(sum(taus) / len(taus), 3), "n_full_accept_mean": sum(n_full) / len(n_full),
                **extra_t})
 
@@ -290,6 +398,7 @@ def bench_e2e(args, sv, workloads, torch):
     def step(i):
         state["loss"], _ = sv.sv_tv_e2e_loss(target, draft, T, alpha=alpha, workspace=ws)
 
+    ref = stream_reference(torch, sv, torch.cuda.current_stream())
     tm = Timed(torch, torch.cuda.current_stream()).run(step, min(args.warmup, 3), min(args.steps, 10))
     npos = I * D
     alg_bytes = npos * 2 * V * 2
@@ -299,7 +408,8 @@ def bench_e2e(args, sv, workloads, torch):
                 config={"workload": f"end-to-end TV objective: |I|={I} positions x D={D}, V={V}, bf16 logits, "
                                     f"T={T} ({2 * target.numel() * 2 / 1e9:.1f} GB read per call)",
                         "I": I, "D": D, "V": V, "T": T},
-                extra={"loss": float(state["loss"].item()), "alpha_mean": round(float(alpha.mean()), 4)})
+                extra={"loss": float(state["loss"].item()), "alpha_mean": round(float(alpha.mean()), 4),
+                       "stream_read": ref})
 
 
 def bench_e2e_bwd(args, sv, workloads, torch):
@@ -314,6 +424,7 @@ def bench_e2e_bwd(args, sv, workloads, torch):
     def step(i):
         sv.sv_tv_e2e_backward(target, draft, alpha, T, grad=grad, workspace=ws)
 
+    ref = stream_reference(torch, sv, torch.cuda.current_stream())
     tm = Timed(torch, torch.cuda.current_stream()).run(step, min(args.warmup, 3), min(args.steps, 10))
     npos = I * D
     alg_bytes = npos * V * (2 + 2 + 2)   # read both logit rows, write the gradient row (bf16)
@@ -325,7 +436,7 @@ def bench_e2e_bwd(args, sv, workloads, torch):
                                     f"and gradient, T={T} ({alg_bytes / 1e9:.1f} GB moved per call)",
                         "I": I, "D": D, "V": V, "T": T},
                 extra={"loss": float(loss.item()), "grad_abs_mean_first64": float(gs.abs().mean()),
-                       "grad_row_sum_max_first64": float(gs.sum(-1).abs().max())})
+                       "grad_row_sum_max_first64": float(gs.sum(-1).abs().max()), "stream_read": ref})
 
 
 def bench_sample(args, sv, workloads, torch):
@@ -343,6 +454,7 @@ def bench_sample(args, sv, workloads, torch):
         state["tok"], state["conf"] = sv.sv_sample_drafts(copies[i % len(copies)], T, seed=base.seed, step=i,
                                                           workspace=ws)
 
+    ref = stream_reference(torch, sv, torch.cuda.current_stream())
     tm = Timed(torch, torch.cuda.current_stream()).run(step, args.warmup, args.steps)
     npos = B * K
     alg_bytes = npos * V * 2
@@ -353,7 +465,7 @@ def bench_sample(args, sv, workloads, torch):
                 config={"workload": f"draft tokens and confidences: B={B} requests x {K} drafter rows, V={V}, "
                                     f"bf16 logits, {mode}; cache-cold ({ncopy} rotating input copies)",
                         "B": B, "K": K, "V": V, "T": T},
-                extra={"conf_mean": round(float(state["conf"].mean()), 4)})
+                extra={"conf_mean": round(float(state["conf"].mean()), 4), "stream_read": ref})
 
 
 def main():

@@ -21,6 +21,7 @@ EXPORTS = [
     "sv_workspace_bytes", "sv_workspace_init", "sv_verify_batch", "sv_verify_selected", "sv_accept_len",
     "sv_residual_sample", "sv_tv_e2e_loss", "sv_tv_e2e_backward", "sv_sample_drafts", "sv_alloc_verify_budget",
     "sv_dcut_verify_budget", "sv_uniforms", "sv_device_error", "sv_status_string", "sv_set_wait_bound",
+    "sv_stream_read",
 ]
 
 
@@ -50,7 +51,7 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with "
-                              "`python -m draft_verification_softmax_amd.build` (no CPU fallback exists)")
+                              "`python draft_verification_softmax_amd/build.py` (no CPU fallback exists)")
         L = C.CDLL(LIB_PATH)
         vp, i32, u64, sz = C.c_void_p, C.c_int32, C.c_uint64, C.c_size_t
         P = C.POINTER(Params)
@@ -69,6 +70,7 @@ def lib():
         L.sv_uniforms.argtypes = [u64, vp, i32, vp, vp]
         L.sv_device_error.argtypes = [vp, vp, C.POINTER(C.c_uint32)]
         L.sv_set_wait_bound.argtypes = [C.c_int64]
+        L.sv_stream_read.argtypes = [vp, sz, vp, vp]
         L.sv_status_string.argtypes = [C.c_int]
         L.sv_status_string.restype = C.c_char_p
         for name in EXPORTS:
@@ -393,15 +395,21 @@ def sv_sample_drafts(draft, T, seed=0, step=0, workspace=None, stream=None):
     return tokens, conf
 
 
-def sv_alloc_verify_budget(conf, budget_N, draft_len=None, want_row_list=True, stream=None):
-    """conf [B][K] float32 in [0,1]; returns (lens [B], row_off [B+1], row_list [N'] or None)."""
+def sv_alloc_verify_budget(conf, budget_N, draft_len=None, want_row_list=True, out=None, stream=None):
+    """conf [B][K] float32 in [0,1]; returns (lens [B], row_off [B+1], row_list [N'] or None),
+    written into `out` (such a tuple from an earlier call of at least this budget) if given."""
     B, K = conf.shape
     dev = conf.device
-    lens = torch.empty((B,), dtype=torch.int32, device=dev)
-    row_off = torch.empty((B + 1,), dtype=torch.int32, device=dev)
     n = min(int(budget_N), B * K)  # upper bound on the selected count
-    row_list = torch.empty((max(n, 1),), dtype=torch.int32, device=dev) if want_row_list else None
-    _record(_foreign(stream), lens, row_off, row_list)
+    if out is not None:
+        lens, row_off, row_list = out
+        if lens.shape != (B,) or row_off.shape != (B + 1,) or (row_list is not None and row_list.numel() < max(n, 1)):
+            raise ValueError("out does not fit this allocation")
+    else:
+        lens = torch.empty((B,), dtype=torch.int32, device=dev)
+        row_off = torch.empty((B + 1,), dtype=torch.int32, device=dev)
+        row_list = torch.empty((max(n, 1),), dtype=torch.int32, device=dev) if want_row_list else None
+        _record(_foreign(stream), lens, row_off, row_list)
     _check("sv_alloc_verify_budget", lib().sv_alloc_verify_budget(
         _p(conf), _p(draft_len), B, K, int(budget_N), _p(lens), _p(row_off), _p(row_list), _stream(stream)))
     return lens, row_off, row_list
@@ -434,6 +442,13 @@ def sv_uniforms(seed, counters, stream=None):
     _record(_foreign(stream), out)
     _check("sv_uniforms", lib().sv_uniforms(C.c_uint64(seed), _p(counters), n, _p(out), _stream(stream)))
     return out
+
+
+def sv_stream_read(data: torch.Tensor, sink: torch.Tensor, stream=None):
+    """Read every byte of `data` once (the read-only streaming reference); sink: a device
+    tensor of at least 4 bytes."""
+    _check("sv_stream_read", lib().sv_stream_read(_p(data), data.numel() * data.element_size(), _p(sink),
+                                                  _stream(stream)))
 
 
 def sv_device_error(ws: torch.Tensor, stream=None) -> int:

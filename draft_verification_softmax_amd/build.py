@@ -1,6 +1,6 @@
 """Build ``libspecverify.so`` for gfx950 with hipcc, in-tree.
 
-    python -m draft_verification_softmax_amd.build [-v]
+    python draft_verification_softmax_amd/build.py [-v]
 
 Each source compiles to its own object (in parallel; every object carries its own device
 code, no relocatable device code), then one hipcc line links the shared library.

@@ -524,6 +524,27 @@ __global__ void uniforms_kernel(uint64_t seed, const uint64_t *ctr, int n, float
     if (i < n) out[i] = uniform24(seed, ctr[4 * i], ctr[4 * i + 1], ctr[4 * i + 2], ctr[4 * i + 3]);
 }
 
+// Read-only streaming reference: workgroup b reads 16-byte words [b * 2048, (b + 1) * 2048)
+// once (eight non-temporal loads in flight per lane) and exits, the access pattern of the
+// verification members without their arithmetic.  The loads feed an xor that reaches memory
+// only when it equals an arbitrary constant, so the compiler cannot drop them.
+constexpr int kStreamLoads = 8;
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4 *p, size_t n16, uint32_t *sink) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const size_t base = (size_t)blockIdx.x * (256 * kStreamLoads) + threadIdx.x;
+    u32x4 v[kStreamLoads];
+#pragma unroll
+    for (int u = 0; u < kStreamLoads; ++u) {
+        const size_t i = base + (size_t)u * 256;
+        v[u] = i < n16 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p) + i) : u32x4{0, 0, 0, 0};
+    }
+    u32x4 acc = v[0];
+#pragma unroll
+    for (int u = 1; u < kStreamLoads; ++u) acc ^= v[u];
+    const uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+    if (x == 0x9e3779b9u) sink[0] = x;
+}
+
 __global__ void fill_zero_kernel(uint4 *p, size_t n16) {
     for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
         p[i] = make_uint4(0, 0, 0, 0);
@@ -840,6 +861,18 @@ int sv_uniforms(uint64_t seed, const uint64_t *counters, int32_t n, float *out, 
     if (n == 0) return SV_OK;
     hipLaunchKernelGGL(uniforms_kernel, dim3((n + 255) / 256), dim3(256), 0, (hipStream_t)stream, seed, counters, n,
                        out);
+    return launch_status();
+}
+
+int sv_stream_read(const void *data, size_t bytes, uint32_t *sink, void *stream) {
+    if (!data || !sink || !aligned16(data) || bytes % 16 != 0) return SV_EINVAL;
+    const size_t n16 = bytes / 16;
+    if (n16 == 0) return SV_OK;
+    const size_t per = (size_t)256 * kStreamLoads;
+    const size_t grid = (n16 + per - 1) / per;
+    if (grid > 0x7fffffffull) return SV_EINVAL;
+    hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream,
+                       (const uint4 *)data, n16, sink);
     return launch_status();
 }
 

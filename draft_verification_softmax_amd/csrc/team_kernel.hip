@@ -350,10 +350,12 @@ __device__ __forceinline__ void bonus_member(const TeamArgs &a, int j, int64_t r
     }
 }
 
+// Request r's draft length (r workgroup-uniform): a scalar load, so the member's chunk loads
+// that follow do not wait behind it on the vector memory counter.
 __device__ __forceinline__ int request_limit(const TeamArgs &a, int r, bool report) {
     int L = a.K;
     if (a.draft_len) {
-        const int l0 = a.draft_len[r];
+        const int l0 = load_uniform(a.draft_len + r);
         if ((l0 < 0 || l0 > a.K) && report) atomicOr(a.err, SV_DEVERR_DRAFT_LEN);
         L = l0 < 0 ? 0 : (l0 > a.K ? a.K : l0);
     }

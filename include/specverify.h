@@ -232,6 +232,15 @@ int sv_dcut_verify_budget(const float *conf, const int32_t *draft_len, int32_t B
 /* The library's uniforms, for testing the generator: out[i] = U(seed; counters[i][0..3]). */
 int sv_uniforms(uint64_t seed, const uint64_t *counters, int32_t n, float *out, void *stream);
 
+/* Measurement aid, not a step of verification: the plain read-only streaming kernel against
+ * which the verification kernels' HBM throughput is judged.  Reads every 16-byte word of
+ * data[0 .. bytes) once with non-temporal loads, in workgroups of 256 lanes that each take
+ * 32 KiB and exit (the verification members' access pattern without their arithmetic).
+ * sink: one uint32 of device memory that the kernel writes only for one particular xor of
+ * the data (it keeps the loads from being removed).  data 16-byte aligned, bytes a multiple
+ * of 16.  Errors: SV_EINVAL, SV_EHIP. */
+int sv_stream_read(const void *data, size_t bytes, uint32_t *sink, void *stream);
+
 /* Synchronise `stream`, return the device error flags left in `workspace` (SV_DEVERR_*)
  * in *flags and clear them.  Returns SV_EDEVICE when any flag was set. */
 int sv_device_error(void *workspace, void *stream, uint32_t *flags);

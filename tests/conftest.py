@@ -25,3 +25,25 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """Totals of the GPU/oracle verification comparisons: requests compared, and the
+    near-threshold cases (accept flags within 1e-6 of p(x)/q(x), tokens within 1e-6 R of a
+    CDF boundary) that the parity contract counts instead of comparing bit for bit."""
+    try:
+        import parity
+    except Exception:  # pragma: no cover
+        return
+    reps = parity.REPORTS
+    if not reps:
+        return
+    tot = {k: sum(r[k] for r in reps) for k in ("requests", "accept_tests", "near_accept", "near_token",
+                                                 "token_equal")}
+    terminalreporter.write_line(
+        f"verification parity: {len(reps)} comparisons, {tot['requests']} requests, {tot['accept_tests']} accept "
+        f"tests; near_accept {tot['near_accept']}, near_token {tot['near_token']}, tokens equal {tot['token_equal']}")
+    for r in reps:
+        if r["near_accept"] or r["near_token"]:
+            terminalreporter.write_line(f"  {r['label'] or '?'}: requests {r['requests']}, near_accept "
+                                        f"{r['near_accept']}, near_token {r['near_token']}")

@@ -6,8 +6,15 @@ Tolerances (from the stated goal for this path):
     threshold p(x)/q(x); such requests are counted and their tokens are not compared;
   * correction / bonus tokens: bit-exact unless the oracle's CDF target u*R lies within
     1e-6*R of every CDF boundary between the two tokens; counted;
-  * alpha, log-normalisers: 1e-5 relative (binary32 accumulation);
+  * alpha, log-normalisers: 1e-5 relative (binary32 accumulation).  alpha is a sum of V
+    binary32 exponentials, and the exponential flushes results below the binary32 normal
+    range (2^-126) to zero, so alpha also carries an absolute error of at most V * 2^-126;
+    that is its only absolute floor (it matters only for overlaps below ~1e-30);
   * the L_e2e gradient: see compare_grad.
+
+Every comparison adds its counts to REPORTS; the test session prints their totals (the
+near-threshold counts the goal asks to be reported), and compare_verify fails when they
+exceed what the bands can explain (near_accept_max, near_token_max).
 """
 import numpy as np
 
@@ -16,21 +23,41 @@ from oracle import svref
 ACCEPT_BAND = 1e-6
 CDF_BAND = 1e-6
 REL_TOL = 1e-5
+FLUSH = 2.0 ** -126
+
+REPORTS = []
 
 
-def compare_verify(gpu, ora, target_np, draft_np, dtype, T, check=None, L=None):
+def near_accept_max(tests):
+    """A flag may differ only where the oracle's uniform lies within ACCEPT_BAND of the ratio
+    p(x)/q(x): probability 2e-6 per test, so even one is rare; one per call (plus one per 1000
+    tests) is allowed before the count itself fails the comparison."""
+    return 1 + tests // 1000
+
+
+def near_token_max(compared):
+    """A token may differ only where u R lies within CDF_BAND * R of a boundary between the two
+    tokens; the boundary next to the target moves by the binary32 rounding of the weights and
+    of the range masses (~1e-7 R), against a spacing of the drawn token's weight (~R / V on
+    average).  Up to a tenth of the compared draws (at least two) is allowed."""
+    return max(2, compared // 10)
+
+
+def compare_verify(gpu, ora, target_np, draft_np, dtype, T, check=None, L=None, label=""):
     """gpu/ora: dicts of numpy arrays.  check: request indices to compare (default all).
     Returns a report dict; raises AssertionError on any mismatch outside the bands."""
     B, K = ora["alpha"].shape
     reqs = range(B) if check is None else check
-    rep = dict(requests=0, near_accept=0, near_token=0, token_equal=0)
+    rep = dict(requests=0, near_accept=0, near_token=0, token_equal=0, accept_tests=0)
     for r in reqs:
         rep["requests"] += 1
         Lr = K if L is None else int(L[r])
         ks = slice(0, Lr)
         # alpha and lse within REL_TOL; unverified tail exactly the fill values
-        np.testing.assert_allclose(gpu["alpha"][r, ks], ora["alpha"][r, ks], rtol=REL_TOL, atol=1e-7,
+        V = target_np.shape[-1]
+        np.testing.assert_allclose(gpu["alpha"][r, ks], ora["alpha"][r, ks], rtol=REL_TOL, atol=V * FLUSH,
                                    err_msg=f"alpha r={r}")
+        rep["accept_tests"] += Lr
         assert (gpu["alpha"][r, Lr:] == 0).all() and (gpu["accept"][r, Lr:] == 0).all()
         if T > 0 and gpu.get("lse_t") is not None:
             np.testing.assert_allclose(gpu["lse_t"][r, ks], ora["lse_t"][r, ks], rtol=REL_TOL, err_msg=f"lse_t r={r}")
@@ -68,6 +95,10 @@ def compare_verify(gpu, ora, target_np, draft_np, dtype, T, check=None, L=None):
             gap = t - far
         assert 0 <= gap <= CDF_BAND * R, f"token r={r}: gpu {tg} oracle {to}, gap {gap} R {R}"
         rep["near_token"] += 1
+    assert rep["near_accept"] <= near_accept_max(rep["accept_tests"]), rep
+    compared = rep["requests"] - rep["near_accept"]
+    assert rep["near_token"] <= near_token_max(compared), rep
+    REPORTS.append(dict(rep, label=label))
     return rep
 
 
