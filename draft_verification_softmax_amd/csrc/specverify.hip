@@ -17,6 +17,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <string.h>
 
 #include "sv_device.hpp"
 #include "specverify.h"
@@ -615,6 +616,19 @@ void fill_team_args(TeamArgs &a, const sv_params *p, const TeamLayout &L, char *
     a.nseg = L.nseg;
     a.nseg_b = L.nseg_b;
     a.c = p->temperature > 0.f ? (float)(kLog2e / (double)p->temperature) : 0.f;
+    // c as beta * gamma (beta the nearest bfloat16, rounded to nearest even) for the overlap
+    // pass of bfloat16 rows; gamma and 1 / gamma from binary64
+    uint32_t cb;
+    memcpy(&cb, &a.c, sizeof cb);
+    const uint32_t hb = (cb + 0x7fffu + ((cb >> 16) & 1u)) >> 16;
+    const uint32_t bbits = hb << 16;
+    float beta;
+    memcpy(&beta, &bbits, sizeof beta);
+    const bool d2 = a.c > 0.f && beta >= 0x1p-100f && beta <= 0x1p100f;
+    a.d2_blo = hb;
+    a.d2_gamma = d2 ? (float)((double)a.c / (double)beta) : 0.f;
+    a.d2_rgamma = d2 ? (float)((double)beta / (double)a.c) : 0.f;
+    a.d2_ok = (d2 && isfinite(a.d2_gamma) && a.d2_gamma > 0.f) ? 1 : 0;
     a.seed = p->seed;
     a.step = p->step;
     a.spin_ticks = g_wait_ticks;  // then a member hands its share over (to the finalize)

@@ -94,6 +94,13 @@ struct TeamArgs {
     int32_t n_rows;
     int64_t spin_ticks;  // bounded wait for teammates' partials (10 ns ticks)
     int64_t fin_ticks;   // bounded wait of a finalize workgroup for its request's words
+    // c as beta * gamma: beta the nearest bfloat16 (bits in d2_blo), gamma = c / beta and
+    // d2_rgamma = beta / c in binary32 (from binary64 on the host); d2_ok = 0 when beta is
+    // not a normal bfloat16 or the logits are not bfloat16 (the overlap pass then takes the
+    // fma form)
+    uint32_t d2_blo;
+    float d2_gamma, d2_rgamma;
+    int32_t d2_ok;
 };
 
 // Grid sizes are derived from a (rows * S + B workgroups at most; the caller checks they fit).

@@ -393,6 +393,81 @@ __device__ __forceinline__ float min_sum(LaneRow<DTT> &t, LaneRow<DTD> &d, float
     return split ? (a0 + a1) * exp2_fast(-nt.lo) : a0 + a1;
 }
 
+// Four logit pairs (two packed words of each row) of the dot2 form of the overlap pass: per
+// pair, the NaN-propagating minimum of dot2(t, beta, ct) and dot2(d, beta, cd), where
+// v_dot2_f32_bf16 in its three-operand form gives a.lo * b.lo + a.hi * b.hi + c with exact
+// products and one rounding (beta sits in one half of blo / bhi, 0 in the other).  Inline
+// assembly keeps the compiler from choosing the two-operand accumulating form, which needs a
+// copy of c into the destination before each use.  A DOT result read by another VALU
+// instruction needs three wait states, which the compiler does not know to leave after
+// assembly it cannot see into: so the eight products come first and each minimum reads them
+// at least three instructions later.  m[0..3]: words (t0, d0) low, high halves, then
+// (t1, d1) low, high.
+__device__ __forceinline__ void dot2_min4(uint32_t t0, uint32_t t1, uint32_t d0, uint32_t d1, uint32_t blo,
+                                          uint32_t bhi, float ct, float cd, float (&m)[4]) {
+    float y0, y1, y2, y3, y4, y5, y6, y7;
+    asm("v_dot2_f32_bf16 %4, %12, %16, %18\n\t"
+        "v_dot2_f32_bf16 %5, %14, %16, %19\n\t"
+        "v_dot2_f32_bf16 %6, %12, %17, %18\n\t"
+        "v_dot2_f32_bf16 %7, %14, %17, %19\n\t"
+        "v_dot2_f32_bf16 %8, %13, %16, %18\n\t"
+        "v_dot2_f32_bf16 %9, %15, %16, %19\n\t"
+        "v_dot2_f32_bf16 %10, %13, %17, %18\n\t"
+        "v_dot2_f32_bf16 %11, %15, %17, %19\n\t"
+        "v_minimum3_f32 %0, %4, %5, %5\n\t"
+        "v_minimum3_f32 %1, %6, %7, %7\n\t"
+        "v_minimum3_f32 %2, %8, %9, %9\n\t"
+        "v_minimum3_f32 %3, %10, %11, %11"
+        : "=v"(m[0]), "=v"(m[1]), "=v"(m[2]), "=v"(m[3]), "=&v"(y0), "=&v"(y1), "=&v"(y2), "=&v"(y3),
+          "=&v"(y4), "=&v"(y5), "=&v"(y6), "=&v"(y7)
+        : "v"(t0), "v"(t1), "v"(d0), "v"(d1), "s"(blo), "s"(bhi), "v"(ct), "v"(cd));
+}
+
+// The scale c = log2(e) / T as beta * gamma for the dot2 form of the overlap pass (beta a
+// bfloat16, gamma = c / beta), from the kernel arguments.
+struct Dot2Scale {
+    uint32_t blo, bhi;   // beta in the low / high half of a bfloat16 pair, 0 in the other
+    float gamma, rgamma;
+    bool ok;
+};
+__device__ __forceinline__ Dot2Scale dot2_scale(const TeamArgs &a) {
+    return Dot2Scale{a.d2_blo, a.d2_blo << 16, a.d2_gamma, a.d2_rgamma, a.d2_ok != 0};
+}
+
+// -n / gamma with about half an ulp of error: the product with 1 / gamma, then one correction
+// step from its residual (so that gamma times the result gives -n back to within an ulp).
+__device__ __forceinline__ float neg_over_gamma(float n, const Dot2Scale &ds) {
+    const float q = -n * ds.rgamma;
+    const float r = __builtin_fmaf(q, ds.gamma, n);   // gamma q + n, the error of q times gamma
+    return __builtin_fmaf(-r, ds.rgamma, q);
+}
+
+// sum_i min(p_i, q_i) of bfloat16 rows with both low parts left out (as in min_sum's unsplit
+// form), in the dot2 form: per logit pair, the minimum of dot2(t, beta, -Nt/gamma) and
+// dot2(d, beta, -Nd/gamma) (each the logit times beta less the row's normaliser over gamma,
+// one rounding, centred near 0 for the terms that matter), times gamma, into 2^x: six
+// instructions per pair instead of seven.  A logit pair whose other half is infinite (a masked
+// logit) gives a NaN there, which the NaN-propagating minimum carries into the sum: the caller
+// then takes the fma form for the wave.
+__device__ __forceinline__ float min_sum_dot2(LaneRow<kDtBF16> &t, LaneRow<kDtBF16> &d, Norm2 nt, Norm2 nd,
+                                             const Dot2Scale &ds) {
+    float ct = neg_over_gamma(nt.hi, ds), cd = neg_over_gamma(nd.hi, ds);
+    // wait states between the VALU writes of ct, cd and the first DOT that reads them
+    asm volatile("s_nop 4" : "+v"(ct), "+v"(cd));
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int q = 0; q < LaneRow<kDtBF16>::kWords; q += 2) {
+        // no refresh: the packed words are consumed as they are, nothing widened is kept
+        float m[4];
+        dot2_min4(t.w[q], t.w[q + 1], d.w[q], d.w[q + 1], ds.blo, ds.bhi, ct, cd, m);
+        a0 += exp2_fast(m[0] * ds.gamma);
+        a1 += exp2_fast(m[1] * ds.gamma);
+        a0 += exp2_fast(m[2] * ds.gamma);
+        a1 += exp2_fast(m[3] * ds.gamma);
+    }
+    return a0 + a1;
+}
+
 // Pass 1 of a lane: base-2 log-sum-exp state (M, s = sum 2^{x c - M}) per row, M uniform
 // across the wave.
 struct ThreadStats {
@@ -415,10 +490,20 @@ __device__ __forceinline__ ThreadStats pass1(LaneRow<DTT> &t, LaneRow<DTD> &d, f
 // Pass 2 of a lane: its share of alpha and of the residual mass sum max(p - q, 0).
 template <int DTT, int DTD>
 __device__ __forceinline__ void pass2(LaneRow<DTT> &t, LaneRow<DTD> &d, const ThreadStats &s, float c,
-                                      Norm2 nt, Norm2 nd, float &alpha, float &resid) {
+                                      Norm2 nt, Norm2 nd, float &alpha, float &resid, const Dot2Scale &ds) {
     // the low parts matter only at large |hi| (low temperatures); the test is uniform
     const int split = __builtin_amdgcn_readfirstlane(
         (__builtin_fabsf(nt.lo) > kLoNegligible || __builtin_fabsf(nd.lo) > kLoNegligible) ? 1 : 0);
+    if constexpr (DTT == kDtBF16 && DTD == kDtBF16) {
+        if (!split && ds.ok) {
+            alpha = min_sum_dot2(t, d, nt, nd, ds);
+            if (!__ballot(__builtin_isnan(alpha))) {   // wave-uniform: no infinite logit in the wave's range
+                const float P = (s.Mt == neg_inf()) ? 0.f : s.st * exp2_fast((s.Mt - nt.hi) - nt.lo);
+                resid = P - alpha;
+                return;
+            }
+        }
+    }
     alpha = min_sum(t, d, c, nt, nd, split);
     const float P = (s.Mt == neg_inf()) ? 0.f : s.st * exp2_fast((s.Mt - nt.hi) - nt.lo);   // this lane's target mass
     resid = P - alpha;

@@ -198,7 +198,7 @@ __device__ __forceinline__ void finish_row(const TeamArgs &a, int64_t row, int j
     const Norm2 nt = s_tot[0], nd = s_tot[1];
     float al, rs;
     if constexpr (KEEP) pass2_keep(et, ed, ts, nt, nd, al, rs);
-    else pass2(tr, dr, ts, c, nt, nd, al, rs);
+    else pass2(tr, dr, ts, c, nt, nd, al, rs, dot2_scale(opaque_args()));   // read here, not held from the start
     if constexpr (MODE == kTeamStoch) {
         rs = fmaxf(wave_sum(rs), 0.f);
         if (lane_id() == 0) putf(a.dir + row * a.nseg + j * kTeamWaves + w, rs, tag);
