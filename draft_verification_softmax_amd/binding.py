@@ -15,6 +15,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libspecverify.so")
 
 SV_F32, SV_BF16 = 0, 1
+# device error flags (sv_device_error)
+SV_DEVERR_TOKEN, SV_DEVERR_DRAFT_LEN, SV_DEVERR_TIMEOUT, SV_DEVERR_POISONED = 1, 2, 4, 8
 _STATUS = {0: "SV_OK", 1: "SV_EINVAL", 2: "SV_EUNSUPPORTED", 3: "SV_EHIP", 4: "SV_EWORKSPACE", 5: "SV_EDEVICE"}
 
 EXPORTS = [
@@ -452,6 +454,9 @@ def sv_stream_read(data: torch.Tensor, sink: torch.Tensor, stream=None):
 
 
 def sv_device_error(ws: torch.Tensor, stream=None) -> int:
+    """Synchronises the stream and returns (and clears) the workspace's SV_DEVERR_* flags.
+    After SV_DEVERR_TIMEOUT or SV_DEVERR_POISONED the library zero-fills the workspace again
+    (one that sv_workspace_init set up, as Workspace does), so the next call verifies."""
     flags = C.c_uint32(0)
     rc = lib().sv_device_error(_p(ws), _stream(stream), C.byref(flags))
     if rc not in (0, 5):

@@ -314,7 +314,7 @@ __global__ __launch_bounds__(kReduceThreads) void e2e_reduce_kernel(const float 
     if (threadIdx.x == 0) {
         *loss = (float)(1.0 - part[0] / ((double)I * (double)D));
         // the team kernels of this call are complete: advance the workspace epoch
-        __hip_atomic_store(epoch, *epoch + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(epoch, epoch_after(epoch_tag(*epoch), false), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -546,9 +546,10 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4 *p, size_t
     if (x == 0x9e3779b9u) sink[0] = x;
 }
 
-__global__ void fill_zero_kernel(uint4 *p, size_t n16) {
+// Zero-fills a workspace of n16 16-byte words and records its byte count in the header.
+__global__ void init_workspace_kernel(uint4 *p, size_t n16, size_t bytes) {
     for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
-        p[i] = make_uint4(0, 0, 0, 0);
+        p[i] = i == kOffWsBytes / 16 ? make_uint4((uint32_t)bytes, (uint32_t)(bytes >> 32), 0, 0) : make_uint4(0, 0, 0, 0);
 }
 
 }  // namespace sv
@@ -561,6 +562,12 @@ using namespace sv;
 namespace {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// A workspace must be zero-filled again after a wait gave up (its epoch is then poisoned)
+// or once a call found it poisoned.
+bool workspace_needs_init(uint32_t flags, uint32_t epoch) {
+    return (flags & (SV_DEVERR_TIMEOUT | SV_DEVERR_POISONED)) != 0u || epoch_poisoned(epoch);
+}
 
 int check_logits(const void *p, int dtype, int64_t ld, int V) {
     if (dtype != SV_F32 && dtype != SV_BF16) return SV_EUNSUPPORTED;
@@ -600,8 +607,8 @@ const int64_t kFinalizeWaitTicks = 2000000;   // 20 ms beyond it
 void fill_team_args(TeamArgs &a, const sv_params *p, const TeamLayout &L, char *ws) {
     a.err = (uint32_t *)(ws + L.off_err);
     a.epoch = (uint32_t *)(ws + L.off_epoch);
-    a.gdone = (int32_t *)(ws + L.off_gdone);
-    a.arrive = (int32_t *)(ws + L.off_arrive);
+    a.gdone = (uint32_t *)(ws + L.off_gdone);
+    a.arrive = (uint32_t *)(ws + L.off_arrive);
     a.part = (uint64_t *)(ws + L.off_part);
     a.apart = (uint64_t *)(ws + L.off_apart);
     a.dir = (uint64_t *)(ws + L.off_dir);
@@ -658,7 +665,8 @@ int sv_workspace_init(void *workspace, size_t workspace_bytes, void *stream) {
     const size_t n16 = workspace_bytes / 16;
     if (n16 == 0) return SV_OK;
     const unsigned grid = (unsigned)((n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024);
-    hipLaunchKernelGGL(fill_zero_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, (uint4 *)workspace, n16);
+    hipLaunchKernelGGL(init_workspace_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, (uint4 *)workspace, n16,
+                       workspace_bytes);
     return launch_status();
 }
 
@@ -892,16 +900,26 @@ int sv_stream_read(const void *data, size_t bytes, uint32_t *sink, void *stream)
 
 int sv_device_error(void *workspace, void *stream, uint32_t *flags) {
     if (!workspace || !flags) return SV_EINVAL;
-    uint32_t v = 0;
-    if (hipMemcpyAsync(&v, workspace, sizeof v, hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess) return SV_EHIP;
+    if (!aligned16(workspace)) return SV_EINVAL;
+    uint64_t hdr[kOffArrive / 8] = {};   // err .. recorded byte count
+    if (hipMemcpyAsync(hdr, workspace, sizeof hdr, hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess)
+        return SV_EHIP;
     if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return SV_EHIP;
+    const uint32_t v = (uint32_t)hdr[kOffErr / 8];
+    const size_t recorded = (size_t)hdr[kOffWsBytes / 8];
     *flags = v;
-    if (v) {
+    if (!v) return SV_OK;
+    if (workspace_needs_init(v, (uint32_t)hdr[kOffEpoch / 8]) && recorded >= kOffArrive) {
+        // a wait gave up, or the epoch is poisoned: zero-fill the whole workspace again
+        // (every kernel of the stream is complete, so no workgroup still writes to it)
+        const int st = sv_workspace_init(workspace, recorded, stream);
+        if (st) return st;
+        if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return SV_EHIP;
+    } else {
         const uint32_t z = 0;
         if (hipMemcpy(workspace, &z, sizeof z, hipMemcpyHostToDevice) != hipSuccess) return SV_EHIP;
-        return SV_EDEVICE;
     }
-    return SV_OK;
+    return SV_EDEVICE;
 }
 
 const char *sv_status_string(int status) {

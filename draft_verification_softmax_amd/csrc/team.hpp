@@ -31,6 +31,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "epoch.h"
+
 namespace sv {
 
 constexpr int kTeamThreads = 256;                   // 4 waves
@@ -44,6 +46,11 @@ constexpr int kAccWords = 8;                        // tagged words of a row's a
 constexpr int kArriveSingle = 256;                  // calls of this many units arrive on one counter
 constexpr int kArriveSlots = 32;                    // first-level arrival counters of a call
 constexpr int kArriveStride = 32;                   // int32 words between them (128 bytes)
+
+// Workspace header (byte offsets, each word on a 64-byte line of its own): device error
+// flags, call epoch, second-level arrival counter, the byte count sv_workspace_init recorded
+// (uint64; 0 when the workspace was zero-filled some other way), first-level counters.
+constexpr size_t kOffErr = 0, kOffEpoch = 64, kOffGdone = 128, kOffWsBytes = 192, kOffArrive = 256;
 
 enum TeamMode { kTeamStoch = 0, kTeamGreedy = 1, kTeamAlpha = 2 };
 
@@ -71,8 +78,8 @@ struct TeamArgs {
     int32_t *amax_t, *amax_d;
     int32_t *accept_len, *out_tokens, *n_out;
     uint32_t *err, *epoch;
-    int32_t *gdone;    // second-level arrival counter
-    int32_t *arrive;   // [kArriveSlots][kArriveStride] first-level arrival counters
+    uint32_t *gdone;    // second-level arrival counter
+    uint32_t *arrive;   // [kArriveSlots][kArriveStride] first-level arrival counters
     uint64_t *part;    // [rows][8][S]: M_t, s_t, M_d, s_d, argmax value/index of both rows;
                        // bonus slots: the member's base-2 reference (stochastic)
     // dir of a bonus slot: per wave range, sum 2^{z c - M_member}

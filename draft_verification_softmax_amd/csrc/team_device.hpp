@@ -54,27 +54,17 @@ __device__ __forceinline__ uint32_t read_epoch(const uint32_t *e) {
     return __hip_atomic_load(const_cast<uint32_t *>(e), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Arrival of unit i of n (one call of one thread per unit) at the end of a call; true for
-// exactly one unit, whose arrival completes the call.  Up to kArriveSingle units share the
-// second-level counter directly (one returning atomic on the last unit's path).  More land on
-// kArriveSlots counters (i modulo the slot count) and the arrival that fills a slot moves on
-// to the second-level counter, so at most about n / kArriveSlots + kArriveSlots returning
-// atomics queue on one address.  Each counter is back at zero once it is full.
-__device__ inline bool last_arrival(const TeamArgs &a, int64_t i, int64_t n) {
-    if (n <= kArriveSingle) {
-        if (atomicAdd(a.gdone, 1) != (int)n - 1) return false;
-        __hip_atomic_store(a.gdone, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return true;
-    }
-    const int slot = (int)(i % kArriveSlots);
-    const int in_slot = (int)((n - 1 - slot) / kArriveSlots) + 1;   // units i < n on this slot
-    const int slots = (int)(n < kArriveSlots ? n : kArriveSlots);
-    int32_t *c = a.arrive + slot * kArriveStride;
-    if (atomicAdd(c, 1) != in_slot - 1) return false;
-    __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (atomicAdd(a.gdone, 1) != slots - 1) return false;
-    __hip_atomic_store(a.gdone, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return true;
+// Arrival of unit i of n (one thread per unit) at the end of a call, on the workspace's
+// counters: Arrival::last for exactly one unit, whose arrival completes the call, with
+// Arrival::gave_up when a unit of the call gave up a wait.  Up to kArriveSingle units share
+// the second-level counter directly (one returning atomic on the last unit's path); more land
+// on kArriveSlots first-level counters, so at most about n / kArriveSlots + kArriveSlots
+// returning atomics queue on one address.
+__device__ inline Arrival last_arrival(const TeamArgs &a, int64_t i, int64_t n, bool gave_up) {
+    return arrive(
+        i, n, gave_up, a.gdone, [&](int s) { return a.arrive + s * kArriveStride; }, kArriveSingle, kArriveSlots,
+        [](uint32_t *p, uint32_t v) { return atomicAdd(p, v); }, [](uint32_t *p, uint32_t v) { return atomicOr(p, v); },
+        [](uint32_t *p) { __hip_atomic_store(p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); });
 }
 
 // The kernel's argument block (a TeamArgs, the kernel's first parameter, at the start of the
@@ -556,6 +546,12 @@ __device__ __forceinline__ void pass2_keep(const float (&et)[kTeamE], const floa
     }
     const float P = (s.Mt == neg_inf()) ? 0.f : s.st * exp2_fast(lA);   // this lane's target mass
     resid = P - alpha;
+}
+
+// A wave-uniform pair held in scalar registers.
+__device__ __forceinline__ Norm2 uniform_norm(Norm2 n) {
+    return Norm2{__uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(n.hi))),
+                 __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(n.lo)))};
 }
 
 // Orders this wave's LDS writes before its lanes' later LDS reads of each other's words.

@@ -135,7 +135,7 @@ __device__ __forceinline__ void grad_member(const TeamArgs &a, const GradArgs &g
     tr.template load<FULL>(trow, base, V);
     dr.template load<FULL>(drow, base, V);
     sched_fence();
-    const uint32_t tag = epoch + 1;
+    const uint32_t tag = epoch_tag(epoch);
 
     // ---- first exchange: the row normalisers ----
     ThreadStats ts;
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(kTeamThreads) void fixup_kernel(TeamArgs a, GradArg
     __shared__ int s_list[kTeamThreads], s_n;
     const int64_t rows = a.rows;
     const int64_t row = (int64_t)blockIdx.x * kTeamThreads + threadIdx.x;
-    const uint32_t tag = read_epoch(a.epoch) + 1;
+    const uint32_t tag = epoch_tag(read_epoch(a.epoch));
     const int S = a.S;
     const float c = a.c;
     if (threadIdx.x == 0) s_n = 0;
@@ -279,8 +279,10 @@ __global__ __launch_bounds__(kTeamThreads) void fixup_kernel(TeamArgs a, GradArg
         __syncthreads();
     }
     if (threadIdx.x == 0) {
-        // the last workgroup of the call advances the epoch for the next call
-        if (last_arrival(a, blockIdx.x, gridDim.x)) __hip_atomic_store(a.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // the last workgroup of the call advances the epoch for the next call (every
+        // workgroup that reads the epoch has arrived by then: the member grid is complete)
+        if (last_arrival(a, blockIdx.x, gridDim.x, false).last)
+            __hip_atomic_store(a.epoch, epoch_after(tag, false), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

@@ -35,11 +35,11 @@ TeamLayout team_layout(int B, int slots, int V, size_t ws_bytes) {
     L.rows = (int64_t)(B > 0 ? B : 1) * (slots > 0 ? slots : 1);
     const size_t nB = (size_t)(B > 0 ? B : 1);
     // counters, from the start
-    L.off_err = 0;
-    L.off_epoch = 64;
-    L.off_gdone = 128;
-    L.off_arrive = 256;
-    const size_t counters = 256 + sizeof(int32_t) * kArriveSlots * kArriveStride;
+    L.off_err = kOffErr;
+    L.off_epoch = kOffEpoch;
+    L.off_gdone = kOffGdone;
+    L.off_arrive = kOffArrive;
+    const size_t counters = kOffArrive + sizeof(int32_t) * kArriveSlots * kArriveStride;
     // tagged words and scratch, relative to their own base
     size_t o = 0;
     L.off_part = o;  o = al(o + sizeof(uint64_t) * 8 * (size_t)L.S * (size_t)L.rows);
@@ -195,7 +195,9 @@ __device__ __forceinline__ void finish_row(const TeamArgs &a, int64_t row, int j
         if (threadIdx.x == 0) put(a.apart + row * S + j, kGaveUp, tag);   // the finalize takes over
         return;
     }
-    const Norm2 nt = s_tot[0], nd = s_tot[1];
+    // the row normalisers are uniform: scalar registers, so no vector register holds them
+    // through pass 2
+    const Norm2 nt = uniform_norm(s_tot[0]), nd = uniform_norm(s_tot[1]);
     float al, rs;
     if constexpr (KEEP) pass2_keep(et, ed, ts, nt, nd, al, rs);
     else pass2(tr, dr, ts, c, nt, nd, al, rs, dot2_scale(opaque_args()));   // read here, not held from the start
@@ -254,7 +256,7 @@ __device__ __forceinline__ void row_member(const TeamArgs &a, int j, int64_t row
     tr.template load<FULL>(trow, base, V);
     dr.template load<FULL>(drow, base, V);
     sched_fence();   // what uses the scalar loads goes after the chunk loads, not before
-    const uint32_t tag = epoch + 1;
+    const uint32_t tag = epoch_tag(epoch);
 
     float zx_t = 0.f, zx_d = 0.f;
     bool owner = false;
@@ -265,6 +267,9 @@ __device__ __forceinline__ void row_member(const TeamArgs &a, int j, int64_t row
         token_logits<DTT, DTD>(trow, drow, x, V, j, zx_t, zx_d, owner);
         if (x >= 0 && x < V && x / kTeamChunk == j) ua = accept_uniform(a.seed, r, k, a.step);
     }
+
+    // a poisoned workspace verifies nothing: the member publishes nothing
+    if (MODE != kTeamAlpha && epoch_poisoned(epoch)) return;
 
     constexpr bool want_amax = MODE == kTeamGreedy || AMAX;
     float mt = 0.f, md = 0.f;
@@ -321,7 +326,8 @@ __device__ __forceinline__ void bonus_member(const TeamArgs &a, int j, int64_t r
     LaneRow<DTT> br;
     br.template load<false>(brow, base, V);
     sched_fence();
-    const uint32_t tag = epoch + 1;
+    if (epoch_poisoned(epoch)) return;
+    const uint32_t tag = epoch_tag(epoch);
     if constexpr (MODE == kTeamGreedy) {
         float wb;
         int ib;
@@ -417,6 +423,7 @@ struct FinShared {
     int x[kTeamThreads];       // drafted tokens of the rows of a batch
     Norm2 n[2];                // normalisers of the row the draw uses (target, drafter)
     int tau, tok, flags, at;
+    int gave;                  // (thread 0) a wait before the arrival gave up
 };
 
 // Members and finalize workgroups run the same kernel: their LDS overlays.  The L_e2e grid
@@ -437,7 +444,7 @@ __device__ __forceinline__ MemberShared &member_lds(TeamShared &u) { return u.m;
 __device__ __forceinline__ MemberShared &member_lds(MemberShared &m) { return m; }
 
 // One wave (every lane) waits for words p[0..n) with the call's tag; on timeout it flags
-// the call.
+// the call and returns false (wave-uniform).
 __device__ __forceinline__ bool wave_wait(const TeamArgs &a, const uint64_t *p, int n, uint32_t tag, uint32_t *dst) {
     const bool got = wave_poll(p, n, tag, dst, a.fin_ticks);
     if (!got && lane_id() == 0) atomicOr(a.err, SV_DEVERR_TIMEOUT);
@@ -445,6 +452,27 @@ __device__ __forceinline__ bool wave_wait(const TeamArgs &a, const uint64_t *p, 
 }
 
 }  // namespace
+
+// The outputs of request r on a poisoned workspace: nothing verified (accept_len 0, no output
+// token, alpha and accept 0, log-sum-exps 0, argmax -1), and the device error flag raised.
+__device__ __forceinline__ void nothing_verified(const TeamArgs &a, int r) {
+    const int K = a.K;
+    for (int q = threadIdx.x; q <= K; q += kTeamThreads) a.out_tokens[(size_t)r * (K + 1) + q] = -1;
+    for (int k = threadIdx.x; k < K; k += kTeamThreads) {
+        const size_t i = (size_t)r * K + k;
+        a.alpha[i] = 0.f;
+        a.accept[i] = 0;
+        if (a.lse_t) a.lse_t[i] = 0.f;
+        if (a.lse_d) a.lse_d[i] = 0.f;
+        if (a.amax_t) a.amax_t[i] = -1;
+        if (a.amax_d) a.amax_d[i] = -1;
+    }
+    if (threadIdx.x == 0) {
+        a.accept_len[r] = 0;
+        a.n_out[r] = 0;
+        atomicOr(a.err, SV_DEVERR_POISONED);
+    }
+}
 
 // =======================================================================================
 // Finalize: the last B workgroups of the verification grid, one per request
@@ -464,7 +492,12 @@ __device__ __forceinline__ void finalize_request(const TeamArgs &a, int r, FinSh
     const int S = a.S;
     const int nseg = a.nseg;
     const int L = row_limit(a, r);
-    const uint32_t tag = read_epoch(a.epoch) + 1;
+    const uint32_t epoch = read_epoch(a.epoch);
+    if (epoch_poisoned(epoch)) {
+        nothing_verified(a, r);
+        return;
+    }
+    const uint32_t tag = epoch_tag(epoch);
     const int64_t row0 = (int64_t)r * a.slots;
     const int64_t brow = row0 + K;   // the bonus slot
     const float c = a.c;
@@ -477,7 +510,7 @@ __device__ __forceinline__ void finalize_request(const TeamArgs &a, int r, FinSh
     auto tau_u = [&](int t) {
         return pre_u ? sh.u[t] : uniform24(a.seed, (uint64_t)r, (uint64_t)t, kPurposeCorrection, a.step);
     };
-    if (threadIdx.x == 0) { sh.tau = L; sh.at = 0; sh.n[0] = sh.n[1] = Norm2{0.f, 0.f}; }
+    if (threadIdx.x == 0) { sh.tau = L; sh.at = 0; sh.gave = 0; sh.n[0] = sh.n[1] = Norm2{0.f, 0.f}; }
     if (pre_u && threadIdx.x <= K)
         sh.u[threadIdx.x] = uniform24(a.seed, (uint64_t)r, (uint64_t)threadIdx.x, kPurposeCorrection, a.step);
     __syncthreads();
@@ -555,7 +588,10 @@ __device__ __forceinline__ void finalize_request(const TeamArgs &a, int r, FinSh
                 // Not published within the bound: shares (and the shares of members whose
                 // directory words are missing) are recomputed here; an incomplete accept
                 // record sends the row to the partials below.
-                if (threadIdx.x == 0) atomicOr(a.err, SV_DEVERR_TIMEOUT);
+                if (threadIdx.x == 0) {
+                    atomicOr(a.err, SV_DEVERR_TIMEOUT);
+                    sh.gave = 1;
+                }
                 for (int u = 0; u < kFinWords / kTeamThreads; ++u) {
                     if (!((pend >> u) & 1u)) continue;
                     int i = u * kTeamThreads + (int)threadIdx.x - nb * nA;
@@ -591,7 +627,10 @@ __device__ __forceinline__ void finalize_request(const TeamArgs &a, int r, FinSh
                 if (whole) continue;
                 if (threadIdx.x < kWave) {
                     const bool got = wave_poll(a.part + (row0 + k0 + q) * 8 * S, 4 * S, tag, sh.pay, a.fin_ticks);
-                    if (!got && threadIdx.x == 0) atomicOr(a.err, SV_DEVERR_DRAFT_LEN);   // the row was never streamed
+                    if (!got && threadIdx.x == 0) {   // the row was never streamed
+                        atomicOr(a.err, SV_DEVERR_DRAFT_LEN);
+                        sh.gave = 1;
+                    }
                 }
                 __syncthreads();
                 if (threadIdx.x < kWave) {
@@ -614,7 +653,9 @@ __device__ __forceinline__ void finalize_request(const TeamArgs &a, int r, FinSh
                     if (MODE == kTeamStoch) {
                         get_norms(sx + q * kAccUsed, nt, nd);
                     } else {
-                        if (threadIdx.x < kWave) wave_wait(a, a.part + (row0 + k0 + q) * 8 * S, 4 * S, tag, sh.pay);
+                        if (threadIdx.x < kWave && !wave_wait(a, a.part + (row0 + k0 + q) * 8 * S, 4 * S, tag, sh.pay) &&
+                            threadIdx.x == 0)
+                            sh.gave = 1;
                         __syncthreads();
                         team_totals(sh.pay, S, nt, nd);
                     }
@@ -703,9 +744,14 @@ __device__ __forceinline__ void finalize_request(const TeamArgs &a, int r, FinSh
     // last batch of rows when there were rows).  After that no workgroup of the call still
     // reads the epoch, so the request arrives now, and the last arrival advances it while
     // the draws still run.
-    if (L == 0 && threadIdx.x < kWave) wave_wait(a, bonus_final, S, tag, sh.pay);
-    if (threadIdx.x == 0 && last_arrival(a, r, a.B))
-        __hip_atomic_store(a.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // If a wait before the arrival gave up, a workgroup of the request may not have read the
+    // epoch yet: the call then ends with the epoch poisoned.
+    bool gave = false;
+    if (L == 0 && threadIdx.x < kWave) gave = !wave_wait(a, bonus_final, S, tag, sh.pay);
+    if (threadIdx.x == 0) {
+        const Arrival ar = last_arrival(a, r, a.B, gave || sh.gave != 0);
+        if (ar.last) __hip_atomic_store(a.epoch, epoch_after(tag, ar.gave_up), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 
     const int tau = sh.tau;
     int tok = 0;

@@ -47,7 +47,8 @@ __device__ __forceinline__ void sample_member(const TeamArgs &a, int j, int64_t 
     LaneRow<DT> dr;
     dr.template load<FULL>(drow, base, V);
     sched_fence();
-    const uint32_t tag = epoch + 1;
+    if (epoch_poisoned(epoch)) return;   // the workspace samples nothing
+    const uint32_t tag = epoch_tag(epoch);
     if constexpr (GREEDY) {
         float m;
         int im;
@@ -213,7 +214,16 @@ __device__ __forceinline__ void sample_finalize(const TeamArgs &a, int fb, Sampl
     const int S = a.S;
     const int nseg = a.nseg;
     const int r = (int)(row / a.K), k = (int)(row % a.K);
-    const uint32_t tag = read_epoch(a.epoch) + 1;
+    const uint32_t epoch = read_epoch(a.epoch);
+    if (epoch_poisoned(epoch)) {   // nothing sampled: token -1, confidence 0, flag raised
+        if (lane == 0) {
+            tokens[row] = -1;
+            conf[row] = 0.f;
+            atomicOr(a.err, SV_DEVERR_POISONED);
+        }
+        return;
+    }
+    const uint32_t tag = epoch_tag(epoch);
     const uint64_t *part = a.part + row * (int64_t)(8 * S);
     const void *drow = row_ptr<DT>(a.draft, row, a.ld_d);
     // the draw's uniform depends on the row alone: drawn before the wait for the members
@@ -223,9 +233,11 @@ __device__ __forceinline__ void sample_finalize(const TeamArgs &a, int fb, Sampl
     else got = wave_gather(part, S, a.dir + row * nseg, nseg, tag, pay, a.fin_ticks);
     if (lane == 0) {
         if (!got) atomicOr(a.err, SV_DEVERR_TIMEOUT);
-        // every member of the row has published: the row arrives, the last one advancing the
-        // epoch while the draws still run
-        if (last_arrival(a, row, a.rows)) __hip_atomic_store(a.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // every member of the row has published (unless the wait gave up: then the call ends
+        // with the epoch poisoned): the row arrives, the last one advancing the epoch while
+        // the draws still run
+        const Arrival ar = last_arrival(a, row, a.rows, !got);
+        if (ar.last) __hip_atomic_store(a.epoch, epoch_after(tag, ar.gave_up), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     wave_lds_sync();
     int tok = 0;

@@ -67,7 +67,11 @@ enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 };
                                   match its lengths (sv_verify_selected) */
 #define SV_DEVERR_TIMEOUT 4u   /* an internal wait for other workgroups' stores of the same call
                                   exceeded its bound (the member wait bound plus 20 ms); the call
-                                  recomputed what was missing */
+                                  recomputed what was missing and left its workspace poisoned
+                                  (see sv_workspace_bytes) */
+#define SV_DEVERR_POISONED 8u  /* the call found its workspace poisoned and verified (sampled)
+                                  nothing: accept_len 0, n_out 0, out_tokens -1, alpha and
+                                  accept 0, lse 0, argmax -1 (sampling: token -1, confidence 0) */
 
 typedef struct sv_params {
     int32_t B;          /* requests (or |I| for sv_tv_e2e_loss) */
@@ -86,7 +90,20 @@ typedef struct sv_params {
  * The workspace must be zero-filled before its first use (sv_workspace_init); every call
  * leaves it ready for the next one.  One workspace may serve calls of different shapes if
  * it is large enough for each and is always passed with the same workspace_bytes.  Calls
- * that share a workspace must not overlap (same stream, or ordered by events). */
+ * that share a workspace must not overlap (same stream, or ordered by events).
+ *
+ * Poisoning.  Workgroups of one call exchange words tagged with the call's epoch, which the
+ * call advances as it ends, once every workgroup that reads the epoch has done so.  When one
+ * of the call's bounded waits gives up (SV_DEVERR_TIMEOUT, or SV_DEVERR_DRAFT_LEN for a row
+ * that was never streamed) that is no longer known, so the call ends with the epoch
+ * poisoned instead: a workgroup still on its way then writes nothing, and every later
+ * verification or sampling call on the workspace verifies nothing and raises
+ * SV_DEVERR_POISONED (see there for its outputs), so no word of the late workgroup can be
+ * taken for one of a later call.  L_e2e and gradient calls have no such late workgroup and
+ * run as usual.  Rule: after SV_DEVERR_TIMEOUT or SV_DEVERR_POISONED, zero-fill the workspace
+ * again.  sv_device_error() does so itself for a workspace that sv_workspace_init() set up;
+ * a workspace zero-filled some other way must be passed to sv_workspace_init().  The tags
+ * are 31-bit: after 2^31 - 1 calls on one workspace it is poisoned the same way. */
 size_t sv_workspace_bytes(int32_t B, int32_t K_max, int32_t V);
 
 /* Bound, in nanoseconds, of the wait inside a verification, L_e2e or gradient launch for the
@@ -99,7 +116,8 @@ size_t sv_workspace_bytes(int32_t B, int32_t K_max, int32_t V);
  * synchronised with calls being issued from other host threads.  Errors: SV_EINVAL (ns < 0). */
 int sv_set_wait_bound(int64_t ns);
 
-/* Zero-fill a workspace (a fill kernel on `stream`; no host synchronisation). */
+/* Zero-fill a workspace and record workspace_bytes in its header, where sv_device_error()
+ * finds it (a fill kernel on `stream`; no host synchronisation). */
 int sv_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
 
 /* Fused batched verification [TV] [ABS].
@@ -242,7 +260,11 @@ int sv_uniforms(uint64_t seed, const uint64_t *counters, int32_t n, float *out, 
 int sv_stream_read(const void *data, size_t bytes, uint32_t *sink, void *stream);
 
 /* Synchronise `stream`, return the device error flags left in `workspace` (SV_DEVERR_*)
- * in *flags and clear them.  Returns SV_EDEVICE when any flag was set. */
+ * in *flags and clear them.  Returns SV_EDEVICE when any flag was set.  When the flags hold
+ * SV_DEVERR_TIMEOUT or SV_DEVERR_POISONED, or the epoch is poisoned, and sv_workspace_init()
+ * recorded the workspace's size, the whole workspace is zero-filled again (and the stream
+ * synchronised) before it returns, so the next call verifies as usual.  Errors: SV_EINVAL
+ * (null or misaligned pointer), SV_EHIP. */
 int sv_device_error(void *workspace, void *stream, uint32_t *flags);
 
 /* Human-readable name of a status code (static storage). */
