@@ -15,12 +15,14 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libspecverify.so")
 
 SV_F32, SV_BF16 = 0, 1
+SV_NOALLOC_SCRATCH_BYTES = 16 << 20   # the per-device array of sv_verify_batch_noalloc
+
 # device error flags (sv_device_error)
 SV_DEVERR_TOKEN, SV_DEVERR_DRAFT_LEN, SV_DEVERR_TIMEOUT, SV_DEVERR_POISONED = 1, 2, 4, 8
 _STATUS = {0: "SV_OK", 1: "SV_EINVAL", 2: "SV_EUNSUPPORTED", 3: "SV_EHIP", 4: "SV_EWORKSPACE", 5: "SV_EDEVICE"}
 
 EXPORTS = [
-    "sv_workspace_bytes", "sv_workspace_init", "sv_verify_batch", "sv_verify_selected", "sv_accept_len",
+    "sv_workspace_bytes", "sv_workspace_init", "sv_verify_batch", "sv_verify_batch_noalloc", "sv_verify_selected", "sv_accept_len",
     "sv_residual_sample", "sv_tv_e2e_loss", "sv_tv_e2e_backward", "sv_sample_drafts", "sv_alloc_verify_budget",
     "sv_dcut_verify_budget", "sv_uniforms", "sv_device_error", "sv_status_string", "sv_set_wait_bound",
     "sv_stream_read",
@@ -61,6 +63,7 @@ def lib():
         L.sv_workspace_bytes.restype = sz
         L.sv_workspace_init.argtypes = [vp, sz, vp]
         L.sv_verify_batch.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.sv_verify_batch_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.sv_verify_selected.argtypes = [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.sv_accept_len.argtypes = [vp, vp, i32, i32, vp, vp]
         L.sv_residual_sample.argtypes = [P, vp, vp, vp, vp, vp, vp]
@@ -212,6 +215,17 @@ def sv_verify_batch(target, draft, draft_tokens, T, seed=0, step=0, draft_len=No
                    out, stream)
 
 
+def sv_verify_batch_noalloc(target, draft, draft_tokens, T, seed=0, step=0, draft_len=None, want_lse=True,
+                            want_amax=False, out=None, stream=None):
+    """sv_verify_batch on the library's own per-device scratch array (no workspace; the C
+    entry point allocates nothing).  Outputs are allocated here unless `out` (a dict as
+    returned by sv_verify_batch) is given."""
+    fn, args, _, out, _ = _prepare_verify(target, draft, draft_tokens, T, seed, step, draft_len, None, 0, want_lse,
+                                          want_amax, None, out, stream, noalloc=True)
+    _check("sv_verify_batch_noalloc", fn(*args))
+    return out
+
+
 def sv_verify_selected(target, draft, draft_tokens, T, lens, row_list, n_rows, seed=0, step=0, want_lse=True,
                        want_amax=False, workspace=None, out=None, stream=None):
     """Verification of the rows one sv_alloc_verify_budget call selected: lens [B] and
@@ -227,9 +241,10 @@ def sv_verify_selected(target, draft, draft_tokens, T, lens, row_list, n_rows, s
 
 
 def _prepare_verify(target, draft, draft_tokens, T, seed, step, draft_len, row_list, n_rows, want_lse, want_amax,
-                    workspace, out, stream, selected=False):
+                    workspace, out, stream, selected=False, noalloc=False):
     """Checks shapes and marshals one verification call: returns (entry point, argument
-    tuple, the Params it points to, outputs, the workspace)."""
+    tuple, the Params it points to, outputs, the workspace or None for the no-allocation
+    entry point)."""
     B, K1, V = target.shape
     K = K1 - 1
     if draft.shape != (B, K, V) or draft_tokens.shape != (B, K):
@@ -255,11 +270,14 @@ def _prepare_verify(target, draft, draft_tokens, T, seed, step, draft_len, row_l
             n_out=torch.empty((B,), dtype=torch.int32, device=dev),
         )
         _record(fs, *out.values())
-    ws = _ws_for(workspace, dev, B, K, V, stream)
+    ws = None if noalloc else _ws_for(workspace, dev, B, K, V, stream)
     prm = _params(B, K, V, target, draft, T, seed, step)
     outs = (_p(out["alpha"]), _p(out["accept"]), _p(out["lse_t"]), _p(out["lse_d"]), _p(out["amax_t"]),
             _p(out["amax_d"]), _p(out["accept_len"]), _p(out["out_tokens"]), _p(out["n_out"]))
-    if selected:
+    if noalloc:
+        fn = lib().sv_verify_batch_noalloc
+        args = (C.byref(prm), _p(target), _p(draft), _p(draft_tokens), _p(draft_len), *outs, _stream(stream))
+    elif selected:
         fn = lib().sv_verify_selected
         args = (C.byref(prm), _p(target), _p(draft), _p(draft_tokens), _p(draft_len), _p(row_list), n_rows, *outs,
                 _p(ws), ws.numel(), _stream(stream))
@@ -453,10 +471,11 @@ def sv_stream_read(data: torch.Tensor, sink: torch.Tensor, stream=None):
                                                   _stream(stream)))
 
 
-def sv_device_error(ws: torch.Tensor, stream=None) -> int:
+def sv_device_error(ws, stream=None) -> int:
     """Synchronises the stream and returns (and clears) the workspace's SV_DEVERR_* flags.
     After SV_DEVERR_TIMEOUT or SV_DEVERR_POISONED the library zero-fills the workspace again
-    (one that sv_workspace_init set up, as Workspace does), so the next call verifies."""
+    (one that sv_workspace_init set up, as Workspace does), so the next call verifies.
+    ws None: the current device's sv_verify_batch_noalloc array."""
     flags = C.c_uint32(0)
     rc = lib().sv_device_error(_p(ws), _stream(stream), C.byref(flags))
     if rc not in (0, 5):

@@ -19,6 +19,9 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "sv_device.hpp"
 #include "specverify.h"
 #include "team.hpp"
@@ -713,6 +716,55 @@ static int verify_impl(const sv_params *p, const void *target, const void *draft
     return e == hipSuccess ? SV_OK : SV_EHIP;
 }
 
+// ---------------------------------------------------------------------------------------
+// The workspace of sv_verify_batch_noalloc: a file-scope device array.  Every device the
+// library runs on holds its own copy until the process ends; calls on one device share it.
+// ---------------------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kScratchDevices = 64;
+
+struct ScratchSlot {
+    std::once_flag once;
+    void *ptr = nullptr;   // device address of this device's copy of `scratch`
+    int status = SV_EHIP;
+    std::atomic<bool> ready{false};   // ptr set and its zero-fill enqueued
+};
+ScratchSlot g_scratch[kScratchDevices];
+
+// The device address of the current device's copy of `scratch`.  The first call on a
+// device takes it with hipGetSymbolAddress (the host-side name is no device address) and
+// zero-fills the array with a kernel on `stream`, recording its size (so sv_device_error can
+// zero-fill it again); later calls return the kept address.  Nothing is allocated.
+int device_scratch(void **out, hipStream_t stream) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return SV_EHIP;
+    if (dev < 0 || dev >= kScratchDevices) return SV_EUNSUPPORTED;
+    ScratchSlot &slot = g_scratch[dev];
+    std::call_once(slot.once, [&] {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return;
+        slot.ptr = p;
+        slot.status = sv_workspace_init(p, SV_NOALLOC_SCRATCH_BYTES, stream);
+        slot.ready.store(slot.status == SV_OK, std::memory_order_release);
+    });
+    if (slot.status) return slot.status;
+    *out = slot.ptr;
+    return SV_OK;
+}
+
+// The current device's scratch if a call set it up, else nullptr.
+void *device_scratch_if_set() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return nullptr;
+    const ScratchSlot &slot = g_scratch[dev];
+    return slot.ready.load(std::memory_order_acquire) ? slot.ptr : nullptr;
+}
+
+}  // namespace
+
 extern "C" {
 
 int sv_verify_batch(const sv_params *p, const void *target, const void *draft,
@@ -722,6 +774,21 @@ int sv_verify_batch(const sv_params *p, const void *target, const void *draft,
                     void *workspace, size_t workspace_bytes, void *stream) {
     return verify_impl(p, target, draft, draft_tokens, draft_len, false, nullptr, 0, alpha, accept, lse_t, lse_d, amax_t,
                        amax_d, accept_len, out_tokens, n_out, workspace, workspace_bytes, stream);
+}
+
+int sv_verify_batch_noalloc(const sv_params *p, const void *target, const void *draft,
+                            const int32_t *draft_tokens, const int32_t *draft_len, float *alpha,
+                            uint8_t *accept, float *lse_t, float *lse_d, int32_t *amax_t,
+                            int32_t *amax_d, int32_t *accept_len, int32_t *out_tokens, int32_t *n_out,
+                            void *stream) {
+    if (!p || p->B < 0 || p->K_max < 0 || p->K_max > SV_K_MAX || p->V <= 0) return SV_EINVAL;
+    if (p->V > SV_V_MAX) return SV_EUNSUPPORTED;
+    if (sv_workspace_bytes(p->B, p->K_max, p->V) > (size_t)SV_NOALLOC_SCRATCH_BYTES) return SV_EWORKSPACE;
+    void *ws = nullptr;
+    const int st = device_scratch(&ws, (hipStream_t)stream);
+    if (st) return st;
+    return verify_impl(p, target, draft, draft_tokens, draft_len, false, nullptr, 0, alpha, accept, lse_t, lse_d, amax_t,
+                       amax_d, accept_len, out_tokens, n_out, ws, SV_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int sv_verify_selected(const sv_params *p, const void *target, const void *draft,
@@ -899,7 +966,14 @@ int sv_stream_read(const void *data, size_t bytes, uint32_t *sink, void *stream)
 }
 
 int sv_device_error(void *workspace, void *stream, uint32_t *flags) {
-    if (!workspace || !flags) return SV_EINVAL;
+    if (!flags) return SV_EINVAL;
+    if (!workspace) {   // the current device's sv_verify_batch_noalloc scratch
+        workspace = device_scratch_if_set();
+        if (!workspace) {
+            *flags = 0;
+            return SV_OK;
+        }
+    }
     if (!aligned16(workspace)) return SV_EINVAL;
     uint64_t hdr[kOffArrive / 8] = {};   // err .. recorded byte count
     if (hipMemcpyAsync(hdr, workspace, sizeof hdr, hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess)

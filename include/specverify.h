@@ -150,6 +150,25 @@ int sv_verify_batch(const sv_params *params, const void *target, const void *dra
                     int32_t *amax_d, int32_t *accept_len, int32_t *out_tokens, int32_t *n_out,
                     void *workspace, size_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): sv_verify_batch with the library's own
+ * workspace, a file-scope device array of SV_NOALLOC_SCRATCH_BYTES that each device holds
+ * from the first such call until the process ends.  Arguments, outputs and results as
+ * sv_verify_batch (bit-identical for the same inputs); no workspace argument.  The first
+ * call on a device looks up the array's device address and zero-fills it with a kernel on
+ * `stream`; no call allocates or frees anything.  Every call on one device shares the array
+ * and leaves it ready for the next: calls that overlap on one device (different streams not
+ * ordered by events, host threads racing) race on it and give undefined results.  Device
+ * error flags: sv_device_error(NULL, ...) on that device.  Errors: SV_EWORKSPACE when
+ * sv_workspace_bytes(B, K_max, V) > SV_NOALLOC_SCRATCH_BYTES (nothing enqueued), else as
+ * sv_verify_batch. */
+#define SV_NOALLOC_SCRATCH_BYTES (16u << 20)
+int sv_verify_batch_noalloc(const sv_params *params, const void *target, const void *draft,
+                            const int32_t *draft_tokens, const int32_t *draft_len, float *alpha,
+                            uint8_t *accept, float *lse_t, float *lse_d, int32_t *amax_t,
+                            int32_t *amax_d, int32_t *accept_len, int32_t *out_tokens, int32_t *n_out,
+                            void *stream);
+
 /* Verification of the rows a budget allocation selected [RT]: as sv_verify_batch with
  * draft_len = lens, but the work is laid out over the n_rows listed rows only (plus each
  * request's bonus row), so unselected rows cost nothing.  lens [B] and row_list [n_rows]
@@ -263,8 +282,9 @@ int sv_stream_read(const void *data, size_t bytes, uint32_t *sink, void *stream)
  * in *flags and clear them.  Returns SV_EDEVICE when any flag was set.  When the flags hold
  * SV_DEVERR_TIMEOUT or SV_DEVERR_POISONED, or the epoch is poisoned, and sv_workspace_init()
  * recorded the workspace's size, the whole workspace is zero-filled again (and the stream
- * synchronised) before it returns, so the next call verifies as usual.  Errors: SV_EINVAL
- * (null or misaligned pointer), SV_EHIP. */
+ * synchronised) before it returns, so the next call verifies as usual.  workspace NULL:
+ * the current device's sv_verify_batch_noalloc array (flags 0 before its first call).
+ * Errors: SV_EINVAL (null flags, misaligned workspace), SV_EHIP. */
 int sv_device_error(void *workspace, void *stream, uint32_t *flags);
 
 /* Human-readable name of a status code (static storage). */
