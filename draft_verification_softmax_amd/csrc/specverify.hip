@@ -25,268 +25,108 @@
 #include "sv_device.hpp"
 #include "specverify.h"
 #include "team.hpp"
+#include "team_device.hpp"
 #include "team_grad.hpp"
 #include "team_sample.hpp"
 
 namespace sv {
 
-constexpr int kThreads = 512;                 // 8 waves per workgroup
-constexpr int kWaves = kThreads / kWave;
-constexpr int kElems = 8;                     // logits per lane per tile (one 16-byte bf16 load)
-constexpr int kTile = kThreads * kElems;      // 4096 logits per tile
-constexpr int kSeg = kWave * kElems;          // 512: one wave's contiguous share of a tile
-
-// Arguments of the stand-alone correction/bonus sampler.
-struct VerifyArgs {
+// ---------------------------------------------------------------------------------------
+// Stand-alone correction / bonus draw (sv_residual_sample): one workgroup per request runs
+// the finalize's draws on the row pair at its accepted length
+// ---------------------------------------------------------------------------------------
+struct ResidualArgs {
     const void *target, *draft;
-    const int32_t *tokens, *draft_len;
-    float *alpha;
-    uint8_t *accept;
-    float *lse_t, *lse_d;
-    int32_t *amax_t, *amax_d;
-    int32_t *accept_len, *out_tokens, *n_out;
-    uint32_t *err;
+    const int32_t *draft_len, *accept_len;
+    int32_t *out_tokens;
     int64_t ld_t, ld_d;
-    int32_t B, K, V, nseg;
-    int32_t trows;         // target rows per request: K+1 (verify) or K (e2e)
-    float c;               // log2(e) / T   (0 in greedy mode)
-    float inv_t;           // 1 / T
+    int32_t K, V;
+    float c;   // log2(e) / T (0: greedy)
     uint64_t seed, step;
-    int32_t want_amax;
 };
 
-template <int DT>
-__device__ __forceinline__ const void *row_at(const void *base, int64_t row, int64_t ld) {
-    constexpr size_t esz = DT == kDtBF16 ? 2 : 4;
-    return static_cast<const char *>(base) + (size_t)(row * ld) * esz;
-}
-
-// ---------------------------------------------------------------------------------------
-// Workgroup reductions (fixed order: xor-shuffle tree inside a wave, waves in index order)
-// ---------------------------------------------------------------------------------------
-struct Red {
-    float m[2][kWaves], s[2][kWaves];
-    float v[2][kWaves];
-    int i[2][kWaves];
-    double d[kWaves];
-    float f[kWaves];
-};
-
-__device__ void block_lse2(float &mt, float &st, float &md, float &sd, float c, Red &red) {
-    wave_lse(mt, st, c);
-    wave_lse(md, sd, c);
-    const int w = threadIdx.x / kWave;
-    if (lane_id() == 0) { red.m[0][w] = mt; red.s[0][w] = st; red.m[1][w] = md; red.s[1][w] = sd; }
-    __syncthreads();
-    mt = red.m[0][0]; st = red.s[0][0]; md = red.m[1][0]; sd = red.s[1][0];
-    for (int j = 1; j < kWaves; ++j) {
-        lse_merge(mt, st, red.m[0][j], red.s[0][j], c);
-        lse_merge(md, sd, red.m[1][j], red.s[1][j], c);
-    }
-    __syncthreads();
-}
-
-__device__ void block_amax2(float &vt, int &it, float &vd, int &id, Red &red) {
-    wave_amax(vt, it);
-    wave_amax(vd, id);
-    const int w = threadIdx.x / kWave;
-    if (lane_id() == 0) { red.v[0][w] = vt; red.i[0][w] = it; red.v[1][w] = vd; red.i[1][w] = id; }
-    __syncthreads();
-    vt = red.v[0][0]; it = red.i[0][0]; vd = red.v[1][0]; id = red.i[1][0];
-    for (int j = 1; j < kWaves; ++j) {
-        amax_merge(vt, it, red.v[0][j], red.i[0][j]);
-        amax_merge(vd, id, red.v[1][j], red.i[1][j]);
-    }
-    __syncthreads();
-}
-
-__device__ float block_sum(float x, Red &red) {
-    x = wave_sum(x);
-    const int w = threadIdx.x / kWave;
-    if (lane_id() == 0) red.f[w] = x;
-    __syncthreads();
-    float t = 0.f;
-    for (int j = 0; j < kWaves; ++j) t += red.f[j];
-    __syncthreads();
-    return t;
-}
-
-__device__ double block_sum_d(double x, Red &red) {
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, kWave);
-    const int w = threadIdx.x / kWave;
-    if (lane_id() == 0) red.d[w] = x;
-    __syncthreads();
-    double t = 0.0;
-    for (int j = 0; j < kWaves; ++j) t += red.d[j];
-    __syncthreads();
-    return t;
-}
-
-// ---------------------------------------------------------------------------------------
-// Single-row streams used by the finalize and the stand-alone sampler
-// ---------------------------------------------------------------------------------------
-
-// Argmax of one row (lowest index among maxima), broadcast to every thread.
-template <int DT>
-__device__ int row_argmax(const void *row, int V, Red &red) {
-    float v = neg_inf(), vd = neg_inf();
-    int i = 0x7fffffff, id = 0x7fffffff;
-    for (int base = 0; base < V; base += kTile) {
-        const int e = base + threadIdx.x * kElems;
-        float z[8];
-        load8<DT>(row, e, V, z);
-        amax_update8(v, i, z, e);
-    }
-    block_amax2(v, i, vd, id, red);
-    return i == 0x7fffffff ? 0 : i;
-}
-
-// Draw from p = softmax(row / T) by inverse CDF at target u * R.  Sweep 1 streams the row
-// once, keeping (m, s) of every 512-logit segment in seg[0..nseg) / seg[nseg..2 nseg);
-// those become the segment masses, one wave finds the segment, and re-reads it to find
-// the token.  seg: 2*nseg floats of scratch (workspace or LDS).
-template <int DT>
-__device__ int draw_from_row(const void *row, int V, float c, float u, float *seg, int nseg, Red &red) {
-    const int w = threadIdx.x / kWave;
-    float m = neg_inf(), s = 0.f;
-    int it = 0;
-    for (int base = 0; base < V; base += kTile, ++it) {
-        const int e = base + threadIdx.x * kElems;
-        float z[8];
-        load8<DT>(row, e, V, z);
-        float cm = neg_inf(), cs = 0.f;
-        lse_update8(cm, cs, z, c);
-        lse_merge(m, s, cm, cs, c);
-        wave_lse(cm, cs, c);
-        if (lane_id() == 0) {
-            const int sidx = it * kWaves + w;
-            if (sidx < nseg) { seg[sidx] = cm; seg[nseg + sidx] = cs; }
-        }
-    }
-    float md = neg_inf(), sd = 0.f;
-    block_lse2(m, s, md, sd, c, red);
-    const float ls2 = log2f(s);
-    __threadfence_block();
-    __syncthreads();
-    for (int j = threadIdx.x; j < nseg; j += kThreads) {
-        const float sm = seg[j], ss = seg[nseg + j];
-        seg[j] = (sm == neg_inf()) ? 0.f : ss * exp2_fast(log2p(sm, m, c, ls2));
-    }
-    __threadfence_block();
-    __syncthreads();
-    double part = 0.0;
-    for (int j = threadIdx.x; j < nseg; j += kThreads) part += (double)seg[j];
-    const double R = block_sum_d(part, red);
-    __shared__ int s_tok;
-    if (w == 0) {
-        const double t = (double)u * R;
-        double ex;
-        const float *segw = seg;
-        int sidx = wave_find([&](int j) { return segw[j]; }, nseg, t, &ex);
-        int tok = 0;
-        if (sidx >= 0) {
-            const int e0 = sidx * kSeg;
-            const int n = min(kSeg, V - e0);
-            double ex2;
-            tok = wave_find([&](int j) { return exp2_fast(log2p(load1<DT>(row, e0 + j), m, c, ls2)); },
-                            n, t - ex, &ex2);
-            tok = tok < 0 ? e0 : e0 + tok;
-        }
-        if (lane_id() == 0) s_tok = tok;
-    }
-    __syncthreads();
-    return s_tok;
-}
-
-// ---------------------------------------------------------------------------------------
-// Stand-alone correction / bonus draw
-// ---------------------------------------------------------------------------------------
-constexpr int kResidualSegMax = (SV_V_MAX + kSeg - 1) / kSeg;  // 2048
+constexpr int kResidualSegMax = (SV_V_MAX + kBonusSeg - 1) / kBonusSeg;   // draw_from_row segments
+constexpr int kRowStep = kTeamThreads * 8;                                 // logits per workgroup sweep step
 
 template <int DTT, int DTD>
-__global__ __launch_bounds__(kThreads) void residual_kernel(VerifyArgs a) {
-    __shared__ Red red;
-    __shared__ float seg[2 * kResidualSegMax];
+__global__ __launch_bounds__(kTeamThreads) void residual_kernel(ResidualArgs a) {
+    __shared__ TeamRed red;
+    __shared__ DrawShared draw;
+    __shared__ float seg[2 * kResidualSegMax];   // range masses, then draw_from_row's segments
     __shared__ int s_tok;
     const int r = blockIdx.x;
     const int K = a.K, V = a.V;
+    const int w = threadIdx.x / kWave;
+    const int lane = lane_id();
     int L = a.draft_len ? a.draft_len[r] : K;
     if (L < 0 || L > K) L = L < 0 ? 0 : K;
     int tau = a.accept_len[r];
     if (tau < 0 || tau > L) tau = tau < 0 ? 0 : L;
-    const void *trow = row_at<DTT>(a.target, (int64_t)r * (K + 1) + tau, a.ld_t);
-    int tok;
+    const void *trow = row_ptr<DTT>(a.target, (int64_t)r * (K + 1) + tau, a.ld_t);
+    int tok = -1;
     if (a.c == 0.f) {
-        tok = row_argmax<DTT>(trow, V, red);
+        // greedy: the lowest index of the target row's maximum
+        float v = neg_inf(), vd = neg_inf();
+        int i = 0x7fffffff, id = 0x7fffffff;
+        for (int base = 0; base < V; base += kRowStep) {
+            float z[8];
+            load8<DTT>(trow, base + threadIdx.x * 8, V, z);
+            amax_update8(v, i, z, base + threadIdx.x * 8);
+        }
+        block_amax2(v, i, vd, id, red);
+        tok = i == 0x7fffffff ? 0 : i;
     } else {
         const float c = a.c;
         const float u = uniform24(a.seed, (uint64_t)r, (uint64_t)tau, kPurposeCorrection, a.step);
-        bool done = false;
-        tok = 0;
         if (tau < L) {
-            const void *drow = row_at<DTD>(a.draft, (int64_t)r * K + tau, a.ld_d);
-            float mt = neg_inf(), st = 0.f, md = neg_inf(), sd = 0.f;
-            for (int base = 0; base < V; base += kTile) {
-                const int e = base + threadIdx.x * kElems;
-                float zt[8], zd[8];
-                load8<DTT>(trow, e, V, zt);
-                load8<DTD>(drow, e, V, zd);
-                lse_update8(mt, st, zt, c);
-                lse_update8(md, sd, zd, c);
-            }
-            block_lse2(mt, st, md, sd, c, red);
-            const float ls2t = log2f(st), ls2d = log2f(sd);
-            const int w = threadIdx.x / kWave;
-            int itn = 0;
-            for (int base = 0; base < V; base += kTile, ++itn) {
-                const int e = base + threadIdx.x * kElems;
-                float zt[8], zd[8];
-                load8<DTT>(trow, e, V, zt);
-                load8<DTD>(drow, e, V, zd);
-                float res = 0.f;
+            // rejection at tau: the residual max(p - q, 0) of the row pair.  Normalisers of
+            // both rows in base 2, then the residual mass of each kTeamSeg-logit range (wave
+            // w takes ranges w, w + 4, ...), then the finalize's range draw.
+            const void *drow = row_ptr<DTD>(a.draft, (int64_t)r * K + tau, a.ld_d);
+            float Mt = neg_inf(), st = 0.f, Md = neg_inf(), sd = 0.f;
+            auto lane_ms8 = [&](const float (&z)[8], float &M, float &s) {
+                float cm = neg_inf();
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float p = exp2_fast(log2p(zt[j], mt, c, ls2t));
-                    const float q = exp2_fast(log2p(zd[j], md, c, ls2d));
-                    res += p - fminf(p, q);
+                for (int e = 0; e < 8; ++e) cm = fmaxf(cm, z[e]);
+                if (cm == neg_inf()) return;
+                const float cM = cm * c;
+                float cs = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) cs += exp2_fast(__builtin_fmaf(z[e], c, -cM));
+                ms_merge(M, s, cM, cs);
+            };
+            for (int base = 0; base < V; base += kRowStep) {
+                float zt[8], zd[8];
+                load8<DTT>(trow, base + threadIdx.x * 8, V, zt);
+                load8<DTD>(drow, base + threadIdx.x * 8, V, zd);
+                lane_ms8(zt, Mt, st);
+                lane_ms8(zd, Md, sd);
+            }
+            block_ms2_lanes(Mt, st, Md, sd, red);
+            const Norm2 nt = norm2(Mt, log2f(st)), nd = norm2(Md, log2f(sd));
+            const int nr = (V + kTeamSeg - 1) / kTeamSeg;
+            for (int q = w; q < nr; q += kTeamWaves) {
+                float m = 0.f;
+                for (int e8 = lane * 8; e8 < kTeamSeg; e8 += kWave * 8) {
+                    const int e = q * kTeamSeg + e8;
+                    float zt[8], zd[8];
+                    load8<DTT>(trow, e, V, zt);
+                    load8<DTD>(drow, e, V, zd);
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const float p = exp2_fast(log2prob(zt[k], c, nt));
+                        m += p - fminf(p, exp2_fast(log2prob(zd[k], c, nd)));
+                    }
                 }
-                res = wave_sum(res);
-                const int sidx = itn * kWaves + w;
-                if (lane_id() == 0 && sidx < a.nseg) seg[sidx] = res;
+                m = wave_sum(m);
+                if (lane == 0) seg[q] = m;
             }
             __syncthreads();
-            double part = 0.0;
-            for (int j = threadIdx.x; j < a.nseg; j += kThreads) part += (double)seg[j];
-            const double R = block_sum_d(part, red);
-            if (R > 0.0) {
-                if (threadIdx.x < kWave) {
-                    const double t = (double)u * R;
-                    double ex;
-                    int sidx = wave_find([&](int j) { return seg[j]; }, a.nseg, t, &ex);
-                    int tk = 0;
-                    if (sidx >= 0) {
-                        const int e0 = sidx * kSeg;
-                        const int n = min(kSeg, V - e0);
-                        double ex2;
-                        tk = wave_find(
-                            [&](int j) {
-                                const float p = exp2_fast(log2p(load1<DTT>(trow, e0 + j), mt, c, ls2t));
-                                const float q = exp2_fast(log2p(load1<DTD>(drow, e0 + j), md, c, ls2d));
-                                return p - fminf(p, q);
-                            },
-                            n, t - ex, &ex2);
-                        tk = tk < 0 ? e0 : e0 + tk;
-                    }
-                    if (threadIdx.x == 0) s_tok = tk;
-                }
-                __syncthreads();
-                tok = s_tok;
-                done = true;
-            }
+            tok = draw_ranges<DTT, DTD, true>(trow, drow, V, c, nt, nd, seg, nr, u, draw);
             __syncthreads();
         }
-        if (!done) tok = draw_from_row<DTT>(trow, V, c, u, seg, a.nseg, red);
+        // the bonus row (tau = L), or an empty residual (p == q in binary32): a draw from p_tau
+        if (tok < 0) tok = draw_from_row<DTT>(trow, V, c, u, seg, (V + kBonusSeg - 1) / kBonusSeg, red, s_tok);
     }
     if (threadIdx.x == 0) a.out_tokens[r] = tok;
 }
@@ -595,8 +435,8 @@ int dispatch_dtypes(int dt, int dd, Args &&...args) {
 
 template <int DTT, int DTD>
 struct ResidualLauncher {
-    static int run(const VerifyArgs &a, unsigned grid, hipStream_t s) {
-        hipLaunchKernelGGL((residual_kernel<DTT, DTD>), dim3(grid), dim3(kThreads), 0, s, a);
+    static int run(const ResidualArgs &a, unsigned grid, hipStream_t s) {
+        hipLaunchKernelGGL((residual_kernel<DTT, DTD>), dim3(grid), dim3(kTeamThreads), 0, s, a);
         return launch_status();
     }
 };
@@ -827,13 +667,11 @@ int sv_residual_sample(const sv_params *p, const void *target, const void *draft
         if (st) return st;
     }
     if (!accept_len || !token) return SV_EINVAL;
-    VerifyArgs a{};
-    a.target = target; a.draft = draft; a.draft_len = draft_len; a.accept_len = (int32_t *)accept_len;
+    ResidualArgs a{};
+    a.target = target; a.draft = draft; a.draft_len = draft_len; a.accept_len = accept_len;
     a.out_tokens = token;
-    a.err = nullptr;
     a.ld_t = p->ld_t; a.ld_d = p->ld_d;
-    a.B = p->B; a.K = p->K_max; a.V = p->V; a.nseg = (p->V + kSeg - 1) / kSeg;
-    a.trows = p->K_max + 1;
+    a.K = p->K_max; a.V = p->V;
     const bool greedy = p->temperature == 0.f;
     a.c = greedy ? 0.f : (float)(kLog2e / (double)p->temperature);
     a.seed = p->seed; a.step = p->step;

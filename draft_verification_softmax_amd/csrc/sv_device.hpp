@@ -96,24 +96,6 @@ __device__ __forceinline__ void lse_merge(float &m, float &s, float m2, float s2
     m = mn;
 }
 
-// Fold eight logits into (m, s).
-__device__ __forceinline__ void lse_update8(float &m, float &s, const float (&z)[8], float c) {
-    float cm = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
-    const float mn = fmaxf(m, cm);
-    if (mn == neg_inf()) return;
-    float acc = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc += exp2_fast((z[j] - mn) * c);
-    s = s * exp2_fast((m - mn) * c) + acc;
-    m = mn;
-}
-
-// log2 of a probability: (z - m) c - ls2 with ls2 = log2 s.  One helper so that every
-// kernel that recomputes a probability gets the identical binary32 value.
-__device__ __forceinline__ float log2p(float z, float m, float c, float ls2) {
-    return __builtin_fmaf(z - m, c, -ls2);
-}
-
 // Argmax state: larger value wins, equal values -> lower index.
 __device__ __forceinline__ void amax_merge(float &v, int &i, float v2, int i2) {
     if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }

@@ -66,69 +66,6 @@ constexpr int kMaxDevices = 64;
 
 // ---- request-level helpers --------------------------------------------------------------
 
-// Token of one row drawn from p = softmax(row / T) at target u * R by inverse CDF: one sweep
-// keeps (max, sum) of every 512-logit segment in `seg` (workspace, this workgroup only),
-// then a wave finds the segment and re-reads it.
-template <int DT>
-__device__ __forceinline__ int draw_from_row(const void *row, int V, float c, float u, float *seg, int nseg, TeamRed &red, int &s_tok) {
-    const int w = threadIdx.x / kWave;
-    float M = neg_inf(), s = 0.f;
-    int it = 0;
-    for (int base = 0; base < V; base += kTeamThreads * 8, ++it) {
-        float z[8];
-        load8<DT>(row, base + threadIdx.x * 8, V, z);
-        float cm = neg_inf();
-#pragma unroll
-        for (int e = 0; e < 8; ++e) cm = fmaxf(cm, z[e]);
-        const float cM = (cm == neg_inf()) ? neg_inf() : cm * c;   // base-2 reference
-        float cs = 0.f;
-        if (cm != neg_inf()) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) cs += exp2_fast(__builtin_fmaf(z[e], c, -cM));
-        }
-        ms_merge(M, s, cM, cs);
-        float wM = cM, ws = cs;
-        wave_ms(wM, ws);
-        if (lane_id() == 0) {
-            const int sidx = it * kTeamWaves + w;
-            if (sidx < nseg) { seg[sidx] = wM; seg[nseg + sidx] = ws; }
-        }
-    }
-    float Md = neg_inf(), sd = 0.f;
-    block_ms2_lanes(M, s, Md, sd, red);
-    const Norm2 nb = norm2(M, log2f(s));
-    __threadfence_block();
-    __syncthreads();
-    for (int q = threadIdx.x; q < nseg; q += kTeamThreads) {
-        const float sM = seg[q], ss = seg[nseg + q];
-        seg[q] = (sM == neg_inf()) ? 0.f : ss * exp2_fast((sM - nb.hi) - nb.lo);
-    }
-    __threadfence_block();
-    __syncthreads();
-    if (w == 0) {
-        double part = 0.0;
-        for (int q = lane_id(); q < nseg; q += kWave) part += (double)seg[q];
-#pragma unroll
-        for (int d = 32; d >= 1; d >>= 1) part += __shfl_xor(part, d, kWave);
-        const double R = part;
-        const double t = (double)u * R;
-        double ex;
-        const int sidx = wave_find([&](int q) { return seg[q]; }, nseg, t, &ex);
-        int tok = 0;
-        if (sidx >= 0) {
-            const int e0 = sidx * kBonusSeg;
-            const int n = min(kBonusSeg, V - e0);
-            double ex2;
-            const int k = wave_find([&](int q) { return exp2_fast(log2prob(load1<DT>(row, e0 + q), c, nb)); }, n,
-                                    t - ex, &ex2);
-            tok = k < 0 ? e0 : e0 + k;
-        }
-        if (lane_id() == 0) s_tok = tok;
-    }
-    __syncthreads();
-    return s_tok;
-}
-
 // Row normalisers in LDS words 1..4 of a row's accept record (the layout the stream
 // kernel publishes: flag, t.hi, d.hi, t.lo, d.lo).
 __device__ __forceinline__ void put_norms(uint32_t *w, Norm2 nt, Norm2 nd) {

@@ -188,10 +188,18 @@ int sv_verify_selected(const sv_params *params, const void *target, const void *
 int sv_accept_len(const uint8_t *accept, const int32_t *draft_len, int32_t B, int32_t K_max,
                   int32_t *accept_len, void *stream);
 
-/* Correction / bonus token per request given its accepted length (for callers with their
- * own accept logic).  Same layout, draw and counters as sv_verify_batch, so
- * token[r] == out_tokens[r][accept_len[r]] of a verify call with the same arguments.
- * Reads target row tau (and drafter row tau when tau < L_r). */
+/* Correction / bonus token per request given its accepted length [TV] [ABS] (for callers
+ * with their own accept logic).  [TV]: a draft position is accepted by rejection sampling
+ * with probability alpha = sum_v min(p, q), and the first rejection at tau voids every later
+ * draft, so one token follows position tau; [ABS]: that token must leave the output
+ * distributed as the target's, which the residual draw norm(max(p_tau - q_tau, 0)) after a
+ * rejection, and the draw from p at row L_r after a fully accepted draft, do (the standard
+ * speculative-sampling rule named above, where the pages give no formula).  Same layout,
+ * draw rule and counters as sv_verify_batch: token[r] is out_tokens[r][accept_len[r]] of a
+ * verify call with the same arguments, up to the summation order of the draw's total (the
+ * two compute their normalisers separately).  Reads target row tau (and drafter row tau
+ * when tau < L_r).  accept_len [B] int32 on the device (clamped to [0, L_r]); token [B]
+ * int32.  Errors: SV_EINVAL, SV_EUNSUPPORTED, SV_EHIP. */
 int sv_residual_sample(const sv_params *params, const void *target, const void *draft,
                        const int32_t *draft_len, const int32_t *accept_len, int32_t *token,
                        void *stream);

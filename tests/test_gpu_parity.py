@@ -177,10 +177,22 @@ def test_accept_len_and_residual_sample(sv):
     assert np.array_equal(al.cpu().numpy(), svref.accept_len(out["accept"].cpu().numpy(), draft_len=dl.cpu().numpy()))
     tok = sv.sv_residual_sample(v.target, v.draft, out["accept_len"], 0.9, seed=v.seed, step=4, draft_len=dl)
     want = out["out_tokens"].gather(1, out["accept_len"].long()[:, None])[:, 0]
-    assert torch.equal(tok, want)
-    # oracle on forced accepted lengths (including 0 and L_r): equal, or within the CDF band
     tn, dn = workloads.to_oracle(v.target), workloads.to_oracle(v.draft)
     dln = dl.cpu().numpy()
+    # the stand-alone draw and the fused one sum their normalisers separately: equal tokens,
+    # or (counted) both equal to the oracle's or within its CDF band
+    tok_np, want_np, al_np = tok.cpu().numpy(), want.cpu().numpy(), al.cpu().numpy()
+    otok0 = svref.residual_sample(tn, dn, al_np, 0.9, "bf16", seed=v.seed, step=4, draft_len=dln)
+    differ = 0
+    for r in range(8):
+        if tok_np[r] != want_np[r]:
+            differ += 1
+            for g in (int(tok_np[r]), int(want_np[r])):
+                assert g == otok0[r] or _token_in_band(tn, dn, 0.9, "bf16", r, int(al_np[r]), int(dln[r]), g,
+                                                       int(otok0[r]), v.seed, 4), (r, g, otok0[r])
+    _say(f"residual_sample vs fused: {differ} of 8 differ")
+    assert differ <= near_token_max(8)
+    # oracle on forced accepted lengths (including 0 and L_r): equal, or within the CDF band
     near = 0
     for seed, step, forced in [(2, 0, [0, 3, 0, 2, 16, 1, 5, 12]), (9, 3, [15, 2, 0, 7, 0, 0, 8, 11]),
                                (v.seed, 1, [16, 1, 0, 6, 3, 1, 9, 0])]:
