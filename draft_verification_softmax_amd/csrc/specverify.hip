@@ -227,47 +227,8 @@ __device__ int dcut_choose(const uint64_t *keys, int total, int B, const float *
     return s_n[0];
 }
 
-__global__ __launch_bounds__(kReduceThreads) void budget_kernel(const float *conf, const int32_t *draft_len,
-                                                                int B, int K, int N, int32_t *lens,
-                                                                int32_t *row_off, int32_t *row_list,
-                                                                uint32_t *err, const float *cost, int n_cost,
-                                                                int32_t *n_chosen, double *utility) {
-    __shared__ uint64_t keys[SV_BUDGET_MAX];
-    __shared__ int cnt[SV_BUDGET_MAX];
-    __shared__ int scan[kReduceThreads];
-    __shared__ int s_total;
-    const int n = B * K;
-    int np2 = 1;
-    while (np2 < n) np2 <<= 1;
-    if (threadIdx.x == 0) s_total = 0;
-    for (int i = threadIdx.x; i < np2; i += kReduceThreads) keys[i] = ~0ull;
-    // the confidences are staged in LDS first (one coalesced sweep; cnt serves as the
-    // staging area) so that the per-request products below read no global memory
-    float *cstage = reinterpret_cast<float *>(cnt);
-    for (int i = threadIdx.x; i < n; i += kReduceThreads) cstage[i] = conf[i];
-    __syncthreads();
-    // cumulative confidence per request: one thread per request, sequential binary32 products
-    int local_total = 0;
-    for (int r = threadIdx.x; r < B; r += kReduceThreads) {
-        int L = draft_len ? draft_len[r] : K;
-        if (L < 0 || L > K) {
-            if (err) atomicOr(err, SV_DEVERR_DRAFT_LEN);
-            L = L < 0 ? 0 : K;
-        }
-        float C = 1.f;
-        for (int k = 0; k < L; ++k) {
-            const float ck = cstage[r * K + k];
-            C = (k == 0) ? ck : __fmul_rn(C, ck);
-            // ascending key = descending C (non-negative binary32 bits are monotone), then (r, k)
-            keys[r * K + k] = ((uint64_t)(~__float_as_uint(C)) << 32) | (uint32_t)(r * K + k);
-        }
-        local_total += L;
-    }
-    atomicAdd(&s_total, local_total);
-    __syncthreads();
-    for (int r = threadIdx.x; r < B; r += kReduceThreads) cnt[r] = 0;
-    __syncthreads();
-    // bitonic sort, ascending
+// Bitonic sort of keys[0..np2), ascending (np2 a power of two); every thread of the block calls it.
+__device__ void sort_keys(uint64_t *keys, int np2) {
     if (np2 <= kReduceThreads) {
         // one key per thread in registers: exchanges within a wave (partner distance < 64)
         // by lane shuffles, wider ones through LDS
@@ -306,13 +267,138 @@ __global__ __launch_bounds__(kReduceThreads) void budget_kernel(const float *con
             }
         }
     }
+}
+
+// The kth smallest (0-based) of keys[0..n) (distinct), by radix selection from the top
+// 4-bit digit down.  Each pass counts the keys that agree with the digits chosen so far, per
+// value of the next digit: one ballot per value in every wave, each wave's 16 counts to its
+// own LDS row (wcnt[wave][16]); then wave 0 sums the rows per digit value (lane d takes value
+// d), scans them and keeps the digit whose count holds rank kth.  Once a single key agrees,
+// it is the answer.  Every thread of the block calls it; wcnt, s_prefix, s_rank, s_one are LDS.
+__device__ uint64_t select_kth(const uint64_t *keys, int n, int kth, int (*wcnt)[16], uint64_t *s_prefix,
+                               int *s_rank, int *s_one) {
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+    constexpr int kWavesPerBlock = kReduceThreads / kWave;
+    uint64_t prefix = 0;
+    int rank = kth;
+    for (int shift = 60; shift >= 0; shift -= 4) {
+        const uint64_t known = shift == 60 ? 0ull : ~0ull << (shift + 4);   // digits chosen so far
+        int c = 0;   // lane d < 16: this wave's count of digit value d
+        for (int base = 0; base < n; base += kReduceThreads) {   // the same trip count in every thread
+            const int i = base + (int)threadIdx.x;
+            const uint64_t key = i < n ? keys[i] : 0ull;
+            const int d = (i < n && (key & known) == prefix) ? (int)((key >> shift) & 15u) : -1;
+#pragma unroll
+            for (int b = 0; b < 16; ++b) {
+                const int m = __popcll(__ballot(d == b));
+                if (lane == b) c += m;
+            }
+        }
+        if (lane < 16) wcnt[wv][lane] = c;
+        __syncthreads();
+        if (wv == 0) {
+            int h = 0;
+            if (lane < 16)
+                for (int w = 0; w < kWavesPerBlock; ++w) h += wcnt[w][lane];
+            // inclusive scan over the 16 digit values
+            int incl = h;
+#pragma unroll
+            for (int dd = 1; dd < 16; dd <<= 1) {
+                const int y = __shfl_up(incl, dd, kWave);
+                if (lane >= dd) incl += y;
+            }
+            // the first value whose running count passes rank
+            const uint64_t hit = __ballot(lane < 16 && incl > rank);
+            const int b = hit ? __builtin_ctzll(hit) : 15;
+            if (lane == b) {
+                *s_prefix = prefix | ((uint64_t)b << shift);
+                *s_rank = rank - (incl - h);
+                *s_one = h == 1 ? 1 : 0;
+            }
+        }
+        __syncthreads();
+        prefix = *s_prefix;
+        rank = *s_rank;
+        if (*s_one != 0 && shift > 0) {   // the one key that agrees with the chosen digits
+            const uint64_t mask = ~0ull << shift;
+            __syncthreads();   // every thread has read s_prefix before it is overwritten
+            for (int i = threadIdx.x; i < n; i += kReduceThreads)
+                if ((keys[i] & mask) == prefix) *s_prefix = keys[i];
+            __syncthreads();
+            prefix = *s_prefix;
+            break;
+        }
+    }
+    __syncthreads();   // s_prefix and wcnt may be reused by the caller
+    return prefix;
+}
+
+__global__ __launch_bounds__(kReduceThreads) void budget_kernel(const float *conf, const int32_t *draft_len,
+                                                                int B, int K, int N, int32_t *lens,
+                                                                int32_t *row_off, int32_t *row_list,
+                                                                uint32_t *err, const float *cost, int n_cost,
+                                                                int32_t *n_chosen, double *utility) {
+    __shared__ uint64_t keys[SV_BUDGET_MAX];
+    __shared__ int cnt[SV_BUDGET_MAX];
+    __shared__ int scan[kReduceThreads];
+    __shared__ int s_total;
+    const int n = B * K;
+    int np2 = 1;
+    while (np2 < n) np2 <<= 1;
+    if (threadIdx.x == 0) s_total = 0;
+    for (int i = threadIdx.x; i < np2; i += kReduceThreads) keys[i] = ~0ull;
+    for (int r = threadIdx.x; r < B; r += kReduceThreads) cnt[r] = 0;
+    __syncthreads();
+    // cumulative confidence per request: one thread per request, sequential binary32 products
+    // (the confidences read from global memory 32 at a time, ahead of the products)
+    int local_total = 0;
+    for (int r = threadIdx.x; r < B; r += kReduceThreads) {
+        int L = draft_len ? draft_len[r] : K;
+        if (L < 0 || L > K) {
+            if (err) atomicOr(err, SV_DEVERR_DRAFT_LEN);
+            L = L < 0 ? 0 : K;
+        }
+        float C = 1.f;
+        for (int k0 = 0; k0 < L; k0 += 32) {
+            // every load of the batch issued before the products use them, at clamped (valid)
+            // indices so that no load sits under a branch
+            float ck[32];
+            const int last = r * K + L - 1;
+#pragma unroll
+            for (int e = 0; e < 32; ++e) ck[e] = conf[min(r * K + k0 + e, last)];
+#pragma unroll
+            for (int e = 0; e < 32; ++e) {
+                const int k = k0 + e;
+                if (k >= L) break;
+                C = (k == 0) ? ck[e] : __fmul_rn(C, ck[e]);
+                // ascending key = descending C (non-negative binary32 bits are monotone), then (r, k)
+                keys[r * K + k] = ((uint64_t)(~__float_as_uint(C)) << 32) | (uint32_t)(r * K + k);
+            }
+        }
+        local_total += L;
+    }
+    atomicAdd(&s_total, local_total);
+    __syncthreads();
     __shared__ double dscan[kReduceThreads / kWave], s_ratio[kReduceThreads / kWave], s_E[kReduceThreads / kWave];
     __shared__ int s_n[kReduceThreads / kWave];
-    const int keep = cost ? dcut_choose(keys, s_total, B, cost, n_cost, dscan, s_ratio, s_n, s_E, n_chosen, utility)
-                          : min(N, s_total);
-    for (int i = threadIdx.x; i < keep; i += kReduceThreads) {
-        const int flat = (int)(keys[i] & 0xffffffffu);
-        atomicAdd(&cnt[flat / K], 1);
+    __shared__ int wcnt[kReduceThreads / kWave][16], s_rank, s_one;
+    __shared__ uint64_t s_prefix;
+    int keep;
+    uint64_t thr = 0;   // the keep-th smallest key: the selection is every key <= thr
+    if (!cost) {
+        keep = min(N, s_total);
+        if (keep > 0) thr = select_kth(keys, n, keep - 1, wcnt, &s_prefix, &s_rank, &s_one);
+    } else {
+        sort_keys(keys, np2);   // the D-cut choice sums the candidates in order
+        keep = dcut_choose(keys, s_total, B, cost, n_cost, dscan, s_ratio, s_n, s_E, n_chosen, utility);
+        if (keep > 0) thr = keys[keep - 1];
+    }
+    // selected rows per request: the keys <= thr, wherever they sit in keys[]
+    if (keep > 0) {
+        for (int i = threadIdx.x; i < n; i += kReduceThreads) {
+            const uint64_t key = keys[i];
+            if (key <= thr) atomicAdd(&cnt[(int)(key & 0xffffffffu) / K], 1);
+        }
     }
     __syncthreads();
     // exclusive scan of cnt over B: contiguous chunk per thread, then a scan of chunk sums
