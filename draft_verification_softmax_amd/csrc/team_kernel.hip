@@ -778,13 +778,18 @@ __device__ __forceinline__ void finalize_request(const TeamArgs &a, int r, FinSh
 // bonus slots, then one finalize workgroup per request
 // =======================================================================================
 // AMAX: also publish the argmax partials (always in greedy mode; on request otherwise).
-// At most 96 registers per lane, so five waves share each SIMD.  KEEP (not greedy): each lane
+// Bfloat16 rows: at most 96 registers per lane, so five waves share each SIMD.  A binary32
+// row takes 64 registers of chunk instead of 32: four waves (128 registers) with one such row,
+// three with two, so that the chunk stays in registers.  KEEP (not greedy): each lane
 // keeps pass 1's terms in binary32 for pass 2, which then costs a multiply, a min and an add per
 // logit pair instead of two widenings, two FMAs, a min, an exponential and an add; the terms
 // take ~160 registers, so three waves share a SIMD.  The launch takes it only for a grid that
 // fits on the device at once at that occupancy, where fewer waves per SIMD cost nothing.
+template <int DTT, int DTD>
+constexpr int kStreamWaves = 2 + (DTT == kDtBF16 ? 1 : 0) + (DTD == kDtBF16 ? 1 : 0) + (DTT == kDtBF16 && DTD == kDtBF16 ? 1 : 0);
+
 template <int DTT, int DTD, int MODE, bool AMAX, bool KEEP>
-__global__ __launch_bounds__(kTeamThreads) __attribute__((amdgpu_waves_per_eu(KEEP ? 3 : 5))) void stream_kernel(
+__global__ __launch_bounds__(kTeamThreads) __attribute__((amdgpu_waves_per_eu(KEEP ? 3 : kStreamWaves<DTT, DTD>))) void stream_kernel(
     TeamArgs a) {
     __shared__ typename KernelShared<MODE>::type sh;
 
