@@ -475,10 +475,12 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4 *p, size_t
     if (x == 0x9e3779b9u) sink[0] = x;
 }
 
-// Zero-fills a workspace of n16 16-byte words and records its byte count in the header.
+// Zero-fills a workspace of n16 16-byte words and records its byte count in the header,
+// followed by its complement (a record is trusted only when the two agree).
 __global__ void init_workspace_kernel(uint4 *p, size_t n16, size_t bytes) {
+    const uint4 rec = make_uint4((uint32_t)bytes, (uint32_t)(bytes >> 32), ~(uint32_t)bytes, ~(uint32_t)(bytes >> 32));
     for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
-        p[i] = i == kOffWsBytes / 16 ? make_uint4((uint32_t)bytes, (uint32_t)(bytes >> 32), 0, 0) : make_uint4(0, 0, 0, 0);
+        p[i] = i == kOffWsBytes / 16 ? rec : make_uint4(0, 0, 0, 0);
 }
 
 }  // namespace sv
@@ -904,7 +906,9 @@ int sv_device_error(void *workspace, void *stream, uint32_t *flags) {
         return SV_EHIP;
     if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return SV_EHIP;
     const uint32_t v = (uint32_t)hdr[kOffErr / 8];
-    const size_t recorded = (size_t)hdr[kOffWsBytes / 8];
+    // the byte count sv_workspace_init recorded, trusted only next to its complement
+    const uint64_t rec = hdr[kOffWsBytes / 8], rec_check = hdr[kOffWsBytes / 8 + 1];
+    const size_t recorded = rec_check == ~rec ? (size_t)rec : 0;
     *flags = v;
     if (!v) return SV_OK;
     if (workspace_needs_init(v, (uint32_t)hdr[kOffEpoch / 8]) && recorded >= kOffArrive) {

@@ -136,3 +136,24 @@ def test_e2e_runs_on_a_poisoned_workspace(sv):
     assert _epoch(buf) & 0x80000000   # still poisoned
     sv.sv_workspace_init(buf)
     assert _epoch(buf) == 0
+
+
+def test_size_record_without_its_complement_is_not_trusted(sv):
+    """sv_device_error zero-fills again only a workspace whose recorded byte count sits next
+    to its complement: with the complement overwritten it clears the flag and leaves the
+    workspace poisoned, as for a workspace zeroed by the caller."""
+    _say("poisoned verify, damaged size record")
+    t, d, x = _inputs()
+    B, K = x.shape
+    ws = sv.Workspace(DEV)
+    buf = ws.get(B, K, t.shape[2])
+    _poison(buf)
+    buf.view(torch.int32)[200 // 4] = 12345   # the complement's low word (bytes 200..203)
+    torch.cuda.synchronize()
+    got = _np(sv.sv_verify_batch(t, d, x, 0.9, seed=3, workspace=ws))
+    assert (got["n_out"] == 0).all()
+    assert sv.sv_device_error(buf) == sv.SV_DEVERR_POISONED
+    assert _epoch(buf) == POISONED_EPOCH & 0xffffffff   # not zero-filled
+    sv.sv_workspace_init(buf)
+    again = _np(sv.sv_verify_batch(t, d, x, 0.9, seed=3, workspace=ws))
+    assert sv.sv_device_error(buf) == 0 and (again["n_out"] >= 1).all()
