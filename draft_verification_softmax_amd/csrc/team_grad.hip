@@ -64,20 +64,89 @@ __device__ __forceinline__ float beta_sum(LaneRow<DTT> &t, LaneRow<DTD> &d, floa
     return b0 + b1;
 }
 
+// The dot2 form of the two gradient passes over bfloat16 rows (as in the overlap pass of the
+// verification): v_dot2_f32_bf16 with beta = bf16(c) in one half of its second operand widens
+// one logit and applies the scale and the normaliser in one instruction, y = z beta - N.hi /
+// gamma, so x = z c - N.hi is y gamma, and q < p is yd < yt (gamma > 0).  The low parts of the
+// normalisers are left out (the caller takes this form only when both are below 2^-20).  A
+// masked (-inf) logit in the other half of a packed word makes y NaN: a NaN-propagating running
+// maximum of every y tells the caller to take the FMA form for the wave instead.
+// Eight products of two packed words of each row: yt[e], yd[e] for slots 2q + e (words q, q+1
+// of the lane; e = 0, 1 from word q, e = 2, 3 from word q + 1).  A DOT result read by another
+// VALU instruction needs three wait states, which the closing s_nop gives the last ones.
+__device__ __forceinline__ void dot2_y8(uint32_t t0, uint32_t t1, uint32_t d0, uint32_t d1, uint32_t blo,
+                                        uint32_t bhi, float ct, float cd, float (&yt)[4], float (&yd)[4]) {
+    asm("v_dot2_f32_bf16 %0, %8, %12, %14\n\t"
+        "v_dot2_f32_bf16 %1, %8, %13, %14\n\t"
+        "v_dot2_f32_bf16 %2, %9, %12, %14\n\t"
+        "v_dot2_f32_bf16 %3, %9, %13, %14\n\t"
+        "v_dot2_f32_bf16 %4, %10, %12, %15\n\t"
+        "v_dot2_f32_bf16 %5, %10, %13, %15\n\t"
+        "v_dot2_f32_bf16 %6, %11, %12, %15\n\t"
+        "v_dot2_f32_bf16 %7, %11, %13, %15\n\t"
+        "s_nop 2"
+        : "=&v"(yt[0]), "=&v"(yt[1]), "=&v"(yt[2]), "=&v"(yt[3]), "=&v"(yd[0]), "=&v"(yd[1]), "=&v"(yd[2]),
+          "=&v"(yd[3])
+        : "v"(t0), "v"(t1), "v"(d0), "v"(d1), "s"(blo), "s"(bhi), "v"(ct), "v"(cd));
+}
+
+// beta_sum in the dot2 form; chk: the running NaN-propagating maximum of every y.
+__device__ __forceinline__ float beta_sum_dot2(LaneRow<kDtBF16> &t, LaneRow<kDtBF16> &d, Norm2 nt, Norm2 nd,
+                                               const Dot2Scale &ds, float &chk) {
+    float ct = neg_over_gamma(nt.hi, ds), cd = neg_over_gamma(nd.hi, ds);
+    // wait states between the VALU writes of ct, cd and the first DOT that reads them
+    asm volatile("s_nop 4" : "+v"(ct), "+v"(cd));
+    float b0 = 0.f, b1 = 0.f;
+    chk = neg_inf();
+#pragma unroll
+    for (int q = 0; q < LaneRow<kDtBF16>::kWords; q += 2) {
+        float yt[4], yd[4];
+        dot2_y8(t.w[q], t.w[q + 1], d.w[q], d.w[q + 1], ds.blo, ds.bhi, ct, cd, yt, yd);
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+            b0 += (yd[e] < yt[e]) ? exp2_fast(yd[e] * ds.gamma) : 0.f;
+            b1 += (yd[e + 1] < yt[e + 1]) ? exp2_fast(yd[e + 1] * ds.gamma) : 0.f;
+            chk = __builtin_elementwise_maximum(chk, __builtin_elementwise_maximum(yt[e], yd[e]));
+            chk = __builtin_elementwise_maximum(chk, __builtin_elementwise_maximum(yt[e + 1], yd[e + 1]));
+        }
+    }
+    return b0 + b1;
+}
+
 // Gradient of a member's chunk: slot i of lane l in wave w is token
 // base + (i / 8) * 512 + l * 8 + i % 8 (base = chunk start + w * kTeamSeg).
-template <int DTT, int DTD, int DTG, bool FULL>
+// D2: the dot2 form (bfloat16 rows, low parts below 2^-20, no NaN in the wave's y).
+template <int DTT, int DTD, int DTG, bool FULL, bool D2>
 __device__ __forceinline__ void write_chunk(LaneRow<DTT> &t, LaneRow<DTD> &d, float c, Norm2 nt, Norm2 nd,
-                                            float beta, float scale, void *grow, int base, int V) {
+                                            float beta, float scale, void *grow, int base, int V,
+                                            const Dot2Scale &ds) {
+    float ct = 0.f, cd = 0.f;
+    if constexpr (D2) {
+        ct = neg_over_gamma(nt.hi, ds);
+        cd = neg_over_gamma(nd.hi, ds);
+        asm volatile("s_nop 4" : "+v"(ct), "+v"(cd));
+    }
 #pragma unroll
     for (int g = 0; g < kTeamE; g += 8) {
-        t.refresh8(g);
-        d.refresh8(g);
         float gv[8];
+        if constexpr (D2) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float xt = log2prob(t.get(g + e), c, nt), xd = log2prob(d.get(g + e), c, nd);
-            gv[e] = scale * exp2_fast(xd) * ((xd < xt ? 1.f : 0.f) - beta);
+            for (int h = 0; h < 2; ++h) {
+                const int q = g / 2 + 2 * h;   // words q, q + 1: slots g + 4 h .. g + 4 h + 3
+                float yt[4], yd[4];
+                dot2_y8(t.w[q], t.w[q + 1], d.w[q], d.w[q + 1], ds.blo, ds.bhi, ct, cd, yt, yd);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    gv[4 * h + e] = scale * exp2_fast(yd[e] * ds.gamma) * ((yd[e] < yt[e] ? 1.f : 0.f) - beta);
+            }
+        } else {
+            t.refresh8(g);
+            d.refresh8(g);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float xt = log2prob(t.get(g + e), c, nt), xd = log2prob(d.get(g + e), c, nd);
+                gv[e] = scale * exp2_fast(xd) * ((xd < xt ? 1.f : 0.f) - beta);
+            }
         }
         const int v0 = base + g * 64 + lane_id() * 8;
         if (FULL || v0 + 8 <= V) {
@@ -159,7 +228,21 @@ __device__ __forceinline__ void grad_member(const TeamArgs &a, const GradArgs &g
     const Norm2 nt = s_tot[0], nd = s_tot[1];
 
     // ---- second exchange: beta ----
-    const float b = block_sumf(beta_sum(tr, dr, c, nt, nd), red);
+    // the dot2 form for bfloat16 rows when both low parts are negligible and no y of the
+    // wave is NaN (no masked logit next to another in a packed word); else the FMA form
+    bool d2 = false;
+    float bl;
+    if constexpr (DTT == kDtBF16 && DTD == kDtBF16) {
+        const Dot2Scale ds = dot2_scale(opaque_args());
+        const bool small_lo = __builtin_fabsf(nt.lo) <= kLoNegligible && __builtin_fabsf(nd.lo) <= kLoNegligible;
+        if (ds.ok && small_lo) {
+            float chk;
+            bl = beta_sum_dot2(tr, dr, nt, nd, ds, chk);
+            d2 = !__ballot(__builtin_isnan(chk));   // wave-uniform
+        }
+    }
+    if (!d2) bl = beta_sum(tr, dr, c, nt, nd);
+    const float b = block_sumf(bl, red);
     if (threadIdx.x == 0) putf(a.apart + row * S + j, b, tag);
     if (threadIdx.x < kWave) {
         const bool got = wave_poll(a.apart + row * S, S, tag, pay, a.spin_ticks);
@@ -178,7 +261,15 @@ __device__ __forceinline__ void grad_member(const TeamArgs &a, const GradArgs &g
     }
     __syncthreads();
     if (!*s_ok) return;
-    write_chunk<DTT, DTD, DTG, FULL>(tr, dr, c, nt, nd, s_bs[0], s_bs[1], grad_row<DTG>(g, row), base, V);
+    if constexpr (DTT == kDtBF16 && DTD == kDtBF16) {
+        if (d2) {
+            write_chunk<DTT, DTD, DTG, FULL, true>(tr, dr, c, nt, nd, s_bs[0], s_bs[1], grad_row<DTG>(g, row), base, V,
+                                                   dot2_scale(opaque_args()));
+            return;
+        }
+    }
+    write_chunk<DTT, DTD, DTG, FULL, false>(tr, dr, c, nt, nd, s_bs[0], s_bs[1], grad_row<DTG>(g, row), base, V,
+                                            Dot2Scale{});
 }
 
 }  // namespace
@@ -274,7 +365,8 @@ __global__ __launch_bounds__(kTeamThreads) void fixup_kernel(TeamArgs a, GradArg
             const int base = m * kTeamChunk + w * kTeamSeg;
             tr.template load<false>(trow, base, a.V);
             dr.template load<false>(drow, base, a.V);
-            write_chunk<DTT, DTD, DTG, false>(tr, dr, c, nt, nd, (float)beta, scale, grad_row<DTG>(g, rr), base, a.V);
+            write_chunk<DTT, DTD, DTG, false, false>(tr, dr, c, nt, nd, (float)beta, scale, grad_row<DTG>(g, rr), base,
+                                                     a.V, Dot2Scale{});
         }
         __syncthreads();
     }
