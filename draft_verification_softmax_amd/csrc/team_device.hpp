@@ -252,16 +252,26 @@ struct LaneRow {
         idx = sl < 0 ? 0x7fffffff : base + (sl >> 3) * 512 + lane_id() * 8 + (sl & 7);
     }
 
+    // The wave's first logit (lane 0, slot 0), the same value in every lane: the packed word
+    // is read into a scalar register and widened there.
+    __device__ __forceinline__ float wave_first() const {
+        const uint32_t u = __builtin_amdgcn_readfirstlane(w[0]);
+        if constexpr (DT == kDtBF16) {
+            return __uint_as_float(u << 16);
+        } else {
+            return __uint_as_float(u);
+        }
+    }
+
     // (M, s) of this lane's logits in base 2 (s = sum_i 2^{x_i c - M}) without a pass for
-    // the maximum.  The reference M is the same for the whole wave, c times the largest of
-    // the lanes' first 8 logits, so the wave's sums add up without rescaling.  Should a
-    // logit lie so far above it that some lane's sum leaves range (or every first 8 be
-    // -inf), the wave takes its exact maximum instead.  Every lane of the wave must call it.
+    // the maximum.  The reference M is the same for the whole wave, c times the wave's first
+    // logit, so the wave's sums add up without rescaling; as that logit is one of the wave's,
+    // the wave's largest term is at least 1 and none that matters underflows.  Should a logit
+    // lie so far above it that some lane's sum leaves range (or the first logit be -inf or
+    // NaN), the wave takes its exact maximum instead.  Every lane of the wave must call it.
     __device__ __forceinline__ void lane_ms(float c, float &M, float &s) {
         refresh8(0);
-        const float m8 = fmaxf(fmaxf(fmaxf(get(0), get(1)), fmaxf(get(2), get(3))),
-                               fmaxf(fmaxf(get(4), get(5)), fmaxf(get(6), get(7))));
-        const float mw = wave_max(m8);
+        const float mw = wave_first();
         M = (mw == neg_inf()) ? neg_inf() : mw * c;
         s = (mw == neg_inf()) ? 0.f : exp_sum(c, M);
         if (__ballot(mw == neg_inf() || !(s < 0x1p100f))) {   // wave-uniform
@@ -291,14 +301,12 @@ struct LaneRow {
     }
 
     // lane_ms with the terms kept in e.  The packed words are dead once e holds the terms:
-    // should the first-8 reference fail, the chunk is read again from the row.
+    // should the first-logit reference fail, the chunk is read again from the row.
     template <bool FULL>
     __device__ __forceinline__ void lane_ms_keep(float c, float &M, float &s, float (&e)[kTeamE], const void *row,
                                                  int base, int V) {
         refresh8(0);
-        const float m8 = fmaxf(fmaxf(fmaxf(get(0), get(1)), fmaxf(get(2), get(3))),
-                               fmaxf(fmaxf(get(4), get(5)), fmaxf(get(6), get(7))));
-        const float mw = wave_max(m8);
+        const float mw = wave_first();
         M = (mw == neg_inf()) ? neg_inf() : mw * c;
         s = exp_keep(c, M, e);
         if (__ballot(mw == neg_inf() || !(s < 0x1p100f))) {   // wave-uniform

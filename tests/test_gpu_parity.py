@@ -96,7 +96,7 @@ def test_ragged_vocab_several_tiles(sv, dtype, T):
 @pytest.mark.parametrize("T,want_amax", [(0.9, False), (0.9, True), (0.0, True)])
 def test_mtp_full(sv, T, want_amax):
     """The MTP workload (16 x 3 x 131072): its grid fits on the device at once, so the
-    kept-term instance runs; without argmax outputs its pass 1 takes the first-8 reference
+    kept-term instance runs; without argmax outputs its pass 1 takes the first-logit reference
     (the configuration a caller gets by default), with them the exact maxima."""
     v = _move(workloads.make_verify_inputs("mtp", device="cpu", T=T))
     _run_pair(sv, v, T, want_amax=want_amax)
@@ -674,10 +674,10 @@ def test_masked_logits(sv, B, want_amax):
     """-inf logits (masked vocabulary): p or q is exactly 0 there; drafted tokens inside the
     target's mask are always rejected, and no emitted token is a masked one.  B = 4 runs the
     kept-term instance, B = 64 (832 workgroups) the other; in both, the drafter's wave range
-    [8192, 12288) starts with 512 masked logits, so every lane's first 8 are -inf, its
+    [8192, 12288) starts with 512 masked logits, so the wave's first logit is -inf, its
     provisional reference is -inf and the exact-maximum fallback runs.  That holds without
-    argmax outputs (want_amax False), where pass 1 takes the provisional first-8 reference; with
-    them, pass 1 takes the exact maxima and no fallback is needed."""
+    argmax outputs (want_amax False), where pass 1 takes the provisional first-logit reference;
+    with them, pass 1 takes the exact maxima and no fallback is needed."""
     g = torch.Generator(device=DEV).manual_seed(5)
     K, V = 5, 20000
     assert (_grid(B, K, V) > _keep_limit()) == (B == 64)
@@ -698,12 +698,33 @@ def test_masked_logits(sv, B, want_amax):
             assert (gg["accept"][:, 0] == 0).all()
 
 
+@pytest.mark.parametrize("low", [-12.0, -40.0])
+@pytest.mark.parametrize("B", [4, 64])
+def test_low_reference_logit(sv, B, low):
+    """Every wave range (4096 logits) starts with a logit far below the rest of its row, and
+    that first logit is the provisional pass-1 reference of its wave.  At T = 0.3 (c = 4.81)
+    -12 leaves the lane sums near 2^85, inside range, with no fallback; -40 takes them past
+    2^100, so each wave falls back to its exact maximum.  At T = 0.9 both stay in range.
+    B = 4 runs the kept-term instance, B = 64 the other."""
+    g = torch.Generator(device=DEV).manual_seed(11)
+    K, V = 4, 40000
+    assert (_grid(B, K, V) > _keep_limit()) == (B == 64)
+    t = 1.5 * torch.randn((B, K + 1, V), generator=g, device=DEV)
+    d = t[:, :K] + 0.5 * torch.randn((B, K, V), generator=g, device=DEV)
+    t[..., ::4096] = low
+    d[..., ::4096] = low
+    t, d = t.to(torch.bfloat16), d.to(torch.bfloat16)
+    toks = torch.randint(0, V, (B, K), generator=g, device=DEV, dtype=torch.int32)
+    for T in (0.3, 0.9):
+        _run_pair(sv, _custom(t, d, toks, T, f"low first logit {low}"), T, want_amax=False)
+
+
 @pytest.mark.parametrize("want_amax", [False, True])
 @pytest.mark.parametrize("T,B", [(0.005, 4), (0.02, 4), (25.0, 4), (0.005, 48), (0.02, 48)])
 def test_extreme_temperatures(sv, T, B, want_amax):
     """Very low temperatures (base-2 normalisers of several hundred to a few thousand, past
     what one binary32 value holds to 1e-5, and sums far from the provisional reference: the
-    exact-maximum fallback when pass 1 takes the provisional first-8 reference, i.e. without
+    exact-maximum fallback when pass 1 takes the provisional first-logit reference, i.e. without
     argmax outputs) and a very high one (nearly uniform rows).  B = 4 runs the kept-term
     instance, B = 48 (816 workgroups) the other."""
     assert (_grid(B, 3, 50000) > _keep_limit()) == (B == 48)
