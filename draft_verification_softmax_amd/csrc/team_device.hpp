@@ -150,6 +150,10 @@ __device__ inline float block_sumf(float x, TeamRed &red) {
     return t;
 }
 
+// A wave's pass-1 lane sums against its provisional reference stay below this, else the wave
+// takes its exact maximum.
+constexpr float kRefSumMax = 0x1p64f;
+
 // ---- one member's chunk, kept as loaded ----------------------------------------------
 // Lane l of wave w of member j holds logits base + g * 512 + l * 8 + (0..7), g < kTeamE / 8,
 // base = j * kTeamChunk + w * kTeamSeg: bfloat16 as packed pairs, binary32 as is.
@@ -266,15 +270,17 @@ struct LaneRow {
     // (M, s) of this lane's logits in base 2 (s = sum_i 2^{x_i c - M}) without a pass for
     // the maximum.  The reference M is the same for the whole wave, c times the wave's first
     // logit, so the wave's sums add up without rescaling; as that logit is one of the wave's,
-    // the wave's largest term is at least 1 and none that matters underflows.  Should a logit
-    // lie so far above it that some lane's sum leaves range (or the first logit be -inf or
-    // NaN), the wave takes its exact maximum instead.  Every lane of the wave must call it.
+    // the wave's largest term is at least 1 and none that matters underflows.  Should some
+    // lane's sum reach 2^64 (or the first logit be -inf or NaN), the wave takes its exact
+    // maximum instead.  The bound also keeps the exponent x c - M of every term that counts
+    // below 64, where the fma's rounding moves a term by at most 2^-19 ln 2 relative.  Every
+    // lane of the wave must call it.
     __device__ __forceinline__ void lane_ms(float c, float &M, float &s) {
         refresh8(0);
         const float mw = wave_first();
         M = (mw == neg_inf()) ? neg_inf() : mw * c;
         s = (mw == neg_inf()) ? 0.f : exp_sum(c, M);
-        if (__ballot(mw == neg_inf() || !(s < 0x1p100f))) {   // wave-uniform
+        if (__ballot(mw == neg_inf() || !(s < kRefSumMax))) {   // wave-uniform
             const float m = wave_max(max());
             M = (m == neg_inf()) ? neg_inf() : m * c;
             s = (m == neg_inf()) ? 0.f : exp_sum(c, M);
@@ -309,7 +315,7 @@ struct LaneRow {
         const float mw = wave_first();
         M = (mw == neg_inf()) ? neg_inf() : mw * c;
         s = exp_keep(c, M, e);
-        if (__ballot(mw == neg_inf() || !(s < 0x1p100f))) {   // wave-uniform
+        if (__ballot(mw == neg_inf() || !(s < kRefSumMax))) {   // wave-uniform
             load<FULL>(row, base, V);
             const float m = wave_max(max());
             M = (m == neg_inf()) ? neg_inf() : m * c;
