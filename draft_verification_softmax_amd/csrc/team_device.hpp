@@ -87,6 +87,20 @@ __device__ __forceinline__ T load_uniform(const T *p) {
     return *(const __attribute__((address_space(4))) T *)(uintptr_t)p;
 }
 
+// One logit at a workgroup-uniform index i of a row by a scalar load of the 4-byte word that
+// holds it (rows are 16-byte aligned with a pitch of a multiple of 16 bytes, so that word
+// lies inside the row): the value lands in a scalar register, so no vector register holds
+// it while the passes run.
+template <int DT>
+__device__ __forceinline__ float load1_uniform(const void *row, int i) {
+    if constexpr (DT == kDtBF16) {
+        const uint32_t w = load_uniform(static_cast<const uint32_t *>(row) + (i >> 1));
+        return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+    } else {
+        return __uint_as_float(load_uniform(static_cast<const uint32_t *>(row) + i));
+    }
+}
+
 // ---- row chunk loads -----------------------------------------------------------------
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 

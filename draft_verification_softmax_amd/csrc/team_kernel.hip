@@ -156,14 +156,14 @@ __device__ __forceinline__ void finish_row(const TeamArgs &a, int64_t row, int j
     }
 }
 
-// The token's two logits, fetched by every lane at a clamped index (only the member whose
+// The token's two logits, read by scalar loads at a clamped index (only the member whose
 // chunk holds the token uses them; thread 0 of that member is the owner).
 template <int DTT, int DTD>
 __device__ __forceinline__ void token_logits(const void *trow, const void *drow, int x, int V, int j, float &zx_t,
                                              float &zx_d, bool &owner) {
     const int xs = x < 0 ? 0 : (x >= V ? V - 1 : x);
-    zx_t = load1<DTT>(trow, xs);
-    zx_d = load1<DTD>(drow, xs);
+    zx_t = load1_uniform<DTT>(trow, xs);
+    zx_d = load1_uniform<DTD>(drow, xs);
     owner = threadIdx.x == 0 && x >= 0 && x < V && x / kTeamChunk == j;
 }
 
