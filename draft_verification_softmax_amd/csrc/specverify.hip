@@ -269,51 +269,57 @@ __device__ void sort_keys(uint64_t *keys, int np2) {
     }
 }
 
-// The kth smallest (0-based) of keys[0..n) (distinct), by radix selection from the top
-// 4-bit digit down.  Each pass counts the keys that agree with the digits chosen so far, per
-// value of the next digit: one ballot per value in every wave, each wave's 16 counts to its
-// own LDS row (wcnt[wave][16]); then wave 0 sums the rows per digit value (lane d takes value
-// d), scans them and keeps the digit whose count holds rank kth.  Once a single key agrees,
-// it is the answer.  Every thread of the block calls it; wcnt, s_prefix, s_rank, s_one are LDS.
-__device__ uint64_t select_kth(const uint64_t *keys, int n, int kth, int (*wcnt)[16], uint64_t *s_prefix,
-                               int *s_rank, int *s_one) {
+// The kth smallest (0-based) of keys[0..n) (distinct keys) by radix selection, 8-bit digits
+// from the top: per digit a histogram of the digit values of the keys that agree with the
+// digits chosen so far (LDS atomic adds into 256 bins), then one wave scans it, four bins a
+// lane, for the value whose running count passes the rank.  A digit value held by a single
+// candidate ends the search: that key is the one.  Every thread of the block calls it, and
+// every thread gets the result.
+__device__ uint64_t select_kth(const uint64_t *keys, int n, int kth, int *hist, uint64_t *s_prefix, int *s_rank,
+                               int *s_one) {
     const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-    constexpr int kWavesPerBlock = kReduceThreads / kWave;
     uint64_t prefix = 0;
     int rank = kth;
-    for (int shift = 60; shift >= 0; shift -= 4) {
-        const uint64_t known = shift == 60 ? 0ull : ~0ull << (shift + 4);   // digits chosen so far
-        int c = 0;   // lane d < 16: this wave's count of digit value d
-        for (int base = 0; base < n; base += kReduceThreads) {   // the same trip count in every thread
-            const int i = base + (int)threadIdx.x;
-            const uint64_t key = i < n ? keys[i] : 0ull;
-            const int d = (i < n && (key & known) == prefix) ? (int)((key >> shift) & 15u) : -1;
-#pragma unroll
-            for (int b = 0; b < 16; ++b) {
-                const int m = __popcll(__ballot(d == b));
-                if (lane == b) c += m;
-            }
+    for (int shift = 56; shift >= 0; shift -= 8) {
+        const uint64_t known = shift == 56 ? 0ull : ~0ull << (shift + 8);   // digits chosen so far
+        if (threadIdx.x < 256) hist[threadIdx.x] = 0;
+        __syncthreads();
+        for (int i = threadIdx.x; i < n; i += kReduceThreads) {
+            const uint64_t key = keys[i];
+            if ((key & known) == prefix) atomicAdd(&hist[(int)((key >> shift) & 255u)], 1);
         }
-        if (lane < 16) wcnt[wv][lane] = c;
         __syncthreads();
         if (wv == 0) {
-            int h = 0;
-            if (lane < 16)
-                for (int w = 0; w < kWavesPerBlock; ++w) h += wcnt[w][lane];
-            // inclusive scan over the 16 digit values
-            int incl = h;
+            const int h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+            const int local = h0 + h1 + h2 + h3;
+            int incl = local;
 #pragma unroll
-            for (int dd = 1; dd < 16; dd <<= 1) {
-                const int y = __shfl_up(incl, dd, kWave);
-                if (lane >= dd) incl += y;
+            for (int d = 1; d < kWave; d <<= 1) {
+                const int y = __shfl_up(incl, d, kWave);
+                if (lane >= d) incl += y;
             }
-            // the first value whose running count passes rank
-            const uint64_t hit = __ballot(lane < 16 && incl > rank);
-            const int b = hit ? __builtin_ctzll(hit) : 15;
-            if (lane == b) {
-                *s_prefix = prefix | ((uint64_t)b << shift);
-                *s_rank = rank - (incl - h);
-                *s_one = h == 1 ? 1 : 0;
+            // the first lane whose running count passes rank, then the bin inside it
+            const uint64_t hit = __ballot(incl > rank);
+            const int l = hit ? __builtin_ctzll(hit) : kWave - 1;
+            if (lane == l) {
+                int before = incl - local, b = 3, hb = h3;
+                if (before + h0 > rank) {
+                    b = 0;
+                    hb = h0;
+                } else if (before + h0 + h1 > rank) {
+                    b = 1;
+                    hb = h1;
+                    before += h0;
+                } else if (before + h0 + h1 + h2 > rank) {
+                    b = 2;
+                    hb = h2;
+                    before += h0 + h1;
+                } else {
+                    before += h0 + h1 + h2;
+                }
+                *s_prefix = prefix | ((uint64_t)(4 * l + b) << shift);
+                *s_rank = rank - before;
+                *s_one = hb == 1 ? 1 : 0;
             }
         }
         __syncthreads();
@@ -329,7 +335,7 @@ __device__ uint64_t select_kth(const uint64_t *keys, int n, int kth, int (*wcnt)
             break;
         }
     }
-    __syncthreads();   // s_prefix and wcnt may be reused by the caller
+    __syncthreads();   // s_prefix and hist may be reused by the caller
     return prefix;
 }
 
@@ -371,23 +377,29 @@ __global__ __launch_bounds__(kReduceThreads) void budget_kernel(const float *con
                 const int k = k0 + e;
                 if (k >= L) break;
                 C = (k == 0) ? ck[e] : __fmul_rn(C, ck[e]);
-                // ascending key = descending C (non-negative binary32 bits are monotone), then (r, k)
-                keys[r * K + k] = ((uint64_t)(~__float_as_uint(C)) << 32) | (uint32_t)(r * K + k);
+                // ascending key = descending C (non-negative binary32 bits are monotone), then (r, k);
+                // stored position-major (k * B + r: the requests' threads write consecutive words),
+                // since nothing below depends on where a key sits
+                keys[k * B + r] = ((uint64_t)(~__float_as_uint(C)) << 32) | (uint32_t)(r * K + k);
             }
         }
         local_total += L;
     }
-    atomicAdd(&s_total, local_total);
+    // one LDS atomic per wave that holds requests, not one per thread on the same word
+    if (threadIdx.x < ((B + kWave - 1) / kWave) * kWave) {
+        for (int d = kWave / 2; d >= 1; d >>= 1) local_total += __shfl_xor(local_total, d, kWave);
+        if ((threadIdx.x & (kWave - 1)) == 0) atomicAdd(&s_total, local_total);
+    }
     __syncthreads();
     __shared__ double dscan[kReduceThreads / kWave], s_ratio[kReduceThreads / kWave], s_E[kReduceThreads / kWave];
     __shared__ int s_n[kReduceThreads / kWave];
-    __shared__ int wcnt[kReduceThreads / kWave][16], s_rank, s_one;
+    __shared__ int hist[256], s_rank, s_one;
     __shared__ uint64_t s_prefix;
     int keep;
     uint64_t thr = 0;   // the keep-th smallest key: the selection is every key <= thr
     if (!cost) {
         keep = min(N, s_total);
-        if (keep > 0) thr = select_kth(keys, n, keep - 1, wcnt, &s_prefix, &s_rank, &s_one);
+        if (keep > 0) thr = select_kth(keys, n, keep - 1, hist, &s_prefix, &s_rank, &s_one);
     } else {
         sort_keys(keys, np2);   // the D-cut choice sums the candidates in order
         keep = dcut_choose(keys, s_total, B, cost, n_cost, dscan, s_ratio, s_n, s_E, n_chosen, utility);
