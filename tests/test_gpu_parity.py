@@ -241,6 +241,23 @@ def test_budget_matches_oracle(sv):
         assert np.array_equal(rl.cpu().numpy()[: len(orl)], orl), trial
 
 
+@pytest.mark.parametrize("B,K,value,N", [(64, 16, 1.0, 300), (64, 128, 1.0, 4097), (128, 64, 0.5, 1000),
+                                         (128, 64, 0.5, 8191)])
+def test_budget_all_equal_confidences(sv, B, K, value, N):
+    """Equal confidences: every request's cumulative products are the same sequence, so keys
+    tie in C across requests (all of them at C = 1) and the allocation is decided by the
+    (r, k) order alone; the selection has to run through the keys' low digits.  Up to the
+    8192-candidate maximum."""
+    c = np.full((B, K), value, np.float32)
+    _say(f"budget equal conf B={B} K={K} c={value} N={N}")
+    lens, off, rl = sv.sv_alloc_verify_budget(torch.as_tensor(c, device=DEV), N)
+    torch.cuda.synchronize()
+    ol, oo, orl = svref.alloc_verify_budget(c, N)
+    assert np.array_equal(lens.cpu().numpy(), ol)
+    assert np.array_equal(off.cpu().numpy(), oo)
+    assert np.array_equal(rl.cpu().numpy()[: len(orl)], orl)
+
+
 def test_budget_then_ragged_verify(sv):
     v, conf, N = workloads.make_budget_inputs(device=DEV)
     lens, off, _ = sv.sv_alloc_verify_budget(conf, N)
