@@ -357,6 +357,10 @@ def _dcut_ratios(conf, cost, draft_len=None):
 def test_dcut_matches_oracle(sv):
     rng = np.random.default_rng(21)
     cases = [(64, 16, 40.0 + 0.05 * np.arange(1025)), (64, 16, 1.0 + 0.002 * np.arange(1025) ** 1.3)]
+    # candidate counts at and between powers of two: the sort pads to one (one key per thread
+    # up to 1024 candidates, exchanges in LDS beyond)
+    for B, K in [(16, 16), (16, 17), (20, 20), (30, 30), (32, 32), (40, 40)]:
+        cases.append((B, K, 1.0 + 0.01 * np.arange(B * K + 1)))
     for trial in range(30):
         B, K = int(rng.integers(1, 40)), int(rng.integers(1, 40))
         if B * K > 8192:
