@@ -11,8 +11,9 @@
 // min(p, q) and of the residual mass from registers and publishes them.  The member whose
 // chunk holds the drafted token runs the accept test and publishes it with the row
 // normalisers.  The wait for partials is bounded:
-// a member that gives up publishes a hand-over marker instead of its share.  The kernel
-// has no other waits and no atomic read-modify-writes, so every schedule terminates.
+// a member that gives up publishes a hand-over marker instead of its share.  Members have
+// no other waits and no atomic read-modify-writes (the finalize's arrival counts are the
+// kernel's only ones), so every schedule terminates.
 //
 // Each request also has a bonus slot: its members read the target row at the request's
 // draft length L_r (the row the bonus token is drawn from when every draft is accepted)
