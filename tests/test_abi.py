@@ -57,6 +57,8 @@ def test_host_validation_rejects_without_launch(svlib):
     args17 = lambda prm, t=nul: (C.byref(prm), t, nul, nul, nul, nul, nul, nul, nul, nul, nul, nul, nul, nul, nul, 0, nul)
     # negative sizes
     assert svlib.sv_verify_batch(*args17(Params(-1, 3, 100, 0, 0, 1.0, 0, 0, 100, 100))) == EINVAL
+    # more draft positions than SV_K_MAX
+    assert svlib.sv_verify_batch(*args17(Params(1, 4097, 100, 0, 0, 1.0, 0, 0, 100, 100))) == EINVAL
     # V too large
     assert svlib.sv_verify_batch(*args17(Params(1, 3, (1 << 20) + 1, 0, 0, 1.0, 0, 0, (1 << 20) + 8, (1 << 20) + 8))) == EUNSUP
     # negative / NaN temperature

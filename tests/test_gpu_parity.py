@@ -683,6 +683,34 @@ def test_largest_vocabulary(sv):
         _run_pair(sv, _custom(t, d, toks, T, "V=2^20"), T)
 
 
+@pytest.mark.parametrize("K", [300, 4096])
+@pytest.mark.parametrize("T,want_amax", [(0.9, False), (0.9, True), (0.0, True)])
+def test_longest_drafts(sv, K, T, want_amax):
+    """Draft blocks of 300 and SV_K_MAX = 4096 positions with long accepted prefixes: the
+    finalize stages its rows in several batches and, past 255 positions, computes the draw's
+    uniform for the scanned tau on demand.  Request 0 has a certain reject at 3/4 of its block
+    (the target masks the drafted token there), request 1 accepts every draft (bonus row K),
+    request 2 follows the target up to position 260 and an independent drafter after it."""
+    g = torch.Generator(device=DEV).manual_seed(K + int(10 * T))
+    B, V = 3, 2000
+    t = (2.0 * torch.randn((B, K + 1, V), generator=g, device=DEV)).to(torch.bfloat16)
+    d = t[:, :K].clone()
+    d[2, 260:] = (2.0 * torch.randn((K - 260, V), generator=g, device=DEV)).to(torch.bfloat16)
+    z = d.float()
+    if T > 0:
+        u = torch.rand(z.shape, generator=g, device=DEV).clamp_(min=1e-20)
+        z = z / T - torch.log(-torch.log(u))
+    toks = torch.argmax(z, -1).to(torch.int32)
+    k0 = 3 * K // 4
+    t[0, k0, toks[0, k0]] = float("-inf")
+    w = _custom(t, d, toks, T, f"long drafts K={K}", seed=K)
+    _, o, _ = _run_pair(sv, w, T, want_amax=want_amax)
+    assert o["accept_len"][0] == k0 and o["accept_len"][1] == K and o["accept_len"][2] >= 260
+    dl = np.array([K, K - 37, 290], np.int32)
+    _, o2, _ = _run_pair(sv, w, T, draft_len=dl, want_amax=want_amax)
+    assert o2["accept_len"][0] == k0 and o2["accept_len"][1] == K - 37 and o2["accept_len"][2] >= 260
+
+
 def _grid(B, K, V):
     """Workgroups of a dense verification grid: members of every row and bonus slot, then the
     finalize workgroups."""
