@@ -112,20 +112,45 @@ def compare_verify(gpu, ora, target_np, draft_np, dtype, T, check=None, L=None, 
 # binary32 normal range (2^-126) the kernels' exponential flushes q to zero, so an element is
 # also allowed an absolute error of GRAD_FLOOR = 2^-126 times a bound (2^6) on the row scale
 # |s| = |grad_loss| w / (|I| D T) of the test cases.
+# beta also depends on which side of the tie a token falls: the kernels decide q < p on
+# binary32 log-values (errors of a few 1e-6 in ln), so a token with |ln p - ln q| below
+# BETA_BAND (about twice that) may be counted in beta or not.  Given ln q, each row's beta is
+# allowed to move by the q-mass of those tokens: element v by |s q_v| times that mass, with
+# |s q_v| = |g_v| / |[q_v < p_v] - beta|.
 GRAD_RTOL = 1e-5
 GRAD_ROW_ATOL = 2e-6
 GRAD_FLOOR = 2.0 ** -120
 TIE_BAND = 1e-4
+BETA_BAND = 1e-5
 
 
-def compare_grad(gpu, ora, log_ratio, rtol=GRAD_RTOL, bf16=False):
-    """gpu, ora, log_ratio: [..., V] arrays.  Returns a report; raises AssertionError."""
+def drafter_log_q(d, T):
+    """ln q (binary64) of drafter logits d (a torch tensor [..., V]) at temperature T, for the
+    tie band of beta in compare_grad."""
+    from scipy.special import log_softmax
+    return log_softmax(d.detach().double().cpu().numpy() / T, axis=-1)
+
+
+def compare_grad(gpu, ora, log_ratio, rtol=GRAD_RTOL, bf16=False, log_q=None):
+    """gpu, ora, log_ratio (ln p - ln q), log_q (ln q, optional): [..., V] arrays.  Returns a
+    report; raises AssertionError."""
     g = np.asarray(gpu, np.float64)
     o = np.asarray(ora, np.float64)
     ties = np.abs(log_ratio) < TIE_BAND
     assert np.isfinite(g).all(), "non-finite gradient"
     row_max = np.abs(o).max(-1, keepdims=True)
     tol = (rtol + (2.0 ** -8 if bf16 else 0.0)) * np.abs(o) + GRAD_ROW_ATOL * row_max + GRAD_FLOOR
+    band_rows = 0
+    if log_q is not None:
+        q = np.exp(np.asarray(log_q, np.float64))
+        with np.errstate(invalid="ignore"):
+            ind = (log_ratio > 0).astype(np.float64)
+            near = np.abs(log_ratio) < BETA_BAND
+        beta = (q * ind).sum(-1, keepdims=True)
+        band = (q * near).sum(-1, keepdims=True)
+        sq = np.abs(o) / np.maximum(np.abs(ind - beta), 1e-300)
+        tol = tol + sq * band
+        band_rows = int((band > 0).sum())
     bad = (np.abs(g - o) > tol) & ~ties
     if bad.any():
         i = np.argwhere(bad)[0]
@@ -134,4 +159,4 @@ def compare_grad(gpu, ora, log_ratio, rtol=GRAD_RTOL, bf16=False):
     normal = ~ties & (np.abs(o) >= 2.0 ** -100)   # relative error where binary32 carries it
     rel = np.abs(g - o)[normal] / np.abs(o)[normal]
     return {"elements": int(o.size), "ties": int(ties.sum()), "below_normal": int((~ties & ~normal).sum()),
-            "max_rel": float(rel.max()) if rel.size else 0.0}
+            "beta_band_rows": band_rows, "max_rel": float(rel.max()) if rel.size else 0.0}

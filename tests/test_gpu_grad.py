@@ -6,7 +6,7 @@ import torch
 
 import workloads
 from oracle import svref
-from parity import compare_grad
+from parity import compare_grad, drafter_log_q
 
 pytestmark = pytest.mark.gpu
 
@@ -66,7 +66,8 @@ def test_backward_matches_oracle(sv, dt, gdt):
     alpha = torch.as_tensor(oa, dtype=torch.float32, device=DEV)
     g = sv.sv_tv_e2e_backward(t, d, alpha, T, grad_dtype=gdt)
     torch.cuda.synchronize()
-    rep = compare_grad(g.float().cpu().numpy(), og, lr, bf16=gdt == torch.bfloat16)
+    rep = compare_grad(g.float().cpu().numpy(), og, lr, bf16=gdt == torch.bfloat16,
+                       log_q=drafter_log_q(d, T))
     _say(f"report {rep}")
 
 
@@ -81,7 +82,7 @@ def test_backward_after_gpu_forward(sv):
     g = sv.sv_tv_e2e_backward(t, d, alpha, T, grad_dtype=torch.float32)
     torch.cuda.synchronize()
     np.testing.assert_allclose(alpha.cpu().numpy(), oa, rtol=1e-5)
-    rep = compare_grad(g.cpu().numpy(), og, lr, rtol=D * 1e-5)
+    rep = compare_grad(g.cpu().numpy(), og, lr, rtol=D * 1e-5, log_q=drafter_log_q(d, T))
     _say(f"report {rep}")
     # rows of the gradient sum to zero (a constant added to a drafter row changes nothing)
     gs = g.double().sum(-1).abs().cpu().numpy()
@@ -100,7 +101,38 @@ def test_backward_edge_vocabularies(sv, V):
         alpha = torch.as_tensor(oa, dtype=torch.float32, device=DEV)
         g = sv.sv_tv_e2e_backward(t, d, alpha, 1.3, grad_dtype=torch.float32)
         torch.cuda.synchronize()
-        compare_grad(g.cpu().numpy(), og, lr)
+        compare_grad(g.cpu().numpy(), og, lr, log_q=drafter_log_q(d, 1.3))
+
+
+@pytest.mark.parametrize("D", [16, 512, 4096])
+def test_e2e_deep_blocks(sv, D):
+    """Depth 16 (a DFly block), 512 and SV_K_MAX = 4096, with drafter rows close to the target
+    (alpha about 0.97..0.9998), so the running products stay in binary32's normal range to the
+    end of the block (about 1e-20 at depth 4096).  Forward: alpha within 1e-5, and L_e2e within
+    the bound that a relative error of 1e-5 per alpha carries through the products (term m
+    has m + 1 factors).  Backward, from the oracle's alpha (its plain weights cost O(D^3), so
+    up to depth 512): the gradient of every row."""
+    I, V, T = 2, 2000, 1.0
+    g = torch.Generator().manual_seed(D)
+    t = 3.0 * torch.randn((I, D, V), generator=g)
+    d = t + 0.03 * torch.randn((I, D, V), generator=g)
+    t, d = _padded(t), _padded(d)
+    _say(f"e2e deep I={I} D={D} V={V}")
+    ol, oa = svref.tv_e2e_loss(workloads.to_oracle(t), workloads.to_oracle(d), T, "f32")
+    loss, alpha = sv.sv_tv_e2e_loss(t, d, T)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(alpha.cpu().numpy(), oa, rtol=1e-5)
+    P = np.cumprod(oa, axis=1)
+    bound = (P * (np.arange(D) + 1) * 1e-5).sum() / (I * D) + 2.0 ** -24
+    assert abs(loss.item() - ol) <= bound, (loss.item(), ol, bound)
+    if D > 512:
+        return
+    og, _, _, lr = _oracle(t, d, T)
+    gg = sv.sv_tv_e2e_backward(t, d, torch.as_tensor(oa, dtype=torch.float32, device=DEV), T,
+                               grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rep = compare_grad(gg.cpu().numpy(), og, lr, log_q=drafter_log_q(d, T))
+    _say(f"report {rep}")
 
 
 def test_backward_grad_loss_and_padded_rows(sv):
@@ -114,7 +146,7 @@ def test_backward_grad_loss_and_padded_rows(sv):
     _say("backward grad_loss and padded rows")
     g = sv.sv_tv_e2e_backward(t, d, alpha, T, grad_loss=gl, grad=buf[:, :, :V])
     torch.cuda.synchronize()
-    compare_grad(g.cpu().numpy(), og, lr)
+    compare_grad(g.cpu().numpy(), og, lr, log_q=drafter_log_q(d, T))
     assert (buf[:, :, V:] == 7.0).all()
 
 
@@ -132,7 +164,7 @@ def test_backward_workspace_reuse(sv):
         v = workloads.make_verify_inputs("tiny", device="cpu", T=1.0)
         sv.sv_verify_batch(v.target.to(DEV), v.draft.to(DEV), v.draft_tokens.to(DEV), 1.0, workspace=buf)
         torch.cuda.synchronize()
-        compare_grad(g.cpu().numpy(), og, lr, rtol=D * 1e-5)
+        compare_grad(g.cpu().numpy(), og, lr, rtol=D * 1e-5, log_q=drafter_log_q(d, 1.0))
     assert sv.sv_device_error(buf) == 0
 
 
@@ -147,7 +179,7 @@ def test_backward_low_temperature(sv):
     g = sv.sv_tv_e2e_backward(t, d, alpha, T, grad_dtype=torch.float32)
     torch.cuda.synchronize()
     np.testing.assert_allclose(alpha.cpu().numpy(), oa, rtol=1e-5)
-    rep = compare_grad(g.cpu().numpy(), og, lr, rtol=D * 1e-5)
+    rep = compare_grad(g.cpu().numpy(), og, lr, rtol=D * 1e-5, log_q=drafter_log_q(d, T))
     _say(f"report {rep}")
 
 
@@ -169,7 +201,8 @@ def test_backward_full_size_sampled(sv):
     for i in idx:
         og, oa, _, lr = _oracle(t[i:i + 1], d[i:i + 1], T)
         np.testing.assert_allclose(alpha[i].cpu().numpy(), oa[0], rtol=1e-5)
-        rep = compare_grad(g[i:i + 1].float().cpu().numpy(), og / I, lr, rtol=D * 1e-5, bf16=True)
+        rep = compare_grad(g[i:i + 1].float().cpu().numpy(), og / I, lr, rtol=D * 1e-5, bf16=True,
+                           log_q=drafter_log_q(d[i:i + 1], T))
         worst = max(worst, rep["max_rel"])
     _say(f"64 sequences compared, largest relative error {worst:.3g}")
     assert torch.isfinite(g).all()

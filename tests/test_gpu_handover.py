@@ -8,7 +8,7 @@ import torch
 
 import workloads
 from oracle import svref
-from parity import compare_grad, compare_verify
+from parity import compare_grad, compare_verify, drafter_log_q
 
 pytestmark = pytest.mark.gpu
 
@@ -86,4 +86,4 @@ def test_e2e_forward_and_backward_with_every_share_handed_over(sv):
     torch.cuda.synchronize()
     np.testing.assert_allclose(alpha.cpu().numpy(), oa, rtol=1e-5)
     assert abs(loss.item() - oloss) <= 1e-5 * abs(oloss)
-    _say(f"report {compare_grad(g.cpu().numpy(), og, lr, rtol=D * 1e-5)}")
+    _say(f"report {compare_grad(g.cpu().numpy(), og, lr, rtol=D * 1e-5, log_q=drafter_log_q(d, T))}")
