@@ -746,8 +746,9 @@ int sv_verify_selected(const sv_params *p, const void *target, const void *draft
 
 int sv_accept_len(const uint8_t *accept, const int32_t *draft_len, int32_t B, int32_t K_max,
                   int32_t *accept_len, void *stream) {
-    if (B < 0 || K_max < 0 || !accept_len || (K_max > 0 && !accept)) return SV_EINVAL;
-    if (B == 0) return SV_OK;
+    if (B < 0 || K_max < 0) return SV_EINVAL;
+    if (B == 0) return SV_OK;   // an empty batch: its (empty) arrays may be NULL
+    if (!accept_len || (K_max > 0 && !accept)) return SV_EINVAL;
     hipLaunchKernelGGL(accept_len_kernel, dim3((B + 255) / 256), dim3(256), 0, (hipStream_t)stream, accept,
                        draft_len, B, K_max, accept_len, (uint32_t *)nullptr);
     return launch_status();
@@ -863,7 +864,7 @@ int sv_sample_drafts(const sv_params *p, const void *draft, int32_t *tokens, flo
 int sv_alloc_verify_budget(const float *conf, const int32_t *draft_len, int32_t B, int32_t K_max,
                            int32_t budget_N, int32_t *lens, int32_t *row_off, int32_t *row_list,
                            void *stream) {
-    if (B < 0 || K_max < 0 || budget_N < 0 || !lens || !row_off) return SV_EINVAL;
+    if (B < 0 || K_max < 0 || budget_N < 0 || !row_off || (B > 0 && !lens)) return SV_EINVAL;
     if ((int64_t)B * K_max > SV_BUDGET_MAX || B > SV_BUDGET_MAX) return SV_EUNSUPPORTED;
     if (B > 0 && K_max > 0 && !conf) return SV_EINVAL;
     hipLaunchKernelGGL(budget_kernel, dim3(1), dim3(kReduceThreads), 0, (hipStream_t)stream, conf, draft_len, B,
@@ -875,7 +876,8 @@ int sv_alloc_verify_budget(const float *conf, const int32_t *draft_len, int32_t 
 int sv_dcut_verify_budget(const float *conf, const int32_t *draft_len, int32_t B, int32_t K_max,
                           const float *cost, int32_t n_cost, int32_t *n_chosen, double *utility, int32_t *lens,
                           int32_t *row_off, int32_t *row_list, void *stream) {
-    if (B < 0 || K_max < 0 || n_cost < 1 || !cost || !n_chosen || !utility || !lens || !row_off) return SV_EINVAL;
+    if (B < 0 || K_max < 0 || n_cost < 1 || !cost || !n_chosen || !utility || !row_off || (B > 0 && !lens))
+        return SV_EINVAL;
     if ((int64_t)B * K_max > SV_BUDGET_MAX || B > SV_BUDGET_MAX || n_cost > SV_BUDGET_MAX + 1) return SV_EUNSUPPORTED;
     if (B > 0 && K_max > 0 && !conf) return SV_EINVAL;
     hipLaunchKernelGGL(budget_kernel, dim3(1), dim3(kReduceThreads), 0, (hipStream_t)stream, conf, draft_len, B,

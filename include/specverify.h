@@ -184,7 +184,8 @@ int sv_verify_selected(const sv_params *params, const void *target, const void *
                        int32_t *n_out, void *workspace, size_t workspace_bytes, void *stream);
 
 /* First-reject prefix length per request [TV]: accept [B][K_max] uint8, draft_len [B] or
- * NULL; accept_len[r] = first k < L_r with accept == 0, else L_r. */
+ * NULL; accept_len[r] = first k < L_r with accept == 0, else L_r.  B == 0 is a no-op (its
+ * arrays may be NULL). */
 int sv_accept_len(const uint8_t *accept, const int32_t *draft_len, int32_t B, int32_t K_max,
                   int32_t *accept_len, void *stream);
 
@@ -209,7 +210,8 @@ int sv_residual_sample(const sv_params *params, const void *target, const void *
  * params->B = |I|, params->K_max = D, params->temperature > 0 (1 for raw logits).
  * target, draft [|I|][D][ld] (no bonus row: target row (i,k) at (i*D + k) * ld_t).
  * alpha [|I|][D] float or NULL; loss: one float (device).  Deterministic summation order.
- * workspace: sv_workspace_bytes(|I|, D, V) bytes. */
+ * workspace: sv_workspace_bytes(|I|, D, V) bytes.  |I| and D must be positive (the mean over
+ * an empty set is undefined): SV_EINVAL otherwise. */
 int sv_tv_e2e_loss(const sv_params *params, const void *target, const void *draft,
                    float *alpha, float *loss, void *workspace, size_t workspace_bytes,
                    void *stream);
@@ -250,7 +252,8 @@ int sv_sample_drafts(const sv_params *params, const void *draft, int32_t *tokens
  * (C desc, r asc, k asc) are kept.  conf [B][K_max] float in [0, 1]; draft_len [B] or
  * NULL.  Outputs: lens [B] (selected prefix length per request; pass it as draft_len to
  * sv_verify_batch), row_off [B+1] (exclusive scan of lens), row_list [min(N, sum L)] or
- * NULL (r*K_max + k of each selected row in (r, k) order).  B*K_max <= SV_BUDGET_MAX. */
+ * NULL (r*K_max + k of each selected row in (r, k) order).  B*K_max <= SV_BUDGET_MAX.
+ * B == 0 writes row_off[0] = 0 (lens may then be NULL). */
 int sv_alloc_verify_budget(const float *conf, const int32_t *draft_len, int32_t B,
                            int32_t K_max, int32_t budget_N, int32_t *lens, int32_t *row_off,
                            int32_t *row_list, void *stream);

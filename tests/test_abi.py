@@ -86,6 +86,11 @@ def test_host_validation_rejects_without_launch(svlib):
     assert svlib.sv_uniforms(0, nul, -1, nul, nul) == EINVAL
     # B = 0 is a no-op
     assert svlib.sv_verify_batch(*args17(Params(0, 3, 100, 0, 0, 1.0, 0, 0, 100, 100))) == 0
+    # an empty batch's arrays may be NULL (an empty tensor's address is 0)
+    assert svlib.sv_accept_len(nul, nul, 0, 3, nul, nul) == 0
+    assert svlib.sv_accept_len(nul, nul, 2, 3, nul, nul) == EINVAL
+    # L_e2e over an empty set is undefined
+    assert svlib.sv_tv_e2e_loss(C.byref(Params(0, 3, 96, 1, 1, 1.0, 0, 0, 96, 96)), fake, fake, nul, fake, fake, 1 << 30, nul) == EINVAL
 
 
 def test_verify_selected_host_validation(svlib):

@@ -711,6 +711,49 @@ def test_longest_drafts(sv, K, T, want_amax):
     assert o2["accept_len"][0] == k0 and o2["accept_len"][1] == K - 37 and o2["accept_len"][2] >= 260
 
 
+def test_empty_batches(sv):
+    """Empty batches through every entry point: no requests (B = 0), no draft positions
+    (K = 0) for the budget and the sampler, no counters.  Verification returns empty outputs;
+    the budget and the D-cut choice equal the oracle's (row_off = [0] for no requests); an
+    L_e2e over an empty set is refused (its mean is undefined)."""
+    V = 1000
+    t = torch.zeros((0, 4, V), dtype=torch.bfloat16, device=DEV)
+    d = torch.zeros((0, 3, V), dtype=torch.bfloat16, device=DEV)
+    x = torch.zeros((0, 3), dtype=torch.int32, device=DEV)
+    ws = sv.Workspace(DEV)
+    for T in (0.9, 0.0):
+        _say(f"empty verify T={T}")
+        outs = [sv.sv_verify_batch(t, d, x, T, want_amax=True, workspace=ws),
+                sv.sv_verify_batch_noalloc(t, d, x, T, want_amax=True),
+                sv.sv_verify_selected(t, d, x, T, torch.zeros((0,), dtype=torch.int32, device=DEV), None, 0,
+                                      want_amax=True, workspace=ws)]
+        for o in outs:
+            assert o["alpha"].shape == (0, 3) and o["out_tokens"].shape == (0, 4) and o["n_out"].shape == (0,)
+    torch.cuda.synchronize()
+    assert sv.sv_device_error(ws.get(0, 3, V)) == 0
+    _say("empty accept_len, residual_sample, sample_drafts, uniforms")
+    assert sv.sv_accept_len(torch.zeros((0, 3), dtype=torch.uint8, device=DEV)).shape == (0,)
+    assert sv.sv_residual_sample(t, d, torch.zeros((0,), dtype=torch.int32, device=DEV), 0.9).shape == (0,)
+    for dd in (d, torch.zeros((2, 0, V), dtype=torch.bfloat16, device=DEV)):
+        tok, conf = sv.sv_sample_drafts(dd, 0.9)
+        assert tok.shape == dd.shape[:2] and conf.shape == dd.shape[:2]
+    assert sv.sv_uniforms(1, torch.zeros((0, 4), dtype=torch.int64, device=DEV)).shape == (0,)
+    cost = (40.0 + 0.05 * np.arange(9)).astype(np.float32)
+    for shape in [(0, 4), (3, 0)]:
+        _say(f"empty budget {shape}")
+        conf = np.zeros(shape, np.float32)
+        lens, off, _ = sv.sv_alloc_verify_budget(torch.as_tensor(conf, device=DEV), 10)
+        ol, oo, _ = svref.alloc_verify_budget(conf, 10)
+        assert np.array_equal(lens.cpu().numpy(), ol) and np.array_equal(off.cpu().numpy(), oo)
+        n, u, lens, off, _ = sv.sv_dcut_verify_budget(torch.as_tensor(conf, device=DEV), torch.as_tensor(cost, device=DEV))
+        on, ou, ol, oo, _ = svref.dcut_budget(conf, cost)
+        assert int(n.item()) == on and float(u.item()) == ou
+        assert np.array_equal(lens.cpu().numpy(), ol) and np.array_equal(off.cpu().numpy(), oo)
+    with pytest.raises(sv.SVError):
+        sv.sv_tv_e2e_loss(torch.zeros((0, 3, V), dtype=torch.bfloat16, device=DEV),
+                          torch.zeros((0, 3, V), dtype=torch.bfloat16, device=DEV), 1.0)
+
+
 def _grid(B, K, V):
     """Workgroups of a dense verification grid: members of every row and bonus slot, then the
     finalize workgroups."""
