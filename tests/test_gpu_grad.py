@@ -135,6 +135,33 @@ def test_e2e_deep_blocks(sv, D):
     _say(f"report {rep}")
 
 
+def test_e2e_rows_beyond_2gib(sv):
+    """L_e2e forward and backward on 1100 x 2 rows of a 2 MiB + 16 byte stride (bfloat16
+    logits and gradient, 4.6 GB per tensor): rows past the first 1024 lie beyond 2^31 bytes,
+    in the logits and in the gradient."""
+    I, D, V, T = 1100, 2, 1000, 1.0
+    ld = (1 << 20) + 8
+    g = torch.Generator().manual_seed(ld)
+    t0 = (3.0 * torch.randn((I, D, V), generator=g)).to(torch.bfloat16)
+    d0 = (t0.float() + torch.randn((I, D, V), generator=g)).to(torch.bfloat16)
+
+    def big(x):
+        buf = torch.empty((I, D, ld), dtype=x.dtype, device=DEV)
+        buf[..., :V] = x.to(DEV)
+        return buf[..., :V]
+    t, d = big(t0), big(d0)
+    _say(f"e2e rows beyond 2 GiB I={I} D={D} V={V} ld={ld}")
+    og, oa, oloss, lr = _oracle(t, d, T)
+    loss, alpha = sv.sv_tv_e2e_loss(t, d, T)
+    grad = torch.empty((I, D, ld), dtype=torch.bfloat16, device=DEV)[..., :V]
+    gg = sv.sv_tv_e2e_backward(t, d, alpha, T, grad=grad)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(alpha.cpu().numpy(), oa, rtol=1e-5)
+    assert abs(loss.item() - oloss) <= 1e-5 * abs(oloss)
+    rep = compare_grad(gg.float().cpu().numpy(), og, lr, rtol=D * 1e-5, bf16=True, log_q=drafter_log_q(d, T))
+    _say(f"report {rep}")
+
+
 def test_backward_grad_loss_and_padded_rows(sv):
     """A device grad_loss scales the result; rows with a stride above V keep their padding."""
     I, D, V, T = 2, 3, 3000, 1.0

@@ -711,6 +711,44 @@ def test_longest_drafts(sv, K, T, want_amax):
     assert o2["accept_len"][0] == k0 and o2["accept_len"][1] == K - 37 and o2["accept_len"][2] >= 260
 
 
+BIG_LD = (1 << 20) + 8   # a row stride of 2 MiB + 16 bytes (bfloat16): row 1024 starts past 2^31 bytes
+
+
+def _big_stride(x):
+    """x [..., V] copied into rows of stride BIG_LD on the GPU (padding left uninitialised,
+    never read): rows past the first 1024 sit beyond 2^31 bytes from the start."""
+    buf = torch.empty(x.shape[:-1] + (BIG_LD,), dtype=x.dtype, device=DEV)
+    buf[..., :x.shape[-1]] = x.to(DEV)
+    return buf[..., :x.shape[-1]]
+
+
+@pytest.mark.parametrize("T,want_amax", [(0.9, False), (0.9, True), (0.0, True)])
+def test_rows_beyond_2gib(sv, T, want_amax):
+    """Row offsets past 2^31 bytes (3 requests x 700 drafts in rows of a 2 MiB stride, 4.4 GB
+    per tensor): every row address is 64-bit.  Request 1 accepts up to a certain reject at
+    position 600 (row 1301, beyond 2 GiB: its residual draw reads there); request 2 accepts
+    every draft (its bonus row 2102); dense and ragged lengths."""
+    g = torch.Generator().manual_seed(1 << 20)
+    B, K, V = 3, 700, 1000
+    t = (2.0 * torch.randn((B, K + 1, V), generator=g)).to(torch.bfloat16)
+    d = (t[:, :K].float() + 0.5 * torch.randn((B, K, V), generator=g)).to(torch.bfloat16)
+    d[1, :600] = t[1, :600]
+    d[2] = t[2, :K]
+    z = d.float()
+    if T > 0:
+        u = torch.rand(z.shape, generator=g).clamp_(min=1e-20)
+        z = z / T - torch.log(-torch.log(u))
+    toks = torch.argmax(z, -1).to(torch.int32)
+    t[1, 600, toks[1, 600]] = float("-inf")
+    w = workloads.VerifyInputs(_big_stride(t), _big_stride(d), toks.to(DEV), T, 9, "rows beyond 2 GiB")
+    assert w.target.stride(1) == BIG_LD and (B * (K + 1) - 1) * BIG_LD * 2 > (1 << 31)
+    _, o, _ = _run_pair(sv, w, T, want_amax=want_amax)
+    assert o["accept_len"][1] == 600 and o["accept_len"][2] == K
+    dl = np.array([K, 650, K - 1], np.int32)
+    _, o2, _ = _run_pair(sv, w, T, draft_len=dl, want_amax=want_amax)
+    assert o2["accept_len"][1] == 600 and o2["accept_len"][2] == K - 1
+
+
 def test_empty_batches(sv):
     """Empty batches through every entry point: no requests (B = 0), no draft positions
     (K = 0) for the budget and the sampler, no counters.  Verification returns empty outputs;

@@ -117,3 +117,20 @@ def test_sample_full_dfly_batch(sv):
         tok, conf = sv.sv_sample_drafts(d, 0.9, seed=123, step=step, workspace=ws)
         torch.cuda.synchronize()
         _say(f"report {_compare(tok, conf, d, 0.9, 123, step)}")
+
+
+def test_sample_rows_beyond_2gib(sv):
+    """2 x 1100 drafter rows of a 2 MiB + 16 byte stride (4.6 GB): rows past the first 1024
+    lie beyond 2^31 bytes."""
+    B, K, V = 2, 1100, 1000
+    ld = (1 << 20) + 8
+    g = torch.Generator().manual_seed(ld)
+    x = (3.0 * torch.randn((B, K, V), generator=g)).to(torch.bfloat16)
+    buf = torch.empty((B, K, ld), dtype=torch.bfloat16, device=DEV)
+    buf[..., :V] = x.to(DEV)
+    d = buf[..., :V]
+    for T in (0.9, 0.0):
+        _say(f"sample rows beyond 2 GiB T={T}")
+        tok, conf = sv.sv_sample_drafts(d, T, seed=5, step=1)
+        torch.cuda.synchronize()
+        _say(f"report {_compare(tok, conf, d, T, 5, 1)}")
