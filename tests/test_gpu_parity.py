@@ -747,6 +747,16 @@ def test_rows_beyond_2gib(sv, T, want_amax):
     dl = np.array([K, 650, K - 1], np.int32)
     _, o2, _ = _run_pair(sv, w, T, draft_len=dl, want_amax=want_amax)
     assert o2["accept_len"][1] == 600 and o2["accept_len"][2] == K - 1
+    # the stand-alone draw at the oracle's accepted lengths reads the same far rows
+    if not want_amax:
+        tn, dn = workloads.to_oracle(w.target), workloads.to_oracle(w.draft)
+        al = o2["accept_len"].astype(np.int32)
+        tok = sv.sv_residual_sample(w.target, w.draft, torch.as_tensor(al, device=DEV), T, seed=9,
+                                    draft_len=torch.as_tensor(dl, device=DEV)).cpu().numpy()
+        otok = svref.residual_sample(tn, dn, al, T, "bf16", seed=9, draft_len=dl)
+        for r in range(B):
+            assert tok[r] == otok[r] or _token_in_band(tn, dn, T, "bf16", r, int(al[r]), int(dl[r]), int(tok[r]),
+                                                       int(otok[r]), 9, 0), (r, tok[r], otok[r])
 
 
 def test_empty_batches(sv):
