@@ -121,6 +121,10 @@ __device__ __forceinline__ void write_chunk(LaneRow<DTT> &t, LaneRow<DTD> &d, fl
                                             float beta, float scale, void *grow, int base, int V,
                                             const Dot2Scale &ds) {
     float ct = 0.f, cd = 0.f;
+    // the lane index through an opaque copy: the store addresses are formed here, so the
+    // compiler does not keep the row loads' per-lane addresses live through the passes
+    int lane = lane_id();
+    asm volatile("" : "+v"(lane));
     if constexpr (D2) {
         ct = neg_over_gamma(nt.hi, ds);
         cd = neg_over_gamma(nd.hi, ds);
@@ -148,7 +152,7 @@ __device__ __forceinline__ void write_chunk(LaneRow<DTT> &t, LaneRow<DTD> &d, fl
                 gv[e] = scale * exp2_fast(xd) * ((xd < xt ? 1.f : 0.f) - beta);
             }
         }
-        const int v0 = base + g * 64 + lane_id() * 8;
+        const int v0 = base + g * 64 + lane * 8;
         if (FULL || v0 + 8 <= V) {
             if constexpr (DTG == kDtBF16) {
                 u32x4 q;
