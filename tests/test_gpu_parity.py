@@ -648,6 +648,14 @@ def test_no_drafts_only_bonus(sv, T):
     toks = torch.empty((B, 0), dtype=torch.int32, device=DEV)
     _, o, _ = _run_pair(sv, _custom(t, d, toks, T, "K=0"), T)
     assert (o["accept_len"] == 0).all()
+    # the stand-alone draw with no drafts: the bonus token from target row 0
+    tok = sv.sv_residual_sample(t, d, torch.zeros((B,), dtype=torch.int32, device=DEV), T, seed=13).cpu().numpy()
+    tn, dn = workloads.to_oracle(t), workloads.to_oracle(d)
+    otok = svref.residual_sample(tn, dn, np.zeros(B, np.int32), T, "bf16", seed=13)
+    assert np.array_equal(otok, o["out_tokens"][:, 0])
+    for r in range(B):
+        assert tok[r] == otok[r] or (T > 0 and _token_in_band(tn, dn, T, "bf16", r, 0, 0, int(tok[r]), int(otok[r]),
+                                                              13, 0)), (r, tok[r], otok[r])
 
 
 @pytest.mark.parametrize("V", [1, 7, 8, 4095, 4097])
