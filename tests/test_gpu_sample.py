@@ -66,8 +66,10 @@ def _compare(sv_tok, sv_conf, d, T, seed, step):
     return {"rows": B * K, "near_boundary": near}
 
 
-@pytest.mark.parametrize("T", [0.3, 0.9, 1.5])
+@pytest.mark.parametrize("T", [0.02, 0.3, 0.9, 1.5, 25.0])
 def test_sample_matches_oracle(sv, T):
+    """T = 0.02 puts the base-2 normalisers near 700 (kept as hi + lo) and q near one-hot;
+    T = 25 makes q nearly flat."""
     d = _drafts(4, 5, 50000)
     _say(f"sample B=4 K=5 V=50000 T={T}")
     tok, conf = sv.sv_sample_drafts(d, T, seed=17, step=3)
