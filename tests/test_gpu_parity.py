@@ -767,6 +767,36 @@ def test_rows_beyond_2gib(sv, T, want_amax):
                                                        int(otok[r]), 9, 0), (r, tok[r], otok[r])
 
 
+def test_two_streams_at_once(sv):
+    """Verification calls issued together on two streams, each with its own workspace, eight
+    rounds (where the device runs the two grids at once they compete for the CUs; a team
+    member that cannot get a slot is covered by the bounded wait and its hand-over): both
+    match the oracle and neither workspace reports a device error."""
+    va = workloads.make_verify_inputs("dfly", device=DEV, T=0.9, B=24, seed=101)
+    vb = workloads.make_verify_inputs("mtp", device=DEV, T=0.9, B=40, seed=202)
+    wa, wb = sv.Workspace(DEV), sv.Workspace(DEV)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    outs = []
+    for it in range(8):
+        _say(f"two streams, round {it}")
+        with torch.cuda.stream(sa):
+            oa = sv.sv_verify_batch(va.target, va.draft, va.draft_tokens, 0.9, seed=va.seed, step=it, workspace=wa,
+                                    stream=sa)
+        with torch.cuda.stream(sb):
+            ob = sv.sv_verify_batch(vb.target, vb.draft, vb.draft_tokens, 0.9, seed=vb.seed, step=it, workspace=wb,
+                                    stream=sb)
+        outs.append((it, oa, ob))
+    torch.cuda.synchronize()
+    assert sv.sv_device_error(wa.buf) == 0 and sv.sv_device_error(wb.buf) == 0
+    for v, k in ((va, 1), (vb, 2)):
+        tn, dn = workloads.to_oracle(v.target), workloads.to_oracle(v.draft)
+        for it in (0, 7):
+            o = svref.verify_batch(tn, dn, v.draft_tokens.cpu().numpy(), 0.9, "bf16", seed=v.seed, step=it,
+                                   diagnostics=True)
+            compare_verify(_np(outs[it][k]), o, tn, dn, "bf16", 0.9, label=f"two streams {v.name} step {it}")
+
+
 def test_empty_batches(sv):
     """Empty batches through every entry point: no requests (B = 0), no draft positions
     (K = 0) for the budget and the sampler, no counters.  Verification returns empty outputs;
