@@ -840,6 +840,27 @@ def test_empty_batches(sv):
                           torch.zeros((0, 3, V), dtype=torch.bfloat16, device=DEV), 1.0)
 
 
+@pytest.mark.parametrize("T,want_amax", [(0.9, False), (0.9, True), (0.0, True)])
+def test_largest_vocabulary_full_block(sv, T, want_amax):
+    """V = 2^20 (64 members a row) with blocks of 16: a row then carries 256 directory words
+    and the finalize stages its rows in batches of 12 (6 with argmax outputs), so a block
+    takes two or three batches at the largest team.  Request 3 drafts with the target's own
+    logits (every draft accepted, its bonus drawn from the 64-member bonus slot)."""
+    v = workloads.make_verify_inputs("dfly", device=DEV, T=T, B=4, V=1 << 20, seed=77)
+    d = v.draft.clone()
+    d[3] = v.target[3, :-1]
+    toks = v.draft_tokens.clone()
+    z = d[3].float()
+    if T > 0:
+        g = torch.Generator(device=DEV).manual_seed(78)
+        u = torch.rand(z.shape, generator=g, device=DEV).clamp_(min=1e-20)
+        z = z / T - torch.log(-torch.log(u))
+    toks[3] = torch.argmax(z, -1).to(torch.int32)
+    w = workloads.VerifyInputs(v.target, d, toks, T, v.seed, "V=2^20 block 16")
+    _, o, _ = _run_pair(sv, w, T, want_amax=want_amax)
+    assert o["accept_len"][3] == 16
+
+
 def _grid(B, K, V):
     """Workgroups of a dense verification grid: members of every row and bonus slot, then the
     finalize workgroups."""
