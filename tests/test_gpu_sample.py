@@ -136,3 +136,14 @@ def test_sample_rows_beyond_2gib(sv):
         tok, conf = sv.sv_sample_drafts(d, T, seed=5, step=1)
         torch.cuda.synchronize()
         _say(f"report {_compare(tok, conf, d, T, 5, 1)}")
+
+
+def test_sample_largest_vocabulary(sv):
+    """V = SV_V_MAX = 2^20: 64 members a row, so a finalize wave gathers S + 4S = 320 words
+    (greedy: 4S = 256), the most it holds."""
+    d = _drafts(2, 3, 1 << 20, seed=20)
+    for T in (0.9, 0.0):
+        _say(f"sample V=2^20 T={T}")
+        tok, conf = sv.sv_sample_drafts(d, T, seed=3, step=2)
+        torch.cuda.synchronize()
+        _say(f"report {_compare(tok, conf, d, T, 3, 2)}")
