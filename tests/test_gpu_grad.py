@@ -90,10 +90,10 @@ def test_backward_after_gpu_forward(sv):
     assert (gs <= 1e-5 * ga).all()
 
 
-@pytest.mark.parametrize("V", [1, 7, 4097, 16384, 16385])
+@pytest.mark.parametrize("V", [1, 7, 4097, 16384, 16385, 1 << 20])
 def test_backward_edge_vocabularies(sv, V):
-    """Tiny, ragged, exactly one member, one member plus one token; mixed logit dtypes and
-    depth 1 and 5."""
+    """Tiny, ragged, exactly one member, one member plus one token, and SV_V_MAX (64 members
+    a row); mixed logit dtypes and depth 1 and 5."""
     for I, D in [(2, 1), (1, 5)]:
         t, d = _inputs(I, D, V, torch.bfloat16, torch.float32, seed=V + D)
         og, oa, _, lr = _oracle(t, d, 1.3)
