@@ -687,8 +687,17 @@ def test_largest_vocabulary(sv):
     d = (t[:, :K].float() + torch.randn((B, K, V), generator=g, device=DEV)).to(torch.bfloat16)
     toks = torch.argmax(d.float(), -1).to(torch.int32)
     toks[:, 1] = torch.randint(0, V, (B,), generator=g, device=DEV, dtype=torch.int32)
+    tn, dn = workloads.to_oracle(t), workloads.to_oracle(d)
     for T in (0.9, 0.0):
-        _run_pair(sv, _custom(t, d, toks, T, "V=2^20"), T)
+        _, o, _ = _run_pair(sv, _custom(t, d, toks, T, "V=2^20"), T)
+        # the stand-alone draw at every accepted length 0..K (a correction, or the bonus at K)
+        for tau in range(K + 1):
+            al = np.full(B, tau, np.int32)
+            tok = sv.sv_residual_sample(t, d, torch.as_tensor(al, device=DEV), T, seed=13).cpu().numpy()
+            otok = svref.residual_sample(tn, dn, al, T, "bf16", seed=13)
+            for r in range(B):
+                assert tok[r] == otok[r] or (T > 0 and _token_in_band(tn, dn, T, "bf16", r, tau, K, int(tok[r]),
+                                                                      int(otok[r]), 13, 0)), (T, tau, r)
 
 
 @pytest.mark.parametrize("K", [300, 4096])
