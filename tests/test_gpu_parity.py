@@ -437,6 +437,25 @@ def test_device_error_flag_for_bad_token(sv):
 
 
 @pytest.mark.parametrize("T", [0.9, 0.0])
+def test_draft_len_out_of_range_is_clamped_and_flagged(sv, T):
+    """draft_len entries outside [0, K_max] (K_max + 5, -3) verify as K_max and 0, the same
+    outputs as a call with the clamped lengths, and raise SV_DEVERR_DRAFT_LEN."""
+    v = workloads.make_verify_inputs("dfly", device=DEV, T=T, B=4, K=6, V=20000, seed=5)
+    ws = sv.Workspace(DEV)
+    _say(f"draft_len out of range T={T}")
+    bad = torch.tensor([11, -3, 2, 6], dtype=torch.int32, device=DEV)
+    ok = torch.tensor([6, 0, 2, 6], dtype=torch.int32, device=DEV)
+    a = _np(sv.sv_verify_batch(v.target, v.draft, v.draft_tokens, T, seed=3, draft_len=bad, want_amax=True,
+                               workspace=ws))
+    assert sv.sv_device_error(ws.buf) == sv.SV_DEVERR_DRAFT_LEN
+    b = _np(sv.sv_verify_batch(v.target, v.draft, v.draft_tokens, T, seed=3, draft_len=ok, want_amax=True,
+                               workspace=ws))
+    assert sv.sv_device_error(ws.buf) == 0
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("T", [0.9, 0.0])
 def test_selected_with_zero_budget(sv, T):
     """A budget of 0 selects no row: every request gets its bonus token from target row 0,
     the same as dense verification with every draft length 0 (the grid holds only the bonus
