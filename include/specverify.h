@@ -253,7 +253,9 @@ int sv_sample_drafts(const sv_params *params, const void *draft, int32_t *tokens
  * NULL.  Outputs: lens [B] (selected prefix length per request; pass it as draft_len to
  * sv_verify_batch), row_off [B+1] (exclusive scan of lens), row_list [min(N, sum L)] or
  * NULL (r*K_max + k of each selected row in (r, k) order).  B*K_max <= SV_BUDGET_MAX.
- * B == 0 writes row_off[0] = 0 (lens may then be NULL). */
+ * B == 0 writes row_off[0] = 0 (lens may then be NULL).  draft_len entries outside
+ * [0, K_max] are a caller error; they are clamped to that range (there is no workspace to
+ * carry a device flag here). */
 int sv_alloc_verify_budget(const float *conf, const int32_t *draft_len, int32_t B,
                            int32_t K_max, int32_t budget_N, int32_t *lens, int32_t *row_off,
                            int32_t *row_list, void *stream);

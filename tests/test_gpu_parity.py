@@ -274,6 +274,33 @@ def test_budget_then_ragged_verify(sv):
     _say(f"report {rep}")
 
 
+def test_budget_clamps_draft_lengths(sv):
+    """draft_len entries outside [0, K_max] (a caller error) allocate as the clamped lengths,
+    for the plain budget and the D-cut choice; the clamped allocation equals the oracle's."""
+    rng = np.random.default_rng(8)
+    B, K = 6, 5
+    conf = rng.beta(5, 2, size=(B, K)).astype(np.float32)
+    bad = np.array([9, -2, 3, 5, 0, 7], np.int32)
+    ok = np.clip(bad, 0, K).astype(np.int32)
+    cost = (40.0 + 0.05 * np.arange(B * K + 1)).astype(np.float32)
+    cd = torch.as_tensor(conf, device=DEV)
+    _say("budget with draft lengths out of range")
+    for N in (0, 7, 30):
+        got = [x.cpu().numpy() for x in sv.sv_alloc_verify_budget(cd, N, torch.as_tensor(bad, device=DEV))]
+        want = [x.cpu().numpy() for x in sv.sv_alloc_verify_budget(cd, N, torch.as_tensor(ok, device=DEV))]
+        ol, oo, orl = svref.alloc_verify_budget(conf, N, draft_len=ok)
+        n = int(oo[-1])
+        for g_, w_ in zip(got[:2], want[:2]):
+            assert np.array_equal(g_, w_)
+        assert np.array_equal(got[0], ol) and np.array_equal(got[1], oo)
+        assert np.array_equal(got[2][:n], want[2][:n]) and np.array_equal(got[2][:n], orl)
+    got = [x.cpu().numpy() for x in sv.sv_dcut_verify_budget(cd, torch.as_tensor(cost, device=DEV),
+                                                              torch.as_tensor(bad, device=DEV))]
+    on, ou, ol, oo, _ = svref.dcut_budget(conf, cost, draft_len=ok)
+    assert int(got[0][0]) == on and abs(float(got[1][0]) - ou) <= 1e-12 * abs(ou)
+    assert np.array_equal(got[2], ol) and np.array_equal(got[3], oo)
+
+
 def test_budget_selected_verify(sv):
     """sv_verify_selected over the allocation's row list equals sv_verify_batch with
     draft_len = lens (same kernels, same member order), and the oracle on sampled requests."""
