@@ -185,7 +185,7 @@ int sv_verify_selected(const sv_params *params, const void *target, const void *
 
 /* First-reject prefix length per request [TV]: accept [B][K_max] uint8, draft_len [B] or
  * NULL; accept_len[r] = first k < L_r with accept == 0, else L_r.  B == 0 is a no-op (its
- * arrays may be NULL). */
+ * arrays may be NULL).  draft_len entries outside [0, K_max] are clamped to that range. */
 int sv_accept_len(const uint8_t *accept, const int32_t *draft_len, int32_t B, int32_t K_max,
                   int32_t *accept_len, void *stream);
 

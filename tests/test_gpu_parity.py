@@ -152,6 +152,11 @@ def test_accept_len_matches_oracle(sv):
         assert np.array_equal(got, svref.accept_len(acc)), trial
         got = sv.sv_accept_len(acc_d, torch.as_tensor(dl, device=DEV)).cpu().numpy()
         assert np.array_equal(got, svref.accept_len(acc, draft_len=dl)), trial
+        if B > 2:   # lengths outside [0, K] are clamped
+            dl2 = dl.copy()
+            dl2[0], dl2[1] = -4, K + 3
+            got = sv.sv_accept_len(acc_d, torch.as_tensor(dl2, device=DEV)).cpu().numpy()
+            assert np.array_equal(got, svref.accept_len(acc, draft_len=np.clip(dl2, 0, K))), trial
 
 
 def _token_in_band(tn, dn, T, dtype, r, tau, L, tg, to, seed, step):
