@@ -199,8 +199,9 @@ int sv_accept_len(const uint8_t *accept, const int32_t *draft_len, int32_t B, in
  * draw rule and counters as sv_verify_batch: token[r] is out_tokens[r][accept_len[r]] of a
  * verify call with the same arguments, up to the summation order of the draw's total (the
  * two compute their normalisers separately).  Reads target row tau (and drafter row tau
- * when tau < L_r).  accept_len [B] int32 on the device (clamped to [0, L_r]); token [B]
- * int32.  Errors: SV_EINVAL, SV_EUNSUPPORTED, SV_EHIP. */
+ * when tau < L_r).  accept_len [B] int32 on the device (clamped to [0, L_r]; draft_len
+ * entries are clamped to [0, K_max] first); token [B] int32.  Errors: SV_EINVAL,
+ * SV_EUNSUPPORTED, SV_EHIP. */
 int sv_residual_sample(const sv_params *params, const void *target, const void *draft,
                        const int32_t *draft_len, const int32_t *accept_len, int32_t *token,
                        void *stream);
