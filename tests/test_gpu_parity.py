@@ -857,6 +857,28 @@ def test_two_streams_at_once(sv):
             compare_verify(_np(outs[it][k]), o, tn, dn, "bf16", 0.9, label=f"two streams {v.name} step {it}")
 
 
+def test_stream_read_covers_every_word(sv):
+    """The read-only streaming reference reads every 16-byte word: a single word holding its
+    sink value (the rest zero) reaches the sink wherever it sits, including the ragged last
+    workgroup; an all-zero buffer leaves the sink untouched."""
+    marker = 0x9E3779B9
+    n16 = 2048 * 3 + 5                        # three full workgroups of 2048 words and five more
+    buf = torch.zeros(n16 * 4, dtype=torch.int32, device=DEV)
+    sink = torch.zeros(4, dtype=torch.int32, device=DEV)
+    sv.sv_stream_read(buf, sink)
+    torch.cuda.synchronize()
+    assert int(sink[0].item()) == 0
+    for word in (0, 1, 255, 256, 2047, 2048, 4100, n16 - 5, n16 - 1):
+        for comp in (0, 3):
+            _say(f"stream_read word {word} component {comp}")
+            buf.zero_()
+            sink.zero_()
+            buf[4 * word + comp] = marker - (1 << 32)   # the same 32 bits as a signed int32
+            sv.sv_stream_read(buf, sink)
+            torch.cuda.synchronize()
+            assert int(sink[0].item()) & 0xFFFFFFFF == marker, (word, comp)
+
+
 def test_empty_batches(sv):
     """Empty batches through every entry point: no requests (B = 0), no draft positions
     (K = 0) for the budget and the sampler, no counters.  Verification returns empty outputs;
